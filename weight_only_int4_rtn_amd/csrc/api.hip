@@ -1,0 +1,245 @@
+// Host side of the C ABI declared in include/w4a16.h: argument validation, workspace
+// layout and kernel dispatch.  Nothing here allocates device memory or synchronises.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "w4a16.h"
+
+using namespace w4a16;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_status(hipError_t err, const char* what) {
+    if (err == hipSuccess) return W4A16_OK;
+    return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Shape checks shared by the workspace query and the forward call.
+int check_shapes(const moe_w4a16_args* a) {
+    if (!a) return fail(W4A16_ERR_INVALID_ARG, "args is NULL");
+    if (a->T < 0) return fail(W4A16_ERR_INVALID_ARG, "T = %lld < 0", (long long)a->T);
+    if (a->group != kGroup) return fail(W4A16_ERR_INVALID_ARG, "group = %d, only 128 is supported", a->group);
+    if (a->bits != 4 && a->bits != 8) return fail(W4A16_ERR_INVALID_ARG, "bits = %d, must be 4 or 8", a->bits);
+    if (a->H <= 0 || a->H % kGroup) return fail(W4A16_ERR_INVALID_ARG, "H = %lld is not a positive multiple of 128", (long long)a->H);
+    if (a->I <= 0 || a->I % kGroup) return fail(W4A16_ERR_INVALID_ARG, "I = %lld is not a positive multiple of 128", (long long)a->I);
+    if (a->E < 1) return fail(W4A16_ERR_INVALID_ARG, "E = %lld < 1", (long long)a->E);
+    if (a->top_k < 1 || a->top_k > a->E) return fail(W4A16_ERR_INVALID_ARG, "top_k = %lld not in [1, E]", (long long)a->top_k);
+    if (a->H > 16384) return fail(W4A16_ERR_UNSUPPORTED, "H = %lld > 16384", (long long)a->H);
+    if (a->I > 8192) return fail(W4A16_ERR_UNSUPPORTED, "I = %lld > 8192", (long long)a->I);
+    if (a->E > 1024) return fail(W4A16_ERR_UNSUPPORTED, "E = %lld > 1024", (long long)a->E);
+    if (a->top_k > 16) return fail(W4A16_ERR_UNSUPPORTED, "top_k = %lld > 16", (long long)a->top_k);
+    if (a->T * a->top_k >= (int64_t(1) << 31) || a->T >= (int64_t(1) << 24))
+        return fail(W4A16_ERR_UNSUPPORTED, "T = %lld too large", (long long)a->T);
+    if (a->shared_bits != 0) {
+        if (a->shared_bits != 4 && a->shared_bits != 8)
+            return fail(W4A16_ERR_INVALID_ARG, "shared_bits = %d, must be 0, 4 or 8", a->shared_bits);
+        if (a->shared_I <= 0 || a->shared_I % kGroup)
+            return fail(W4A16_ERR_INVALID_ARG, "shared_I = %lld is not a positive multiple of 128", (long long)a->shared_I);
+        if (a->shared_I > 8192) return fail(W4A16_ERR_UNSUPPORTED, "shared_I = %lld > 8192", (long long)a->shared_I);
+    }
+    return W4A16_OK;
+}
+
+// Offsets of every scratch buffer inside the caller's workspace.
+WsLayout layout(const moe_w4a16_args* a) {
+    WsLayout L{};
+    const int64_t T = a->T, H = a->H, E = a->E, k = a->top_k, P = T * k;
+    const bool shared = a->shared_bits != 0;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L.ids = take(P * 4);
+    L.wts = take(P * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.sorted = take(P * 4);
+    L.active = take(E * 4);
+    L.meta = take(64);
+    L.rows_a = P + (shared ? T : 0);
+    L.width_a = std::max(a->I, shared ? a->shared_I : (int64_t)0);
+    L.abuf = take((size_t)L.rows_a * L.width_a * 2);
+    if (T <= kSmallT) {
+        const int64_t units = std::min(E, P) + (shared ? 1 : 0);
+        L.splits = (int)std::min<int64_t>(16, std::max<int64_t>(1, (units + 15) / 16));
+        if (L.splits > 1) L.part = take((size_t)L.splits * T * H * 4);
+    } else {
+        L.splits = 1;
+        L.nblk = (int)((T + kRouteBlockT - 1) / kRouteBlockT);
+        L.hist = take((size_t)L.nblk * E * 4);
+        L.lrank = take(P * 4);
+        L.max_tiles = (P + kPrefillMT - 1) / kPrefillMT + std::min(E, P);
+        L.tiles = take((size_t)L.max_tiles * 8);
+        L.xsum = take((size_t)T * (H / kGroup) * 4);
+        L.y32 = take((size_t)T * H * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "W4A16_OK";
+        case W4A16_ERR_INVALID_ARG: return "W4A16_ERR_INVALID_ARG";
+        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED";
+        case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE";
+        case W4A16_ERR_HIP: return "W4A16_ERR_HIP";
+        default: return "W4A16_UNKNOWN_STATUS";
+    }
+}
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols, int bits, int group,
+                      int32_t* packed, uint16_t* scales, void* stream) {
+    g_last_error.clear();
+    if (w_dtype != W4A16_F32 && w_dtype != W4A16_BF16) return fail(W4A16_ERR_INVALID_ARG, "w_dtype = %d", w_dtype);
+    if (bits != 4 && bits != 8) return fail(W4A16_ERR_INVALID_ARG, "bits = %d, must be 4 or 8", bits);
+    if (group != kGroup) return fail(W4A16_ERR_INVALID_ARG, "group = %d, only 128 is supported", group);
+    if (n_mats < 0 || rows < 0 || cols < 0) return fail(W4A16_ERR_INVALID_ARG, "negative size");
+    if (cols % kGroup) return fail(W4A16_ERR_INVALID_ARG, "cols = %lld is not a multiple of 128", (long long)cols);
+    if (n_mats != 0 && rows > INT64_MAX / n_mats) return fail(W4A16_ERR_INVALID_ARG, "size overflow");
+    const int64_t total_rows = n_mats * rows;
+    if (total_rows == 0 || cols == 0) return W4A16_OK;
+    if (cols > (int64_t(1) << 40) / total_rows) return fail(W4A16_ERR_UNSUPPORTED, "matrix too large");
+    if (!w || !packed || !scales) return fail(W4A16_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(scales))
+        return fail(W4A16_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    return hip_status(launch_quantize(w, w_dtype == W4A16_BF16, total_rows, cols, bits, packed, scales,
+                                      static_cast<hipStream_t>(stream)),
+                      "rtn_quantize_pack launch");
+}
+
+size_t moe_w4a16_workspace_size(const moe_w4a16_args* args) {
+    if (check_shapes(args) != W4A16_OK) return 0;
+    return layout(args).total;
+}
+
+int moe_w4a16_forward(const moe_w4a16_args* a, void* stream) {
+    g_last_error.clear();
+    if (int st = check_shapes(a)) return st;
+    if (a->T == 0) return W4A16_OK;
+    if (!a->x || !a->w13 || !a->s13 || !a->w2 || !a->s2 || !a->y)
+        return fail(W4A16_ERR_INVALID_ARG, "NULL x, w13, s13, w2, s2 or y");
+    if (!a->router_logits && (!a->topk_ids || !a->topk_w))
+        return fail(W4A16_ERR_INVALID_ARG, "router_logits is NULL, so topk_ids and topk_w must be given");
+    if (a->shared_bits && (!a->shared_w13 || !a->shared_s13 || !a->shared_w2 || !a->shared_s2))
+        return fail(W4A16_ERR_INVALID_ARG, "NULL shared expert pointer");
+    const void* ptrs[] = {a->x, a->router_logits, a->w13, a->s13, a->w2, a->s2, a->shared_w13, a->shared_s13,
+                          a->shared_w2, a->shared_s2, a->residual, a->y, a->topk_ids, a->topk_w,
+                          a->expert_counts, a->expert_offsets, a->sorted_pairs, a->workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(W4A16_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (a->y == a->x) return fail(W4A16_ERR_INVALID_ARG, "y must not alias x");
+
+    const WsLayout L = layout(a);
+    if (!a->workspace || a->workspace_bytes < L.total)
+        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    char* ws = static_cast<char*>(a->workspace);
+    auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    RouteArgs r{};
+    r.logits = a->router_logits;
+    r.T = (int)a->T;
+    r.E = (int)a->E;
+    r.k = (int)a->top_k;
+    r.ids = a->topk_ids ? a->topk_ids : static_cast<int32_t*>(at(L.ids));
+    r.wts = a->topk_w ? a->topk_w : static_cast<float*>(at(L.wts));
+    r.counts = a->expert_counts ? a->expert_counts : static_cast<int32_t*>(at(L.counts));
+    r.offsets = a->expert_offsets ? a->expert_offsets : static_cast<int32_t*>(at(L.offsets));
+    r.sorted = a->sorted_pairs ? a->sorted_pairs : static_cast<int32_t*>(at(L.sorted));
+    r.active = static_cast<int32_t*>(at(L.active));
+    r.meta = static_cast<int32_t*>(at(L.meta));
+    r.x = a->x;
+    r.H = a->H;
+
+    ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits};
+    ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits};
+    uint16_t* abuf = static_cast<uint16_t*>(at(L.abuf));
+
+    if (a->T <= kSmallT) {
+        if (int st = hip_status(launch_route_small(r, s), "routing launch")) return st;
+        DecodeArgs d{};
+        d.x = a->x;
+        d.T = (int)a->T;
+        d.E = (int)a->E;
+        d.k = (int)a->top_k;
+        d.H = a->H;
+        d.routed = routed;
+        d.shared = shared;
+        d.ids = r.ids;
+        d.wts = r.wts;
+        d.offsets = r.offsets;
+        d.sorted = r.sorted;
+        d.active = r.active;
+        d.meta = r.meta;
+        d.abuf = abuf;
+        d.width_a = L.width_a;
+        d.part = L.splits > 1 ? static_cast<float*>(at(L.part)) : nullptr;
+        d.splits = L.splits;
+        d.residual = a->residual;
+        d.y = a->y;
+        return hip_status(launch_decode(d, s), "decode launch");
+    }
+
+    r.hist = static_cast<int32_t*>(at(L.hist));
+    r.lrank = static_cast<int32_t*>(at(L.lrank));
+    r.tiles = static_cast<int32_t*>(at(L.tiles));
+    r.xsum = static_cast<float*>(at(L.xsum));
+    r.nblk = L.nblk;
+    r.max_tiles = L.max_tiles;
+    if (int st = hip_status(launch_route_large(r, s), "routing launch")) return st;
+    PrefillArgs p{};
+    p.x = a->x;
+    p.T = (int)a->T;
+    p.E = (int)a->E;
+    p.k = (int)a->top_k;
+    p.H = a->H;
+    p.routed = routed;
+    p.shared = shared;
+    p.ids = r.ids;
+    p.wts = r.wts;
+    p.offsets = r.offsets;
+    p.sorted = r.sorted;
+    p.meta = r.meta;
+    p.tiles = r.tiles;
+    p.max_tiles = L.max_tiles;
+    p.xsum = r.xsum;
+    p.abuf = abuf;
+    p.width_a = L.width_a;
+    p.y32 = static_cast<float*>(at(L.y32));
+    p.residual = a->residual;
+    p.y = a->y;
+    return hip_status(launch_prefill(p, s), "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Internal device helpers and kernel-launch declarations of the W4A16 MoE library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------- MFMA
+
+// D = A * B + C with A 16x32, B 32x16 bf16 and C/D 16x16 fp32 (gfx950).
+// Lane l supplies A[l % 16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l % 16] and holds
+// D[4*(l/16) + r][l % 16] in element r.  The K order inside each lane's 8-element
+// slice is free as long as A and B use the same one.
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------- code -> bf16 operand packing
+//
+// A packed code u (offset binary) becomes an exact bf16 integer by OR-ing it into the
+// mantissa of a power of two: bits 0x4300|n are 128 + n, bits 0x4500|n are 2048 + 16n
+// (n < 16).  The MFMA then forms sum_k x_k (q_k + OFF) and the offset term
+// OFF * sum_k x_k is cancelled by seeding the accumulator with an MFMA against the
+// constant -OFF.  INT4: OFF = 136 (q = u - 8 = (128 + u) - 136).
+// INT8: the byte splits into nibbles lo + 16 hi, two MFMAs with (128 + lo) and
+// (2048 + 16 hi) give u + 2176, so q = u - 128 has OFF = 2304.
+//
+// INT4 word w holds k0..k7 (k0 lowest).  dq4 returns the bf16 pairs
+// (k0,k4) (k1,k5) (k2,k6) (k3,k7); the activation slice must use that order.
+__device__ __forceinline__ u32x4_t dq4(uint32_t w) {
+    const uint32_t M = 0x000f000fu, C = 0x43004300u;
+    u32x4_t r;
+    r[0] = (w & M) | C;
+    r[1] = ((w >> 4) & M) | C;
+    r[2] = ((w >> 8) & M) | C;
+    r[3] = ((w >> 12) & M) | C;
+    return r;
+}
+
+// INT8 words w0 = k0..k3, w1 = k4..k7.  Low and high nibbles in the order
+// (k0,k2) (k1,k3) (k4,k6) (k5,k7).
+__device__ __forceinline__ u32x4_t dq8_lo(uint32_t w0, uint32_t w1) {
+    const uint32_t M = 0x000f000fu, C = 0x43004300u;
+    u32x4_t r;
+    r[0] = (w0 & M) | C;
+    r[1] = ((w0 >> 8) & M) | C;
+    r[2] = (w1 & M) | C;
+    r[3] = ((w1 >> 8) & M) | C;
+    return r;
+}
+__device__ __forceinline__ u32x4_t dq8_hi(uint32_t w0, uint32_t w1) {
+    const uint32_t M = 0x000f000fu, C = 0x45004500u;
+    u32x4_t r;
+    r[0] = ((w0 >> 4) & M) | C;
+    r[1] = ((w0 >> 12) & M) | C;
+    r[2] = ((w1 >> 4) & M) | C;
+    r[3] = ((w1 >> 12) & M) | C;
+    return r;
+}
+
+// Reorder eight natural-order bf16 activations X = (x0,x1)(x2,x3)(x4,x5)(x6,x7) to the
+// K order of the matching weight operand.
+template <int BITS>
+__device__ __forceinline__ u32x4_t perm_act(u32x4_t X) {
+    u32x4_t a;
+    if constexpr (BITS == 4) {   // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+        a[0] = (X[0] & 0xffffu) | (X[2] << 16);
+        a[1] = (X[0] >> 16) | (X[2] & 0xffff0000u);
+        a[2] = (X[1] & 0xffffu) | (X[3] << 16);
+        a[3] = (X[1] >> 16) | (X[3] & 0xffff0000u);
+    } else {                     // (x0,x2) (x1,x3) (x4,x6) (x5,x7)
+        a[0] = (X[0] & 0xffffu) | (X[1] << 16);
+        a[1] = (X[0] >> 16) | (X[1] & 0xffff0000u);
+        a[2] = (X[2] & 0xffffu) | (X[3] << 16);
+        a[3] = (X[2] >> 16) | (X[3] & 0xffff0000u);
+    }
+    return a;
+}
+
+// bf16 pair of -OFF (see above): -136 = 0xC308, -2304 = 0xC510.
+template <int BITS>
+__device__ __forceinline__ u32x4_t neg_offset_operand() {
+    const uint32_t v = BITS == 4 ? 0xC308C308u : 0xC510C510u;
+    u32x4_t r = {v, v, v, v};
+    return r;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ------------------------------------------------------------ workspace layout
+
+struct WsLayout {
+    size_t ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
+        y32, total;
+    int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
+    int64_t width_a;    // columns of that buffer: max(I, shared_I)
+    int nblk;           // routing blocks of the large-batch path
+    int splits;         // expert splits of the small-batch down kernel
+    int64_t max_tiles;  // M-tiles of the large-batch grouped GEMM
+};
+
+constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
+constexpr int kRouteBlockT = 64; // tokens per routing block on the large-batch path
+constexpr int kPrefillMT = 128;  // tokens per M-tile of the large-batch grouped GEMM
+
+// ----------------------------------------------------------- kernel launchers
+// Each returns hipGetLastError() after the launch.
+
+hipError_t launch_quantize(const void* w, bool bf16_in, int64_t total_rows, int64_t cols, int bits,
+                           int32_t* packed, uint16_t* scales, hipStream_t s);
+
+struct RouteArgs {
+    const float* logits;  // NULL: ids/wts are inputs
+    int T, E, k;
+    int32_t* ids;
+    float* wts;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted;
+    int32_t* active;
+    int32_t* meta;        // [0] active experts, [1] M-tiles
+    int32_t* hist;        // large path: [nblk, E]
+    int32_t* lrank;       // large path: [T*k]
+    int32_t* tiles;       // large path: [max_tiles, 2] (expert, first row)
+    const uint16_t* x;    // large path: activations for the group sums
+    float* xsum;          // large path: [T, H/128] sums of bf16 activations per group
+    int64_t H;
+    int nblk;
+    int64_t max_tiles;
+};
+hipError_t launch_route_small(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_large(const RouteArgs& a, hipStream_t s);
+
+struct ExpertSet {       // one family of experts sharing a code width
+    const int32_t* w13;
+    const uint16_t* s13;
+    const int32_t* w2;
+    const uint16_t* s2;
+    int64_t I;
+    int bits;
+};
+
+struct DecodeArgs {
+    const uint16_t* x;
+    int T, E, k;
+    int64_t H;
+    ExpertSet routed, shared;   // shared.bits == 0: none
+    const int32_t* ids;
+    const float* wts;
+    const int32_t* offsets;
+    const int32_t* sorted;
+    const int32_t* active;
+    const int32_t* meta;
+    uint16_t* abuf;             // [rows_a, width_a]
+    int64_t width_a;
+    float* part;                // [splits, T, H]
+    int splits;
+    const uint16_t* residual;
+    uint16_t* y;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+    const uint16_t* x;
+    int T, E, k;
+    int64_t H;
+    ExpertSet routed, shared;
+    const int32_t* ids;
+    const float* wts;
+    const int32_t* offsets;
+    const int32_t* sorted;
+    const int32_t* meta;
+    const int32_t* tiles;
+    int64_t max_tiles;
+    const float* xsum;
+    uint16_t* abuf;
+    int64_t width_a;
+    float* y32;
+    const uint16_t* residual;
+    uint16_t* y;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace w4a16
