@@ -155,6 +155,19 @@ size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
  */
 int moe_w4a16_forward(const moe_w4a16_args* args, void* stream);
 
+/*
+ * moe_w4a16_forward_timed - the same work as moe_w4a16_forward, with a HIP event recorded
+ * on `stream` before the first kernel and after each kernel, then a wait for the last
+ * event (this call synchronises with the stream's work up to that point).
+ *   kernel_ms     out, [max_kernels]: elapsed time of each kernel in launch order, in ms
+ *                 (the interval between consecutive events)
+ *   kernel_names  out, [max_kernels]: static name of each kernel (owned by the library)
+ *   n_kernels     out: number of entries written (<= max_kernels)
+ * A profiling aid for per-kernel roofline measurements; the output y is identical.
+ */
+int moe_w4a16_forward_timed(const moe_w4a16_args* args, void* stream, int max_kernels, float* kernel_ms,
+                            const char** kernel_names, int* n_kernels);
+
 #ifdef __cplusplus
 }
 #endif

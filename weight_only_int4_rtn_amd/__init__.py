@@ -14,8 +14,8 @@ import ctypes as C
 from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
-__all__ = ["rtn_quantize_pack", "moe_w4a16_forward", "moe_w4a16_workspace_size", "w4a16_abi_version",
-           "W4A16Error", "library_path"]
+__all__ = ["rtn_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
+           "w4a16_abi_version", "W4A16Error", "library_path"]
 
 GROUP = 128
 
@@ -126,7 +126,7 @@ def moe_w4a16_workspace_size(T: int, H: int, I: int, E: int, top_k: int, shared_
 
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,
                       topk_ids=None, topk_w=None, shared=None, residual=None, out=None, workspace=None,
-                      routing_out: bool = False, stream=None):
+                      routing_out: bool = False, stream=None, _timed=None):
     """One routed-expert MoE FFN on the GPU.
 
     ``x`` bf16 ``[T, H]``; ``w13`` int32 ``[E, 2I, H*bits/32]`` and ``s13`` bf16
@@ -181,6 +181,22 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
         workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
     a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
               counts, offsets, sorted_pairs, workspace)
-    st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, stream))
-    _lib.check(st, "moe_w4a16_forward")
+    if _timed is None:
+        st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, stream))
+        _lib.check(st, "moe_w4a16_forward")
+    else:
+        n = C.c_int(0)
+        ms = (C.c_float * 16)()
+        names = (C.c_char_p * 16)()
+        st = _lib.lib().moe_w4a16_forward_timed(C.byref(a), _stream(dev, stream), 16, ms, names, C.byref(n))
+        _lib.check(st, "moe_w4a16_forward_timed")
+        _timed.extend((names[i].decode(), float(ms[i])) for i in range(n.value))
     return (out, routing) if routing_out else out
+
+
+def moe_w4a16_forward_timed(*args, **kwargs):
+    """:func:`moe_w4a16_forward` that also returns ``[(kernel name, ms), ...]`` measured
+    with HIP events around each kernel (synchronises the stream)."""
+    timings = []
+    res = moe_w4a16_forward(*args, _timed=timings, **kwargs)
+    return res, timings

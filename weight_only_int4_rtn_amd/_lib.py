@@ -30,6 +30,7 @@ EXPORTED = (
     "rtn_quantize_pack",
     "moe_w4a16_workspace_size",
     "moe_w4a16_forward",
+    "moe_w4a16_forward_timed",
 )
 
 
@@ -83,6 +84,9 @@ def lib():
     L.moe_w4a16_workspace_size.argtypes = [C.POINTER(MoeArgs)]
     L.moe_w4a16_forward.restype = C.c_int
     L.moe_w4a16_forward.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
+    L.moe_w4a16_forward_timed.restype = C.c_int
+    L.moe_w4a16_forward_timed.argtypes = [C.POINTER(MoeArgs), C.c_void_p, C.c_int, C.POINTER(C.c_float),
+                                          C.POINTER(C.c_char_p), C.POINTER(C.c_int)]
     if L.w4a16_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH}: ABI version {L.w4a16_abi_version()}, expected {ABI_VERSION}")
     _lib = L

@@ -77,11 +77,15 @@ WsLayout layout(const moe_w4a16_args* a) {
     L.sorted = take(P * 4);
     L.active = take(E * 4);
     L.meta = take(64);
+    L.tokw = take(P * 8);
+    L.rec = take(std::min(E, P) * 16);
     L.rows_a = P + (shared ? T : 0);
     L.width_a = std::max(a->I, shared ? a->shared_I : (int64_t)0);
     L.abuf = take((size_t)L.rows_a * L.width_a * 2);
     if (T <= kSmallT) {
-        const int64_t units = std::min(E, P) + (shared ? 1 : 0);
+        // down-kernel work units: 2-group K chunks of every expert that can be active
+        auto chunks = [](int64_t I_e) { return (I_e / kGroup + 1) / 2; };
+        const int64_t units = std::min(E, P) * chunks(a->I) + (shared ? chunks(a->shared_I) : 0);
         L.splits = (int)std::min<int64_t>(16, std::max<int64_t>(1, (units + 15) / 16));
         if (L.splits > 1) L.part = take((size_t)L.splits * T * H * 4);
     } else {
@@ -96,6 +100,115 @@ WsLayout layout(const moe_w4a16_args* a) {
     }
     L.total = off;
     return L;
+}
+
+int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
+    if (int st = check_shapes(a)) return st;
+    if (a->T == 0) return W4A16_OK;
+    if (!a->x || !a->w13 || !a->s13 || !a->w2 || !a->s2 || !a->y)
+        return fail(W4A16_ERR_INVALID_ARG, "NULL x, w13, s13, w2, s2 or y");
+    if (!a->router_logits && (!a->topk_ids || !a->topk_w))
+        return fail(W4A16_ERR_INVALID_ARG, "router_logits is NULL, so topk_ids and topk_w must be given");
+    if (a->shared_bits && (!a->shared_w13 || !a->shared_s13 || !a->shared_w2 || !a->shared_s2))
+        return fail(W4A16_ERR_INVALID_ARG, "NULL shared expert pointer");
+    const void* ptrs[] = {a->x, a->router_logits, a->w13, a->s13, a->w2, a->s2, a->shared_w13, a->shared_s13,
+                          a->shared_w2, a->shared_s2, a->residual, a->y, a->topk_ids, a->topk_w,
+                          a->expert_counts, a->expert_offsets, a->sorted_pairs, a->workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(W4A16_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (a->y == a->x) return fail(W4A16_ERR_INVALID_ARG, "y must not alias x");
+
+    const WsLayout L = layout(a);
+    if (!a->workspace || a->workspace_bytes < L.total)
+        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    char* ws = static_cast<char*>(a->workspace);
+    auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (timer) {
+        timer->stream = s;
+        if (int st = hip_status(hipEventRecord(timer->ev[0], s), "hipEventRecord")) return st;
+    }
+
+    RouteArgs r{};
+    r.logits = a->router_logits;
+    r.T = (int)a->T;
+    r.E = (int)a->E;
+    r.k = (int)a->top_k;
+    r.ids = a->topk_ids ? a->topk_ids : static_cast<int32_t*>(at(L.ids));
+    r.wts = a->topk_w ? a->topk_w : static_cast<float*>(at(L.wts));
+    r.counts = a->expert_counts ? a->expert_counts : static_cast<int32_t*>(at(L.counts));
+    r.offsets = a->expert_offsets ? a->expert_offsets : static_cast<int32_t*>(at(L.offsets));
+    r.sorted = a->sorted_pairs ? a->sorted_pairs : static_cast<int32_t*>(at(L.sorted));
+    r.active = static_cast<int32_t*>(at(L.active));
+    r.meta = static_cast<int32_t*>(at(L.meta));
+    r.x = a->x;
+    r.H = a->H;
+    r.tokw = static_cast<int2*>(at(L.tokw));
+    r.rec = static_cast<int4*>(at(L.rec));
+    r.max_slots = (int)std::min(a->E, a->T * a->top_k);
+
+    ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits};
+    ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits};
+    uint16_t* abuf = static_cast<uint16_t*>(at(L.abuf));
+
+    if (a->T <= kSmallT) {
+        if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
+        DecodeArgs d{};
+        d.x = a->x;
+        d.T = (int)a->T;
+        d.E = (int)a->E;
+        d.k = (int)a->top_k;
+        d.H = a->H;
+        d.routed = routed;
+        d.shared = shared;
+        d.ids = r.ids;
+        d.wts = r.wts;
+        d.offsets = r.offsets;
+        d.sorted = r.sorted;
+        d.active = r.active;
+        d.meta = r.meta;
+        d.rec = r.rec;
+        d.tokw = r.tokw;
+        d.abuf = abuf;
+        d.width_a = L.width_a;
+        d.part = L.splits > 1 ? static_cast<float*>(at(L.part)) : nullptr;
+        d.splits = L.splits;
+        d.residual = a->residual;
+        d.y = a->y;
+        return hip_status(launch_decode(d, s, timer), "decode launch");
+    }
+
+    r.hist = static_cast<int32_t*>(at(L.hist));
+    r.lrank = static_cast<int32_t*>(at(L.lrank));
+    r.tiles = static_cast<int32_t*>(at(L.tiles));
+    r.xsum = static_cast<float*>(at(L.xsum));
+    r.nblk = L.nblk;
+    r.max_tiles = L.max_tiles;
+    if (int st = hip_status(launch_route_large(r, s, timer), "routing launch")) return st;
+    PrefillArgs p{};
+    p.x = a->x;
+    p.T = (int)a->T;
+    p.E = (int)a->E;
+    p.k = (int)a->top_k;
+    p.H = a->H;
+    p.routed = routed;
+    p.shared = shared;
+    p.ids = r.ids;
+    p.wts = r.wts;
+    p.offsets = r.offsets;
+    p.sorted = r.sorted;
+    p.meta = r.meta;
+    p.tiles = r.tiles;
+    p.tokw = r.tokw;
+    p.max_tiles = L.max_tiles;
+    p.xsum = r.xsum;
+    p.abuf = abuf;
+    p.width_a = L.width_a;
+    p.y32 = static_cast<float*>(at(L.y32));
+    p.residual = a->residual;
+    p.y = a->y;
+    return hip_status(launch_prefill(p, s, timer), "prefill launch");
 }
 
 }  // namespace
@@ -144,102 +257,31 @@ size_t moe_w4a16_workspace_size(const moe_w4a16_args* args) {
 
 int moe_w4a16_forward(const moe_w4a16_args* a, void* stream) {
     g_last_error.clear();
-    if (int st = check_shapes(a)) return st;
-    if (a->T == 0) return W4A16_OK;
-    if (!a->x || !a->w13 || !a->s13 || !a->w2 || !a->s2 || !a->y)
-        return fail(W4A16_ERR_INVALID_ARG, "NULL x, w13, s13, w2, s2 or y");
-    if (!a->router_logits && (!a->topk_ids || !a->topk_w))
-        return fail(W4A16_ERR_INVALID_ARG, "router_logits is NULL, so topk_ids and topk_w must be given");
-    if (a->shared_bits && (!a->shared_w13 || !a->shared_s13 || !a->shared_w2 || !a->shared_s2))
-        return fail(W4A16_ERR_INVALID_ARG, "NULL shared expert pointer");
-    const void* ptrs[] = {a->x, a->router_logits, a->w13, a->s13, a->w2, a->s2, a->shared_w13, a->shared_s13,
-                          a->shared_w2, a->shared_s2, a->residual, a->y, a->topk_ids, a->topk_w,
-                          a->expert_counts, a->expert_offsets, a->sorted_pairs, a->workspace};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return fail(W4A16_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-    if (a->y == a->x) return fail(W4A16_ERR_INVALID_ARG, "y must not alias x");
+    return forward_impl(a, stream, nullptr);
+}
 
-    const WsLayout L = layout(a);
-    if (!a->workspace || a->workspace_bytes < L.total)
-        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
-                    a->workspace ? a->workspace_bytes : (size_t)0);
-    char* ws = static_cast<char*>(a->workspace);
-    auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
-    hipStream_t s = static_cast<hipStream_t>(stream);
-
-    RouteArgs r{};
-    r.logits = a->router_logits;
-    r.T = (int)a->T;
-    r.E = (int)a->E;
-    r.k = (int)a->top_k;
-    r.ids = a->topk_ids ? a->topk_ids : static_cast<int32_t*>(at(L.ids));
-    r.wts = a->topk_w ? a->topk_w : static_cast<float*>(at(L.wts));
-    r.counts = a->expert_counts ? a->expert_counts : static_cast<int32_t*>(at(L.counts));
-    r.offsets = a->expert_offsets ? a->expert_offsets : static_cast<int32_t*>(at(L.offsets));
-    r.sorted = a->sorted_pairs ? a->sorted_pairs : static_cast<int32_t*>(at(L.sorted));
-    r.active = static_cast<int32_t*>(at(L.active));
-    r.meta = static_cast<int32_t*>(at(L.meta));
-    r.x = a->x;
-    r.H = a->H;
-
-    ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits};
-    ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits};
-    uint16_t* abuf = static_cast<uint16_t*>(at(L.abuf));
-
-    if (a->T <= kSmallT) {
-        if (int st = hip_status(launch_route_small(r, s), "routing launch")) return st;
-        DecodeArgs d{};
-        d.x = a->x;
-        d.T = (int)a->T;
-        d.E = (int)a->E;
-        d.k = (int)a->top_k;
-        d.H = a->H;
-        d.routed = routed;
-        d.shared = shared;
-        d.ids = r.ids;
-        d.wts = r.wts;
-        d.offsets = r.offsets;
-        d.sorted = r.sorted;
-        d.active = r.active;
-        d.meta = r.meta;
-        d.abuf = abuf;
-        d.width_a = L.width_a;
-        d.part = L.splits > 1 ? static_cast<float*>(at(L.part)) : nullptr;
-        d.splits = L.splits;
-        d.residual = a->residual;
-        d.y = a->y;
-        return hip_status(launch_decode(d, s), "decode launch");
+int moe_w4a16_forward_timed(const moe_w4a16_args* a, void* stream, int max_kernels, float* kernel_ms,
+                            const char** kernel_names, int* n_kernels) {
+    g_last_error.clear();
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0)
+        return fail(W4A16_ERR_INVALID_ARG, "NULL timing output or negative max_kernels");
+    *n_kernels = 0;
+    StageTimer t{};
+    int created = 0, st = W4A16_OK;
+    for (; created <= kMaxStages; ++created)
+        if ((st = hip_status(hipEventCreate(&t.ev[created]), "hipEventCreate"))) break;
+    if (!st) st = forward_impl(a, stream, &t);
+    if (!st && t.n > 0) st = hip_status(hipEventSynchronize(t.ev[t.n]), "hipEventSynchronize");
+    if (!st) {
+        const int n = std::min(t.n, max_kernels);
+        for (int i = 0; i < n && !st; ++i) {
+            kernel_names[i] = t.name[i];
+            st = hip_status(hipEventElapsedTime(&kernel_ms[i], t.ev[i], t.ev[i + 1]), "hipEventElapsedTime");
+        }
+        if (!st) *n_kernels = n;
     }
-
-    r.hist = static_cast<int32_t*>(at(L.hist));
-    r.lrank = static_cast<int32_t*>(at(L.lrank));
-    r.tiles = static_cast<int32_t*>(at(L.tiles));
-    r.xsum = static_cast<float*>(at(L.xsum));
-    r.nblk = L.nblk;
-    r.max_tiles = L.max_tiles;
-    if (int st = hip_status(launch_route_large(r, s), "routing launch")) return st;
-    PrefillArgs p{};
-    p.x = a->x;
-    p.T = (int)a->T;
-    p.E = (int)a->E;
-    p.k = (int)a->top_k;
-    p.H = a->H;
-    p.routed = routed;
-    p.shared = shared;
-    p.ids = r.ids;
-    p.wts = r.wts;
-    p.offsets = r.offsets;
-    p.sorted = r.sorted;
-    p.meta = r.meta;
-    p.tiles = r.tiles;
-    p.max_tiles = L.max_tiles;
-    p.xsum = r.xsum;
-    p.abuf = abuf;
-    p.width_a = L.width_a;
-    p.y32 = static_cast<float*>(at(L.y32));
-    p.residual = a->residual;
-    p.y = a->y;
-    return hip_status(launch_prefill(p, s), "prefill launch");
+    for (int i = 0; i < created; ++i) (void)hipEventDestroy(t.ev[i]);
+    return st;
 }
 
 }  // extern "C"

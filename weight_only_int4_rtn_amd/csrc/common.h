@@ -100,6 +100,16 @@ __device__ __forceinline__ u32x4_t perm_act(u32x4_t X) {
     return a;
 }
 
+// Guarded 16-byte load without a branch: reads `p` when `ok`, otherwise reads `fallback`
+// (any valid address) and returns zeros.  A load inside a divergent branch makes the
+// compiler wait for every outstanding load at that point, which serialises independent
+// HBM requests; this form keeps all loads of a pass in flight together.
+__device__ __forceinline__ u32x4_t load16_or_zero(const void* p, bool ok, const void* fallback) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ok ? p : fallback);
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    return u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
+}
+
 // bf16 pair of -OFF (see above): -136 = 0xC308, -2304 = 0xC510.
 template <int BITS>
 __device__ __forceinline__ u32x4_t neg_offset_operand() {
@@ -114,7 +124,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 
 struct WsLayout {
     size_t ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
-        y32, total;
+        y32, tokw, rec, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
     int nblk;           // routing blocks of the large-batch path
@@ -125,6 +135,25 @@ struct WsLayout {
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
 constexpr int kRouteBlockT = 64; // tokens per routing block on the large-batch path
 constexpr int kPrefillMT = 128;  // tokens per M-tile of the large-batch grouped GEMM
+
+// ------------------------------------------------------------- stage timer
+
+// Optional per-kernel timing: a launcher calls mark(t, name) right after each kernel it
+// enqueues; with t != nullptr an event is recorded on the stream at that point.
+constexpr int kMaxStages = 16;
+struct StageTimer {
+    hipStream_t stream;
+    hipEvent_t ev[kMaxStages + 1];
+    const char* name[kMaxStages];
+    int n;
+};
+inline void mark(StageTimer* t, const char* name) {
+    if (t && t->n < kMaxStages) {
+        t->name[t->n] = name;
+        (void)hipEventRecord(t->ev[t->n + 1], t->stream);
+        ++t->n;
+    }
+}
 
 // ----------------------------------------------------------- kernel launchers
 // Each returns hipGetLastError() after the launch.
@@ -147,12 +176,16 @@ struct RouteArgs {
     int32_t* tiles;       // large path: [max_tiles, 2] (expert, first row)
     const uint16_t* x;    // large path: activations for the group sums
     float* xsum;          // large path: [T, H/128] sums of bf16 activations per group
+    int2* tokw;           // [T*k] (token, weight bits) of each pair, in sorted order
+    int4* rec;            // small path: [max_slots] (expert, first sorted row, count, 0);
+                          // count 0 marks a slot beyond the active experts
+    int max_slots;
     int64_t H;
     int nblk;
     int64_t max_tiles;
 };
-hipError_t launch_route_small(const RouteArgs& a, hipStream_t s);
-hipError_t launch_route_large(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
+hipError_t launch_route_large(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 struct ExpertSet {       // one family of experts sharing a code width
     const int32_t* w13;
@@ -174,6 +207,8 @@ struct DecodeArgs {
     const int32_t* sorted;
     const int32_t* active;
     const int32_t* meta;
+    const int4* rec;            // per active-expert slot: (expert, first sorted row, count, 0)
+    const int2* tokw;           // per sorted row: (token, weight bits)
     uint16_t* abuf;             // [rows_a, width_a]
     int64_t width_a;
     float* part;                // [splits, T, H]
@@ -181,7 +216,7 @@ struct DecodeArgs {
     const uint16_t* residual;
     uint16_t* y;
 };
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 struct PrefillArgs {
     const uint16_t* x;
@@ -194,6 +229,7 @@ struct PrefillArgs {
     const int32_t* sorted;
     const int32_t* meta;
     const int32_t* tiles;
+    const int2* tokw;
     int64_t max_tiles;
     const float* xsum;
     uint16_t* abuf;
@@ -202,6 +238,6 @@ struct PrefillArgs {
     const uint16_t* residual;
     uint16_t* y;
 };
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 }  // namespace w4a16

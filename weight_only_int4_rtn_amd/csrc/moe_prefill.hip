@@ -89,12 +89,15 @@ __device__ void gk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
     // staging assignment: 8 chunks of 16 B per thread, rows (tid>>4) + 16 j, column slice tid & 15
     const int col8 = (tid & 15) * 8;
     const uint16_t* xrow[8];
+    uint32_t xok = 0;   // bit j: row (tid >> 4) + 16 j is a real token
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int t = s_tok[(tid >> 4) + 16 * j];
-        xrow[j] = t >= 0 ? a.x + (int64_t)t * H + col8 : nullptr;
+        xok |= (t >= 0 ? 1u : 0u) << j;
+        xrow[j] = a.x + (int64_t)(t >= 0 ? t : s_tok[0]) * H + col8;
     }
     const int xs_tok = tid < MT ? s_tok[tid] : -1;
+    const float* xs_row = a.xsum + (int64_t)(xs_tok >= 0 ? xs_tok : s_tok[0]) * G;
 
     // code rows of the four B subtiles: gate/up x two 16-column halves
     const uint8_t* brow[4];
@@ -117,9 +120,9 @@ __device__ void gk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
     auto load_stage = [&](int g) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            stage[j] = xrow[j] ? *reinterpret_cast<const u32x4_t*>(xrow[j] + (int64_t)g * kGroup)
-                               : u32x4_t{0u, 0u, 0u, 0u};
-        xs_stage = xs_tok >= 0 ? -kOff * a.xsum[(int64_t)xs_tok * G + g] : 0.f;
+            stage[j] = load16_or_zero(xrow[j] + (int64_t)g * kGroup, xok >> j & 1u, xrow[j]);
+        const float xs = xs_row[g];
+        xs_stage = xs_tok >= 0 ? -kOff * xs : 0.f;
     };
     auto store_stage = [&](int buf) {
         uint16_t* dst = s_a + buf * (MT * kRowPad);
@@ -235,10 +238,12 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
 
     const int col8 = (tid & 15) * 8;
     const uint16_t* arow[8];
+    uint32_t aok = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int r = (tid >> 4) + 16 * j;
-        arow[j] = r < tr.count ? a.abuf + (int64_t)(tr.orow_base + r) * a.width_a + col8 : nullptr;
+        aok |= (r < tr.count ? 1u : 0u) << j;
+        arow[j] = a.abuf + (int64_t)(tr.orow_base + (r < tr.count ? r : 0)) * a.width_a + col8;
     }
     const uint8_t* brow[4];
     const uint16_t* srow[4];
@@ -259,8 +264,7 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
     auto load_stage = [&](int g) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            stage[j] = arow[j] ? *reinterpret_cast<const u32x4_t*>(arow[j] + (int64_t)g * kGroup)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+            stage[j] = load16_or_zero(arow[j] + (int64_t)g * kGroup, aok >> j & 1u, arow[j]);
     };
     auto store_stage = [&](int buf) {
         uint16_t* dst = s_a + buf * (MT * kRowPad);
@@ -432,30 +436,33 @@ unsigned persistent_grid(int64_t max_items) {
 }
 
 template <int BITS, int SBITS>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
     const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
     const int64_t shared_tiles = SBITS ? (a.T + MT - 1) / MT : 0;
     const int64_t gk_items = (a.max_tiles + shared_tiles) * (Imax / kGkCols);
     const int64_t dk_items = (a.max_tiles + shared_tiles) * (a.H / kDkRows);
     gk_prefill_kernel<BITS, SBITS><<<persistent_grid(gk_items), 256, 0, s>>>(a);
+    mark(t, "gk_prefill");
     dk_prefill_kernel<BITS, SBITS><<<persistent_grid(dk_items), 256, 0, s>>>(a);
+    mark(t, "dk_prefill");
     const int64_t n = (int64_t)a.T * a.H;
     finalize_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.y32, n, a.residual, a.y);
+    mark(t, "finalize");
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
     const int sb = a.shared.bits;
     if (a.routed.bits == 4) {
-        if (sb == 0) return launch_prefill_t<4, 0>(a, s);
-        if (sb == 4) return launch_prefill_t<4, 4>(a, s);
-        return launch_prefill_t<4, 8>(a, s);
+        if (sb == 0) return launch_prefill_t<4, 0>(a, s, t);
+        if (sb == 4) return launch_prefill_t<4, 4>(a, s, t);
+        return launch_prefill_t<4, 8>(a, s, t);
     }
-    if (sb == 0) return launch_prefill_t<8, 0>(a, s);
-    if (sb == 4) return launch_prefill_t<8, 4>(a, s);
-    return launch_prefill_t<8, 8>(a, s);
+    if (sb == 0) return launch_prefill_t<8, 0>(a, s, t);
+    if (sb == 4) return launch_prefill_t<8, 4>(a, s, t);
+    return launch_prefill_t<8, 8>(a, s, t);
 }
 
 }  // namespace w4a16

@@ -30,54 +30,85 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
-// Top-k of one token by one wave.  Lane j < k ends holding the j-th chosen expert and
-// its logit in (*my_id, *my_val).
-__device__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_id, float* my_val) {
-    const int lane = threadIdx.x & 63;
-    constexpr int NV = kMaxE / 64;
-    float v[NV];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : 0.0f;
-        if (e >= E) taken |= 1u << i;
-    }
-    *my_id = -1;
-    *my_val = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = -1;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if (64 * i < E) {
-                const int e = lane + 64 * i;
-                if (!(taken >> i & 1u) && ranks_before(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        bv = __shfl(bv, 0);
-        bi = __shfl(bi, 0);
-        if (bi >= 0 && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == j) { *my_id = bi; *my_val = bv; }
-    }
+// Order-preserving unsigned key of a finite float (-0 is taken as +0, so equal logits
+// get equal keys); larger logit <=> larger key, and no finite value maps to 0.
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u << 1) == 0) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// Softmax weights of the k chosen logits; lanes j < k write slot j to global memory.
-__device__ __forceinline__ void wave_weights(int my_id, float my_val, int k, int32_t* ids, float* wts) {
+// Lane-wise max of a 64-bit key across the wave, returned in every lane.  DPP moves
+// (quad permutes, row mirrors, then row broadcasts of lanes 15 and 31) keep every step
+// in registers; the full maximum lands in lane 63 and is read back as a scalar.
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v, uint64_t o) { return o > v ? o : v; }
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+    return (uint64_t)nhi << 32 | nlo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_step(v, dpp_u64<0xb1, 0xf>(v));    // quad_perm [1,0,3,2]
+    v = dpp_max_step(v, dpp_u64<0x4e, 0xf>(v));    // quad_perm [2,3,0,1]
+    v = dpp_max_step(v, dpp_u64<0x141, 0xf>(v));   // row_half_mirror
+    v = dpp_max_step(v, dpp_u64<0x140, 0xf>(v));   // row_mirror: each row of 16 holds its max
+    v = dpp_max_step(v, dpp_u64<0x142, 0xa>(v));   // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step(v, dpp_u64<0x143, 0xc>(v));   // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return (uint64_t)hi << 32 | lo;
+}
+
+// Top-k of one token by one wave: k rounds of a wave-wide maximum over 64-bit keys
+// (ordered logit in the high half, the inverted expert index in the low half, so equal
+// logits resolve to the lower index); the round's winner is marked taken by its lane.
+// Lane j < k returns slot j's expert and its softmax weight over the chosen logits.
+template <int NV>   // logits per lane: E <= 64 * NV
+__device__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_id, float* my_w) {
     const int lane = threadIdx.x & 63;
-    const float v0 = __shfl(my_val, 0);
-    float den = 0.0f;
-    for (int j = 0; j < k; ++j) den += __expf(__shfl(my_val, j) - v0);
-    if (lane < k) {
-        wts[lane] = __expf(my_val - v0) / den;
-        ids[lane] = my_id;
+    uint64_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {   // unconditional (clamped) loads: all in flight together
+        const int e = lane + 64 * i;
+        const float v = row[min(e, E - 1)];
+        key[i] = e < E ? ((uint64_t)ordered_key(v) << 32 | (uint32_t)~e) : 0ull;
     }
+    float v0 = 0.f, den = 0.f, mine = 0.f;
+    int id = -1;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) best = key[i] > best ? key[i] : best;
+        const uint64_t win = wave_max_u64(best);
+        const int widx = (int)~(uint32_t)win;
+        const float wval = key_value((uint32_t)(win >> 32));
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (key[i] == win) key[i] = 0;   // only the owner lane holds this key
+        if (j == 0) v0 = wval;
+        const float ex = __expf(wval - v0);
+        den += ex;
+        if (lane == j) {
+            id = widx;
+            mine = ex;
+        }
+    }
+    *my_id = lane < k ? id : -1;
+    *my_w = lane < k ? mine / den : 0.f;
+}
+
+__device__ __forceinline__ void wave_topk_any(const float* __restrict__ row, int E, int k, int* my_id,
+                                              float* my_w) {
+    if (E <= 256) wave_topk<4>(row, E, k, my_id, my_w);
+    else if (E <= 512) wave_topk<8>(row, E, k, my_id, my_w);
+    else wave_topk<16>(row, E, k, my_id, my_w);
 }
 
 // Checked copy of caller-supplied ids: out of range or repeated within the token -> -1.
@@ -122,6 +153,7 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 
 __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
     __shared__ int s_ids[kSmallT * kMaxK];
+    __shared__ float s_w[kSmallT * kMaxK];
     __shared__ int s_cnt[kMaxE];
     __shared__ uint32_t s_mlo[kMaxE], s_mhi[kMaxE];
     __shared__ int s_off[kMaxE];
@@ -134,13 +166,20 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
     if (a.logits) {
         for (int t = wave; t < T; t += blockDim.x >> 6) {
             int my_id;
-            float my_val;
-            wave_topk(a.logits + (int64_t)t * E, E, k, &my_id, &my_val);
-            wave_weights(my_id, my_val, k, a.ids + t * k, a.wts + t * k);
-            if (lane < k) s_ids[t * k + lane] = my_id;
+            float my_w;
+            wave_topk_any(a.logits + (int64_t)t * E, E, k, &my_id, &my_w);
+            if (lane < k) {
+                a.ids[t * k + lane] = my_id;
+                a.wts[t * k + lane] = my_w;
+                s_ids[t * k + lane] = my_id;
+                s_w[t * k + lane] = my_w;
+            }
         }
     } else {
-        for (int p = tid; p < P; p += blockDim.x) s_ids[p] = checked_id(a.ids + (p / k) * k, p % k, E);
+        for (int p = tid; p < P; p += blockDim.x) {
+            s_ids[p] = checked_id(a.ids + (p / k) * k, p % k, E);
+            s_w[p] = a.wts[p];
+        }
     }
     __syncthreads();
 
@@ -155,17 +194,23 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
     }
     __syncthreads();
 
-    // offsets (exclusive scan of counts) and the ascending list of active experts
-    int total = 0, n_active = 0;
+    // offsets (exclusive scan of counts) and the ascending list of active experts, from one
+    // scan of count << 16 | (count > 0) (both sums stay below 2^16 for T * k <= 1024)
+    int packed_total = 0;
     const int c = tid < E ? s_cnt[tid] : 0;
-    const int off = block_exclusive_scan(c, s_tmp, &total);
-    const int act = block_exclusive_scan(c > 0 ? 1 : 0, s_tmp, &n_active);
+    const int packed = block_exclusive_scan((c << 16) | (c > 0 ? 1 : 0), s_tmp, &packed_total);
+    const int off = packed >> 16, act = packed & 0xffff;
+    const int total = packed_total >> 16, n_active = packed_total & 0xffff;
     if (tid < E) {
         s_off[tid] = off;
         a.offsets[tid] = off;
         a.counts[tid] = c;
-        if (c > 0) a.active[act] = tid;
+        if (c > 0) {
+            a.active[act] = tid;
+            a.rec[act] = int4{tid, off, c, 0};
+        }
     }
+    for (int sl = n_active + tid; sl < a.max_slots; sl += blockDim.x) a.rec[sl] = int4{0, 0, 0, 0};
     if (tid == 0) {
         a.offsets[E] = total;
         a.meta[0] = n_active;
@@ -181,14 +226,15 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
             const int rank = t < 32 ? __popc(lo & ((1u << t) - 1u))
                                     : __popc(lo) + __popc(hi & ((1u << (t - 32)) - 1u));
             a.sorted[s_off[e] + rank] = p;
+            a.tokw[s_off[e] + rank] = int2{t, __float_as_int(s_w[p])};
         }
     }
 }
 
 // ------------------------------------------------------------------ large batch
 
-// One workgroup per block of kRouteBlockT tokens (4 waves, 16 tokens each).
-__global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
+// One workgroup per block of kRouteBlockT tokens (16 waves, 4 tokens each).
+__global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
     __shared__ int s_ids[kRouteBlockT * kMaxK];
     __shared__ int s_cnt[kMaxE];
     __shared__ uint32_t s_mlo[kMaxE], s_mhi[kMaxE];
@@ -199,14 +245,17 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
     const int nt = min(kRouteBlockT, a.T - t0);
     for (int e = tid; e < E; e += blockDim.x) { s_cnt[e] = 0; s_mlo[e] = 0; s_mhi[e] = 0; }
 
-    for (int tl = wave; tl < nt; tl += 4) {
+    for (int tl = wave; tl < nt; tl += 16) {
         const int t = t0 + tl;
         if (a.logits) {
             int my_id;
-            float my_val;
-            wave_topk(a.logits + (int64_t)t * E, E, k, &my_id, &my_val);
-            wave_weights(my_id, my_val, k, a.ids + (int64_t)t * k, a.wts + (int64_t)t * k);
-            if (lane < k) s_ids[tl * k + lane] = my_id;
+            float my_w;
+            wave_topk_any(a.logits + (int64_t)t * E, E, k, &my_id, &my_w);
+            if (lane < k) {
+                a.ids[(int64_t)t * k + lane] = my_id;
+                a.wts[(int64_t)t * k + lane] = my_w;
+                s_ids[tl * k + lane] = my_id;
+            }
         } else if (lane < k) {
             s_ids[tl * k + lane] = checked_id(a.ids + (int64_t)t * k, lane, E);
         }
@@ -257,31 +306,64 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
 
 // One 1024-thread workgroup: per-expert totals over blocks, offsets, per-block bases
 // (written over the histogram), the active list and the M-tile list of the grouped GEMM.
+// Thread (e, part) owns expert e and a contiguous range of blocks, so the histogram is
+// read with many loads in flight instead of one long dependent walk.
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
     __shared__ int s_tmp[64];
+    __shared__ int s_part[1024];
     const int tid = threadIdx.x, E = a.E, nblk = a.nblk;
-    int c = 0;
-    if (tid < E)
-        for (int b = 0; b < nblk; ++b) c += a.hist[(int64_t)b * E + tid];
+    const int Epad = (E + 63) & ~63;
+    const int parts = max(1, (int)blockDim.x / Epad);
+    const int e = tid % Epad, part = tid / Epad;
+    const bool owner = e < E && part < parts;
+    const int per = (nblk + parts - 1) / parts;
+    const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
+    int mine = 0;
+    if (owner) {
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = a.hist[(int64_t)(b + j) * E + e];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mine += v[j];
+        }
+        for (; b < b1; ++b) mine += a.hist[(int64_t)b * E + e];
+    }
+    s_part[tid] = mine;
+    __syncthreads();
+    int c = 0, lower = 0;
+    if (owner) {
+        for (int p = 0; p < parts; ++p) {
+            const int v = s_part[p * Epad + e];
+            c += v;
+            if (p < part) lower += v;
+        }
+    }
+    const bool lead = owner && part == 0;
     int total = 0, n_active = 0, n_tiles = 0;
-    const int off = block_exclusive_scan(c, s_tmp, &total);
-    const int act = block_exclusive_scan(c > 0 ? 1 : 0, s_tmp, &n_active);
-    const int nt = (c + kPrefillMT - 1) / kPrefillMT;
+    const int off = block_exclusive_scan(lead ? c : 0, s_tmp, &total);
+    const int act = block_exclusive_scan(lead && c > 0 ? 1 : 0, s_tmp, &n_active);
+    const int nt = lead ? (c + kPrefillMT - 1) / kPrefillMT : 0;
     const int toff = block_exclusive_scan(nt, s_tmp, &n_tiles);
-    if (tid < E) {
-        a.offsets[tid] = off;
-        a.counts[tid] = c;
-        if (c > 0) a.active[act] = tid;
-        int run = off;
-        for (int b = 0; b < nblk; ++b) {
-            const int64_t i = (int64_t)b * E + tid;
+    if (lead) {
+        s_part[e] = off;   // every part of this expert reads the offset below
+        a.offsets[e] = off;
+        a.counts[e] = c;
+        if (c > 0) a.active[act] = e;
+        for (int i = 0; i < nt && toff + i < a.max_tiles; ++i) {
+            a.tiles[2 * (toff + i)] = e;
+            a.tiles[2 * (toff + i) + 1] = i * kPrefillMT;
+        }
+    }
+    __syncthreads();
+    if (owner) {
+        int run = s_part[e] + lower;
+        for (int b = b0; b < b1; ++b) {
+            const int64_t i = (int64_t)b * E + e;
             const int h = a.hist[i];
             a.hist[i] = run;
             run += h;
-        }
-        for (int i = 0; i < nt && toff + i < a.max_tiles; ++i) {
-            a.tiles[2 * (toff + i)] = tid;
-            a.tiles[2 * (toff + i) + 1] = i * kPrefillMT;
         }
     }
     if (tid == 0) {
@@ -297,20 +379,27 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
     const int v = a.lrank[p];
     if (v < 0) return;
     const int e = v >> 8, rank = v & 255;
-    const int b = (int)(p / a.k) / kRouteBlockT;
-    a.sorted[a.hist[(int64_t)b * a.E + e] + rank] = (int)p;
+    const int t = (int)(p / a.k);
+    const int b = t / kRouteBlockT;
+    const int pos = a.hist[(int64_t)b * a.E + e] + rank;
+    a.sorted[pos] = (int)p;
+    a.tokw[pos] = int2{t, __float_as_int(a.wts[p])};
 }
 
-hipError_t launch_route_small(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t) {
     route_small_kernel<<<1, 1024, 0, s>>>(a);
+    mark(t, "route_small");
     return hipGetLastError();
 }
 
-hipError_t launch_route_large(const RouteArgs& a, hipStream_t s) {
-    route_block_kernel<<<a.nblk, 256, 0, s>>>(a);
+hipError_t launch_route_large(const RouteArgs& a, hipStream_t s, StageTimer* t) {
+    route_block_kernel<<<a.nblk, 1024, 0, s>>>(a);
+    mark(t, "route_block");
     route_scan_kernel<<<1, 1024, 0, s>>>(a);
+    mark(t, "route_scan");
     const int64_t P = (int64_t)a.T * a.k;
     route_scatter_kernel<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(a);
+    mark(t, "route_scatter");
     return hipGetLastError();
 }
 
