@@ -49,6 +49,10 @@ int check_shapes(const moe_w4a16_args* a) {
     if (a->top_k > 16) return fail(W4A16_ERR_UNSUPPORTED, "top_k = %lld > 16", (long long)a->top_k);
     if (a->T * a->top_k >= (int64_t(1) << 31) || a->T >= (int64_t(1) << 24))
         return fail(W4A16_ERR_UNSUPPORTED, "T = %lld too large", (long long)a->T);
+    // staged activation arrays and one expert's codes are addressed with 32-bit byte offsets
+    if (a->T * a->H * 2 >= (int64_t(1) << 32) ||
+        (a->T + a->T * a->top_k) * std::max(a->I, a->shared_bits ? a->shared_I : (int64_t)0) * 2 >= (int64_t(1) << 32))
+        return fail(W4A16_ERR_UNSUPPORTED, "T = %lld too large for these shapes", (long long)a->T);
     if (a->shared_bits != 0) {
         if (a->shared_bits != 4 && a->shared_bits != 8)
             return fail(W4A16_ERR_INVALID_ARG, "shared_bits = %d, must be 0, 4 or 8", a->shared_bits);
@@ -96,6 +100,7 @@ WsLayout layout(const moe_w4a16_args* a) {
         L.max_tiles = (P + kPrefillMT - 1) / kPrefillMT + std::min(E, P);
         L.tiles = take((size_t)L.max_tiles * 8);
         L.xsum = take((size_t)T * (H / kGroup) * 4);
+        L.xp = take((size_t)T * H * 2);
         L.y32 = take((size_t)T * H * 4);
     }
     L.total = off;
@@ -183,6 +188,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     r.lrank = static_cast<int32_t*>(at(L.lrank));
     r.tiles = static_cast<int32_t*>(at(L.tiles));
     r.xsum = static_cast<float*>(at(L.xsum));
+    r.xp = static_cast<uint16_t*>(at(L.xp));
     r.nblk = L.nblk;
     r.max_tiles = L.max_tiles;
     if (int st = hip_status(launch_route_large(r, s, timer), "routing launch")) return st;
@@ -203,7 +209,9 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     p.tokw = r.tokw;
     p.max_tiles = L.max_tiles;
     p.xsum = r.xsum;
+    p.xp = r.xp;
     p.abuf = abuf;
+    p.rows_a = L.rows_a;
     p.width_a = L.width_a;
     p.y32 = static_cast<float*>(at(L.y32));
     p.residual = a->residual;

@@ -50,8 +50,16 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 //
 // INT4 word w holds k0..k7 (k0 lowest).  dq4 returns the bf16 pairs
 // (k0,k4) (k1,k5) (k2,k6) (k3,k7); the activation slice must use that order.
-__device__ __forceinline__ u32x4_t dq4(uint32_t w) {
-    const uint32_t M = 0x000f000fu, C = 0x43004300u;
+// A VOP3 instruction can read only one scalar or literal operand on gfx9, so the nibble
+// mask is kept in a vector register (nibble_mask()) to let (w & mask) | C fuse into a
+// single v_and_or_b32.
+__device__ __forceinline__ uint32_t nibble_mask() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m));
+    return m;
+}
+__device__ __forceinline__ u32x4_t dq4(uint32_t w, uint32_t M) {
+    const uint32_t C = 0x43004300u;
     u32x4_t r;
     r[0] = (w & M) | C;
     r[1] = ((w >> 4) & M) | C;
@@ -59,46 +67,35 @@ __device__ __forceinline__ u32x4_t dq4(uint32_t w) {
     r[3] = ((w >> 12) & M) | C;
     return r;
 }
+__device__ __forceinline__ u32x4_t dq4(uint32_t w) { return dq4(w, 0x000f000fu); }
 
-// INT8 words w0 = k0..k3, w1 = k4..k7.  Low and high nibbles in the order
-// (k0,k2) (k1,k3) (k4,k6) (k5,k7).
-__device__ __forceinline__ u32x4_t dq8_lo(uint32_t w0, uint32_t w1) {
-    const uint32_t M = 0x000f000fu, C = 0x43004300u;
-    u32x4_t r;
-    r[0] = (w0 & M) | C;
-    r[1] = ((w0 >> 8) & M) | C;
-    r[2] = (w1 & M) | C;
-    r[3] = ((w1 >> 8) & M) | C;
-    return r;
-}
-__device__ __forceinline__ u32x4_t dq8_hi(uint32_t w0, uint32_t w1) {
-    const uint32_t M = 0x000f000fu, C = 0x45004500u;
-    u32x4_t r;
-    r[0] = ((w0 >> 4) & M) | C;
-    r[1] = ((w0 >> 12) & M) | C;
-    r[2] = ((w1 >> 4) & M) | C;
-    r[3] = ((w1 >> 12) & M) | C;
-    return r;
+// INT8 words w0 = k0..k3, w1 = k4..k7 (one byte each).  Each byte splits into its low
+// and high nibble; v_perm gathers bytes j and j+4 into one word so the pairs come out
+// in the same K order as dq4: (k0,k4) (k1,k5) (k2,k6) (k3,k7).
+__device__ __forceinline__ void dq8(uint32_t w0, uint32_t w1, u32x4_t& lo, u32x4_t& hi, uint32_t M = 0x000f000fu) {
+    const uint32_t CL = 0x43004300u, CH = 0x45004500u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // bytes: [w0.byte j, 0, w1.byte j, 0]   (selector 0x0c yields a zero byte)
+        const uint32_t sel = (uint32_t)j | 0x0c00u | ((uint32_t)(4 + j) << 16) | 0x0c000000u;
+        const uint32_t t = __builtin_amdgcn_perm(w1, w0, sel);
+        lo[j] = (t & M) | CL;
+        hi[j] = ((t >> 4) & M) | CH;
+    }
 }
 
 // Reorder eight natural-order bf16 activations X = (x0,x1)(x2,x3)(x4,x5)(x6,x7) to the
-// K order of the matching weight operand.
-template <int BITS>
+// K order of the weight operands: (x0,x4) (x1,x5) (x2,x6) (x3,x7).  Within each block
+// of 8 columns, logical column j sits at position 2*(j % 4) + j / 4.
 __device__ __forceinline__ u32x4_t perm_act(u32x4_t X) {
     u32x4_t a;
-    if constexpr (BITS == 4) {   // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-        a[0] = (X[0] & 0xffffu) | (X[2] << 16);
-        a[1] = (X[0] >> 16) | (X[2] & 0xffff0000u);
-        a[2] = (X[1] & 0xffffu) | (X[3] << 16);
-        a[3] = (X[1] >> 16) | (X[3] & 0xffff0000u);
-    } else {                     // (x0,x2) (x1,x3) (x4,x6) (x5,x7)
-        a[0] = (X[0] & 0xffffu) | (X[1] << 16);
-        a[1] = (X[0] >> 16) | (X[1] & 0xffff0000u);
-        a[2] = (X[2] & 0xffffu) | (X[3] << 16);
-        a[3] = (X[2] >> 16) | (X[3] & 0xffff0000u);
-    }
+    a[0] = (X[0] & 0xffffu) | (X[2] << 16);
+    a[1] = (X[0] >> 16) | (X[2] & 0xffff0000u);
+    a[2] = (X[1] & 0xffffu) | (X[3] << 16);
+    a[3] = (X[1] >> 16) | (X[3] & 0xffff0000u);
     return a;
 }
+__device__ __forceinline__ int perm_pos(int j) { return (j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1); }
 
 // Guarded 16-byte load without a branch: reads `p` when `ok`, otherwise reads `fallback`
 // (any valid address) and returns zeros.  A load inside a divergent branch makes the
@@ -110,6 +107,19 @@ __device__ __forceinline__ u32x4_t load16_or_zero(const void* p, bool ok, const 
     return u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
 }
 
+// Raw buffer resource over `bytes` bytes at p (gfx9-family descriptor word 3).  Buffer
+// loads take a per-lane 32-bit offset plus a scalar offset, so loop-varying parts of an
+// address cost no vector instructions; reads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+
 // bf16 pair of -OFF (see above): -136 = 0xC308, -2304 = 0xC510.
 template <int BITS>
 __device__ __forceinline__ u32x4_t neg_offset_operand() {
@@ -118,13 +128,14 @@ __device__ __forceinline__ u32x4_t neg_offset_operand() {
     return r;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// SiLU(g) * u = g / (1 + e^-g) * u, with the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
 // ------------------------------------------------------------ workspace layout
 
 struct WsLayout {
     size_t ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
-        y32, tokw, rec, total;
+        y32, tokw, rec, xp, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
     int nblk;           // routing blocks of the large-batch path
@@ -176,6 +187,7 @@ struct RouteArgs {
     int32_t* tiles;       // large path: [max_tiles, 2] (expert, first row)
     const uint16_t* x;    // large path: activations for the group sums
     float* xsum;          // large path: [T, H/128] sums of bf16 activations per group
+    uint16_t* xp;         // large path: [T, H] activations with each 8-column block reordered
     int2* tokw;           // [T*k] (token, weight bits) of each pair, in sorted order
     int4* rec;            // small path: [max_slots] (expert, first sorted row, count, 0);
                           // count 0 marks a slot beyond the active experts
@@ -232,7 +244,9 @@ struct PrefillArgs {
     const int2* tokw;
     int64_t max_tiles;
     const float* xsum;
+    const uint16_t* xp;
     uint16_t* abuf;
+    int64_t rows_a;
     int64_t width_a;
     float* y32;
     const uint16_t* residual;

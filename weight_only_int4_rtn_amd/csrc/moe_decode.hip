@@ -29,7 +29,7 @@ namespace {
 // zero when the row is padding (`ok` false; `row` then points at any valid row).
 template <int BITS>
 __device__ __forceinline__ u32x4_t load_act(const uint16_t* row, bool ok, int64_t c) {
-    return perm_act<BITS>(load16_or_zero(row + c, ok, row));
+    return perm_act(load16_or_zero(row + c, ok, row));
 }
 
 // One 128-column group: seed with -OFF * sum(x), then add sum_k x_k * (q_k + OFF) for the
@@ -38,15 +38,17 @@ template <int BITS>
 __device__ __forceinline__ f32x4_t group_dot(const u32x4_t (&av)[4], const u32x4_t (&bw)[BITS / 4],
                                              f32x4_t seed) {
     f32x4_t t = seed;
+    const uint32_t M = nibble_mask();
     if constexpr (BITS == 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t = mfma16(av[i], dq4(bw[0][i]), t);
+        for (int i = 0; i < 4; ++i) t = mfma16(av[i], dq4(bw[0][i], M), t);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t w0 = bw[i >> 1][(2 * i) & 3], w1 = bw[i >> 1][(2 * i + 1) & 3];
-            t = mfma16(av[i], dq8_lo(w0, w1), t);
-            t = mfma16(av[i], dq8_hi(w0, w1), t);
+            u32x4_t lo, hi;
+            dq8(bw[i >> 1][(2 * i) & 3], bw[i >> 1][(2 * i + 1) & 3], lo, hi, M);
+            t = mfma16(av[i], lo, t);
+            t = mfma16(av[i], hi, t);
         }
     }
     return t;

@@ -1,18 +1,21 @@
 // Large-batch W4A16 expert FFN as two grouped GEMMs on bf16 MFMA (gfx950).
 //
 // gk_prefill_kernel: items are (M-tile of up to 128 tokens of one expert, 64 output
-//   columns).  The tile's activation rows are gathered from x through the sorted pair
-//   list, K-slice-reordered and staged per 128-column group into LDS (double buffered);
-//   each wave (2 x 2 waves, 64 x 32 outputs) loads its 16 gate + 16 up code rows per
-//   16-column subtile straight from global memory, dequantises them in registers and
-//   runs 16x16x32 MFMAs.  The code offset is cancelled by seeding each group's
-//   accumulator with -OFF * sum(x) over that group (precomputed per token by the
-//   routing kernel), and the group scale is applied to the fp32 partial.  Epilogue:
-//   a = SiLU(g) * u as bf16 rows in sorted-pair order.
-// dk_prefill_kernel: items are (M-tile, 128 output rows); A is the contiguous block of
-//   a-rows, K = I.  The offset seed comes from an MFMA against the constant -OFF.  The
-//   router-weighted result is added into an fp32 [T, H] accumulator with float atomics
-//   (each output element receives top_k addends, in arrival order).
+//   columns = 64 gate rows + the 64 matching up rows).  Per 128-column group of K:
+//     - the tile's activation rows (already K-slice reordered by the routing kernel) are
+//       copied global -> LDS by direct LDS loads (no registers), into an XOR-swizzled
+//       double buffer, the next group's copy overlapping this group's MFMAs;
+//     - each wave (2 x 2 waves, 64 rows x 64 code rows) loads its code rows straight
+//       from global memory, expands them in registers and runs 16x16x32 MFMAs seeded
+//       with -OFF * sum(x) of the group (group sums from the routing kernel); the
+//       group scale is applied to the fp32 partial.
+//   Epilogue: a = SiLU(g) * u as bf16, columns written in the reordered K order the
+//   down GEMM consumes, rows in sorted-pair order.
+// dk_prefill_kernel: items are (M-tile, 128 output rows); A is the tile's contiguous
+//   block of a-rows, K = I, staged the same way.  The offset seed is an MFMA against
+//   the constant -OFF.  The router-weighted result is added into an fp32 [T, H]
+//   accumulator with float atomics (each element receives top_k addends, in arrival
+//   order).
 // finalize_kernel: y = bf16(acc + residual).
 //
 // Both GEMMs walk their items with a persistent grid whose size is a multiple of 8;
@@ -26,7 +29,8 @@ namespace w4a16 {
 namespace {
 
 constexpr int MT = kPrefillMT;       // 128 rows per M-tile
-constexpr int kRowPad = kGroup + 8;  // bf16 per staged LDS row (16 B pad: conflict-free reads)
+constexpr int kChunks = kGroup / 8;  // 16-byte chunks per staged row (one group of K)
+constexpr int kTileElems = MT * kGroup;
 constexpr int kGkCols = 64;          // output columns per gate/up item
 constexpr int kDkRows = 128;         // output rows per down item
 
@@ -37,13 +41,9 @@ struct TileRows {
     bool shared;
 };
 
-__device__ __forceinline__ int tile_token(const PrefillArgs& a, const TileRows& tr, int r) {
-    return tr.shared ? tr.tok_base + r : a.sorted[tr.tok_base + r] / a.k;
-}
-
 // Item L of the persistent walk; false when beyond the real work.
-__device__ __forceinline__ bool item_tile(const PrefillArgs& a, int L, int nb, int SB, int I_shared,
-                                          TileRows* tr, int* e, int* nblk) {
+__device__ __forceinline__ bool item_tile(const PrefillArgs& a, int L, int nb, int SB, TileRows* tr, int* e,
+                                          int* nblk) {
     const int routed_items = a.meta[1] * nb;
     *nblk = L % nb;
     if (L < routed_items) {
@@ -65,8 +65,86 @@ __device__ __forceinline__ bool item_tile(const PrefillArgs& a, int L, int nb, i
     tr->tok_base = st * MT;
     tr->orow_base = a.T * a.k + st * MT;
     tr->shared = true;
-    (void)I_shared;
     return true;
+}
+
+// Swizzled LDS position (in 16-byte chunks) of logical chunk c of tile row r.
+__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 15)); }
+
+// The tile row and logical chunk that lane copies for direct load j of its wave: lane l
+// of load j fills LDS chunk L = (8w + j) * 64 + l, i.e. row L / 16 at logical chunk
+// (L % 16) ^ (row % 16).
+__device__ __forceinline__ void stage_coords(int j, int* row, int* chunk) {
+    const int L = ((threadIdx.x >> 6) * 8 + j) * 64 + (threadIdx.x & 63);
+    *row = L / kChunks;
+    *chunk = (L % kChunks) ^ (*row & 15);
+}
+
+// Direct global -> LDS copy of one 128 x 128 group of a tile: 8 buffer loads of 64 lanes
+// x 16 B per wave.  voff[j] is the byte offset of this lane's source (row and chunk) for
+// the first group; col_bytes (scalar) selects the group.  The host keeps every staged
+// array below 2^32 bytes.
+__device__ __forceinline__ void stage_group(__amdgpu_buffer_rsrc_t src, const uint32_t (&voff)[8], uint32_t col_bytes,
+                                            uint16_t* lds_tile) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, lds_tile + (wave * 8 + j) * 64 * 8, 16, voff[j], col_bytes, 0, 0);
+}
+
+// Expands one lane's codes for MFMA k-step i into bf16 operand(s).
+template <int BITS>
+__device__ __forceinline__ void expand(const u32x4_t (&braw)[BITS / 4], int i, u32x4_t& b0, u32x4_t& b1,
+                                       uint32_t M) {
+    if constexpr (BITS == 4) {
+        b0 = dq4(braw[0][i], M);
+    } else {
+        dq8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3], b0, b1, M);
+    }
+}
+
+// One wave's 64 x 64 block for one group: 4 M-subtiles x 4 code subtiles of 16x16.
+// The group's A fragments (4 M-subtiles x 4 k-steps) are read from LDS once and held;
+// code subtiles are expanded one at a time, so the VALU expansion of subtile b + 1 can
+// run under the MFMAs of subtile b.  seed(mi, av) gives the offset seed of M-subtile mi.
+// With CACHED_SEED the seeds are computed once per group and held; otherwise seed() is
+// called again for every code subtile (cheap when it is an LDS broadcast read).
+template <int BITS, bool CACHED_SEED, typename Seed>
+__device__ __forceinline__ void mfma_group(const uint16_t* A, int wm, const u32x4_t (&braw)[4][BITS / 4],
+                                           const uint32_t (&scp)[2], f32x4_t (&acc)[4][4], Seed&& seed) {
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4, ml = lane & 15;
+    const uint32_t M = nibble_mask();
+    u32x4_t av[4][4];
+    f32x4_t s0[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int r = 64 * wm + 16 * mi + ml;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[mi][i] = *reinterpret_cast<const u32x4_t*>(A + swz(r, 4 * q + i) * 8);
+        if constexpr (CACHED_SEED) s0[mi] = seed(mi, av[mi]);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f32x4_t t[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) t[mi] = CACHED_SEED ? s0[mi] : seed(mi, av[mi]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4_t lo, hi;
+            expand<BITS>(braw[b], i, lo, hi, M);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                t[mi] = mfma16(av[mi][i], lo, t[mi]);
+                if constexpr (BITS == 8) t[mi] = mfma16(av[mi][i], hi, t[mi]);
+            }
+        }
+        const float sc = bf16_to_f32((scp[b >> 1] >> (16 * (b & 1))) & 0xffffu);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) acc[mi][b][r2] += sc * t[mi][r2];
+    }
 }
 
 // ---------------------------------------------------------------- gate / up
@@ -83,31 +161,28 @@ __device__ void gk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
     constexpr int kLaneBytes = 32 * BITS / 8, kGroupBytes = kGroup * BITS / 8;
     const int64_t row_bytes = H * BITS / 8;
 
-    if (tid < MT) s_tok[tid] = tid < tr.count ? tile_token(a, tr, tid) : -1;
+    if (tid < MT) {
+        const int r = min(tid, tr.count - 1);   // padding rows repeat a real row
+        s_tok[tid] = tr.shared ? tr.tok_base + r : a.tokw[tr.tok_base + r].x;
+    }
     __syncthreads();
 
-    // staging assignment: 8 chunks of 16 B per thread, rows (tid>>4) + 16 j, column slice tid & 15
-    const int col8 = (tid & 15) * 8;
-    const uint16_t* xrow[8];
-    uint32_t xok = 0;   // bit j: row (tid >> 4) + 16 j is a real token
+    const __amdgpu_buffer_rsrc_t xp_r = make_rsrc(a.xp, (uint32_t)(a.T * H * 2));
+    uint32_t voff[8];   // byte offset of each staged chunk's source row and chunk
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int t = s_tok[(tid >> 4) + 16 * j];
-        xok |= (t >= 0 ? 1u : 0u) << j;
-        xrow[j] = a.x + (int64_t)(t >= 0 ? t : s_tok[0]) * H + col8;
+        int r, c;
+        stage_coords(j, &r, &c);
+        voff[j] = ((uint32_t)s_tok[r] * (uint32_t)H + c * 8) * 2;
     }
-    const int xs_tok = tid < MT ? s_tok[tid] : -1;
-    const float* xs_row = a.xsum + (int64_t)(xs_tok >= 0 ? xs_tok : s_tok[0]) * G;
+    auto xs_at = [&](int g) { return a.xsum[(int64_t)s_tok[tid & (MT - 1)] * G + g]; };
 
-    // code rows of the four B subtiles: gate/up x two 16-column halves
-    const uint8_t* brow[4];
-    const uint16_t* srow[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int64_t r = (b >= 2 ? I_e : 0) + n0 + 32 * wn + 16 * (b & 1) + ml;
-        brow[b] = reinterpret_cast<const uint8_t*>(w13e) + r * row_bytes + q * kLaneBytes;
-        srow[b] = s13e + r * G;
-    }
+    // this wave's 64 code rows: gate rows n0 + 32 wn + 16 b + ml (b = 0, 1), up rows + I_e;
+    // one vector offset per lane, the subtile and group go into the scalar offset
+    const __amdgpu_buffer_rsrc_t b_r = make_rsrc(w13e, (uint32_t)(2 * I_e * row_bytes));
+    const __amdgpu_buffer_rsrc_t s_r = make_rsrc(s13e, (uint32_t)(2 * I_e * G * 2));
+    const uint32_t bvoff = (uint32_t)((n0 + 32 * wn + ml) * row_bytes + q * kLaneBytes);
+    const uint32_t svoff = (uint32_t)((n0 + 32 * wn + ml) * G * 2);
 
     f32x4_t acc[4][4];
 #pragma unroll
@@ -115,83 +190,47 @@ __device__ void gk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t stage[8];
-    float xs_stage = 0.f;
-    auto load_stage = [&](int g) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            stage[j] = load16_or_zero(xrow[j] + (int64_t)g * kGroup, xok >> j & 1u, xrow[j]);
-        const float xs = xs_row[g];
-        xs_stage = xs_tok >= 0 ? -kOff * xs : 0.f;
-    };
-    auto store_stage = [&](int buf) {
-        uint16_t* dst = s_a + buf * (MT * kRowPad);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x4_t*>(dst + ((tid >> 4) + 16 * j) * kRowPad + col8) = perm_act<BITS>(stage[j]);
-        if (tid < MT) s_xs[buf * MT + tid] = xs_stage;
-    };
-
     u32x4_t braw[4][BITS / 4];
+    uint32_t scp[2];   // the four code subtiles' group scales, bf16 pairs
     auto load_b = [&](int g) {
+        uint32_t s16[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t roff = (uint32_t)((b >= 2 ? I_e : 0) + 16 * (b & 1));
 #pragma unroll
             for (int c = 0; c < BITS / 4; ++c)
-                braw[b][c] = *reinterpret_cast<const u32x4_t*>(brow[b] + (int64_t)g * kGroupBytes + 16 * c);
+                braw[b][c] = buf_load16(b_r, bvoff, roff * (uint32_t)row_bytes + g * kGroupBytes + 16 * c);
+            s16[b] = buf_load_u16(s_r, svoff, (roff * G + g) * 2);
+        }
+        scp[0] = s16[0] | (s16[1] << 16);
+        scp[1] = s16[2] | (s16[3] << 16);
     };
 
-    load_stage(0);
+    stage_group(xp_r, voff, 0, s_a);
+    if (tid < MT) s_xs[tid] = -kOff * xs_at(0);
     load_b(0);
-    store_stage(0);
-    __syncthreads();
 
     for (int g = 0; g < G; ++g) {
         const int buf = g & 1;
-        float sc[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sc[b] = bf16_to_f32(srow[b][g]);
+        __syncthreads();   // group g staged (waits for the direct loads), group g-1 reads done
+        if (g + 1 < G) {
+            stage_group(xp_r, voff, (g + 1) * kGroup * 2, s_a + (buf ^ 1) * kTileElems);
+            if (tid < MT) s_xs[(buf ^ 1) * MT + tid] = -kOff * xs_at(g + 1);
+        }
+        // this group's codes move to bcur; the next group's load into braw
         u32x4_t bcur[4][BITS / 4];
+        const uint32_t scg[2] = {scp[0], scp[1]};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int c = 0; c < BITS / 4; ++c) bcur[b][c] = braw[b][c];
-        if (g + 1 < G) {
-            load_stage(g + 1);
-            load_b(g + 1);
-        }
-        const uint16_t* A = s_a + buf * (MT * kRowPad);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r0 = 64 * wm + 16 * mi;
-            u32x4_t av[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[i] = *reinterpret_cast<const u32x4_t*>(A + (r0 + ml) * kRowPad + 32 * q + 8 * i);
-            const f32x4_t seed = *reinterpret_cast<const f32x4_t*>(s_xs + buf * MT + r0 + 4 * q);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                f32x4_t t = seed;
-                if constexpr (BITS == 4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) t = mfma16(av[i], dq4(bcur[b][0][i]), t);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t w0 = bcur[b][i >> 1][(2 * i) & 3], w1 = bcur[b][i >> 1][(2 * i + 1) & 3];
-                        t = mfma16(av[i], dq8_lo(w0, w1), t);
-                        t = mfma16(av[i], dq8_hi(w0, w1), t);
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mi][b][r] += sc[b] * t[r];
-            }
-        }
-        if (g + 1 < G) store_stage(buf ^ 1);
-        __syncthreads();
+        if (g + 1 < G) load_b(g + 1);
+        const float* xs = s_xs + buf * MT + 64 * wm + 4 * q;
+        mfma_group<BITS, false>(s_a + buf * kTileElems, wm, bcur, scg, acc,
+                                [&](int mi, const u32x4_t(&)[4]) { return *reinterpret_cast<const f32x4_t*>(xs + 16 * mi); });
     }
 
-    // epilogue: a = SiLU(gate) * up, bf16, rows in sorted-pair order
+    // epilogue: a = SiLU(gate) * up, bf16, columns in the reordered K order of the down GEMM
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -201,8 +240,8 @@ __device__ void gk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
                 const int m = 64 * wm + 16 * mi + 4 * q + r;
                 if (m < tr.count) {
                     const float v = silu_mul(acc[mi][ns][r], acc[mi][2 + ns][r]);
-                    a.abuf[(int64_t)(tr.orow_base + m) * a.width_a + n0 + 32 * wn + 16 * ns + ml] =
-                        (uint16_t)f32_to_bf16(v);
+                    const int col = perm_pos(n0 + 32 * wn + 16 * ns + ml);
+                    a.abuf[(int64_t)(tr.orow_base + m) * a.width_a + col] = (uint16_t)f32_to_bf16(v);
                 }
             }
 }
@@ -220,39 +259,34 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
     const int64_t row_bytes = I_e * BITS / 8;
 
     if (tid < MT) {
-        int t = -1;
+        int t = 0;
         float w = 0.f;
         if (tid < tr.count) {
             if (tr.shared) {
                 t = tr.tok_base + tid;
                 w = 1.f;
             } else {
-                const int p = a.sorted[tr.tok_base + tid];
-                t = p / a.k;
-                w = a.wts[p];
+                const int2 tw = a.tokw[tr.tok_base + tid];
+                t = tw.x;
+                w = __int_as_float(tw.y);
             }
         }
         s_tok[tid] = t;
         s_wt[tid] = w;
     }
 
-    const int col8 = (tid & 15) * 8;
-    const uint16_t* arow[8];
-    uint32_t aok = 0;
+    const __amdgpu_buffer_rsrc_t a_r = make_rsrc(a.abuf, (uint32_t)(a.rows_a * a.width_a * 2));
+    uint32_t voff[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int r = (tid >> 4) + 16 * j;
-        aok |= (r < tr.count ? 1u : 0u) << j;
-        arow[j] = a.abuf + (int64_t)(tr.orow_base + (r < tr.count ? r : 0)) * a.width_a + col8;
+        int r, c;
+        stage_coords(j, &r, &c);
+        voff[j] = ((uint32_t)(tr.orow_base + min(r, tr.count - 1)) * (uint32_t)a.width_a + c * 8) * 2;
     }
-    const uint8_t* brow[4];
-    const uint16_t* srow[4];
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-        const int64_t r = h0 + 64 * wn + 16 * ns + ml;
-        brow[ns] = reinterpret_cast<const uint8_t*>(w2e) + r * row_bytes + q * kLaneBytes;
-        srow[ns] = s2e + r * G2;
-    }
+    const __amdgpu_buffer_rsrc_t b_r = make_rsrc(w2e, (uint32_t)(a.H * row_bytes));
+    const __amdgpu_buffer_rsrc_t s_r = make_rsrc(s2e, (uint32_t)(a.H * G2 * 2));
+    const uint32_t bvoff = (uint32_t)((h0 + 64 * wn + ml) * row_bytes + q * kLaneBytes);
+    const uint32_t svoff = (uint32_t)((h0 + 64 * wn + ml) * G2 * 2);
 
     f32x4_t acc[4][4];
 #pragma unroll
@@ -260,78 +294,42 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t stage[8];
-    auto load_stage = [&](int g) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            stage[j] = load16_or_zero(arow[j] + (int64_t)g * kGroup, aok >> j & 1u, arow[j]);
-    };
-    auto store_stage = [&](int buf) {
-        uint16_t* dst = s_a + buf * (MT * kRowPad);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x4_t*>(dst + ((tid >> 4) + 16 * j) * kRowPad + col8) = perm_act<BITS>(stage[j]);
-    };
     u32x4_t braw[4][BITS / 4];
+    uint32_t scp[2];
     auto load_b = [&](int g) {
+        uint32_t s16[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b) {
 #pragma unroll
             for (int c = 0; c < BITS / 4; ++c)
-                braw[b][c] = *reinterpret_cast<const u32x4_t*>(brow[b] + (int64_t)g * kGroupBytes + 16 * c);
+                braw[b][c] = buf_load16(b_r, bvoff, (uint32_t)(16 * b * row_bytes) + g * kGroupBytes + 16 * c);
+            s16[b] = buf_load_u16(s_r, svoff, (16 * b * G2 + g) * 2);
+        }
+        scp[0] = s16[0] | (s16[1] << 16);
+        scp[1] = s16[2] | (s16[3] << 16);
     };
 
-    load_stage(0);
+    stage_group(a_r, voff, 0, s_a);
     load_b(0);
-    store_stage(0);
-    __syncthreads();
     const u32x4_t neg = neg_offset_operand<BITS>();
 
     for (int g = 0; g < G2; ++g) {
         const int buf = g & 1;
-        float sc[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sc[b] = bf16_to_f32(srow[b][g]);
+        __syncthreads();
+        if (g + 1 < G2) stage_group(a_r, voff, (g + 1) * kGroup * 2, s_a + (buf ^ 1) * kTileElems);
         u32x4_t bcur[4][BITS / 4];
+        const uint32_t scg[2] = {scp[0], scp[1]};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int c = 0; c < BITS / 4; ++c) bcur[b][c] = braw[b][c];
-        if (g + 1 < G2) {
-            load_stage(g + 1);
-            load_b(g + 1);
-        }
-        const uint16_t* A = s_a + buf * (MT * kRowPad);
+        if (g + 1 < G2) load_b(g + 1);
+        mfma_group<BITS, true>(s_a + buf * kTileElems, wm, bcur, scg, acc, [&](int, const u32x4_t(&av)[4]) {
+            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r0 = 64 * wm + 16 * mi;
-            u32x4_t av[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[i] = *reinterpret_cast<const u32x4_t*>(A + (r0 + ml) * kRowPad + 32 * q + 8 * i);
-            f32x4_t seed = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) seed = mfma16(av[i], neg, seed);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                f32x4_t t = seed;
-                if constexpr (BITS == 4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) t = mfma16(av[i], dq4(bcur[b][0][i]), t);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t w0 = bcur[b][i >> 1][(2 * i) & 3], w1 = bcur[b][i >> 1][(2 * i + 1) & 3];
-                        t = mfma16(av[i], dq8_lo(w0, w1), t);
-                        t = mfma16(av[i], dq8_hi(w0, w1), t);
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mi][b][r] += sc[b] * t[r];
-            }
-        }
-        if (g + 1 < G2) store_stage(buf ^ 1);
-        __syncthreads();
+            for (int i = 0; i < 4; ++i) s0 = mfma16(av[i], neg, s0);
+            return s0;
+        });
     }
 
 #pragma unroll
@@ -340,11 +338,10 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
         for (int r = 0; r < 4; ++r) {
             const int m = 64 * wm + 16 * mi + 4 * q + r;
             if (m < tr.count) {
-                const int t = s_tok[m];
                 const float w = s_wt[m];
-                float* yrow = a.y32 + (int64_t)t * a.H + h0 + 64 * wn + ml;
+                float* yrow = a.y32 + (int64_t)s_tok[m] * a.H + h0 + 64 * wn + ml;
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns) unsafeAtomicAdd(yrow + 16 * ns, w * acc[mi][ns][r]);
+                for (int b = 0; b < 4; ++b) unsafeAtomicAdd(yrow + 16 * b, w * acc[mi][b][r]);
             }
         }
 }
@@ -363,7 +360,7 @@ __device__ __forceinline__ void for_each_item(int total, F&& f) {
 
 template <int BITS, int SBITS>
 __global__ __launch_bounds__(256, 2) void gk_prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * MT * kRowPad];
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTileElems];   // two staged groups
     __shared__ __attribute__((aligned(16))) float s_xs[2 * MT];
     __shared__ int s_tok[MT];
 
@@ -380,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void gk_prefill_kernel(PrefillArgs a) {
     for_each_item(total, [&](int L) {
         TileRows tr;
         int e, nblk;
-        if (!item_tile(a, L, nb, SBITS, 0, &tr, &e, &nblk)) return;
+        if (!item_tile(a, L, nb, SBITS, &tr, &e, &nblk)) return;
         const int n0 = nblk * kGkCols;
         if (tr.shared) {
             if constexpr (SBITS != 0)
@@ -396,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void gk_prefill_kernel(PrefillArgs a) {
 
 template <int BITS, int SBITS>
 __global__ __launch_bounds__(256, 2) void dk_prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * MT * kRowPad];
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTileElems];
     __shared__ int s_tok[MT];
     __shared__ float s_wt[MT];
     const int nb = (int)(a.H / kDkRows);
@@ -405,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void dk_prefill_kernel(PrefillArgs a) {
     for_each_item(total, [&](int L) {
         TileRows tr;
         int e, nblk;
-        if (!item_tile(a, L, nb, SBITS, 0, &tr, &e, &nblk)) return;
+        if (!item_tile(a, L, nb, SBITS, &tr, &e, &nblk)) return;
         const int h0 = nblk * kDkRows;
         if (tr.shared) {
             if constexpr (SBITS != 0) dk_item<SBITS>(a, tr, a.shared.I, a.shared.w2, a.shared.s2, h0, s_a, s_tok, s_wt);

@@ -259,8 +259,10 @@ __global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
         } else if (lane < k) {
             s_ids[tl * k + lane] = checked_id(a.ids + (int64_t)t * k, lane, E);
         }
-        // sums of the bf16 activations over each group of 128 columns (lane: 32 columns)
+        // sums of the bf16 activations over each group of 128 columns (lane: 32 columns),
+        // and the row copied with every 8-column block in the MFMA operand order
         const uint16_t* xr = a.x + (int64_t)t * a.H;
+        uint16_t* xpr = a.xp + (int64_t)t * a.H;
         for (int64_t c0 = 0; c0 < a.H; c0 += 64 * 32) {
             const int64_t c = c0 + lane * 32;
             float sum = 0.0f;
@@ -268,6 +270,7 @@ __global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const u32x4_t r = *reinterpret_cast<const u32x4_t*>(xr + c + 8 * i);
+                    *reinterpret_cast<u32x4_t*>(xpr + c + 8 * i) = perm_act(r);
 #pragma unroll
                     for (int h = 0; h < 4; ++h)
                         sum += __uint_as_float(r[h] << 16) + __uint_as_float(r[h] & 0xffff0000u);
