@@ -108,11 +108,10 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     distinct = [int(torch.topk(l, K, dim=1).indices.unique().numel()) for l in logits]
     n_copies = len(layers)
+    calls = [w4.MoeCall(xs[0], *lay, top_k=K, workspace=ws) for lay in layers]
 
     def step(i):
-        w13, s13, w2, s2 = layers[i % n_copies]
-        w4.moe_w4a16_forward(xs[i % 8], w13, s13, w2, s2, top_k=K, router_logits=logits[i % n_logits],
-                             out=out, workspace=ws)
+        calls[i % n_copies](xs[i % 8], out, router_logits=logits[i % n_logits])
 
     for i in range(warmup):
         step(i)
@@ -125,8 +124,25 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    ev_ms = start.elapsed_time(end)
-    ms_per_step = ev_ms / steps
+    eager_ms = start.elapsed_time(end) / steps
+
+    # the same steps replayed from a HIP graph (one graph holds a full rotation of n_logits
+    # steps), which removes host launch cost as a decode loop does in serving
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_logits):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // n_logits))
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end) / (reps * n_logits)
+    del graph
+    ms_per_step = graph_ms
 
     # per-kernel durations with HIP events around each kernel, same rotation
     per = {}
@@ -143,7 +159,7 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     weight_bytes = d_mean * (gu + dn)
     flops = 2.0 * T * K * 3 * H * I
     res = {
-        "T": T, "ms_per_step": ms_per_step, "wall_ms_per_step": wall_ms / steps,
+        "T": T, "ms_per_step": ms_per_step, "eager_ms_per_step": eager_ms, "eager_wall_ms_per_step": wall_ms / steps,
         "tok_per_s": T / (ms_per_step / 1e3),
         "distinct_experts_mean": d_mean,
         "expert_weight_bytes_per_step": weight_bytes,
@@ -157,7 +173,8 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     a_bytes = T * K * I * 2
     res["kernel_bytes"] = {"gate_up": d_mean * gu + act_in + a_bytes, "down": d_mean * dn + a_bytes + T * H * 2}
     res["kernel_flops"] = {"gate_up": 2.0 * T * K * 2 * I * H, "down": 2.0 * T * K * H * I}
-    log(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step, {res['tok_per_s']:.1f} tok/s, "
+    log(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step (graph; eager {eager_ms * 1e3:.1f}, host wall "
+        f"{wall_ms / steps * 1e3:.1f}), {res['tok_per_s']:.1f} tok/s, "
         f"{res['expert_weight_GBps']:.0f} GB/s expert weights, {res['TFLOPs']:.1f} TFLOP/s, kernels {res['kernels_us']}")
     del ws, out, logits, xs
     return res
@@ -179,6 +196,101 @@ def roofline_for(res, bound):
     return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
             "flops_per_launch": res["kernel_flops"][key], "us_per_launch": ks[name]}
+
+
+def make_stack_layers(n_layers, int8_layers, seed):
+    """Layers of the decode stack: routed experts (INT4, or INT8 on int8_layers) and one
+    INT8 shared expert (2048 -> 512 -> 2048) per layer, quantized on the GPU."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    out = []
+    chunk = 32
+    for l in range(n_layers):
+        bits = 8 if l in int8_layers else 4
+        w13 = torch.empty((E, 2 * I, H * bits // 32), dtype=torch.int32, device=dev)
+        s13 = torch.empty((E, 2 * I, H // 128), dtype=torch.bfloat16, device=dev)
+        w2 = torch.empty((E, H, I * bits // 32), dtype=torch.int32, device=dev)
+        s2 = torch.empty((E, H, I // 128), dtype=torch.bfloat16, device=dev)
+        base = seed * 100000 + l * 100
+        for e0 in range(0, E, chunk):
+            f13 = synth.device_normal((chunk, 2 * I, H), synth.WEIGHT_STD, base + e0 // chunk, dev)
+            w4.rtn_quantize_pack(f13, bits, packed=w13[e0:e0 + chunk], scales=s13[e0:e0 + chunk])
+            f2 = synth.device_normal((chunk, H, I), synth.WEIGHT_STD, base + 50 + e0 // chunk, dev)
+            w4.rtn_quantize_pack(f2, bits, packed=w2[e0:e0 + chunk], scales=s2[e0:e0 + chunk])
+            del f13, f2
+        sp13, ss13 = w4.rtn_quantize_pack(synth.device_normal((2 * I, H), synth.WEIGHT_STD, base + 98, dev), 8)
+        sp2, ss2 = w4.rtn_quantize_pack(synth.device_normal((H, I), synth.WEIGHT_STD, base + 99, dev), 8)
+        out.append(dict(bits=bits, w=(w13, s13, w2, s2), shared=dict(w13=sp13, s13=ss13, w2=sp2, s2=ss2, bits=8)))
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_stack(T, layers, steps, warmup, seed):
+    """A decode step through every layer of the stack: h <- h + routed(h) + shared(h)."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    n_logits = 8
+    L = len(layers)
+    logits = [[synth.device_normal((T, E), 1.0, seed * 7919 + 1000 * l + i, dev) for i in range(n_logits)]
+              for l in range(L)]
+    ws = torch.empty((w4.moe_w4a16_workspace_size(T, H, I, E, K, 8, I),), dtype=torch.uint8, device=dev)
+    h0 = synth.device_normal((T, H), 1.0, seed, dev, torch.bfloat16)
+    hb = [torch.empty_like(h0), torch.empty_like(h0)]
+    distinct = [[int(torch.topk(g, K, dim=1).indices.unique().numel()) for g in row] for row in logits]
+    calls = [w4.MoeCall(h0, *lay["w"], top_k=K, bits=lay["bits"], shared=lay["shared"], workspace=ws)
+             for lay in layers]
+
+    def step(i):
+        cur = h0
+        for l in range(L):
+            nxt = hb[l & 1]
+            calls[l](cur, nxt, router_logits=logits[l][i % n_logits], residual=cur)
+            cur = nxt
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        step(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    eager_ms = start.elapsed_time(end) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_logits):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // n_logits))
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (reps * n_logits)
+    del graph
+    nbytes = 0.0
+    for i in range(steps):
+        for l, lay in enumerate(layers):
+            gu, dn = expert_bytes(lay["bits"])
+            nbytes += distinct[l][(warmup + i) % n_logits] * (gu + dn) + sum(expert_bytes(8))
+    nbytes /= steps
+    res = {"T": T, "layers": L, "ms_per_step": ms, "eager_ms_per_step": eager_ms,
+           "eager_wall_ms_per_step": wall_ms / steps,
+           "tok_per_s": T / (ms / 1e3), "weight_bytes_per_step": nbytes,
+           "expert_weight_GBps": nbytes / (ms / 1e3) / 1e9}
+    log(f"[bench] stack{L}: {ms * 1e3:.1f} us/step (graph; eager {eager_ms * 1e3:.1f}), {res['tok_per_s']:.1f} tok/s, "
+        f"{res['expert_weight_GBps']:.0f} GB/s expert weights ({nbytes / 1e9:.2f} GB per step)")
+    del ws
+    return res
 
 
 def cpu_baseline(seconds):
@@ -227,7 +339,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=16, help="layer copies rotated through in decode runs")
-    ap.add_argument("--only", default="", help="comma list of decode1,decode32,prefill8192 (default all)")
+    ap.add_argument("--only", default="", help="comma list of decode1,decode32,prefill8192,stack40 (default all)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-quant", action="store_true")
@@ -243,7 +355,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w4._lib.lib()
-    only = set(args.only.split(",")) if args.only else {"decode1", "decode32", "prefill8192"}
+    only = set(args.only.split(",")) if args.only else {"decode1", "decode32", "prefill8192", "stack40"}
 
     log("[bench] building layers")
     layers = make_layers(args.copies, seed=1)
@@ -259,7 +371,27 @@ def main():
     quant = None if args.no_quant else time_quantizer()
     del layers
     torch.cuda.empty_cache()
+    stack = None
+    if "stack40" in only:
+        log("[bench] building the 40-layer stack")
+        stack_layers = make_stack_layers(40, (7, 13, 18, 23, 29, 35), seed=4)
+        stack = measure_stack(4, stack_layers, max(5, args.steps // 20), max(2, args.warmup // 5), 14)
+        del stack_layers
+        torch.cuda.empty_cache()
 
+    if not results:   # only the stack was asked for: it is the headline
+        line = {"metric": METRIC, "value": round(stack["tok_per_s"], 2), "unit": "tok/s", "n_gpus": 1,
+                "steps": max(5, args.steps // 20), "warmup": max(2, args.warmup // 5),
+                "ms_per_step": round(stack["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                "config": {"workload": "stack40: 40-layer decode stack, T=4", "global_batch": 4, "seq_len": 1,
+                           "parallelism": "none (1 GPU)"},
+                "expert_weight_GBps": round(stack["expert_weight_GBps"], 1),
+                "roofline": {"bound": "hbm", "kernel": "whole stack step", "achieved": round(stack["expert_weight_GBps"], 1),
+                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(stack["expert_weight_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}}
+        print(json.dumps(line), flush=True)
+        return
     head_name = "decode1" if "decode1" in results else next(iter(results))
     head = results[head_name]
     line = {
@@ -279,13 +411,27 @@ def main():
                                f"INT4 sym group-128 weights, bf16 activations, T={head['T']} tokens",
                    "global_batch": head["T"], "seq_len": 1, "parallelism": "none (1 GPU)"},
         "expert_weight_GBps": round(head["expert_weight_GBps"], 1),
+        "launch": "HIP graph replay of the timed steps (eager stream launches reported as eager_*)",
+        "eager_tok_per_s": round(head["T"] / head["eager_ms_per_step"] * 1e3, 2),
+        "eager_ms_per_step": round(head["eager_ms_per_step"], 5),
         "roofline": roofline_for(head, "mfma" if head_name == "prefill8192" else "hbm"),
     }
+    if stack is not None:
+        line["stack40"] = {"tok_per_s": round(stack["tok_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
+                           "eager_ms_per_step": round(stack["eager_ms_per_step"], 4),
+                           "expert_weight_GBps": round(stack["expert_weight_GBps"], 1),
+                           "weight_GB_per_step": round(stack["weight_bytes_per_step"] / 1e9, 3),
+                           "frac_hbm": round(stack["expert_weight_GBps"] / HBM_PEAK_GBPS, 4),
+                           "workload": "40 layers x (256 experts top-8, INT4; INT8 on layers 7,13,18,23,29,35) "
+                                       "+ INT8 shared expert per layer, bf16 residual, T=4"}
     for nm, r in results.items():
+        if r is None:
+            continue
         if nm == head_name:
             line["kernels_us"] = r["kernels_us"]
             continue
         line[nm] = {"tok_per_s": round(r["tok_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
+                    "eager_ms_per_step": round(r["eager_ms_per_step"], 5),
                     "expert_weight_GBps": round(r["expert_weight_GBps"], 1), "TFLOPs": round(r["TFLOPs"], 2),
                     "distinct_experts_mean": r["distinct_experts_mean"], "kernels_us": r["kernels_us"],
                     "roofline": roofline_for(r, "mfma" if nm == "prefill8192" else "hbm")}

@@ -1,0 +1,45 @@
+"""The forward call under HIP graph capture: replays, interleaved with eager work and
+synchronisations, must reproduce the eager result (bitwise on the small-batch path,
+which is deterministic; to fp32 summation order on the large-batch path)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import weight_only_int4_rtn_amd as w4
+from gpu_util import DEV, bf16_to_dev, f32_to_dev, gpu_layer, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_graph_replay_matches_eager(T):
+    say(f"graph replay T={T}")
+    E, H, I, k = 64, 512, 256, 8
+    w13, s13, w2, s2 = gpu_layer(21, 0, E, H, I, 4)
+    x = bf16_to_dev(synth.activations_bf16(70 + T, T, H))
+    logits = f32_to_dev(synth.router_logits(70 + T, T, E))
+    ws = torch.empty((w4.moe_w4a16_workspace_size(T, H, I, E, k),), dtype=torch.uint8, device=DEV)
+    call = w4.MoeCall(x, w13, s13, w2, s2, top_k=k, workspace=ws)
+    eager = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    call(x, eager, router_logits=logits)
+    torch.cuda.synchronize()
+
+    out = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(x, out, router_logits=logits)
+    ref = eager.float()
+    for rep in range(4):
+        out.zero_()
+        junk = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+        call(x, junk, router_logits=f32_to_dev(synth.router_logits(80 + rep, T, E)))   # eager work between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        if T <= 64:
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep} differs"
+        else:
+            d = (out.float() - ref).abs().max().item()
+            assert d <= 2 ** -7 * ref.abs().max().item(), (rep, d)

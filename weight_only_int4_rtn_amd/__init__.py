@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
 __all__ = ["rtn_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
-           "w4a16_abi_version", "W4A16Error", "library_path"]
+           "MoeCall", "w4a16_abi_version", "W4A16Error", "library_path"]
 
 GROUP = 128
 
@@ -200,3 +200,56 @@ def moe_w4a16_forward_timed(*args, **kwargs):
     timings = []
     res = moe_w4a16_forward(*args, _timed=timings, **kwargs)
     return res, timings
+
+
+class MoeCall:
+    """A prepared :func:`moe_w4a16_forward` for repeated calls with fixed shapes, weights
+    and workspace (a decode loop): everything is validated once here, and each call
+    only sets the per-call pointers (activations, logits, residual, output) before
+    calling the library.  Tensors passed per call must have the shapes, dtypes and
+    device given at construction.
+    """
+
+    def __init__(self, x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, shared=None, workspace=None,
+                 stream=None):
+        torch = _torch()
+        bf = _bf16_types()
+        _need(x, "x", bf)
+        dev = x.device
+        for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, bf), ("w2", w2, (torch.int32,)),
+                            ("s2", s2, bf)):
+            _need(t, name, dt, dev)
+        self.T, self.H = x.shape
+        self.E, self.top_k = w13.shape[0], top_k
+        sb = shared["bits"] if shared is not None else 0
+        sI = shared["w13"].shape[0] // 2 if shared is not None else 0
+        if shared is not None:
+            for name in ("w13", "s13", "w2", "s2"):
+                _need(shared[name], "shared." + name, (torch.int32,) if name[0] == "w" else bf, dev)
+        need = moe_w4a16_workspace_size(self.T, self.H, w13.shape[1] // 2, self.E, top_k, sb, sI)
+        if workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", (torch.uint8,), dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+        self._keep = (w13, s13, w2, s2, shared, workspace)
+        self.args = _args(x, w13, s13, w2, s2, top_k, bits, None, None, None, shared, None, None, None, None, None,
+                          workspace)
+        self.device = dev
+        self.stream = None if stream is None else _stream(dev, stream)   # None: the current stream per call
+        self._fn = _lib.lib().moe_w4a16_forward
+        self._ref = C.byref(self.args)
+
+    def __call__(self, x, out, router_logits=None, topk_ids=None, topk_w=None, residual=None):
+        a = self.args
+        a.x = x.data_ptr()
+        a.y = out.data_ptr()
+        a.router_logits = None if router_logits is None else router_logits.data_ptr()
+        a.topk_ids = None if topk_ids is None else topk_ids.data_ptr()
+        a.topk_w = None if topk_w is None else topk_w.data_ptr()
+        a.residual = None if residual is None else residual.data_ptr()
+        st = self._fn(self._ref, self.stream if self.stream is not None else
+                      C.c_void_p(_torch().cuda.current_stream(self.device).cuda_stream))
+        if st:
+            _lib.check(st, "moe_w4a16_forward")
+        return out
