@@ -180,22 +180,75 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     return res
 
 
-def roofline_for(res, bound):
+KERNEL_SOURCES = {"gk_decode": "moe_decode.hip", "dk_decode": "moe_decode.hip",
+                  "gk_prefill": "moe_prefill.hip", "dk_prefill": "moe_prefill.hip"}
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.txt")
+
+
+def kernel_source_digest(kernel):
+    """Digest of the sources a kernel is built from (its .hip file and the shared header)."""
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_int4_rtn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter runs, each
+    divided by what the same counter read per byte of a plain copy kernel.  None when no
+    record exists or the kernel's sources changed since the counters were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        if not ln.startswith("kernel="):
+            continue
+        f = dict(kv.split("=", 1) for kv in ln.split())
+        if f.get("kernel") != kernel or f.get("workload") != workload:
+            continue
+        if f.get("sha") != kernel_source_digest(kernel):
+            return None
+        return int(float(f["fetch_kib"]) * 1024 / float(f["fetch_factor"]) +
+                   float(f["write_kib"]) * 1024 / float(f["write_factor"]))
+    return None
+
+
+def copy_calibration():
+    """A plain copy kernel of known size (fp32 out = in * 1, 512 MiB each way) for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: run under the same counter collection as the bench."""
+    import torch
+    n = 128 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: MulFunctor kernel, {n * 4} bytes read and {n * 4} bytes written per launch")
+    del src, dst
+
+
+def roofline_for(res, bound, workload):
     """Roofline object of the dominant (longest) expert kernel of a measurement."""
     ks = res["kernels_us"]
     gk = next(k for k in ks if k.startswith("gk_"))
     dk = next(k for k in ks if k.startswith("dk_") and k != "dk_combine")
     name, key = (gk, "gate_up") if ks[gk] >= ks[dk] else (dk, "down")
     sec = ks[name] / 1e6
+    traffic = measured_traffic(name, workload)
     if bound == "hbm":
         achieved = res["kernel_bytes"][key] / sec / 1e9
         return {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "bytes_per_launch": int(res["kernel_bytes"][key]), "us_per_launch": ks[name]}
     achieved = res["kernel_flops"][key] / sec / 1e12
     return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "flops_per_launch": res["kernel_flops"][key], "us_per_launch": ks[name]}
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "flops_per_launch": res["kernel_flops"][key], "bytes_per_launch": int(res["kernel_bytes"][key]),
+            "us_per_launch": ks[name]}
 
 
 def make_stack_layers(n_layers, int8_layers, seed):
@@ -343,6 +396,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-quant", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain copy kernel of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -357,6 +412,8 @@ def main():
     w4._lib.lib()
     only = set(args.only.split(",")) if args.only else {"decode1", "decode32", "prefill8192", "stack40"}
 
+    if args.copy_calibration:
+        copy_calibration()
     log("[bench] building layers")
     layers = make_layers(args.copies, seed=1)
     results = {}
@@ -414,7 +471,7 @@ def main():
         "launch": "HIP graph replay of the timed steps (eager stream launches reported as eager_*)",
         "eager_tok_per_s": round(head["T"] / head["eager_ms_per_step"] * 1e3, 2),
         "eager_ms_per_step": round(head["eager_ms_per_step"], 5),
-        "roofline": roofline_for(head, "mfma" if head_name == "prefill8192" else "hbm"),
+        "roofline": roofline_for(head, "mfma" if head_name == "prefill8192" else "hbm", head_name),
     }
     if stack is not None:
         line["stack40"] = {"tok_per_s": round(stack["tok_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
@@ -434,7 +491,7 @@ def main():
                     "eager_ms_per_step": round(r["eager_ms_per_step"], 5),
                     "expert_weight_GBps": round(r["expert_weight_GBps"], 1), "TFLOPs": round(r["TFLOPs"], 2),
                     "distinct_experts_mean": r["distinct_experts_mean"], "kernels_us": r["kernels_us"],
-                    "roofline": roofline_for(r, "mfma" if nm == "prefill8192" else "hbm")}
+                    "roofline": roofline_for(r, "mfma" if nm == "prefill8192" else "hbm", nm)}
     if quant:
         line["quantize"] = quant
     if not args.no_cpu:

@@ -156,11 +156,13 @@ size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
 int moe_w4a16_forward(const moe_w4a16_args* args, void* stream);
 
 /*
- * moe_w4a16_forward_timed - the same work as moe_w4a16_forward, with a HIP event recorded
- * on `stream` before the first kernel and after each kernel, then a wait for the last
- * event (this call synchronises with the stream's work up to that point).
- *   kernel_ms     out, [max_kernels]: elapsed time of each kernel in launch order, in ms
- *                 (the interval between consecutive events)
+ * moe_w4a16_forward_timed - the same work as moe_w4a16_forward, each kernel launched with
+ * a start and a stop HIP event bound to its own dispatch (hipExtLaunchKernelGGL), then a
+ * wait for the last stop event (this call synchronises with the stream's work up to that
+ * point).
+ *   kernel_ms     out, [max_kernels]: execution time of each kernel in launch order, in ms
+ *                 (start to stop event of that dispatch; the gap between dispatches is
+ *                 not counted)
  *   kernel_names  out, [max_kernels]: static name of each kernel (owned by the library)
  *   n_kernels     out: number of entries written (<= max_kernels)
  * A profiling aid for per-kernel roofline measurements; the output y is identical.

@@ -130,10 +130,6 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     char* ws = static_cast<char*>(a->workspace);
     auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (timer) {
-        timer->stream = s;
-        if (int st = hip_status(hipEventRecord(timer->ev[0], s), "hipEventRecord")) return st;
-    }
 
     RouteArgs r{};
     r.logits = a->router_logits;
@@ -276,19 +272,28 @@ int moe_w4a16_forward_timed(const moe_w4a16_args* a, void* stream, int max_kerne
     *n_kernels = 0;
     StageTimer t{};
     int created = 0, st = W4A16_OK;
-    for (; created <= kMaxStages; ++created)
-        if ((st = hip_status(hipEventCreate(&t.ev[created]), "hipEventCreate"))) break;
+    for (; created < kMaxStages; ++created) {
+        if ((st = hip_status(hipEventCreate(&t.beg[created]), "hipEventCreate"))) break;
+        if ((st = hip_status(hipEventCreate(&t.end[created]), "hipEventCreate"))) {
+            (void)hipEventDestroy(t.beg[created]);
+            break;
+        }
+    }
     if (!st) st = forward_impl(a, stream, &t);
-    if (!st && t.n > 0) st = hip_status(hipEventSynchronize(t.ev[t.n]), "hipEventSynchronize");
+    if (!st && t.n > 0) st = hip_status(hipEventSynchronize(t.end[t.n - 1]), "hipEventSynchronize");
     if (!st) {
         const int n = std::min(t.n, max_kernels);
         for (int i = 0; i < n && !st; ++i) {
             kernel_names[i] = t.name[i];
-            st = hip_status(hipEventElapsedTime(&kernel_ms[i], t.ev[i], t.ev[i + 1]), "hipEventElapsedTime");
+            st = hip_status(hipEventSynchronize(t.end[i]), "hipEventSynchronize");
+            if (!st) st = hip_status(hipEventElapsedTime(&kernel_ms[i], t.beg[i], t.end[i]), "hipEventElapsedTime");
         }
         if (!st) *n_kernels = n;
     }
-    for (int i = 0; i < created; ++i) (void)hipEventDestroy(t.ev[i]);
+    for (int i = 0; i < created; ++i) {
+        (void)hipEventDestroy(t.beg[i]);
+        (void)hipEventDestroy(t.end[i]);
+    }
     return st;
 }
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 
 #include <algorithm>
@@ -149,20 +150,25 @@ constexpr int kPrefillMT = 128;  // tokens per M-tile of the large-batch grouped
 
 // ------------------------------------------------------------- stage timer
 
-// Optional per-kernel timing: a launcher calls mark(t, name) right after each kernel it
-// enqueues; with t != nullptr an event is recorded on the stream at that point.
+// Optional per-kernel timing.  Launchers enqueue every kernel through launch(); with a
+// timer, the kernel goes out by hipExtLaunchKernelGGL with a start and a stop event bound
+// to its own dispatch, so the elapsed time between them is the kernel's execution (no
+// marker packets between kernels, no dispatch gap counted).
 constexpr int kMaxStages = 16;
 struct StageTimer {
-    hipStream_t stream;
-    hipEvent_t ev[kMaxStages + 1];
+    hipEvent_t beg[kMaxStages], end[kMaxStages];
     const char* name[kMaxStages];
     int n;
 };
-inline void mark(StageTimer* t, const char* name) {
+
+template <typename... KArgs, typename... Args>
+inline void launch(StageTimer* t, const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                   hipStream_t s, Args... args) {
     if (t && t->n < kMaxStages) {
-        t->name[t->n] = name;
-        (void)hipEventRecord(t->ev[t->n + 1], t->stream);
-        ++t->n;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t->beg[t->n], t->end[t->n], 0, args...);
+        t->name[t->n++] = name;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
     }
 }
 

@@ -369,15 +369,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
     const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
     const dim3 gk_grid((unsigned)(Imax / 16), (unsigned)(max_active + (SBITS ? 1 : 0)));
-    gk_decode_kernel<BITS, SBITS><<<gk_grid, 64 * kGkWaves, 0, s>>>(a);
-    mark(t, "gk_decode");
+    launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, a);
     const dim3 dk_grid((unsigned)(a.H / 16), (unsigned)a.splits);
-    dk_decode_kernel<BITS, SBITS><<<dk_grid, 64 * kDkWaves, 0, s>>>(a);
-    mark(t, "dk_decode");
+    launch(t, "dk_decode", dk_decode_kernel<BITS, SBITS>, dk_grid, dim3(64 * kDkWaves), s, a);
     if (a.splits > 1) {
         const int64_t n = (int64_t)a.T * a.H;
-        dk_combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.part, a.splits, n, a.residual, a.y);
-        mark(t, "dk_combine");
+        launch(t, "dk_combine", dk_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s,
+               (const float*)a.part, a.splits, n, a.residual, a.y);
     }
     return hipGetLastError();
 }
