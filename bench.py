@@ -104,7 +104,7 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     n_logits = 64
     logits = [synth.device_normal((T, E), 1.0, seed * 7919 + i, dev) for i in range(n_logits)]
     xs = [synth.device_normal((T, H), 1.0, seed * 104729 + i, dev, torch.bfloat16) for i in range(8)]
-    ws = torch.empty((w4.moe_w4a16_workspace_size(T, H, I, E, K),), dtype=torch.uint8, device=dev)
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, K), dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     distinct = [int(torch.topk(l, K, dim=1).indices.unique().numel()) for l in logits]
     n_copies = len(layers)
@@ -172,7 +172,9 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     act_in = T * H * 2
     a_bytes = T * K * I * 2
     res["kernel_bytes"] = {"gate_up": d_mean * gu + act_in + a_bytes, "down": d_mean * dn + a_bytes + T * H * 2}
+    res["kernel_bytes"]["all"] = d_mean * (gu + dn) + act_in + T * E * 4 + T * H * 2
     res["kernel_flops"] = {"gate_up": 2.0 * T * K * 2 * I * H, "down": 2.0 * T * K * H * I}
+    res["kernel_flops"]["all"] = res["kernel_flops"]["gate_up"] + res["kernel_flops"]["down"]
     log(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step (graph; eager {eager_ms * 1e3:.1f}, host wall "
         f"{wall_ms / steps * 1e3:.1f}), {res['tok_per_s']:.1f} tok/s, "
         f"{res['expert_weight_GBps']:.0f} GB/s expert weights, {res['TFLOPs']:.1f} TFLOP/s, kernels {res['kernels_us']}")
@@ -180,17 +182,17 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     return res
 
 
-KERNEL_SOURCES = {"gk_decode": "moe_decode.hip", "dk_decode": "moe_decode.hip",
+KERNEL_SOURCES = {"tiny_decode": "moe_decode.hip", "gk_decode": "moe_decode.hip", "dk_decode": "moe_decode.hip",
                   "gk_prefill": "moe_prefill.hip", "dk_prefill": "moe_prefill.hip"}
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.txt")
 
 
 def kernel_source_digest(kernel):
-    """Digest of the sources a kernel is built from (its .hip file and the shared header)."""
+    """Digest of the sources a kernel is built from (its .hip file and the shared headers)."""
     import hashlib
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_int4_rtn_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "common.h"):
+    for f in (KERNEL_SOURCES[kernel], "common.h", "route_dev.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -234,9 +236,12 @@ def copy_calibration():
 def roofline_for(res, bound, workload):
     """Roofline object of the dominant (longest) expert kernel of a measurement."""
     ks = res["kernels_us"]
-    gk = next(k for k in ks if k.startswith("gk_"))
-    dk = next(k for k in ks if k.startswith("dk_") and k != "dk_combine")
-    name, key = (gk, "gate_up") if ks[gk] >= ks[dk] else (dk, "down")
+    if "tiny_decode" in ks:   # one launch does the whole layer: its bytes are every expert kernel's
+        name, key = "tiny_decode", "all"
+    else:
+        gk = next(k for k in ks if k.startswith("gk_"))
+        dk = next(k for k in ks if k.startswith("dk_") and k != "dk_combine")
+        name, key = (gk, "gate_up") if ks[gk] >= ks[dk] else (dk, "down")
     sec = ks[name] / 1e6
     traffic = measured_traffic(name, workload)
     if bound == "hbm":
@@ -290,7 +295,7 @@ def measure_stack(T, layers, steps, warmup, seed):
     L = len(layers)
     logits = [[synth.device_normal((T, E), 1.0, seed * 7919 + 1000 * l + i, dev) for i in range(n_logits)]
               for l in range(L)]
-    ws = torch.empty((w4.moe_w4a16_workspace_size(T, H, I, E, K, 8, I),), dtype=torch.uint8, device=dev)
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, K, 8, I), dev)
     h0 = synth.device_normal((T, H), 1.0, seed, dev, torch.bfloat16)
     hb = [torch.empty_like(h0), torch.empty_like(h0)]
     distinct = [[int(torch.topk(g, K, dim=1).indices.unique().numel()) for g in row] for row in logits]

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -139,7 +139,10 @@ typedef struct moe_w4a16_args {
     int32_t* expert_offsets;       /* optional out, int32 [E+1]: exclusive prefix of counts */
     int32_t* sorted_pairs;         /* optional out, int32 [T*top_k]: pair ids t*top_k+j by   */
                                    /* (expert, token) ascending                              */
-    void* workspace;               /* device scratch, >= moe_w4a16_workspace_size(args)     */
+    void* workspace;               /* device scratch, >= moe_w4a16_workspace_size(args);    */
+                                   /* its first 16 KiB must be zero before the first call   */
+                                   /* (moe_w4a16_workspace_init) and stay owned by the      */
+                                   /* library: every forward leaves them zero               */
     size_t workspace_bytes;
 } moe_w4a16_args;
 
@@ -148,10 +151,23 @@ typedef struct moe_w4a16_args {
 size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
 
 /*
+ * moe_w4a16_workspace_init - zero the head of a new workspace (its first 16 KiB), once,
+ * before the workspace's first forward.  The head holds the counters that the
+ * single-launch path for tiny batches (T * top_k <= 16, H <= 4096) uses to hand the
+ * gate/up results to the down projection inside one kernel; each forward returns them
+ * to zero, so a workspace needs this once, not per call (a zero-filled allocation needs
+ * none).  Enqueued on `stream` as a small fill kernel (no memset node, so it may be
+ * captured in a graph).  Errors: W4A16_ERR_INVALID_ARG for NULL or a misaligned pointer,
+ * W4A16_ERR_WORKSPACE when workspace_bytes < 16 KiB.
+ */
+int moe_w4a16_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_w4a16_forward - routing, fused dequant gate/up + SiLU(gate)*up, fused dequant down
  * projection and router-weighted un-permute, enqueued on `stream`.
  * The result for small batches (T <= 64) is bitwise deterministic; for larger batches
  * the fp32 sum over a token's experts may be formed in any order (device atomics).
+ * Two forwards must not use one workspace at the same time (on different streams).
  */
 int moe_w4a16_forward(const moe_w4a16_args* args, void* stream);
 

@@ -47,7 +47,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 1
+    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 2
     assert _lib.status_string(0) == "W4A16_OK"
     assert _lib.status_string(3) == "W4A16_ERR_WORKSPACE"
     assert _lib.status_string(99) == "W4A16_UNKNOWN_STATUS"
@@ -130,6 +130,14 @@ def test_forward_zero_tokens_is_a_noop(L):
     for f in ("x", "router_logits", "w13", "s13", "w2", "s2", "y"):
         setattr(a, f, None)
     assert forward_status(L, a) == _lib.W4A16_OK
+
+
+def test_workspace_init_validation(L):
+    """Rejections happen on the host; nothing is enqueued (no GPU here)."""
+    assert L.moe_w4a16_workspace_init(None, 1 << 20, None) == _lib.W4A16_ERR_INVALID_ARG
+    assert L.moe_w4a16_workspace_init(C.c_void_p(MISALIGNED), 1 << 20, None) == _lib.W4A16_ERR_INVALID_ARG
+    assert L.moe_w4a16_workspace_init(C.c_void_p(FAKE), 16383, None) == _lib.W4A16_ERR_WORKSPACE
+    assert "16" in _lib.last_error()
 
 
 def test_workspace_size(L):

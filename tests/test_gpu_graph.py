@@ -20,7 +20,7 @@ def test_graph_replay_matches_eager(T):
     w13, s13, w2, s2 = gpu_layer(21, 0, E, H, I, 4)
     x = bf16_to_dev(synth.activations_bf16(70 + T, T, H))
     logits = f32_to_dev(synth.router_logits(70 + T, T, E))
-    ws = torch.empty((w4.moe_w4a16_workspace_size(T, H, I, E, k),), dtype=torch.uint8, device=DEV)
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, k), DEV)
     call = w4.MoeCall(x, w13, s13, w2, s2, top_k=k, workspace=ws)
     eager = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     call(x, eager, router_logits=logits)

@@ -124,6 +124,26 @@ def test_route_bitexact(T, E, k):
     assert np.all(bf16_from_dev(y) == 0)        # zero weights give zero output
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (8, 256, 8), (33, 256, 8), (200, 256, 8), (6, 512, 8),
+                                   (70, 1024, 16), (3, 20, 5)])
+def test_route_heavy_ties_bitexact(T, E, k):
+    """Logits drawn from a handful of values (including -0.0, +0.0 and -inf), so most
+    top-k choices are decided by the lower-index rule."""
+    say(f"route heavy ties T={T} E={E} k={k}")
+    rng = np.random.default_rng(1000 + T * 7 + E)
+    vals = np.array([1.5, 0.75, 0.0, -0.0, -0.5, -np.inf], dtype=np.float32)
+    logits = vals[rng.integers(0, len(vals), size=(T, E))]
+    logits[0, :k + 3] = 0.0          # the first token: a tie of more than k values
+    logits[0, 1] = -0.0
+    y, r = _run_route(logits, k, E)
+    ids, w, counts, offsets, pairs = oracle.route(logits, k)
+    assert np.array_equal(r["ids"], ids)
+    assert np.array_equal(r["counts"], counts)
+    assert np.array_equal(r["offsets"], offsets)
+    assert np.array_equal(r["sorted_pairs"], pairs)
+    assert np.abs(r["w"] - w).max() <= 1e-6
+
+
 @pytest.mark.parametrize("T", [3, 100])
 def test_route_from_given_ids(T):
     say(f"route from given ids T={T}")

@@ -15,6 +15,7 @@ from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
 __all__ = ["rtn_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
+           "moe_w4a16_workspace_init", "new_workspace",
            "MoeCall", "w4a16_abi_version", "W4A16Error", "library_path"]
 
 GROUP = 128
@@ -124,6 +125,23 @@ def moe_w4a16_workspace_size(T: int, H: int, I: int, E: int, top_k: int, shared_
     return n
 
 
+def moe_w4a16_workspace_init(workspace, stream=None):
+    """Zero the head of a workspace (once, before its first forward; a zero-filled
+    allocation needs nothing).  ``workspace`` is a uint8 device tensor."""
+    torch = _torch()
+    _need(workspace, "workspace", (torch.uint8,))
+    st = _lib.lib().moe_w4a16_workspace_init(C.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                             _stream(workspace.device, stream))
+    _lib.check(st, "moe_w4a16_workspace_init")
+    return workspace
+
+
+def new_workspace(nbytes: int, device):
+    """A device workspace of ``nbytes`` bytes ready for :func:`moe_w4a16_forward`."""
+    torch = _torch()
+    return moe_w4a16_workspace_init(torch.empty((max(int(nbytes), 16384),), dtype=torch.uint8, device=device))
+
+
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,
                       topk_ids=None, topk_w=None, shared=None, residual=None, out=None, workspace=None,
                       routing_out: bool = False, stream=None, _timed=None):
@@ -178,7 +196,7 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
         sb = shared["bits"] if shared is not None else 0
         sI = shared["w13"].shape[0] // 2 if shared is not None else 0
         n = moe_w4a16_workspace_size(T, H, I, E, top_k, sb, sI) if T > 0 else 0
-        workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros((max(n, 1),), dtype=torch.uint8, device=dev)   # zero head: see workspace_init
     a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
               counts, offsets, sorted_pairs, workspace)
     if _timed is None:
@@ -228,7 +246,7 @@ class MoeCall:
                 _need(shared[name], "shared." + name, (torch.int32,) if name[0] == "w" else bf, dev)
         need = moe_w4a16_workspace_size(self.T, self.H, w13.shape[1] // 2, self.E, top_k, sb, sI)
         if workspace is None:
-            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+            workspace = new_workspace(need, dev)
         _need(workspace, "workspace", (torch.uint8,), dev)
         if workspace.numel() < need:
             raise ValueError(f"workspace needs {need} bytes")

@@ -12,7 +12,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 W4A16_OK = 0
 W4A16_ERR_INVALID_ARG = 1
@@ -29,6 +29,7 @@ EXPORTED = (
     "w4a16_last_error",
     "rtn_quantize_pack",
     "moe_w4a16_workspace_size",
+    "moe_w4a16_workspace_init",
     "moe_w4a16_forward",
     "moe_w4a16_forward_timed",
 )
@@ -82,6 +83,8 @@ def lib():
                                     C.c_void_p, C.c_void_p, C.c_void_p]
     L.moe_w4a16_workspace_size.restype = C.c_size_t
     L.moe_w4a16_workspace_size.argtypes = [C.POINTER(MoeArgs)]
+    L.moe_w4a16_workspace_init.restype = C.c_int
+    L.moe_w4a16_workspace_init.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p]
     L.moe_w4a16_forward.restype = C.c_int
     L.moe_w4a16_forward.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
     L.moe_w4a16_forward_timed.restype = C.c_int

@@ -108,6 +108,12 @@ __device__ __forceinline__ u32x4_t load16_or_zero(const void* p, bool ok, const 
     return u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
 }
 
+// 16 bytes of a weight stream that is read once: a non-temporal load, so the streamed
+// codes do not push reusable lines (activations, routing data, kernel code) out of L2.
+__device__ __forceinline__ u32x4_t load_stream16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 // Raw buffer resource over `bytes` bytes at p (gfx9-family descriptor word 3).  Buffer
 // loads take a per-lane 32-bit offset plus a scalar offset, so loop-varying parts of an
 // address cost no vector instructions; reads past `bytes` return zero.
@@ -120,6 +126,11 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
 }
+
+// Cache-policy operand of buffer loads and stores: sc1 = device-coherent access (a store
+// writes through to memory, a load reads past the XCD's L2), for data exchanged between
+// workgroups of one launch.
+constexpr int kSc1 = 16;
 
 // bf16 pair of -OFF (see above): -136 = 0xC308, -2304 = 0xC510.
 template <int BITS>
@@ -134,8 +145,17 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g * __built
 
 // ------------------------------------------------------------ workspace layout
 
+// Head of every workspace: counters of the single-launch tiny-batch path.  They must be
+// zero before a workspace's first use (moe_w4a16_workspace_init) and every forward leaves
+// them zero.  One counter per 128-byte line (index * 32 words): [0, 64) routed expert
+// slots, 64 the shared expert, [80, 96) down-workgroup groups, 100 the group total,
+// 101 a sticky error word (a wait that timed out).
+constexpr size_t kSyncBytes = 16384;
+constexpr int kSyncShared = 64, kSyncGroup = 80, kSyncTop = 100, kSyncError = 101;
+__device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return sync + i * 32; }
+
 struct WsLayout {
-    size_t ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
+    size_t sync, ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
         y32, tokw, rec, xp, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
@@ -145,6 +165,8 @@ struct WsLayout {
 };
 
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
+constexpr int kTinyP = 16;       // T * k up to this (and H <= kTinyMaxH) take the single-launch path
+constexpr int kTinyMaxH = 4096;
 constexpr int kRouteBlockT = 64; // tokens per routing block on the large-batch path
 constexpr int kPrefillMT = 128;  // tokens per M-tile of the large-batch grouped GEMM
 
@@ -163,12 +185,12 @@ struct StageTimer {
 
 template <typename... KArgs, typename... Args>
 inline void launch(StageTimer* t, const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
-                   hipStream_t s, Args... args) {
+                   hipStream_t s, uint32_t shmem, Args... args) {
     if (t && t->n < kMaxStages) {
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t->beg[t->n], t->end[t->n], 0, args...);
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, t->beg[t->n], t->end[t->n], 0, args...);
         t->name[t->n++] = name;
     } else {
-        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
     }
 }
 
@@ -235,6 +257,35 @@ struct DecodeArgs {
     uint16_t* y;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
+
+// Single-launch path for tiny batches (T * k <= kTinyP): every workgroup routes the batch
+// itself; workgroups [0, n_gk) compute gate/up row blocks and count each finished block
+// on its expert slot's counter; the others compute 16 output rows of the down projection
+// once every active slot is complete.
+struct TinyArgs {
+    const uint16_t* x;
+    int T, E, k;
+    int64_t H;
+    ExpertSet routed, shared;
+    const float* logits;        // NULL: ids / wts are inputs
+    int32_t* ids;               // [T, k]
+    float* wts;                 // [T, k]
+    int32_t* counts;            // [E] out
+    int32_t* offsets;           // [E + 1] out
+    int32_t* sorted;            // [T * k] out
+    uint16_t* abuf;             // [rows_a, width_a]
+    int64_t width_a;
+    uint32_t abuf_bytes;
+    uint32_t* sync;             // workspace head (kSyncBytes), zero on entry and exit
+    const uint16_t* residual;
+    uint16_t* y;
+    int n_gk;                   // gate/up workgroups: (slots + shared) * n_rb
+    int n_rb;                   // 16-row blocks per slot: max(I, shared I) / 16
+    int stage_a;                // down workgroups stage every a row in LDS first
+    uint32_t lds_bytes;         // dynamic LDS per workgroup
+};
+hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t = nullptr);
+hipError_t launch_sync_init(uint32_t* sync, hipStream_t s);
 
 struct PrefillArgs {
     const uint16_t* x;

@@ -15,13 +15,14 @@
 //   w[t,j] * (W2_e a) per token in LDS.  Waves, then splits, are summed in a fixed
 //   order, so the result is bitwise reproducible.
 #include "common.h"
+#include "route_dev.h"
 
 namespace w4a16 {
 
 constexpr int kGkWaves = 8;   // waves per gate/up workgroup (K split 8 ways)
-constexpr int kGkPass = 2;    // groups per wave per pass
+constexpr int kGkPass4 = 2;   // groups per wave per pass (INT4; INT8 codes take twice the registers: 1)
 constexpr int kDkWaves = 8;   // waves per down workgroup
-constexpr int kDkChunk = 2;   // groups of K per down work unit
+constexpr int kDkChunk = 2;   // groups of K per down work unit (group_dot2 assumes 2)
 
 namespace {
 
@@ -63,15 +64,39 @@ __device__ __forceinline__ f32x4_t offset_seed(const u32x4_t (&av)[4]) {
     return c;
 }
 
+// Two groups at once (two independent MFMA chains, interleaved), each started from `t`.
+template <int BITS>
+__device__ __forceinline__ void group_dot2(const u32x4_t (&av)[kDkChunk][4], const u32x4_t (&bw)[kDkChunk][2],
+                                           f32x4_t (&t)[kDkChunk]) {
+    const uint32_t M = nibble_mask();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < kDkChunk; ++j) {
+            if constexpr (BITS == 4) {
+                t[j] = mfma16(av[j][i], dq4(bw[j][0][i], M), t[j]);
+            } else {
+                u32x4_t lo, hi;
+                dq8(bw[j][i >> 1][(2 * i) & 3], bw[j][i >> 1][(2 * i + 1) & 3], lo, hi, M);
+                t[j] = mfma16(av[j][i], lo, t[j]);
+                t[j] = mfma16(av[j][i], hi, t[j]);
+            }
+        }
+}
+
+// The code offset OFF of a BITS-wide code (see neg_offset_operand).
+template <int BITS>
+constexpr float code_offset() { return BITS == 4 ? 136.f : 2304.f; }
+
 // Gate/up of one M-tile (this lane's activation row: token `tok`, zero when !xok) against rows n0..n0+15 of the
 // gate half and the same rows of the up half of one expert's [2I, H] bank.  The 8 waves
 // split K: wave w takes groups w, w+8, ...; two groups per pass, every load of a pass
 // issued before its MFMAs.  (Two groups keep the activation operand, which is K/8
 // registers per lane however few tokens there are, at 32 registers.)
-template <int BITS>
+template <int BITS, bool WT = false>
 __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, const int32_t* __restrict__ w13e,
                         const uint16_t* __restrict__ s13e, int n0, int tok, bool xok, int row_base, int rows,
-                        uint16_t* __restrict__ abuf, int64_t width_a, float* s_red) {
+                        uint16_t* __restrict__ abuf, int64_t width_a, float* s_red, uint32_t abuf_bytes = 0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int G = (int)(H / kGroup);
@@ -85,6 +110,7 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
     const uint16_t* xr = x + (int64_t)tok * H + 32 * q;   // tok is a real token even when !xok
 
     f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kGkPass = BITS == 4 ? kGkPass4 : 1;
     for (int gb = wave; gb < G; gb += kGkWaves * kGkPass) {
         u32x4_t bg[kGkPass][BITS / 4], bu[kGkPass][BITS / 4], av[kGkPass][4];
         float scg[kGkPass], scu[kGkPass];
@@ -94,8 +120,8 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
             if (g < G) {
 #pragma unroll
                 for (int c = 0; c < BITS / 4; ++c) {
-                    bg[j][c] = *reinterpret_cast<const u32x4_t*>(wg + (int64_t)g * kGroupBytes + 16 * c);
-                    bu[j][c] = *reinterpret_cast<const u32x4_t*>(wu + (int64_t)g * kGroupBytes + 16 * c);
+                    bg[j][c] = load_stream16(wg + (int64_t)g * kGroupBytes + 16 * c);
+                    bu[j][c] = load_stream16(wu + (int64_t)g * kGroupBytes + 16 * c);
                 }
                 scg[j] = bf16_to_f32(sg[g]);
                 scu[j] = bf16_to_f32(su[g]);
@@ -132,7 +158,15 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
             us += s_red[(w * 8 + 4 + r) * 64 + lane];
         }
         const int m = 4 * q + r;
-        if (m < rows) abuf[(int64_t)(row_base + m) * width_a + n0 + ml] = (uint16_t)f32_to_bf16(silu_mul(gs, us));
+        const int64_t idx = (int64_t)(row_base + m) * width_a + n0 + ml;
+        const uint32_t v = f32_to_bf16(silu_mul(gs, us));
+        if constexpr (WT) {   // write-through to memory (sc1): another XCD reads it in this launch
+            if (m < rows)
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, make_rsrc(abuf, abuf_bytes),
+                                                      (uint32_t)(idx * 2), 0, kSc1);
+        } else {
+            if (m < rows) abuf[idx] = (uint16_t)v;
+        }
     }
     __syncthreads();
 }
@@ -187,74 +221,94 @@ struct DkUnit {
     const uint16_t* srow;   // scales of row h0 + ml at the chunk's first group
     int pos0, count, ngroups, col0;
     bool shared;
+    float sc[kDkChunk];     // the chunk's group scales, loaded with the codes
 };
 
+// Issues the unit's code and scale loads (nothing waits for them here).
 template <int BITS>
-__device__ __forceinline__ void dk_load_codes(const DkUnit& u, u32x4_t (&bw)[kDkChunk][2]) {
+__device__ __forceinline__ void dk_load_codes(DkUnit& u, u32x4_t (&bw)[kDkChunk][2]) {
     constexpr int kGroupBytes = kGroup * BITS / 8;
 #pragma unroll
     for (int j = 0; j < kDkChunk; ++j)
-        if (j < u.ngroups)
+        if (j < u.ngroups) {
 #pragma unroll
             for (int c = 0; c < BITS / 4; ++c)
-                bw[j][c] = *reinterpret_cast<const u32x4_t*>(u.wrow + (int64_t)j * kGroupBytes + 16 * c);
+                bw[j][c] = load_stream16(u.wrow + (int64_t)j * kGroupBytes + 16 * c);
+            u.sc[j] = bf16_to_f32(u.srow[j]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) bw[j][c] = u32x4_t{0u, 0u, 0u, 0u};
+            u.sc[j] = 0.f;
+        }
 }
 
 // Down projection of one unit for every M-tile of its tokens, accumulated with the
 // router weights into this wave's LDS accumulator yacc[T][16].
-template <int BITS>
-__device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], const uint16_t* __restrict__ abuf,
-                        int64_t width_a, const int2* __restrict__ tokw, float* yacc) {
+// Without group sums (XSUM false) every group's accumulator starts from the MFMA offset
+// seed -OFF * sum(a); with them (xsum(pos, g) = sum of a row's group g, fp32) the MFMA
+// chains start at zero and the offset term is removed with one FMA per element, which
+// halves the MFMAs of a unit.
+template <int BITS, bool XSUM, typename TokW, typename AFetch, typename XSum>
+__device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], TokW tokw, AFetch afetch, XSum xsum,
+                        float* yacc) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, ml = lane & 15;
-    float sc[kDkChunk];
-#pragma unroll
-    for (int j = 0; j < kDkChunk; ++j) sc[j] = j < u.ngroups ? bf16_to_f32(u.srow[j]) : 0.f;
+    const int g0 = u.col0 / kGroup;
     for (int mt = 0; mt < u.count; mt += 16) {
-        int tk[4];
+        int tk[4], pr[4];
         float wk[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {   // token and router weight of D rows 4q + r
+        for (int r = 0; r < 4; ++r) {   // token, router weight and a row of D rows 4q + r
             const int m = min(mt + 4 * q + r, u.count - 1);
+            pr[r] = u.pos0 + m;
             if (u.shared) {
                 tk[r] = m;
                 wk[r] = 1.0f;
             } else {
-                const int2 tw = tokw[u.pos0 + m];
+                const int2 tw = tokw(u.pos0 + m);
                 tk[r] = tw.x;
                 wk[r] = __int_as_float(tw.y);
             }
         }
         const int mload = mt + ml;
         const bool aok = mload < u.count;
-        const uint16_t* arow = abuf + (int64_t)(u.pos0 + (aok ? mload : mt)) * width_a + u.col0 + 32 * q;
+        const int pos = u.pos0 + (aok ? mload : mt);   // a valid row even for padding lanes
+        const int col = u.col0 + 32 * q;
+        // every load unconditional (a missing second group re-reads the first, masked to
+        // zero), so they all issue before the first wait
         u32x4_t av[kDkChunk][4];
 #pragma unroll
-        for (int j = 0; j < kDkChunk; ++j)
-            if (j < u.ngroups)
+        for (int j = 0; j < kDkChunk; ++j) {
+            const bool okj = aok && j < u.ngroups;
+            const int cj = col + (j < u.ngroups ? j : 0) * kGroup;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) av[j][i] = load_act<BITS>(arow, aok, (int64_t)j * kGroup + 8 * i);
+            for (int i = 0; i < 4; ++i) av[j][i] = perm_act(afetch(okj, pos, cj + 8 * i));
+        }
+        f32x4_t t[kDkChunk];
+#pragma unroll
+        for (int j = 0; j < kDkChunk; ++j) t[j] = XSUM ? f32x4_t{0.f, 0.f, 0.f, 0.f} : offset_seed<BITS>(av[j]);
+        group_dot2<BITS>(av, bw, t);   // a missing second group has zero a and scale 0
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < kDkChunk; ++j) {
-            if (j < u.ngroups) {
-                u32x4_t b[BITS / 4];
+        for (int j = 0; j < kDkChunk; ++j)
 #pragma unroll
-                for (int c = 0; c < BITS / 4; ++c) b[c] = bw[j][c];
-                const f32x4_t t = group_dot<BITS>(av[j], b, offset_seed<BITS>(av[j]));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += sc[j] * t[r];
+            for (int r = 0; r < 4; ++r) {
+                float v = t[j][r];
+                if constexpr (XSUM) v -= code_offset<BITS>() * xsum(pr[r], g0 + (j < u.ngroups ? j : 0));
+                acc[r] += u.sc[j] * v;   // sc is 0 for a missing group
             }
-        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (mt + 4 * q + r < u.count) yacc[tk[r] * 16 + ml] += wk[r] * acc[r];
     }
 }
 
-// Unit `u` of the down kernel (routed units first, then the shared expert's).
-__device__ __forceinline__ DkUnit dk_make_unit(const DecodeArgs& a, int u, int n_routed_units, int nch, int nch_s,
-                                               int h0, int* bits) {
+// Unit `u` of the down kernel (routed units first, then the shared expert's); `rec`
+// gives the (expert, first sorted row, count) of an active-expert slot.
+template <typename Rec>
+__device__ __forceinline__ DkUnit dk_make_unit(const ExpertSet& routed, const ExpertSet& shared, int64_t H, int T,
+                                               int k, Rec rec, int u, int n_routed_units, int nch, int nch_s, int h0,
+                                               int* bits) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, ml = lane & 15;
     DkUnit r;
@@ -262,18 +316,18 @@ __device__ __forceinline__ DkUnit dk_make_unit(const DecodeArgs& a, int u, int n
     int64_t ebase = 0;
     int chunk;
     if (u < n_routed_units) {
-        const int4 rr = a.rec[u / nch];
+        const int4 rr = rec(u / nch);
         chunk = u % nch;
-        es = &a.routed;
+        es = &routed;
         ebase = rr.x;
         r.pos0 = rr.y;
         r.count = rr.z;
         r.shared = false;
     } else {
         chunk = (u - n_routed_units) % nch_s;
-        es = &a.shared;
-        r.pos0 = a.T * a.k;
-        r.count = a.T;
+        es = &shared;
+        r.pos0 = T * k;
+        r.count = T;
         r.shared = true;
     }
     *bits = es->bits;
@@ -283,9 +337,9 @@ __device__ __forceinline__ DkUnit dk_make_unit(const DecodeArgs& a, int u, int n
     r.ngroups = min(kDkChunk, G2 - g0);
     r.col0 = g0 * kGroup;
     const int64_t row_bytes = I_e * es->bits / 8;
-    const uint8_t* w2e = reinterpret_cast<const uint8_t*>(es->w2) + ebase * a.H * row_bytes;
+    const uint8_t* w2e = reinterpret_cast<const uint8_t*>(es->w2) + ebase * H * row_bytes;
     r.wrow = w2e + (int64_t)(h0 + ml) * row_bytes + (int64_t)g0 * (kGroup * es->bits / 8) + q * (32 * es->bits / 8);
-    r.srow = es->s2 + ebase * a.H * G2 + (int64_t)(h0 + ml) * G2 + g0;
+    r.srow = es->s2 + ebase * H * G2 + (int64_t)(h0 + ml) * G2 + g0;
     return r;
 }
 
@@ -306,12 +360,14 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
     const int n_units = n_routed_units + nch_s;
     const int V = gridDim.y * kDkWaves;
     int u = blockIdx.y * kDkWaves + wave;
+    const int4* rec = a.rec;
+    auto recf = [rec](int slot) { return rec[slot]; };
     // software pipeline: the next unit's codes are in flight while this one computes
     u32x4_t cur[kDkChunk][2], nxt[kDkChunk][2];
     int bits = BITS;
     DkUnit cu;
     if (u < n_units) {
-        cu = dk_make_unit(a, u, n_routed_units, nch, nch_s, h0, &bits);
+        cu = dk_make_unit(a.routed, a.shared, a.H, a.T, a.k, recf, u, n_routed_units, nch, nch_s, h0, &bits);
         if (bits == BITS) dk_load_codes<BITS>(cu, cur);
         else if constexpr (SBITS != 0) dk_load_codes<SBITS>(cu, cur);
     }
@@ -320,12 +376,21 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
         int nbits = BITS;
         DkUnit nu;
         if (un < n_units) {
-            nu = dk_make_unit(a, un, n_routed_units, nch, nch_s, h0, &nbits);
+            nu = dk_make_unit(a.routed, a.shared, a.H, a.T, a.k, recf, un, n_routed_units, nch, nch_s, h0, &nbits);
             if (nbits == BITS) dk_load_codes<BITS>(nu, nxt);
             else if constexpr (SBITS != 0) dk_load_codes<SBITS>(nu, nxt);
         }
-        if (bits == BITS) dk_unit<BITS>(cu, cur, a.abuf, a.width_a, a.tokw, yacc);
-        else if constexpr (SBITS != 0) dk_unit<SBITS>(cu, cur, a.abuf, a.width_a, a.tokw, yacc);
+        const int2* tokw = a.tokw;
+        auto tw = [tokw](int pos) { return tokw[pos]; };
+        const uint16_t* abuf = a.abuf;
+        const int64_t width_a = a.width_a;
+        auto af = [abuf, width_a](bool ok, int pos, int col) {
+            const uint16_t* p = abuf + (int64_t)pos * width_a + col;
+            return load16_or_zero(p, ok, p);
+        };
+        auto nox = [](int, int) { return 0.f; };
+        if (bits == BITS) dk_unit<BITS, false>(cu, cur, tw, af, nox, yacc);
+        else if constexpr (SBITS != 0) dk_unit<SBITS, false>(cu, cur, tw, af, nox, yacc);
         if (un >= n_units) break;
 #pragma unroll
         for (int j = 0; j < kDkChunk; ++j) {
@@ -362,6 +427,326 @@ __global__ __launch_bounds__(256) void dk_combine_kernel(const float* __restrict
     y[i] = (uint16_t)f32_to_bf16(s);
 }
 
+// ------------------------------------------------------------------ tiny batches
+//
+// T * k <= kTinyP pairs (one or two tokens at top-8):
+// one launch.  Every workgroup routes the batch itself from the logits (a few KB, served
+// by L2 after the first reads), so no workgroup waits on a routing kernel.  Workgroups
+// [0, n_gk) own one 16-row block of one active expert's gate/up bank (as gk_decode) and
+// write their a rows through to memory, then add 1 to that expert slot's counter.
+// The remaining workgroups own 16 output rows each: they issue the loads of their first
+// down-projection codes, wait until every active slot's counter is complete, read a past
+// the caches and finish as dk_decode (one split, so the sum over experts stays in one
+// workgroup and in a fixed order).  Down workgroups count their exits in groups of 16;
+// the last one to leave returns every counter to zero for the next launch.
+//
+// Progress: gate/up workgroups never wait, and at most kTinyMaxH / 16 = 256 down
+// workgroups spin, far fewer than the workgroups the GPU holds at once, so a gate/up
+// workgroup always finds room.  A wait is still bounded: on time-out the workgroup
+// raises the sticky error word and continues.
+
+namespace {
+
+constexpr int kTinySpinLimit = 1 << 22;
+
+struct TinyRoute {
+    int ids[kTinyP];          // per pair (token * k + slot): expert, -1 when dropped
+    float w[kTinyP];          // per pair: router weight
+    int pair_at[kTinyP];      // per sorted position: pair
+    int2 tw[kTinyP];          // per sorted position: (token, weight bits)
+    int4 slot[kTinyP];        // per active expert, ascending: (expert, first position, count, 0)
+    int n_active, n_valid;
+};
+
+// Routing of the whole batch into LDS (all threads of the workgroup take part).
+// `writer` also stores the routing outputs.
+__device__ void tiny_route(const TinyArgs& a, TinyRoute& r, bool writer) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int T = a.T, E = a.E, k = a.k, P = T * k;
+    for (int t = wave; t < T; t += nw) {
+        int id;
+        float w;
+        if (a.logits) {
+            wave_topk_any(a.logits + (int64_t)t * E, E, k, &id, &w);
+            if (writer && lane < k) {
+                a.ids[t * k + lane] = id;
+                a.wts[t * k + lane] = w;
+            }
+        } else {
+            id = lane < k ? checked_id(a.ids + t * k, lane, E) : -1;
+            w = lane < k ? a.wts[t * k + lane] : 0.f;
+        }
+        if (lane < k) {
+            r.ids[t * k + lane] = id;
+            r.w[t * k + lane] = w;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {   // stable order by (expert, pair): rank of each key among the P keys
+        const int e = lane < P ? r.ids[lane] : -1;
+        const int key = e >= 0 ? (e << 6 | lane) : 0x7fffffff;
+        int rank = 0;
+        for (int q = 0; q < P; ++q) rank += __builtin_amdgcn_readlane(key, q) < key;
+        if (e >= 0) r.pair_at[rank] = lane;
+        const uint64_t vm = __ballot(e >= 0);
+        if (lane == 0) r.n_valid = __popcll(vm);
+    }
+    __syncthreads();
+    if (wave == 0) {   // active experts: the first sorted position of each
+        const int nv = r.n_valid;
+        const bool in = lane < nv;
+        const int p = in ? r.pair_at[lane] : 0;
+        const int e = in ? r.ids[p] : -1;
+        const int pe = (in && lane > 0) ? r.ids[r.pair_at[lane - 1]] : -1;
+        const bool first = in && e != pe;
+        const uint64_t fm = __ballot(first);
+        const uint64_t upto = (2ull << lane) - 1ull;   // lanes 0..lane (all lanes at 63)
+        if (in) r.tw[lane] = int2{p / k, __float_as_int(r.w[p])};
+        if (first) {
+            const uint64_t above = fm & ~upto;
+            const int next = above ? (int)__ffsll((long long)above) - 1 : nv;
+            r.slot[__popcll(fm & upto) - 1] = int4{e, lane, next - lane, 0};
+        }
+        if (lane == 0) r.n_active = __popcll(fm);
+        if (writer && in) a.sorted[lane] = p;
+    }
+    __syncthreads();
+    if (writer) {   // counts and offsets of every expert (binary search of the slot list)
+        const int na = r.n_active;
+        for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+            int lo = 0, hi = na;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (r.slot[mid].x < e) lo = mid + 1;
+                else hi = mid;
+            }
+            a.offsets[e] = lo < na ? r.slot[lo].y : r.n_valid;
+            if (e < E) a.counts[e] = (lo < na && r.slot[lo].x == e) ? r.slot[lo].z : 0;
+        }
+    }
+}
+
+template <int BITS, int SBITS>
+__device__ void tiny_gate_up(const TinyArgs& a, const TinyRoute& r, float* s_red) {
+    const int slot = blockIdx.x / a.n_rb, rb = blockIdx.x % a.n_rb;
+    const int P = min(a.E, a.T * a.k);
+    const bool shared = SBITS != 0 && slot == P;
+    const int n0 = rb * 16;
+    int count, pos0, e = 0;
+    int64_t I_e;
+    if (shared) {
+        I_e = a.shared.I;
+        count = a.T;
+        pos0 = a.T * a.k;
+    } else {
+        if (slot >= r.n_active) return;
+        const int4 sl = r.slot[slot];
+        e = sl.x;
+        pos0 = sl.y;
+        count = sl.z;
+        I_e = a.routed.I;
+    }
+    if (n0 >= I_e) return;
+    const int ml = threadIdx.x & 15;
+    for (int mt = 0; mt < count; mt += 16) {
+        const int m = mt + ml;
+        const bool ok = m < count;
+        const int rows = min(16, count - mt);
+        if (shared) {
+            if constexpr (SBITS != 0)
+                gk_tile<SBITS, true>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? m : mt, ok, pos0 + mt, rows,
+                                     a.abuf, a.width_a, s_red, a.abuf_bytes);
+        } else {
+            const int tok = r.tw[pos0 + (ok ? m : mt)].x;
+            const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
+            gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
+                                a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, tok, ok, pos0 + mt, rows,
+                                a.abuf, a.width_a, s_red, a.abuf_bytes);
+        }
+    }
+    // every wave's write-through stores have completed before the block is counted
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(sync_word(a.sync, shared ? kSyncShared : slot), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BITS, int SBITS>
+__device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int d = blockIdx.x - a.n_gk, n_dk = gridDim.x - a.n_gk;
+    const int h0 = d * 16;
+    const int T = a.T;
+    float* yacc = s_dyn + wave * T * 16;                                   // [waves][T][16]
+    uint16_t* stage = reinterpret_cast<uint16_t*>(s_dyn + kDkWaves * T * 16);   // staged a rows
+    float* xs = reinterpret_cast<float*>(stage + (a.abuf_bytes + 1023) / 1024 * 512);   // their group sums
+    for (int i = lane; i < T * 16; i += 64) yacc[i] = 0.f;
+
+    const int n_active = r.n_active;
+    const int nch = (int)((a.routed.I / kGroup + kDkChunk - 1) / kDkChunk);
+    const int nch_s = SBITS != 0 ? (int)((a.shared.I / kGroup + kDkChunk - 1) / kDkChunk) : 0;
+    const int n_routed_units = n_active * nch;
+    const int n_units = n_routed_units + nch_s;
+    auto recf = [&r](int slot) { return r.slot[slot]; };
+    auto tw = [&r](int pos) { return r.tw[pos]; };
+    const int V = kDkWaves;
+    int u = wave;
+    u32x4_t cur[kDkChunk][2], nxt[kDkChunk][2];
+    int bits = BITS, nbits = BITS;
+    DkUnit cu, nu;
+    // the first two units' codes go out before the wait
+    if (u < n_units) {
+        cu = dk_make_unit(a.routed, a.shared, a.H, T, a.k, recf, u, n_routed_units, nch, nch_s, h0, &bits);
+        if (bits == BITS) dk_load_codes<BITS>(cu, cur);
+        else if constexpr (SBITS != 0) dk_load_codes<SBITS>(cu, cur);
+    }
+    if (u + V < n_units) {
+        nu = dk_make_unit(a.routed, a.shared, a.H, T, a.k, recf, u + V, n_routed_units, nch, nch_s, h0, &nbits);
+        if (nbits == BITS) dk_load_codes<BITS>(nu, nxt);
+        else if constexpr (SBITS != 0) dk_load_codes<SBITS>(nu, nxt);
+    }
+    if (wave == 0) {   // wait until every active slot (and the shared expert) is complete
+        const uint32_t need = (uint32_t)(a.routed.I / 16);
+        const uint32_t need_s = SBITS != 0 ? (uint32_t)(a.shared.I / 16) : 0u;
+        for (int spins = 0;; ++spins) {
+            bool ok = true;
+            if (lane < n_active)
+                ok = __hip_atomic_load(sync_word(a.sync, lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
+            if (SBITS != 0)
+                ok = ok && __hip_atomic_load(sync_word(a.sync, kSyncShared), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) >= need_s;
+            if (__all(ok)) break;
+            if (spins >= kTinySpinLimit) {
+                if (lane == 0)
+                    __hip_atomic_store(sync_word(a.sync, kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+
+    // a rows: written in this launch by other workgroups, so read past the caches (sc1).
+    // When the whole a buffer fits in LDS (and its rows have no padding), it is copied
+    // there first by direct-to-LDS loads, all in flight at once; the units then read LDS
+    // at the same offsets.  Otherwise each unit loads its rows itself.
+    const int Tk = T * a.k;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.abuf, a.abuf_bytes);
+    if (a.stage_a) {
+        const int n_chunks = (int)((a.abuf_bytes + 1023) / 1024);   // 64 lanes x 16 bytes
+        for (int c = wave; c < n_chunks; c += kDkWaves)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, stage + c * 512, 16, (uint32_t)(c * 1024 + lane * 16), 0, 0,
+                                                     kSc1);
+        __syncthreads();   // waits for this wave's loads, then for every wave
+        // sum of every staged row's 128-column groups (16 lanes per row and group)
+        const int G = (int)(a.width_a / kGroup);
+        const int n_pairs = (int)(a.abuf_bytes / (uint32_t)(a.width_a * 2)) * G;
+        for (int p = (int)threadIdx.x >> 4; p < n_pairs; p += (int)blockDim.x >> 4) {
+            const int row = p / G, g = p % G;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (int64_t)row * a.width_a + g * kGroup +
+                                                               (threadIdx.x & 15) * 8);
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum += bf16_to_f32(v[e] & 0xffffu) + bf16_to_f32(v[e] >> 16);
+            sum += __shfl_xor(sum, 8, 16);
+            sum += __shfl_xor(sum, 4, 16);
+            sum += __shfl_xor(sum, 2, 16);
+            sum += __shfl_xor(sum, 1, 16);
+            if ((threadIdx.x & 15) == 0) xs[p] = sum;
+        }
+        __syncthreads();
+    }
+    const int64_t width_a = a.width_a;
+    const bool staged = a.stage_a != 0;
+    auto af = [stage, ar, staged, width_a](bool ok, int pos, int col) {
+        if (staged) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + pos * width_a + col);
+            const uint32_t m = ok ? 0xffffffffu : 0u;
+            return u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
+        }
+        // a padded row reads beyond the buffer, which returns zeros
+        const uint32_t off = ok ? (uint32_t)(((int64_t)pos * width_a + col) * 2) : 0xfffff000u;
+        return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, kSc1));
+    };
+
+    while (u < n_units) {
+        const int G = (int)(a.width_a / kGroup);
+        auto xsf = [xs, G](int pos, int g) { return xs[pos * G + g]; };
+        if (staged) {
+            if (bits == BITS) dk_unit<BITS, true>(cu, cur, tw, af, xsf, yacc);
+            else if constexpr (SBITS != 0) dk_unit<SBITS, true>(cu, cur, tw, af, xsf, yacc);
+        } else {
+            if (bits == BITS) dk_unit<BITS, false>(cu, cur, tw, af, xsf, yacc);
+            else if constexpr (SBITS != 0) dk_unit<SBITS, false>(cu, cur, tw, af, xsf, yacc);
+        }
+        u += V;
+        if (u >= n_units) break;
+#pragma unroll
+        for (int j = 0; j < kDkChunk; ++j) {
+            cur[j][0] = nxt[j][0];
+            cur[j][1] = nxt[j][1];
+        }
+        cu = nu;
+        bits = nbits;
+        if (u + V < n_units) {
+            nu = dk_make_unit(a.routed, a.shared, a.H, T, a.k, recf, u + V, n_routed_units, nch, nch_s, h0, &nbits);
+            if (nbits == BITS) dk_load_codes<BITS>(nu, nxt);
+            else if constexpr (SBITS != 0) dk_load_codes<SBITS>(nu, nxt);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDkWaves; ++w) s += s_dyn[w * T * 16 + i];
+        const int t = i >> 4, n = i & 15;
+        const int64_t o = (int64_t)t * a.H + h0 + n;
+        const float res = a.residual ? bf16_to_f32(a.residual[o]) : 0.f;
+        a.y[o] = (uint16_t)f32_to_bf16(s + res);
+    }
+    if (threadIdx.x == 0) {   // exit count; the last down workgroup resets every counter
+        const int g = d >> 4, gsz = min(16, n_dk - (g << 4)), ng = (n_dk + 15) >> 4;
+        if (__hip_atomic_fetch_add(sync_word(a.sync, kSyncGroup + g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)gsz - 1 &&
+            __hip_atomic_fetch_add(sync_word(a.sync, kSyncTop), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)ng - 1) {
+            for (int i = 0; i <= kSyncShared; ++i)
+                __hip_atomic_store(sync_word(a.sync, i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < ng; ++i)
+                __hip_atomic_store(sync_word(a.sync, kSyncGroup + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync_word(a.sync, kSyncTop), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int BITS, int SBITS>
+__device__ __forceinline__ void tiny_decode_body(const TinyArgs& a) {
+    __shared__ TinyRoute route;
+    extern __shared__ float s_dyn[];   // gate/up: [waves * 8][64] partial sums; down: y, then a rows
+    tiny_route(a, route, blockIdx.x == 0);
+    if ((int)blockIdx.x < a.n_gk) tiny_gate_up<BITS, SBITS>(a, route, s_dyn);
+    else tiny_down<BITS, SBITS>(a, route, s_dyn);
+}
+
+// Two workgroups per CU where the registers allow it without spilling (4-bit codes with
+// no 8-bit expert), one otherwise.
+template <int BITS, int SBITS>
+__global__ __launch_bounds__(64 * kDkWaves) __attribute__((amdgpu_waves_per_eu(4))) void tiny_decode_kernel(
+    TinyArgs a) {
+    tiny_decode_body<BITS, SBITS>(a);
+}
+template <int BITS, int SBITS>
+__global__ __launch_bounds__(64 * kDkWaves) void tiny_decode_wide_kernel(TinyArgs a) {
+    tiny_decode_body<BITS, SBITS>(a);
+}
+
+__global__ void sync_init_kernel(uint32_t* sync) {
+    for (int i = threadIdx.x; i < (int)(kSyncBytes / 4); i += blockDim.x) sync[i] = 0u;
+}
+
+}  // namespace
+
 namespace {
 
 template <int BITS, int SBITS>
@@ -369,12 +754,12 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
     const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
     const dim3 gk_grid((unsigned)(Imax / 16), (unsigned)(max_active + (SBITS ? 1 : 0)));
-    launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, a);
+    launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, 0u, a);
     const dim3 dk_grid((unsigned)(a.H / 16), (unsigned)a.splits);
-    launch(t, "dk_decode", dk_decode_kernel<BITS, SBITS>, dk_grid, dim3(64 * kDkWaves), s, a);
+    launch(t, "dk_decode", dk_decode_kernel<BITS, SBITS>, dk_grid, dim3(64 * kDkWaves), s, 0u, a);
     if (a.splits > 1) {
         const int64_t n = (int64_t)a.T * a.H;
-        launch(t, "dk_combine", dk_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s,
+        launch(t, "dk_combine", dk_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u,
                (const float*)a.part, a.splits, n, a.residual, a.y);
     }
     return hipGetLastError();
@@ -392,6 +777,41 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     if (sb == 0) return launch_decode_t<8, 0>(a, s, t);
     if (sb == 4) return launch_decode_t<8, 4>(a, s, t);
     return launch_decode_t<8, 8>(a, s, t);
+}
+
+}  // namespace w4a16
+
+namespace w4a16 {
+
+namespace {
+template <int BITS, int SBITS>
+hipError_t launch_tiny_t(const TinyArgs& a, hipStream_t s, StageTimer* t) {
+    const int n_dk = (int)(a.H / 16);
+    if constexpr (BITS == 4 && SBITS != 8)
+        launch(t, "tiny_decode", tiny_decode_kernel<BITS, SBITS>, dim3((unsigned)(a.n_gk + n_dk)),
+               dim3(64 * kDkWaves), s, a.lds_bytes, a);
+    else
+        launch(t, "tiny_decode", tiny_decode_wide_kernel<BITS, SBITS>, dim3((unsigned)(a.n_gk + n_dk)),
+               dim3(64 * kDkWaves), s, a.lds_bytes, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (a.routed.bits == 4) {
+        if (sb == 0) return launch_tiny_t<4, 0>(a, s, t);
+        if (sb == 4) return launch_tiny_t<4, 4>(a, s, t);
+        return launch_tiny_t<4, 8>(a, s, t);
+    }
+    if (sb == 0) return launch_tiny_t<8, 0>(a, s, t);
+    if (sb == 4) return launch_tiny_t<8, 4>(a, s, t);
+    return launch_tiny_t<8, 8>(a, s, t);
+}
+
+hipError_t launch_sync_init(uint32_t* sync, hipStream_t s) {
+    hipLaunchKernelGGL(sync_init_kernel, dim3(1), dim3(256), 0, s, sync);
+    return hipGetLastError();
 }
 
 }  // namespace w4a16

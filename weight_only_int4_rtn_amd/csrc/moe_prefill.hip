@@ -438,10 +438,10 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) 
     const int64_t shared_tiles = SBITS ? (a.T + MT - 1) / MT : 0;
     const int64_t gk_items = (a.max_tiles + shared_tiles) * (Imax / kGkCols);
     const int64_t dk_items = (a.max_tiles + shared_tiles) * (a.H / kDkRows);
-    launch(t, "gk_prefill", gk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(gk_items)), dim3(256), s, a);
-    launch(t, "dk_prefill", dk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(dk_items)), dim3(256), s, a);
+    launch(t, "gk_prefill", gk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(gk_items)), dim3(256), s, 0u, a);
+    launch(t, "dk_prefill", dk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(dk_items)), dim3(256), s, 0u, a);
     const int64_t n = (int64_t)a.T * a.H;
-    launch(t, "finalize", finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, (const float*)a.y32, n,
+    launch(t, "finalize", finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, (const float*)a.y32, n,
            a.residual, a.y);
     return hipGetLastError();
 }

@@ -291,15 +291,15 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
 }
 
 hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t) {
-    launch(t, "route_small", route_small_kernel, dim3(1), dim3(1024), s, a);
+    launch(t, "route_small", route_small_kernel, dim3(1), dim3(1024), s, 0u, a);
     return hipGetLastError();
 }
 
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t s, StageTimer* t) {
-    launch(t, "route_block", route_block_kernel, dim3(a.nblk), dim3(1024), s, a);
-    launch(t, "route_scan", route_scan_kernel, dim3(1), dim3(1024), s, a);
+    launch(t, "route_block", route_block_kernel, dim3(a.nblk), dim3(1024), s, 0u, a);
+    launch(t, "route_scan", route_scan_kernel, dim3(1), dim3(1024), s, 0u, a);
     const int64_t P = (int64_t)a.T * a.k;
-    launch(t, "route_scatter", route_scatter_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), s, a);
+    launch(t, "route_scatter", route_scatter_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), s, 0u, a);
     return hipGetLastError();
 }
 

@@ -15,70 +15,115 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 
 
-// Order-preserving unsigned key of a finite float (-0 is taken as +0, so equal logits
-// get equal keys); larger logit <=> larger key, and no finite value maps to 0.
-__device__ __forceinline__ uint32_t ordered_key(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u << 1) == 0) u = 0;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t key) {
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-// Lane-wise max of a 64-bit key across the wave, returned in every lane.  DPP moves
-// (quad permutes, row mirrors, then row broadcasts of lanes 15 and 31) keep every step
-// in registers; the full maximum lands in lane 63 and is read back as a scalar.
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v, uint64_t o) { return o > v ? o : v; }
-
+// Wave-wide maximum / minimum by DPP moves (quad permutes, row mirrors, then row
+// broadcasts of lanes 15 and 31): the full result lands in lane 63 and is read back as a
+// scalar, so every lane gets it without LDS.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-    const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
-    const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
-    return (uint64_t)nhi << 32 | nlo;
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ float fdpp_max(float v, int o) { return fmaxf(v, __int_as_float(o)); }
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fdpp_max(v, dpp_i32<0xb1, 0xf>(__float_as_int(v)));    // quad_perm [1,0,3,2]
+    v = fdpp_max(v, dpp_i32<0x4e, 0xf>(__float_as_int(v)));    // quad_perm [2,3,0,1]
+    v = fdpp_max(v, dpp_i32<0x141, 0xf>(__float_as_int(v)));   // row_half_mirror
+    v = fdpp_max(v, dpp_i32<0x140, 0xf>(__float_as_int(v)));   // row_mirror: every row holds its max
+    v = fdpp_max(v, dpp_i32<0x142, 0xa>(__float_as_int(v)));   // row_bcast:15 into rows 1 and 3
+    v = fdpp_max(v, dpp_i32<0x143, 0xc>(__float_as_int(v)));   // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, dpp_i32<0xb1, 0xf>(v));
+    v = min(v, dpp_i32<0x4e, 0xf>(v));
+    v = min(v, dpp_i32<0x141, 0xf>(v));
+    v = min(v, dpp_i32<0x140, 0xf>(v));
+    v = min(v, dpp_i32<0x142, 0xa>(v));
+    v = min(v, dpp_i32<0x143, 0xc>(v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = dpp_max_step(v, dpp_u64<0xb1, 0xf>(v));    // quad_perm [1,0,3,2]
-    v = dpp_max_step(v, dpp_u64<0x4e, 0xf>(v));    // quad_perm [2,3,0,1]
-    v = dpp_max_step(v, dpp_u64<0x141, 0xf>(v));   // row_half_mirror
-    v = dpp_max_step(v, dpp_u64<0x140, 0xf>(v));   // row_mirror: each row of 16 holds its max
-    v = dpp_max_step(v, dpp_u64<0x142, 0xa>(v));   // row_bcast:15 into rows 1 and 3
-    v = dpp_max_step(v, dpp_u64<0x143, 0xc>(v));   // row_bcast:31 into rows 2 and 3
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return (uint64_t)hi << 32 | lo;
-}
-
-// Top-k of one token by one wave: k rounds of a wave-wide maximum over 64-bit keys
-// (ordered logit in the high half, the inverted expert index in the low half, so equal
-// logits resolve to the lower index); the round's winner is marked taken by its lane.
+// Top-k of one token by one wave.  Lane l holds the logits of experts l, l + 64, ...
+// Each of the k rounds takes the wave-wide maximum of the lanes' best remaining logits;
+// when several lanes tie on it, the lowest expert index among them wins (a second,
+// rarely taken reduction).  The winner's lane removes it.  -0 and +0 compare equal, so
+// they tie; NaN logits rank below every other value.  With NV <= 4 logits per lane the
+// lane keeps them sorted (larger first, lower index first on equal values) so its best
+// is its first register; with more, the lane scans them each round.
 // Lane j < k returns slot j's expert and its softmax weight over the chosen logits.
 template <int NV>   // logits per lane: E <= 64 * NV
 __device__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_id, float* my_w) {
+    constexpr bool kSorted = NV <= 4;
     const int lane = threadIdx.x & 63;
-    uint64_t key[NV];
+    float hv[NV];
+    int he[kSorted ? NV : 1];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {   // unconditional (clamped) loads: all in flight together
         const int e = lane + 64 * i;
         const float v = row[min(e, E - 1)];
-        key[i] = e < E ? ((uint64_t)ordered_key(v) << 32 | (uint32_t)~e) : 0ull;
+        hv[i] = (e < E && !__builtin_isnan(v)) ? v : -__builtin_inff();
+        if constexpr (kSorted) he[i] = e < E ? e : 0x7fffffff;
+    }
+    if constexpr (kSorted) {
+#pragma unroll
+        for (int i = 1; i < NV; ++i)     // stable insertion sort, larger value first
+#pragma unroll
+            for (int j = i; j > 0; --j) {
+                const bool sw = hv[j] > hv[j - 1];
+                const float tv = hv[j];
+                const int te = he[j];
+                hv[j] = sw ? hv[j - 1] : hv[j];
+                he[j] = sw ? he[j - 1] : he[j];
+                hv[j - 1] = sw ? tv : hv[j - 1];
+                he[j - 1] = sw ? te : he[j - 1];
+            }
     }
     float v0 = 0.f, den = 0.f, mine = 0.f;
     int id = -1;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
+        float best;
+        int best_e;
+        if constexpr (kSorted) {
+            best = hv[0];
+            best_e = he[0];
+        } else {   // the lane's largest remaining value, lowest index first on ties
+            best = hv[0];
+            int bi = 0;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) best = key[i] > best ? key[i] : best;
-        const uint64_t win = wave_max_u64(best);
-        const int widx = (int)~(uint32_t)win;
-        const float wval = key_value((uint32_t)(win >> 32));
+            for (int i = 1; i < NV; ++i) {
+                const bool gt = hv[i] > best;
+                best = gt ? hv[i] : best;
+                bi = gt ? i : bi;
+            }
+            const int e = lane + 64 * bi;
+            best_e = e < E ? e : 0x7fffffff;
+        }
+        const float m = wave_max_f32(best);
+        const bool at_max = best == m;
+        const uint64_t cand = __ballot(at_max);
+        int wl;
+        if (__popcll(cand) == 1) {
+            wl = (int)__ffsll((long long)cand) - 1;
+        } else {   // equal logits: the lowest expert index among the tied lanes
+            const int emin = wave_min_i32(at_max ? best_e : 0x7fffffff);
+            wl = (int)__ffsll((long long)__ballot(at_max && best_e == emin)) - 1;
+        }
+        const int widx = __builtin_amdgcn_readlane(best_e, wl);
+        const bool pop = lane == wl;
+        if constexpr (kSorted) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (key[i] == win) key[i] = 0;   // only the owner lane holds this key
-        if (j == 0) v0 = wval;
-        const float ex = __expf(wval - v0);
+            for (int i = 0; i + 1 < NV; ++i) {
+                hv[i] = pop ? hv[i + 1] : hv[i];
+                he[i] = pop ? he[i + 1] : he[i];
+            }
+            hv[NV - 1] = pop ? -__builtin_inff() : hv[NV - 1];
+            he[NV - 1] = pop ? 0x7fffffff : he[NV - 1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) hv[i] = (pop && lane + 64 * i == widx) ? -__builtin_inff() : hv[i];
+        }
+        if (j == 0) v0 = m;
+        const float ex = __expf(m - v0);
         den += ex;
         if (lane == j) {
             id = widx;
