@@ -165,8 +165,8 @@ int moe_w4a16_workspace_init(void* workspace, size_t workspace_bytes, void* stre
 /*
  * moe_w4a16_forward - routing, fused dequant gate/up + SiLU(gate)*up, fused dequant down
  * projection and router-weighted un-permute, enqueued on `stream`.
- * The result for small batches (T <= 64) is bitwise deterministic; for larger batches
- * the fp32 sum over a token's experts may be formed in any order (device atomics).
+ * The result is bitwise deterministic: the fp32 sum over a token's experts is formed in
+ * slot order on every path (no atomics take part in it).
  * Two forwards must not use one workspace at the same time (on different streams).
  */
 int moe_w4a16_forward(const moe_w4a16_args* args, void* stream);

@@ -1,6 +1,6 @@
 """The forward call under HIP graph capture: replays, interleaved with eager work and
-synchronisations, must reproduce the eager result (bitwise on the small-batch path,
-which is deterministic; to fp32 summation order on the large-batch path)."""
+synchronisations, must reproduce the eager result bitwise (every path is deterministic:
+no atomics take part in any sum)."""
 
 import numpy as np
 import pytest
@@ -30,7 +30,6 @@ def test_graph_replay_matches_eager(T):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         call(x, out, router_logits=logits)
-    ref = eager.float()
     for rep in range(4):
         out.zero_()
         junk = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
@@ -38,8 +37,4 @@ def test_graph_replay_matches_eager(T):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        if T <= 64:
-            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep} differs"
-        else:
-            d = (out.float() - ref).abs().max().item()
-            assert d <= 2 ** -7 * ref.abs().max().item(), (rep, d)
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep} differs"

@@ -240,6 +240,9 @@ def test_ffn_full_layer_prefill_sampled(full_layer):
     ids, wts, *_ = oracle.route(logits, cfg.k)
     y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), 4, tokens=tokens)
     check_ffn(y[torch.from_numpy(tokens).to(DEV)], y_ref, "prefill8192 sampled")
+    y2 = w4.moe_w4a16_forward(bf16_to_dev(x), w13, s13, w2, s2, top_k=cfg.k, router_logits=f32_to_dev(logits))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "prefill result not bitwise reproducible"
 
 
 @pytest.mark.parametrize("T", [4, 100])

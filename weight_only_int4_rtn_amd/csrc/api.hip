@@ -102,7 +102,8 @@ WsLayout layout(const moe_w4a16_args* a) {
         L.tiles = take((size_t)L.max_tiles * 8);
         L.xsum = take((size_t)T * (H / kGroup) * 4);
         L.xp = take((size_t)T * H * 2);
-        L.y32 = take((size_t)T * H * 4);
+        L.ystage = take((size_t)L.rows_a * H * 4);
+        L.inv = take(P * 4);
     }
     L.total = off;
     return L;
@@ -219,6 +220,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     r.tiles = static_cast<int32_t*>(at(L.tiles));
     r.xsum = static_cast<float*>(at(L.xsum));
     r.xp = static_cast<uint16_t*>(at(L.xp));
+    r.inv = static_cast<int32_t*>(at(L.inv));
     r.nblk = L.nblk;
     r.max_tiles = L.max_tiles;
     if (int st = hip_status(launch_route_large(r, s, timer), "routing launch")) return st;
@@ -243,7 +245,8 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     p.abuf = abuf;
     p.rows_a = L.rows_a;
     p.width_a = L.width_a;
-    p.y32 = static_cast<float*>(at(L.y32));
+    p.ystage = static_cast<float*>(at(L.ystage));
+    p.inv = r.inv;
     p.residual = a->residual;
     p.y = a->y;
     return hip_status(launch_prefill(p, s, timer), "prefill launch");

@@ -156,7 +156,7 @@ __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return s
 
 struct WsLayout {
     size_t sync, ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
-        y32, tokw, rec, xp, total;
+        ystage, inv, tokw, rec, xp, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
     int nblk;           // routing blocks of the large-batch path
@@ -217,6 +217,7 @@ struct RouteArgs {
     float* xsum;          // large path: [T, H/128] sums of bf16 activations per group
     uint16_t* xp;         // large path: [T, H] activations with each 8-column block reordered
     int2* tokw;           // [T*k] (token, weight bits) of each pair, in sorted order
+    int32_t* inv;         // large path: [T*k] sorted position of each pair, -1 when dropped
     int4* rec;            // small path: [max_slots] (expert, first sorted row, count, 0);
                           // count 0 marks a slot beyond the active experts
     int max_slots;
@@ -305,7 +306,8 @@ struct PrefillArgs {
     uint16_t* abuf;
     int64_t rows_a;
     int64_t width_a;
-    float* y32;
+    float* ystage;              // [rows_a, H] fp32: router-weighted down output of each sorted row
+    const int32_t* inv;         // [T*k] sorted position of each pair (-1: dropped)
     const uint16_t* residual;
     uint16_t* y;
 };

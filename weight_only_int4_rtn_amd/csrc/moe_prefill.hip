@@ -332,6 +332,8 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
         });
     }
 
+    // router-weighted rows, stored once each at the row's sorted position (the sum over a
+    // token's experts happens in finalize_kernel, in slot order)
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -339,9 +341,9 @@ __device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, c
             const int m = 64 * wm + 16 * mi + 4 * q + r;
             if (m < tr.count) {
                 const float w = s_wt[m];
-                float* yrow = a.y32 + (int64_t)s_tok[m] * a.H + h0 + 64 * wn + ml;
+                float* yrow = a.ystage + (int64_t)(tr.orow_base + m) * a.H + h0 + 64 * wn + ml;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) unsafeAtomicAdd(yrow + 16 * b, w * acc[mi][b][r]);
+                for (int b = 0; b < 4; ++b) yrow[16 * b] = w * acc[mi][b][r];
             }
         }
 }
@@ -364,12 +366,6 @@ __global__ __launch_bounds__(256, 2) void gk_prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) float s_xs[2 * MT];
     __shared__ int s_tok[MT];
 
-    // zero the fp32 output accumulator for the down kernel
-    {
-        const int64_t n4 = (int64_t)a.T * a.H / 4;
-        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
-            reinterpret_cast<float4*>(a.y32)[i] = float4{0.f, 0.f, 0.f, 0.f};
-    }
     const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
     const int nb = (int)(Imax / kGkCols);
     const int shared_items = SBITS ? ((a.T + MT - 1) / MT) * nb : 0;
@@ -415,13 +411,39 @@ __global__ __launch_bounds__(256, 2) void dk_prefill_kernel(PrefillArgs a) {
     });
 }
 
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ acc, int64_t n,
-                                                       const uint16_t* residual, uint16_t* y) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float s = acc[i];
-    if (residual) s += bf16_to_f32(residual[i]);
-    y[i] = (uint16_t)f32_to_bf16(s);
+// y[t] = sum over slots j in order of the staged row of pair (t, j), then the shared
+// expert's row, then the residual; rounded once to bf16.  A token's row is split over
+// ceil(H / 2048) blocks of 256 threads x 8 columns.  Deterministic: no atomics anywhere.
+__global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
+    const int nbx = (int)((a.H / 8 + 255) / 256);
+    const int t = (int)(blockIdx.x / nbx);
+    const int64_t c = ((int64_t)(blockIdx.x % nbx) * blockDim.x + threadIdx.x) * 8;
+    if (c >= a.H) return;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto add_row = [&](int64_t row) {
+        const float4* p = reinterpret_cast<const float4*>(a.ystage + row * a.H + c);
+        const float4 v0 = p[0], v1 = p[1];
+        s[0] += v0.x; s[1] += v0.y; s[2] += v0.z; s[3] += v0.w;
+        s[4] += v1.x; s[5] += v1.y; s[6] += v1.z; s[7] += v1.w;
+    };
+    for (int j = 0; j < a.k; ++j) {
+        const int pos = a.inv[(int64_t)t * a.k + j];
+        if (pos >= 0) add_row(pos);
+    }
+    if (a.shared.bits) add_row((int64_t)a.T * a.k + t);
+    const int64_t o = (int64_t)t * a.H + c;
+    if (a.residual) {
+        const u32x4_t r = *reinterpret_cast<const u32x4_t*>(a.residual + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[2 * e] += bf16_to_f32(r[e] & 0xffffu);
+            s[2 * e + 1] += bf16_to_f32(r[e] >> 16);
+        }
+    }
+    u32x4_t out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = f32_to_bf16(s[2 * e]) | (f32_to_bf16(s[2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4_t*>(a.y + o) = out;
 }
 
 namespace {
@@ -440,9 +462,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) 
     const int64_t dk_items = (a.max_tiles + shared_tiles) * (a.H / kDkRows);
     launch(t, "gk_prefill", gk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(gk_items)), dim3(256), s, 0u, a);
     launch(t, "dk_prefill", dk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(dk_items)), dim3(256), s, 0u, a);
-    const int64_t n = (int64_t)a.T * a.H;
-    launch(t, "finalize", finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, (const float*)a.y32, n,
-           a.residual, a.y);
+    launch(t, "finalize", finalize_kernel, dim3((unsigned)((a.H / 8 + 255) / 256 * a.T)), dim3(256), s, 0u, a);
     return hipGetLastError();
 }
 

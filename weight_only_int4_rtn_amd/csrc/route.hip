@@ -281,13 +281,17 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= (int64_t)a.T * a.k) return;
     const int v = a.lrank[p];
-    if (v < 0) return;
+    if (v < 0) {
+        a.inv[p] = -1;
+        return;
+    }
     const int e = v >> 8, rank = v & 255;
     const int t = (int)(p / a.k);
     const int b = t / kRouteBlockT;
     const int pos = a.hist[(int64_t)b * a.E + e] + rank;
     a.sorted[pos] = (int)p;
     a.tokw[pos] = int2{t, __float_as_int(a.wts[p])};
+    a.inv[p] = pos;
 }
 
 hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t) {
