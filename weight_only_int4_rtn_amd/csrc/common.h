@@ -156,7 +156,7 @@ __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return s
 
 struct WsLayout {
     size_t sync, ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
-        ystage, inv, tokw, rec, xp, total;
+        ystage, inv, asum, tokw, rec, xp, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
     int nblk;           // routing blocks of the large-batch path
@@ -306,7 +306,8 @@ struct PrefillArgs {
     uint16_t* abuf;
     int64_t rows_a;
     int64_t width_a;
-    float* ystage;              // [rows_a, H] fp32: router-weighted down output of each sorted row
+    float* asum;                // [rows_a, width_a / 128] fp32: sum of each a row over each group
+    float* ystage;              // [rows_a, H] fp32: down output of each sorted row (unweighted)
     const int32_t* inv;         // [T*k] sorted position of each pair (-1: dropped)
     const uint16_t* residual;
     uint16_t* y;

@@ -1,145 +1,327 @@
 // Large-batch W4A16 expert FFN as two grouped GEMMs on bf16 MFMA (gfx950).
 //
-// gk_prefill_kernel: items are (M-tile of up to 128 tokens of one expert, 64 output
-//   columns = 64 gate rows + the 64 matching up rows).  Per 128-column group of K:
-//     - the tile's activation rows (already K-slice reordered by the routing kernel) are
-//       copied global -> LDS by direct LDS loads (no registers), into an XOR-swizzled
-//       double buffer, the next group's copy overlapping this group's MFMAs;
-//     - each wave (2 x 2 waves, 64 rows x 64 code rows) loads its code rows straight
-//       from global memory, expands them in registers and runs 16x16x32 MFMAs seeded
-//       with -OFF * sum(x) of the group (group sums from the routing kernel); the
-//       group scale is applied to the fp32 partial.
-//   Epilogue: a = SiLU(g) * u as bf16, columns written in the reordered K order the
-//   down GEMM consumes, rows in sorted-pair order.
-// dk_prefill_kernel: items are (M-tile, 128 output rows); A is the tile's contiguous
-//   block of a-rows, K = I, staged the same way.  The offset seed is an MFMA against
-//   the constant -OFF.  The router-weighted result is added into an fp32 [T, H]
-//   accumulator with float atomics (each element receives top_k addends, in arrival
-//   order).
-// finalize_kernel: y = bf16(acc + residual).
+// Both GEMMs run as persistent workgroups of 8 waves (2 along M x 4 along N, each wave a
+// 64 x 64 block of 16x16x32 MFMAs) over items of 128 rows of one expert's sorted tokens
+// by 256 code rows:
+//   gk_prefill_kernel: 128 gate rows + the matching 128 up rows (one 128-column group of
+//     the intermediate output), K = H.  Epilogue: a = SiLU(g) * u as bf16 in the K order
+//     the down GEMM consumes, plus the fp32 sum of each a row over that group (the down
+//     GEMM's offset seeds).
+//   dk_prefill_kernel: 256 output rows, K = I.  Epilogue: the unweighted fp32 rows at
+//     their sorted positions; finalize_kernel applies the router weights and sums each
+//     token's rows in slot order (no atomics anywhere).
 //
-// Both GEMMs walk their items with a persistent grid whose size is a multiple of 8;
-// item L is remapped so that each of the 8 XCDs (workgroup id mod 8) takes one
-// contiguous range of items, keeping a tile's activation rows and an expert's codes in
-// that XCD's L2.
+// The K loop is a flat stream of steps (item, 128-column group of K), so the pipeline
+// runs on across item boundaries.  Every operand of a step reaches LDS by direct-to-LDS
+// buffer loads (no registers): the activation tile (XOR-swizzled), the code rows
+// (swizzled so the 16 rows one MFMA fragment reads sit in distinct banks), the code
+// rows' group scales and the activation rows' group sums.  With 4-bit codes steps s+1
+// and s+2 are in flight while step s computes (three LDS stages; 8-bit codes, whose
+// code tile is twice as large, keep two).  Each wave waits for its own step-s loads with
+// s_waitcnt vmcnt and a plain s_barrier covers the other waves; a __syncthreads() there
+// would also wait for the later steps' loads.
+//
+// Codes enter the MFMA as exact bf16 integers (see dq4 / dq8 in common.h): the
+// accumulator of a group starts from -OFF * (sum of the group's activations) and the
+// group scale multiplies the fp32 partial.
+//
+// Routed items (code width BITS) and the shared expert's items (SBITS) are walked as two
+// separate streams by every workgroup.
 #include "common.h"
 
 namespace w4a16 {
 
 namespace {
 
-constexpr int MT = kPrefillMT;       // 128 rows per M-tile
-constexpr int kChunks = kGroup / 8;  // 16-byte chunks per staged row (one group of K)
-constexpr int kTileElems = MT * kGroup;
-constexpr int kGkCols = 64;          // output columns per gate/up item
-constexpr int kDkRows = 128;         // output rows per down item
+constexpr int MT = kPrefillMT;                // 128 rows per item
+constexpr int NT = 256;                       // code rows per item
+constexpr int kPWaves = 8;                    // 2 (M) x 4 (N)
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kAStageBytes = MT * kGroup * 2;   // 32 KB of activations per step
+constexpr int kSeedSlots = 64 * kPWaves;        // 16 real row sums per wave, 4 B each
+constexpr int kScaleSlots = 64 * kPWaves;       // 32 real code-row scale words per wave, 4 B each
+constexpr int kMaxItems = 32;                   // items one workgroup walks (the grid grows if needed)
 
-struct TileRows {
-    int count;        // valid rows in the tile
-    int tok_base;     // routed: first sorted position; shared: first token
-    int orow_base;    // first row of the tile in the gate/up output buffer
-    bool shared;
+template <int BITS>
+struct Pipe {
+    static constexpr int kStages = BITS == 4 ? 3 : 2;
+    static constexpr int kRowBytes = kGroup * BITS / 8;     // one code row's group: 64 / 128 B
+    static constexpr int kChunksPerRow = kRowBytes / 16;    // 4 / 8
+    static constexpr int kBStageBytes = NT * kRowBytes;     // 16 / 32 KB
+    static constexpr int kBLoads = kBStageBytes / (kPThreads * 16);   // per wave per step: 2 / 4
+    static constexpr int kStageBytes = kAStageBytes + kBStageBytes + kSeedSlots * 4 + kScaleSlots * 4;
+    // vector-memory instructions per wave per step: A (4) + B + row sums (1) + scales (1)
+    static constexpr int kLoadsPerStep = 4 + kBLoads + 2;
 };
 
-// Item L of the persistent walk; false when beyond the real work.
-__device__ __forceinline__ bool item_tile(const PrefillArgs& a, int L, int nb, int SB, TileRows* tr, int* e,
-                                          int* nblk) {
-    const int routed_items = a.meta[1] * nb;
-    *nblk = L % nb;
-    if (L < routed_items) {
-        const int tile = L / nb;
-        *e = a.tiles[2 * tile];
+struct Item {        // one work item, resolved into LDS at kernel start
+    int e;           // expert (-1: the shared expert)
+    int row0;        // first row of the tile: sorted position (routed) or token (shared)
+    int orow0;       // first row of the tile in the a / staging buffers
+    int count;       // valid rows
+    int nblk;        // N block
+};
+
+// Item L of a walk with nb N blocks per tile: routed tiles, or (SHARED) the shared
+// expert's tiles of 128 consecutive tokens.  count 0: no work.
+template <bool SHARED>
+__device__ Item make_item(const PrefillArgs& a, int L, int nb) {
+    Item it{};
+    it.nblk = L % nb;
+    const int tile = L / nb;
+    if constexpr (!SHARED) {
+        it.e = a.tiles[2 * tile];
         const int m0 = a.tiles[2 * tile + 1];
-        const int pos0 = a.offsets[*e];
-        tr->count = min(MT, a.offsets[*e + 1] - pos0 - m0);
-        tr->tok_base = pos0 + m0;
-        tr->orow_base = pos0 + m0;
-        tr->shared = false;
-        return true;
-    }
-    if (SB == 0) return false;
-    const int st = (L - routed_items) / nb;
-    if (st * MT >= a.T) return false;
-    *e = -1;
-    tr->count = min(MT, a.T - st * MT);
-    tr->tok_base = st * MT;
-    tr->orow_base = a.T * a.k + st * MT;
-    tr->shared = true;
-    return true;
-}
-
-// Swizzled LDS position (in 16-byte chunks) of logical chunk c of tile row r.
-__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 15)); }
-
-// The tile row and logical chunk that lane copies for direct load j of its wave: lane l
-// of load j fills LDS chunk L = (8w + j) * 64 + l, i.e. row L / 16 at logical chunk
-// (L % 16) ^ (row % 16).
-__device__ __forceinline__ void stage_coords(int j, int* row, int* chunk) {
-    const int L = ((threadIdx.x >> 6) * 8 + j) * 64 + (threadIdx.x & 63);
-    *row = L / kChunks;
-    *chunk = (L % kChunks) ^ (*row & 15);
-}
-
-// Direct global -> LDS copy of one 128 x 128 group of a tile: 8 buffer loads of 64 lanes
-// x 16 B per wave.  voff[j] is the byte offset of this lane's source (row and chunk) for
-// the first group; col_bytes (scalar) selects the group.  The host keeps every staged
-// array below 2^32 bytes.
-__device__ __forceinline__ void stage_group(__amdgpu_buffer_rsrc_t src, const uint32_t (&voff)[8], uint32_t col_bytes,
-                                            uint16_t* lds_tile) {
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, lds_tile + (wave * 8 + j) * 64 * 8, 16, voff[j], col_bytes, 0, 0);
-}
-
-// Expands one lane's codes for MFMA k-step i into bf16 operand(s).
-template <int BITS>
-__device__ __forceinline__ void expand(const u32x4_t (&braw)[BITS / 4], int i, u32x4_t& b0, u32x4_t& b1,
-                                       uint32_t M) {
-    if constexpr (BITS == 4) {
-        b0 = dq4(braw[0][i], M);
+        const int pos0 = a.offsets[it.e];
+        it.count = min(MT, a.offsets[it.e + 1] - pos0 - m0);
+        it.row0 = pos0 + m0;
+        it.orow0 = pos0 + m0;
     } else {
-        dq8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3], b0, b1, M);
+        it.e = -1;
+        it.count = min(MT, a.T - tile * MT);
+        it.row0 = tile * MT;
+        it.orow0 = a.T * a.k + tile * MT;
+    }
+    return it;
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// Workgroup barrier that orders the compiler's memory accesses but waits for nothing
+// (the waits are explicit).
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
+// Direct global -> LDS copies (buffer_load ... lds: lane l's 16 or 4 bytes land at the
+// wave-uniform LDS address + 16 l or + 4 l).  Issued from inline asm so that the compiler,
+// which cannot tell the stages apart, does not wait for every copy in flight before each
+// LDS read; the step waits above carry the ordering instead.  The copies write no
+// registers.  Buffer descriptor: base, num_records = bytes, gfx9-family word 3.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t dma_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return i32x4_t{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), (int32_t)bytes, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is set here, on purpose
+__device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds_offset(lds)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 ::"s"(lds_offset(lds)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every staged array: reads zero
+
+// ------------------------------------------------------------- operand layouts
+//
+// A stage: 128 rows x 16 chunks of 16 B; chunk c of row r sits at r * 16 + (c ^ (r & 15)).
+// A-load j (0..3) of wave w, lane l, fills chunk C = (4w + j) * 64 + l.
+__device__ __forceinline__ int a_swz(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+__device__ __forceinline__ void a_coords(int j, int* r, int* c) {
+    const int C = ((threadIdx.x >> 6) * 4 + j) * 64 + (threadIdx.x & 63);
+    *r = C >> 4;
+    *c = (C & 15) ^ (*r & 15);
+}
+
+// B stage: 256 code rows x kChunksPerRow chunks.  Row R = 64 wn + 16 b + ml holds wave
+// wn's code subtile b, row ml.  Physical chunk p of row R holds logical chunk
+// p ^ swizzle(R), which puts the 16 rows one fragment read touches in distinct banks.
+template <int BITS>
+__device__ __forceinline__ int b_swizzle(int R) {
+    return BITS == 4 ? ((R >> 2) & 3) : ((R >> 1) & 7);
+}
+template <int BITS>
+__device__ __forceinline__ void b_coords(int j, int* R, int* c) {
+    using P = Pipe<BITS>;
+    const int C = ((threadIdx.x >> 6) * P::kBLoads + j) * 64 + (threadIdx.x & 63);
+    *R = C / P::kChunksPerRow;
+    *c = (C % P::kChunksPerRow) ^ b_swizzle<BITS>(*R);
+}
+
+// Row sums: wave w's load covers rows 16 w .. 16 w + 15 in lanes 0..15; row r at slot
+// (r / 16) * 64 + r % 16.  Scales: wave w's load covers code rows 32 w .. 32 w + 31 in
+// lanes 0..31; code row R at slot (R / 32) * 64 + R % 32, as the aligned 4-byte word
+// holding its bf16 scale (the low half when the scale's index is even).
+__device__ __forceinline__ int seed_slot(int r) { return (r >> 4) * 64 + (r & 15); }
+__device__ __forceinline__ int scale_slot(int R) { return (R >> 5) * 64 + (R & 31); }
+
+// Gate/up code row of stage row R for N block nblk (one group of I): wave wn's subtiles
+// 0, 1 are gate rows, 2, 3 the matching up rows.
+__device__ __forceinline__ int gk_code_row(int R, int nblk, int64_t I_e) {
+    const int wn = R >> 6, b = (R >> 4) & 3, ml = R & 15;
+    return (b >= 2 ? (int)I_e : 0) + nblk * kGroup + 32 * wn + 16 * (b & 1) + ml;
+}
+
+// --------------------------------------------------------------- per-item issue state
+
+// What a wave needs to issue the loads of any step of one item.
+struct IssueState {
+    i32x4_t a_r, b_r, seed_r, s_r;
+    uint32_t a_off[4];    // per A-load: the lane's source byte offset at group 0
+    uint32_t b_off[4];    // per B-load (kBLoads used)
+    uint32_t seed_off;    // the lane's row-sum offset at group 0 (kOob: lanes 16..63)
+    uint32_t s_off;       // byte offset of the lane's scale at group 0 (kOob: lanes 32..63)
+};
+
+template <int BITS, bool GATE_UP>
+__device__ void prepare_issue(const PrefillArgs& a, const Item& it, const ExpertSet& es, const int (&tok)[5],
+                              IssueState& st) {
+    using P = Pipe<BITS>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t I_e = es.I;
+    const int64_t eb = it.e < 0 ? 0 : it.e;
+    if constexpr (GATE_UP) {
+        const int64_t H = a.H;
+        const int G = (int)(H / kGroup);
+        const int64_t row_bytes = H * BITS / 8;
+        st.a_r = dma_rsrc(a.xp, (uint32_t)(a.T * H * 2));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int r, c;
+            a_coords(j, &r, &c);
+            st.a_off[j] = ((uint32_t)tok[j] * (uint32_t)H + c * 8) * 2;
+        }
+        st.b_r = dma_rsrc(es.w13 + eb * (2 * I_e * H * BITS / 32), (uint32_t)(2 * I_e * row_bytes));
+#pragma unroll
+        for (int j = 0; j < P::kBLoads; ++j) {
+            int R, c;
+            b_coords<BITS>(j, &R, &c);
+            st.b_off[j] = (uint32_t)(gk_code_row(R, it.nblk, I_e) * row_bytes) + c * 16;
+        }
+        st.seed_r = dma_rsrc(a.xsum, (uint32_t)(a.T * G * 4));
+        st.seed_off = lane < 16 ? (uint32_t)tok[4] * G * 4 : kOob;
+        st.s_r = dma_rsrc(es.s13 + eb * 2 * I_e * G, (uint32_t)(2 * I_e * G * 2));
+        st.s_off = lane < 32 ? (uint32_t)(gk_code_row(32 * wave + lane, it.nblk, I_e) * G * 2) : kOob;
+    } else {
+        const int G2 = (int)(I_e / kGroup);
+        const int GW = (int)(a.width_a / kGroup);
+        const int64_t row_bytes = I_e * BITS / 8;
+        st.a_r = dma_rsrc(a.abuf, (uint32_t)(a.rows_a * a.width_a * 2));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int r, c;
+            a_coords(j, &r, &c);
+            st.a_off[j] = ((uint32_t)(it.orow0 + min(r, it.count - 1)) * (uint32_t)a.width_a + c * 8) * 2;
+        }
+        const int h0 = it.nblk * NT;   // rows past H read zeros (the buffer ends at H)
+        st.b_r = dma_rsrc(es.w2 + eb * (a.H * I_e * BITS / 32), (uint32_t)(a.H * row_bytes));
+#pragma unroll
+        for (int j = 0; j < P::kBLoads; ++j) {
+            int R, c;
+            b_coords<BITS>(j, &R, &c);
+            st.b_off[j] = (uint32_t)((h0 + R) * row_bytes) + c * 16;
+        }
+        st.seed_r = dma_rsrc(a.asum, (uint32_t)(a.rows_a * GW * 4));
+        st.seed_off = lane < 16 ? (uint32_t)(it.orow0 + min(16 * wave + lane, it.count - 1)) * GW * 4 : kOob;
+        st.s_r = dma_rsrc(es.s2 + eb * a.H * G2, (uint32_t)(a.H * G2 * 2));
+        st.s_off = lane < 32 ? (uint32_t)((h0 + 32 * wave + lane) * G2 * 2) : kOob;
     }
 }
 
-// One wave's 64 x 64 block for one group: 4 M-subtiles x 4 code subtiles of 16x16.
-// The group's A fragments (4 M-subtiles x 4 k-steps) are read from LDS once and held;
-// code subtiles are expanded one at a time, so the VALU expansion of subtile b + 1 can
-// run under the MFMAs of subtile b.  seed(mi, av) gives the offset seed of M-subtile mi.
-// With CACHED_SEED the seeds are computed once per group and held; otherwise seed() is
-// called again for every code subtile (cheap when it is an LDS broadcast read).
-template <int BITS, bool CACHED_SEED, typename Seed>
-__device__ __forceinline__ void mfma_group(const uint16_t* A, int wm, const u32x4_t (&braw)[4][BITS / 4],
-                                           const uint32_t (&scp)[2], f32x4_t (&acc)[4][4], Seed&& seed) {
-    const int lane = threadIdx.x & 63;
+// The tokens of the rows a lane's A and row-sum loads read for a gate/up item (padding
+// rows repeat the last real row).
+__device__ __forceinline__ void item_tokens(const PrefillArgs& a, const Item& it, int (&tok)[5]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        int r;
+        if (j < 4) {
+            int c;
+            a_coords(j, &r, &c);
+        } else {
+            r = 16 * wave + (lane & 15);
+        }
+        r = min(r, it.count - 1);
+        tok[j] = it.e < 0 ? it.row0 + r : a.tokw[it.row0 + r].x;
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void issue_step(const IssueState& st, int g, uint8_t* stage) {
+    using P = Pipe<BITS>;
+    const int wave = threadIdx.x >> 6;
+    uint8_t* A = stage;
+    uint8_t* B = stage + kAStageBytes;
+    uint8_t* S = B + P::kBStageBytes;
+    uint8_t* SC = S + kSeedSlots * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(st.a_r, A + ((wave * 4 + j) * 64) * 16, st.a_off[j], (uint32_t)g * kGroup * 2);
+#pragma unroll
+    for (int j = 0; j < P::kBLoads; ++j)
+        dma16(st.b_r, B + ((wave * P::kBLoads + j) * 64) * 16, st.b_off[j], (uint32_t)g * P::kRowBytes);
+    dma4(st.seed_r, S + wave * 64 * 4, st.seed_off, (uint32_t)g * 4);
+    dma4(st.s_r, SC + wave * 64 * 4, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
+}
+
+// ------------------------------------------------------------------- compute
+
+// One step of one wave: its 64 x 64 block (4 M-subtiles x 4 code subtiles) for one
+// group, accumulated into acc with the group scales (D column ml is code row R's).
+// sodd: bit b set when code subtile b's scale sits in the high half of its word.
+template <int BITS>
+__device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4]) {
+    using P = Pipe<BITS>;
+    constexpr float kOff = BITS == 4 ? 136.0f : 2304.0f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
+    const int wm = wave >> 2, wn = wave & 3;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(stage);
+    const uint8_t* B = stage + kAStageBytes;
+    const float* S = reinterpret_cast<const float*>(B + P::kBStageBytes);
+    const uint32_t* SC = reinterpret_cast<const uint32_t*>(S + kSeedSlots);
     const uint32_t M = nibble_mask();
+
     u32x4_t av[4][4];
-    f32x4_t s0[4];
+    f32x4_t seed[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int r = 64 * wm + 16 * mi + ml;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[mi][i] = *reinterpret_cast<const u32x4_t*>(A + swz(r, 4 * q + i) * 8);
-        if constexpr (CACHED_SEED) s0[mi] = seed(mi, av[mi]);
+        for (int i = 0; i < 4; ++i) av[mi][i] = *reinterpret_cast<const u32x4_t*>(A + a_swz(r, 4 * q + i) * 8);
+        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(S + seed_slot(64 * wm + 16 * mi + 4 * q));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) seed[mi][e] = -kOff * xs[e];
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+        const int R = 64 * wn + 16 * b + ml;
+        u32x4_t braw[BITS / 4];
+#pragma unroll
+        for (int c = 0; c < BITS / 4; ++c) {
+            const int lc = (BITS / 4) * q + c;   // logical chunk: this lane's K slice
+            braw[c] = *reinterpret_cast<const u32x4_t*>(B + R * P::kRowBytes + ((lc ^ b_swizzle<BITS>(R)) * 16));
+        }
+        const uint32_t sw = SC[scale_slot(R)];
+        const float sc = bf16_to_f32(((sodd >> b) & 1) ? (sw >> 16) : (sw & 0xffffu));
         f32x4_t t[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) t[mi] = CACHED_SEED ? s0[mi] : seed(mi, av[mi]);
+        for (int mi = 0; mi < 4; ++mi) t[mi] = seed[mi];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             u32x4_t lo, hi;
-            expand<BITS>(braw[b], i, lo, hi, M);
+            if constexpr (BITS == 4) {
+                lo = dq4(braw[0][i], M);
+            } else {
+                dq8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3], lo, hi, M);
+            }
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 t[mi] = mfma16(av[mi][i], lo, t[mi]);
                 if constexpr (BITS == 8) t[mi] = mfma16(av[mi][i], hi, t[mi]);
             }
         }
-        const float sc = bf16_to_f32((scp[b >> 1] >> (16 * (b & 1))) & 0xffffu);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -147,290 +329,231 @@ __device__ __forceinline__ void mfma_group(const uint16_t* A, int wm, const u32x
     }
 }
 
-// ---------------------------------------------------------------- gate / up
+// ------------------------------------------------------------------- epilogues
 
-template <int BITS>
-__device__ void gk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, const int32_t* __restrict__ w13e,
-                        const uint16_t* __restrict__ s13e, int n0, uint16_t* s_a, float* s_xs, int* s_tok) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// a = SiLU(gate) * up for the item's 128 x 128 block, bf16, columns in the reordered K
+// order of the down GEMM; and each row's fp32 sum of those bf16 values (one group of I).
+__device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t (&acc)[4][4], float* s_asum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t H = a.H;
-    const int G = (int)(H / kGroup);
-    constexpr float kOff = BITS == 4 ? 136.0f : 2304.0f;
-    constexpr int kLaneBytes = 32 * BITS / 8, kGroupBytes = kGroup * BITS / 8;
-    const int64_t row_bytes = H * BITS / 8;
-
-    if (tid < MT) {
-        const int r = min(tid, tr.count - 1);   // padding rows repeat a real row
-        s_tok[tid] = tr.shared ? tr.tok_base + r : a.tokw[tr.tok_base + r].x;
-    }
-    __syncthreads();
-
-    const __amdgpu_buffer_rsrc_t xp_r = make_rsrc(a.xp, (uint32_t)(a.T * H * 2));
-    uint32_t voff[8];   // byte offset of each staged chunk's source row and chunk
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int r, c;
-        stage_coords(j, &r, &c);
-        voff[j] = ((uint32_t)s_tok[r] * (uint32_t)H + c * 8) * 2;
-    }
-    auto xs_at = [&](int g) { return a.xsum[(int64_t)s_tok[tid & (MT - 1)] * G + g]; };
-
-    // this wave's 64 code rows: gate rows n0 + 32 wn + 16 b + ml (b = 0, 1), up rows + I_e;
-    // one vector offset per lane, the subtile and group go into the scalar offset
-    const __amdgpu_buffer_rsrc_t b_r = make_rsrc(w13e, (uint32_t)(2 * I_e * row_bytes));
-    const __amdgpu_buffer_rsrc_t s_r = make_rsrc(s13e, (uint32_t)(2 * I_e * G * 2));
-    const uint32_t bvoff = (uint32_t)((n0 + 32 * wn + ml) * row_bytes + q * kLaneBytes);
-    const uint32_t svoff = (uint32_t)((n0 + 32 * wn + ml) * G * 2);
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    u32x4_t braw[4][BITS / 4];
-    uint32_t scp[2];   // the four code subtiles' group scales, bf16 pairs
-    auto load_b = [&](int g) {
-        uint32_t s16[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t roff = (uint32_t)((b >= 2 ? I_e : 0) + 16 * (b & 1));
-#pragma unroll
-            for (int c = 0; c < BITS / 4; ++c)
-                braw[b][c] = buf_load16(b_r, bvoff, roff * (uint32_t)row_bytes + g * kGroupBytes + 16 * c);
-            s16[b] = buf_load_u16(s_r, svoff, (roff * G + g) * 2);
-        }
-        scp[0] = s16[0] | (s16[1] << 16);
-        scp[1] = s16[2] | (s16[3] << 16);
-    };
-
-    stage_group(xp_r, voff, 0, s_a);
-    if (tid < MT) s_xs[tid] = -kOff * xs_at(0);
-    load_b(0);
-
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        __syncthreads();   // group g staged (waits for the direct loads), group g-1 reads done
-        if (g + 1 < G) {
-            stage_group(xp_r, voff, (g + 1) * kGroup * 2, s_a + (buf ^ 1) * kTileElems);
-            if (tid < MT) s_xs[(buf ^ 1) * MT + tid] = -kOff * xs_at(g + 1);
-        }
-        // this group's codes move to bcur; the next group's load into braw
-        u32x4_t bcur[4][BITS / 4];
-        const uint32_t scg[2] = {scp[0], scp[1]};
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int c = 0; c < BITS / 4; ++c) bcur[b][c] = braw[b][c];
-        if (g + 1 < G) load_b(g + 1);
-        const float* xs = s_xs + buf * MT + 64 * wm + 4 * q;
-        mfma_group<BITS, false>(s_a + buf * kTileElems, wm, bcur, scg, acc,
-                                [&](int mi, const u32x4_t(&)[4]) { return *reinterpret_cast<const f32x4_t*>(xs + 16 * mi); });
-    }
-
-    // epilogue: a = SiLU(gate) * up, bf16, columns in the reordered K order of the down GEMM
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 64 * wm + 16 * mi + 4 * q + r;
-                if (m < tr.count) {
-                    const float v = silu_mul(acc[mi][ns][r], acc[mi][2 + ns][r]);
-                    const int col = perm_pos(n0 + 32 * wn + 16 * ns + ml);
-                    a.abuf[(int64_t)(tr.orow_base + m) * a.width_a + col] = (uint16_t)f32_to_bf16(v);
-                }
-            }
-}
-
-// -------------------------------------------------------------------- down
-
-template <int BITS>
-__device__ void dk_item(const PrefillArgs& a, const TileRows& tr, int64_t I_e, const int32_t* __restrict__ w2e,
-                        const uint16_t* __restrict__ s2e, int h0, uint16_t* s_a, int* s_tok, float* s_wt) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int q = lane >> 4, ml = lane & 15;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int G2 = (int)(I_e / kGroup);
-    constexpr int kLaneBytes = 32 * BITS / 8, kGroupBytes = kGroup * BITS / 8;
-    const int64_t row_bytes = I_e * BITS / 8;
-
-    if (tid < MT) {
-        int t = 0;
-        float w = 0.f;
-        if (tid < tr.count) {
-            if (tr.shared) {
-                t = tr.tok_base + tid;
-                w = 1.f;
-            } else {
-                const int2 tw = a.tokw[tr.tok_base + tid];
-                t = tw.x;
-                w = __int_as_float(tw.y);
-            }
-        }
-        s_tok[tid] = t;
-        s_wt[tid] = w;
-    }
-
-    const __amdgpu_buffer_rsrc_t a_r = make_rsrc(a.abuf, (uint32_t)(a.rows_a * a.width_a * 2));
-    uint32_t voff[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int r, c;
-        stage_coords(j, &r, &c);
-        voff[j] = ((uint32_t)(tr.orow_base + min(r, tr.count - 1)) * (uint32_t)a.width_a + c * 8) * 2;
-    }
-    const __amdgpu_buffer_rsrc_t b_r = make_rsrc(w2e, (uint32_t)(a.H * row_bytes));
-    const __amdgpu_buffer_rsrc_t s_r = make_rsrc(s2e, (uint32_t)(a.H * G2 * 2));
-    const uint32_t bvoff = (uint32_t)((h0 + 64 * wn + ml) * row_bytes + q * kLaneBytes);
-    const uint32_t svoff = (uint32_t)((h0 + 64 * wn + ml) * G2 * 2);
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    u32x4_t braw[4][BITS / 4];
-    uint32_t scp[2];
-    auto load_b = [&](int g) {
-        uint32_t s16[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-            for (int c = 0; c < BITS / 4; ++c)
-                braw[b][c] = buf_load16(b_r, bvoff, (uint32_t)(16 * b * row_bytes) + g * kGroupBytes + 16 * c);
-            s16[b] = buf_load_u16(s_r, svoff, (16 * b * G2 + g) * 2);
-        }
-        scp[0] = s16[0] | (s16[1] << 16);
-        scp[1] = s16[2] | (s16[3] << 16);
-    };
-
-    stage_group(a_r, voff, 0, s_a);
-    load_b(0);
-    const u32x4_t neg = neg_offset_operand<BITS>();
-
-    for (int g = 0; g < G2; ++g) {
-        const int buf = g & 1;
-        __syncthreads();
-        if (g + 1 < G2) stage_group(a_r, voff, (g + 1) * kGroup * 2, s_a + (buf ^ 1) * kTileElems);
-        u32x4_t bcur[4][BITS / 4];
-        const uint32_t scg[2] = {scp[0], scp[1]};
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int c = 0; c < BITS / 4; ++c) bcur[b][c] = braw[b][c];
-        if (g + 1 < G2) load_b(g + 1);
-        mfma_group<BITS, true>(s_a + buf * kTileElems, wm, bcur, scg, acc, [&](int, const u32x4_t(&av)[4]) {
-            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s0 = mfma16(av[i], neg, s0);
-            return s0;
-        });
-    }
-
-    // router-weighted rows, stored once each at the row's sorted position (the sum over a
-    // token's experts happens in finalize_kernel, in slot order)
+    const int wm = wave >> 2, wn = wave & 3;
+    const int GW = (int)(a.width_a / kGroup);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 64 * wm + 16 * mi + 4 * q + r;
-            if (m < tr.count) {
-                const float w = s_wt[m];
-                float* yrow = a.ystage + (int64_t)(tr.orow_base + m) * a.H + h0 + 64 * wn + ml;
+            float rs = 0.f;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) yrow[16 * b] = w * acc[mi][b][r];
+            for (int ns = 0; ns < 2; ++ns) {
+                const uint32_t v = f32_to_bf16(silu_mul(acc[mi][ns][r], acc[mi][2 + ns][r]));
+                rs += bf16_to_f32(v);
+                if (m < it.count) {
+                    const int col = perm_pos(it.nblk * kGroup + 32 * wn + 16 * ns + ml);
+                    a.abuf[(int64_t)(it.orow0 + m) * a.width_a + col] = (uint16_t)v;
+                }
+            }
+            rs += __shfl_xor(rs, 1, 16);   // sum over the row's 16 lanes (columns ml)
+            rs += __shfl_xor(rs, 2, 16);
+            rs += __shfl_xor(rs, 4, 16);
+            rs += __shfl_xor(rs, 8, 16);
+            if (ml == 0) s_asum[wn * MT + m] = rs;
+        }
+    wait_lgkm0();
+    bar();
+    if ((int)threadIdx.x < it.count) {
+        const int m = threadIdx.x;
+        const float s = s_asum[m] + s_asum[MT + m] + s_asum[2 * MT + m] + s_asum[3 * MT + m];
+        a.asum[(int64_t)(it.orow0 + m) * GW + it.nblk] = s;
+    }
+    wait_lgkm0();
+    bar();   // s_asum is reused by the next item
+}
+
+// The unweighted fp32 output rows of a down item at their sorted positions.
+__device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t (&acc)[4][4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q = lane >> 4, ml = lane & 15;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int h = it.nblk * NT + 64 * wn + ml;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 64 * wm + 16 * mi + 4 * q + r;
+            if (m < it.count) {
+                float* yrow = a.ystage + (int64_t)(it.orow0 + m) * a.H;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (h + 16 * b < a.H) yrow[h + 16 * b] = acc[mi][b][r];
             }
         }
 }
 
-// Persistent walk over `total` items with the per-XCD contiguous remap.
-template <typename F>
-__device__ __forceinline__ void for_each_item(int total, F&& f) {
+// --------------------------------------------------------------------- driver
+
+// One walk: workgroup b takes items w = b, b + grid, ... of `total` (item index L is
+// remapped so that each XCD, w mod 8, takes one contiguous range: an expert's tiles share
+// that XCD's L2).  The items are resolved once into LDS; the steps of all of them form
+// one pipelined stream.
+template <int BITS, bool GATE_UP, bool SHARED>
+__device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int total, uint8_t* smem,
+                          Item* s_items, float* s_asum, int* s_cnt) {
+    using P = Pipe<BITS>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = (total + 7) / 8;
-    for (int w = blockIdx.x; w < 8 * C; w += gridDim.x) {
-        const int L = (w & 7) * C + (w >> 3);
-        if (L < total) f(L);
+    __syncthreads();   // the previous walk's LDS use is over
+    {
+        const int w = blockIdx.x + tid * (int)gridDim.x;
+        Item it{};
+        bool ok = false;
+        if (tid < kMaxItems && w < 8 * C) {
+            const int L = (w & 7) * C + (w >> 3);
+            if (L < total) {
+                it = make_item<SHARED>(a, L, nb);
+                ok = it.count > 0 && it.nblk * (GATE_UP ? kGroup : NT) < (GATE_UP ? es.I : a.H);
+            }
+        }
+        const uint64_t vm = __ballot(ok);   // compact, keeping the walk order
+        if (lane == 0) s_cnt[wave] = __popcll(vm);
+        __syncthreads();
+        int base = 0;
+        for (int i = 0; i < wave; ++i) base += s_cnt[i];
+        if (ok) s_items[base + __popcll(vm & ((1ull << lane) - 1ull))] = it;
+        __syncthreads();
     }
+    int n_items = 0;
+    for (int i = 0; i < kPWaves; ++i) n_items += s_cnt[i];
+    if (n_items == 0) return;
+    const int G = (int)((GATE_UP ? a.H : es.I) / kGroup);   // groups of K per item
+    const int total_steps = n_items * G;
+
+    // issue side: item ii, group gi; the tokens of the item after it are prefetched
+    int ii = 0, gi = 0, issued = 0;
+    int tok[5] = {0, 0, 0, 0, 0}, tok_next[5] = {0, 0, 0, 0, 0};
+    if constexpr (GATE_UP) {
+        item_tokens(a, s_items[0], tok);
+        if (n_items > 1) item_tokens(a, s_items[1], tok_next);
+    }
+    IssueState st;
+    prepare_issue<BITS, GATE_UP>(a, s_items[0], es, tok, st);
+    auto issue_next = [&]() {
+        issue_step<BITS>(st, gi, smem + (issued % P::kStages) * P::kStageBytes);
+        ++issued;
+        if (++gi == G && ii + 1 < n_items) {
+            ++ii;
+            gi = 0;
+            if constexpr (GATE_UP) {
+#pragma unroll
+                for (int j = 0; j < 5; ++j) tok[j] = tok_next[j];
+                if (ii + 1 < n_items) item_tokens(a, s_items[ii + 1], tok_next);
+            }
+            prepare_issue<BITS, GATE_UP>(a, s_items[ii], es, tok, st);
+        }
+    };
+    for (int p = 0; p < P::kStages - 1 && issued < total_steps; ++p) issue_next();
+
+    // compute side
+    int ci = 0, gc = 0;
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // parity of each of this lane's four code rows' first scale index (row * G) for the
+    // compute item; a step's scale sits in the high half of its word when row * G + g is odd
+    auto row_parity = [&](const Item& it) {
+        const int wn = wave & 3, ml = lane & 15;
+        uint32_t p = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int R = 64 * wn + 16 * b + ml;
+            const int crow = GATE_UP ? gk_code_row(R, it.nblk, es.I) : it.nblk * NT + R;
+            p |= (uint32_t)((crow * G) & 1) << b;
+        }
+        return p;
+    };
+    uint32_t cpar = row_parity(s_items[0]);
+    for (int s = 0; s < total_steps; ++s) {
+        // step s's loads are this wave's oldest outstanding ones; at most the later steps'
+        // (kLoadsPerStep each) may still be out
+        if (issued - s - 1 >= 1) wait_vmcnt<P::kLoadsPerStep>();
+        else wait_vmcnt<0>();
+        bar();   // every wave's step-s data is in LDS, and stage (s - 1) is no longer read
+        if (issued < total_steps) issue_next();
+        compute_step<BITS>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc);
+        if (++gc == G) {
+            const Item cit = s_items[ci];
+            if constexpr (GATE_UP) gk_epilogue(a, cit, acc, s_asum);
+            else dk_epilogue(a, cit, acc);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            gc = 0;
+            if (++ci < n_items) cpar = row_parity(s_items[ci]);
+        }
+    }
+}
+
+template <int BITS>
+constexpr uint32_t pipe_lds_bytes() {
+    return Pipe<BITS>::kStages * Pipe<BITS>::kStageBytes;
 }
 
 }  // namespace
 
+// Dynamic LDS: the stages of the larger pipeline, then the item list and the row-sum
+// scratch.
 template <int BITS, int SBITS>
-__global__ __launch_bounds__(256, 2) void gk_prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTileElems];   // two staged groups
-    __shared__ __attribute__((aligned(16))) float s_xs[2 * MT];
-    __shared__ int s_tok[MT];
-
-    const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
-    const int nb = (int)(Imax / kGkCols);
-    const int shared_items = SBITS ? ((a.T + MT - 1) / MT) * nb : 0;
-    const int total = a.meta[1] * nb + shared_items;
-    for_each_item(total, [&](int L) {
-        TileRows tr;
-        int e, nblk;
-        if (!item_tile(a, L, nb, SBITS, &tr, &e, &nblk)) return;
-        const int n0 = nblk * kGkCols;
-        if (tr.shared) {
-            if constexpr (SBITS != 0)
-                if (n0 < a.shared.I) gk_item<SBITS>(a, tr, a.shared.I, a.shared.w13, a.shared.s13, n0, s_a, s_xs, s_tok);
-        } else if (n0 < a.routed.I) {
-            const int64_t I_e = a.routed.I;
-            gk_item<BITS>(a, tr, I_e, a.routed.w13 + (int64_t)e * (2 * I_e * a.H * BITS / 32),
-                          a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, s_a, s_xs, s_tok);
-        }
-        __syncthreads();
-    });
+__global__ __launch_bounds__(kPThreads) void gk_prefill_kernel(PrefillArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
+    Item* s_items = reinterpret_cast<Item*>(smem + kPipe);
+    float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
+    __shared__ int s_cnt[kPWaves];
+    const int nb = (int)(a.routed.I / kGroup);
+    run_items<BITS, true, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt);
+    if constexpr (SBITS != 0) {
+        const int nbs = (int)(a.shared.I / kGroup);
+        run_items<SBITS, true, true>(a, a.shared, nbs, ((a.T + MT - 1) / MT) * nbs, smem, s_items, s_asum, s_cnt);
+    }
 }
 
 template <int BITS, int SBITS>
-__global__ __launch_bounds__(256, 2) void dk_prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTileElems];
-    __shared__ int s_tok[MT];
-    __shared__ float s_wt[MT];
-    const int nb = (int)(a.H / kDkRows);
-    const int shared_items = SBITS ? ((a.T + MT - 1) / MT) * nb : 0;
-    const int total = a.meta[1] * nb + shared_items;
-    for_each_item(total, [&](int L) {
-        TileRows tr;
-        int e, nblk;
-        if (!item_tile(a, L, nb, SBITS, &tr, &e, &nblk)) return;
-        const int h0 = nblk * kDkRows;
-        if (tr.shared) {
-            if constexpr (SBITS != 0) dk_item<SBITS>(a, tr, a.shared.I, a.shared.w2, a.shared.s2, h0, s_a, s_tok, s_wt);
-        } else {
-            const int64_t I_e = a.routed.I;
-            dk_item<BITS>(a, tr, I_e, a.routed.w2 + (int64_t)e * (a.H * I_e * BITS / 32),
-                          a.routed.s2 + (int64_t)e * a.H * (I_e / kGroup), h0, s_a, s_tok, s_wt);
-        }
-        __syncthreads();
-    });
+__global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
+    Item* s_items = reinterpret_cast<Item*>(smem + kPipe);
+    float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
+    __shared__ int s_cnt[kPWaves];
+    const int nb = (int)((a.H + NT - 1) / NT);
+    run_items<BITS, false, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt);
+    if constexpr (SBITS != 0)
+        run_items<SBITS, false, true>(a, a.shared, nb, ((a.T + MT - 1) / MT) * nb, smem, s_items, s_asum, s_cnt);
 }
 
-// y[t] = sum over slots j in order of the staged row of pair (t, j), then the shared
-// expert's row, then the residual; rounded once to bf16.  A token's row is split over
-// ceil(H / 2048) blocks of 256 threads x 8 columns.  Deterministic: no atomics anywhere.
+// y[t] = sum over slots j in order of w[t, j] times the staged row of pair (t, j), then
+// the shared expert's row, then the residual; rounded once to bf16.  A token's row is
+// split over ceil(H / 2048) blocks of 256 threads x 8 columns.  No atomics anywhere.
 __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
     const int nbx = (int)((a.H / 8 + 255) / 256);
     const int t = (int)(blockIdx.x / nbx);
     const int64_t c = ((int64_t)(blockIdx.x % nbx) * blockDim.x + threadIdx.x) * 8;
     if (c >= a.H) return;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto add_row = [&](int64_t row) {
+    auto add_row = [&](int64_t row, float w) {
         const float4* p = reinterpret_cast<const float4*>(a.ystage + row * a.H + c);
         const float4 v0 = p[0], v1 = p[1];
-        s[0] += v0.x; s[1] += v0.y; s[2] += v0.z; s[3] += v0.w;
-        s[4] += v1.x; s[5] += v1.y; s[6] += v1.z; s[7] += v1.w;
+        s[0] += w * v0.x; s[1] += w * v0.y; s[2] += w * v0.z; s[3] += w * v0.w;
+        s[4] += w * v1.x; s[5] += w * v1.y; s[6] += w * v1.z; s[7] += w * v1.w;
     };
     for (int j = 0; j < a.k; ++j) {
         const int pos = a.inv[(int64_t)t * a.k + j];
-        if (pos >= 0) add_row(pos);
+        if (pos >= 0) add_row(pos, a.wts[(int64_t)t * a.k + j]);
     }
-    if (a.shared.bits) add_row((int64_t)a.T * a.k + t);
+    if (a.shared.bits) add_row((int64_t)a.T * a.k + t, 1.0f);
     const int64_t o = (int64_t)t * a.H + c;
     if (a.residual) {
         const u32x4_t r = *reinterpret_cast<const u32x4_t*>(a.residual + o);
@@ -448,20 +571,31 @@ __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
 
 namespace {
 
-unsigned persistent_grid(int64_t max_items) {
-    int64_t g = std::min<int64_t>(max_items, 512);
-    g = std::max<int64_t>(g, 8);
+unsigned prefill_grid(int64_t max_items) {
+    // one workgroup per CU; more when a workgroup would walk more than kMaxItems items
+    int64_t g = std::max<int64_t>(256, (max_items + 8 + kMaxItems - 1) / kMaxItems);
+    g = std::min<int64_t>(g, std::max<int64_t>(max_items, 8));
     return (unsigned)((g + 7) / 8 * 8);
 }
 
 template <int BITS, int SBITS>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
-    const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
+    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
+    constexpr uint32_t lds = kPipe + kMaxItems * sizeof(Item) + 4 * MT * 4;
+    static_assert(lds + 64 <= 160 * 1024, "LDS budget of one workgroup");
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gk_prefill_kernel<BITS, SBITS>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dk_prefill_kernel<BITS, SBITS>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        return true;
+    }();
+    (void)attr;
     const int64_t shared_tiles = SBITS ? (a.T + MT - 1) / MT : 0;
-    const int64_t gk_items = (a.max_tiles + shared_tiles) * (Imax / kGkCols);
-    const int64_t dk_items = (a.max_tiles + shared_tiles) * (a.H / kDkRows);
-    launch(t, "gk_prefill", gk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(gk_items)), dim3(256), s, 0u, a);
-    launch(t, "dk_prefill", dk_prefill_kernel<BITS, SBITS>, dim3(persistent_grid(dk_items)), dim3(256), s, 0u, a);
+    const int64_t gk_items = std::max(a.max_tiles * (a.routed.I / kGroup), shared_tiles * (a.shared.I / kGroup));
+    const int64_t dk_items = std::max(a.max_tiles, shared_tiles) * ((a.H + NT - 1) / NT);
+    launch(t, "gk_prefill", gk_prefill_kernel<BITS, SBITS>, dim3(prefill_grid(gk_items)), dim3(kPThreads), s, lds, a);
+    launch(t, "dk_prefill", dk_prefill_kernel<BITS, SBITS>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
     launch(t, "finalize", finalize_kernel, dim3((unsigned)((a.H / 8 + 255) / 256 * a.T)), dim3(256), s, 0u, a);
     return hipGetLastError();
 }
