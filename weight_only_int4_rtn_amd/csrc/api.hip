@@ -102,7 +102,7 @@ WsLayout layout(const moe_w4a16_args* a) {
         L.tiles = take((size_t)L.max_tiles * 8);
         L.xsum = take((size_t)T * (H / kGroup) * 4);
         L.xp = take((size_t)T * H * 2);
-        L.ystage = take((size_t)L.rows_a * H * 4);
+        L.ystage = take((size_t)L.rows_a * H * 2);
         L.asum = take((size_t)L.rows_a * (L.width_a / kGroup) * 4);
         L.inv = take(P * 4);
     }
@@ -246,7 +246,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     p.abuf = abuf;
     p.rows_a = L.rows_a;
     p.width_a = L.width_a;
-    p.ystage = static_cast<float*>(at(L.ystage));
+    p.ystage = static_cast<uint16_t*>(at(L.ystage));
     p.asum = static_cast<float*>(at(L.asum));
     p.inv = r.inv;
     p.residual = a->residual;

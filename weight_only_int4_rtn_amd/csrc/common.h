@@ -28,6 +28,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The same rounding for activations and outputs by the hardware conversion
+// (v_cvt_pk_bf16_f32, round to nearest even; a NaN stays a NaN with its own payload).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // ------------------------------------------------------------------- MFMA
 
 // D = A * B + C with A 16x32, B 32x16 bf16 and C/D 16x16 fp32 (gfx950).
@@ -167,7 +176,7 @@ struct WsLayout {
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
 constexpr int kTinyP = 16;       // T * k up to this (and H <= kTinyMaxH) take the single-launch path
 constexpr int kTinyMaxH = 4096;
-constexpr int kRouteBlockT = 64; // tokens per routing block on the large-batch path
+constexpr int kRouteBlockT = 32; // tokens per routing block on the large-batch path
 constexpr int kPrefillMT = 128;  // tokens per M-tile of the large-batch grouped GEMM
 
 // ------------------------------------------------------------- stage timer
@@ -307,7 +316,7 @@ struct PrefillArgs {
     int64_t rows_a;
     int64_t width_a;
     float* asum;                // [rows_a, width_a / 128] fp32: sum of each a row over each group
-    float* ystage;              // [rows_a, H] fp32: down output of each sorted row (unweighted)
+    uint16_t* ystage;           // [rows_a, H] bf16: down output of each sorted row (unweighted)
     const int32_t* inv;         // [T*k] sorted position of each pair (-1: dropped)
     const uint16_t* residual;
     uint16_t* y;

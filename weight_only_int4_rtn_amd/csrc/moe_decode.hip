@@ -159,7 +159,7 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
         }
         const int m = 4 * q + r;
         const int64_t idx = (int64_t)(row_base + m) * width_a + n0 + ml;
-        const uint32_t v = f32_to_bf16(silu_mul(gs, us));
+        const uint32_t v = cvt_bf16(silu_mul(gs, us));
         if constexpr (WT) {   // write-through to memory (sc1): another XCD reads it in this launch
             if (m < rows)
                 __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, make_rsrc(abuf, abuf_bytes),
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
         const int64_t o = (int64_t)t * a.H + h0 + n;
         if (gridDim.y == 1) {
             const float r = a.residual ? bf16_to_f32(a.residual[o]) : 0.f;
-            a.y[o] = (uint16_t)f32_to_bf16(s + r);
+            a.y[o] = (uint16_t)cvt_bf16(s + r);
         } else {
             a.part[(int64_t)blockIdx.y * T * a.H + o] = s;
         }
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(256) void dk_combine_kernel(const float* __restrict
     float s = 0.f;
     for (int sp = 0; sp < splits; ++sp) s += part[(int64_t)sp * n + i];
     if (residual) s += bf16_to_f32(residual[i]);
-    y[i] = (uint16_t)f32_to_bf16(s);
+    y[i] = (uint16_t)cvt_bf16(s);
 }
 
 // ------------------------------------------------------------------ tiny batches
@@ -703,7 +703,7 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn) {
         const int t = i >> 4, n = i & 15;
         const int64_t o = (int64_t)t * a.H + h0 + n;
         const float res = a.residual ? bf16_to_f32(a.residual[o]) : 0.f;
-        a.y[o] = (uint16_t)f32_to_bf16(s + res);
+        a.y[o] = (uint16_t)cvt_bf16(s + res);
     }
     if (threadIdx.x == 0) {   // exit count; the last down workgroup resets every counter
         const int g = d >> 4, gsz = min(16, n_dk - (g << 4)), ng = (n_dk + 15) >> 4;

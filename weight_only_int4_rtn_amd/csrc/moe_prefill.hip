@@ -7,9 +7,9 @@
 //     the intermediate output), K = H.  Epilogue: a = SiLU(g) * u as bf16 in the K order
 //     the down GEMM consumes, plus the fp32 sum of each a row over that group (the down
 //     GEMM's offset seeds).
-//   dk_prefill_kernel: 256 output rows, K = I.  Epilogue: the unweighted fp32 rows at
-//     their sorted positions; finalize_kernel applies the router weights and sums each
-//     token's rows in slot order (no atomics anywhere).
+//   dk_prefill_kernel: 256 output rows, K = I.  Epilogue: the unweighted rows, rounded to
+//     bf16, at their sorted positions; finalize_kernel applies the router weights and sums
+//     each token's rows in fp32 in slot order (no atomics anywhere).
 //
 // The K loop is a flat stream of steps (item, 128-column group of K), so the pipeline
 // runs on across item boundaries.  Every operand of a step reaches LDS by direct-to-LDS
@@ -107,18 +107,19 @@ __device__ __forceinline__ i32x4_t dma_rsrc(const void* p, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     return i32x4_t{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), (int32_t)bytes, 0x00020000};
 }
+// LDS byte address of a pointer into shared memory (wave-uniform).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is set here, on purpose
-__device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void dma16(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds_offset(lds)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void dma4(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds_offset(lds)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -248,21 +249,19 @@ __device__ __forceinline__ void item_tokens(const PrefillArgs& a, const Item& it
     }
 }
 
+// stage: LDS byte address of the stage the step goes to.
 template <int BITS>
-__device__ __forceinline__ void issue_step(const IssueState& st, int g, uint8_t* stage) {
+__device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t stage) {
     using P = Pipe<BITS>;
-    const int wave = threadIdx.x >> 6;
-    uint8_t* A = stage;
-    uint8_t* B = stage + kAStageBytes;
-    uint8_t* S = B + P::kBStageBytes;
-    uint8_t* SC = S + kSeedSlots * 4;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t A = stage, B = stage + kAStageBytes, S = B + P::kBStageBytes, SC = S + kSeedSlots * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(st.a_r, A + ((wave * 4 + j) * 64) * 16, st.a_off[j], (uint32_t)g * kGroup * 2);
+    for (int j = 0; j < 4; ++j) dma16(st.a_r, A + (wave * 4 + j) * 1024, st.a_off[j], (uint32_t)g * kGroup * 2);
 #pragma unroll
     for (int j = 0; j < P::kBLoads; ++j)
-        dma16(st.b_r, B + ((wave * P::kBLoads + j) * 64) * 16, st.b_off[j], (uint32_t)g * P::kRowBytes);
-    dma4(st.seed_r, S + wave * 64 * 4, st.seed_off, (uint32_t)g * 4);
-    dma4(st.s_r, SC + wave * 64 * 4, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
+        dma16(st.b_r, B + (wave * P::kBLoads + j) * 1024, st.b_off[j], (uint32_t)g * P::kRowBytes);
+    dma4(st.seed_r, S + wave * 256, st.seed_off, (uint32_t)g * 4);
+    dma4(st.s_r, SC + wave * 256, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
 }
 
 // ------------------------------------------------------------------- compute
@@ -346,7 +345,7 @@ __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
             float rs = 0.f;
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) {
-                const uint32_t v = f32_to_bf16(silu_mul(acc[mi][ns][r], acc[mi][2 + ns][r]));
+                const uint32_t v = cvt_bf16(silu_mul(acc[mi][ns][r], acc[mi][2 + ns][r]));
                 rs += bf16_to_f32(v);
                 if (m < it.count) {
                     const int col = perm_pos(it.nblk * kGroup + 32 * wn + 16 * ns + ml);
@@ -370,7 +369,8 @@ __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
     bar();   // s_asum is reused by the next item
 }
 
-// The unweighted fp32 output rows of a down item at their sorted positions.
+// The unweighted output rows of a down item, rounded to bf16, at their sorted positions
+// (pairs of adjacent columns, exchanged between neighbouring lanes, go out as 4 bytes).
 __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t (&acc)[4][4]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
@@ -381,11 +381,15 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 64 * wm + 16 * mi + 4 * q + r;
-            if (m < it.count) {
-                float* yrow = a.ystage + (int64_t)(it.orow0 + m) * a.H;
+            uint16_t* yrow = a.ystage + (int64_t)(it.orow0 + m) * a.H;
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    if (h + 16 * b < a.H) yrow[h + 16 * b] = acc[mi][b][r];
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t v = cvt_bf16(acc[mi][b][r]);
+                // the neighbouring column: DPP quad_perm [1,0,3,2] swaps adjacent lanes
+                const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false);
+                // even lanes store (col, col + 1); the row and columns are in range for both lanes
+                if (m < it.count && (ml & 1) == 0 && h + 16 * b < a.H)
+                    *reinterpret_cast<uint32_t*>(yrow + h + 16 * b) = v | (nb << 16);
             }
         }
 }
@@ -437,8 +441,9 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
     }
     IssueState st;
     prepare_issue<BITS, GATE_UP>(a, s_items[0], es, tok, st);
+    const uint32_t lds0 = lds_offset(smem);
     auto issue_next = [&]() {
-        issue_step<BITS>(st, gi, smem + (issued % P::kStages) * P::kStageBytes);
+        issue_step<BITS>(st, gi, lds0 + (uint32_t)(issued % P::kStages) * P::kStageBytes);
         ++issued;
         if (++gi == G && ii + 1 < n_items) {
             ++ii;
@@ -544,10 +549,12 @@ __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
     if (c >= a.H) return;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     auto add_row = [&](int64_t row, float w) {
-        const float4* p = reinterpret_cast<const float4*>(a.ystage + row * a.H + c);
-        const float4 v0 = p[0], v1 = p[1];
-        s[0] += w * v0.x; s[1] += w * v0.y; s[2] += w * v0.z; s[3] += w * v0.w;
-        s[4] += w * v1.x; s[5] += w * v1.y; s[6] += w * v1.z; s[7] += w * v1.w;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.ystage + row * a.H + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[2 * e] += w * bf16_to_f32(v[e] & 0xffffu);
+            s[2 * e + 1] += w * bf16_to_f32(v[e] >> 16);
+        }
     };
     for (int j = 0; j < a.k; ++j) {
         const int pos = a.inv[(int64_t)t * a.k + j];
@@ -565,7 +572,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
     }
     u32x4_t out;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = f32_to_bf16(s[2 * e]) | (f32_to_bf16(s[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) out[e] = cvt_bf16x2(s[2 * e], s[2 * e + 1]);
     *reinterpret_cast<u32x4_t*>(a.y + o) = out;
 }
 

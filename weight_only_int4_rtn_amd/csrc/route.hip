@@ -134,7 +134,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
 
 // ------------------------------------------------------------------ large batch
 
-// One workgroup per block of kRouteBlockT tokens (16 waves, 4 tokens each).
+// One workgroup per block of kRouteBlockT tokens (16 waves, 2 tokens each).
 __global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
     __shared__ int s_ids[kRouteBlockT * kMaxK];
     __shared__ int s_cnt[kMaxE];
