@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 2
+#define W4A16_ABI_VERSION 3
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -140,9 +140,9 @@ typedef struct moe_w4a16_args {
     int32_t* sorted_pairs;         /* optional out, int32 [T*top_k]: pair ids t*top_k+j by   */
                                    /* (expert, token) ascending                              */
     void* workspace;               /* device scratch, >= moe_w4a16_workspace_size(args);    */
-                                   /* its first 16 KiB must be zero before the first call   */
-                                   /* (moe_w4a16_workspace_init) and stay owned by the      */
-                                   /* library: every forward leaves them zero               */
+                                   /* its first W4A16_WORKSPACE_HEAD_BYTES must be zero     */
+                                   /* before the first call (moe_w4a16_workspace_init) and  */
+                                   /* then stay owned by the library across calls           */
     size_t workspace_bytes;
 } moe_w4a16_args;
 
@@ -150,15 +150,20 @@ typedef struct moe_w4a16_args {
  * top_k, shared_bits and shared_I only).  Returns 0 when the shapes are invalid. */
 size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
 
+/* Bytes at the start of every workspace that carry state from one forward to the next. */
+#define W4A16_WORKSPACE_HEAD_BYTES 147456
+
 /*
- * moe_w4a16_workspace_init - zero the head of a new workspace (its first 16 KiB), once,
- * before the workspace's first forward.  The head holds the counters that the
- * single-launch path for tiny batches (T * top_k <= 16, H <= 4096) uses to hand the
- * gate/up results to the down projection inside one kernel; each forward returns them
- * to zero, so a workspace needs this once, not per call (a zero-filled allocation needs
- * none).  Enqueued on `stream` as a small fill kernel (no memset node, so it may be
- * captured in a graph).  Errors: W4A16_ERR_INVALID_ARG for NULL or a misaligned pointer,
- * W4A16_ERR_WORKSPACE when workspace_bytes < 16 KiB.
+ * moe_w4a16_workspace_init - zero the head of a new workspace (its first
+ * W4A16_WORKSPACE_HEAD_BYTES), once, before the workspace's first forward.  The head
+ * belongs to the single-launch path for tiny batches (T * top_k <= 16, H <= 4096), whose
+ * gate/up workgroups hand their results to the down-projection workgroups of the same
+ * kernel: exit counters (zero between calls), an epoch number that each call advances, and
+ * the handed-over values, each tagged with the epoch of the call that wrote it.  A
+ * workspace needs this once, not per call (a zero-filled allocation needs none).
+ * Enqueued on `stream` as a small fill kernel (no memset node, so it may be captured in a
+ * graph).  Errors: W4A16_ERR_INVALID_ARG for NULL or a misaligned pointer,
+ * W4A16_ERR_WORKSPACE when workspace_bytes < W4A16_WORKSPACE_HEAD_BYTES.
  */
 int moe_w4a16_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 

@@ -47,7 +47,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 2
+    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 3
     assert _lib.status_string(0) == "W4A16_OK"
     assert _lib.status_string(3) == "W4A16_ERR_WORKSPACE"
     assert _lib.status_string(99) == "W4A16_UNKNOWN_STATUS"
@@ -136,8 +136,14 @@ def test_workspace_init_validation(L):
     """Rejections happen on the host; nothing is enqueued (no GPU here)."""
     assert L.moe_w4a16_workspace_init(None, 1 << 20, None) == _lib.W4A16_ERR_INVALID_ARG
     assert L.moe_w4a16_workspace_init(C.c_void_p(MISALIGNED), 1 << 20, None) == _lib.W4A16_ERR_INVALID_ARG
-    assert L.moe_w4a16_workspace_init(C.c_void_p(FAKE), 16383, None) == _lib.W4A16_ERR_WORKSPACE
-    assert "16" in _lib.last_error()
+    assert L.moe_w4a16_workspace_init(C.c_void_p(FAKE), _lib.WORKSPACE_HEAD_BYTES - 1, None) == _lib.W4A16_ERR_WORKSPACE
+    assert str(_lib.WORKSPACE_HEAD_BYTES) in _lib.last_error()
+
+
+def test_workspace_head_size_matches_header():
+    hdr = open(HEADER).read()
+    m = re.search(r"#define W4A16_WORKSPACE_HEAD_BYTES (\d+)", hdr)
+    assert m and int(m.group(1)) == _lib.WORKSPACE_HEAD_BYTES
 
 
 def test_workspace_size(L):

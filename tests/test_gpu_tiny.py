@@ -1,9 +1,10 @@
 """The single-launch path for tiny batches (T * top_k <= 16, H <= 4096).
 
-Gate/up and down workgroups of one kernel hand the intermediate rows over through
-counters kept in the head of the workspace; each call must leave those counters at zero.
-These tests run many calls with changing shapes and routing on one workspace, check every
-output against the oracle, and read the workspace head back afterwards.
+Gate/up workgroups hand the intermediate rows to the down workgroups of the same kernel
+through the workspace head: each value is written with the epoch of its call, and the
+last down workgroup resets the exit counters and advances the epoch (clearing the tagged
+values when the epoch wraps).  These tests run many calls with changing shapes and
+routing on one workspace, check every output against the oracle, and read the head back.
 """
 
 import numpy as np
@@ -17,12 +18,28 @@ from gpu_util import DEV, OracleExperts, bf16_to_dev, check_ffn, f32_to_dev, gpu
 
 pytestmark = pytest.mark.gpu
 
-SYNC_BYTES = 16384
+SYNC_BYTES = 16384                       # counters, one per 128-byte line
+HEAD_BYTES = w4._lib.WORKSPACE_HEAD_BYTES  # counters, then the tagged values
+GROUP0, TOP, ERROR, EPOCH = 80, 100, 101, 102
+EPOCHS = 65535
 
 
-def _head_is_zero(ws):
-    head = ws[:SYNC_BYTES].cpu().numpy()
-    return not head.any()
+def _words(ws):
+    return ws[:SYNC_BYTES].cpu().numpy().view(np.uint32)[::32]
+
+
+def _counters_reset(ws):
+    """Every exit counter back at zero and no wait timed out."""
+    w = _words(ws)
+    return not w[GROUP0:ERROR + 1].any()
+
+
+def _epoch_word(ws):
+    return int(_words(ws)[EPOCH])
+
+
+def _set_epoch_word(ws, v):
+    ws[EPOCH * 128:EPOCH * 128 + 4] = torch.from_numpy(np.array([v], dtype=np.uint32).view(np.uint8)).to(ws.device)
 
 
 def test_tiny_calls_share_one_workspace():
@@ -34,6 +51,7 @@ def test_tiny_calls_share_one_workspace():
     sh_ref = OracleExperts(31, 1, H, sI, 8, shared=True)
     need = max(w4.moe_w4a16_workspace_size(T, H, I, E, k, 8, sI) for T in (1, 8))
     ws = w4.new_workspace(need, DEV)
+    assert _epoch_word(ws) == 0
     plan = [(1, 4, False), (8, 4, True), (3, 8, False), (1, 8, True), (8, 8, False), (5, 4, True),
             (2, 4, False), (8, 4, False), (1, 4, True), (7, 8, True)]
     for i, (T, bits, with_shared) in enumerate(plan):
@@ -48,7 +66,8 @@ def test_tiny_calls_share_one_workspace():
         y_ref, _ = oracle.moe_layer(x, logits, k, *refs[bits].as_args(), bits,
                                     shared=sh_ref.shared_dict() if with_shared else None, residual_bits=res)
         check_ffn(y, y_ref, f"call {i}")
-        assert _head_is_zero(ws), f"workspace head not reset after call {i}"
+        assert _counters_reset(ws), f"counters not reset after call {i}"
+        assert _epoch_word(ws) == i + 1, f"epoch not advanced by call {i}"
 
 
 @pytest.mark.parametrize("H", [4096, 4224])
@@ -67,7 +86,7 @@ def test_tiny_boundary_hidden_sizes(H):
         torch.cuda.synchronize()
         y_ref, _ = oracle.moe_layer(x, logits, k, *ref.as_args(), 4)
         check_ffn(y, y_ref, f"H={H} rep {rep}")
-    assert _head_is_zero(ws)
+    assert _counters_reset(ws)
 
 
 def test_tiny_given_ids_with_dropped_pairs():
@@ -97,3 +116,31 @@ def test_tiny_given_ids_with_dropped_pairs():
     w_ok = np.where(keep, w, 0.0).astype(np.float32)
     y_ref = oracle.moe_ffn(x, ids_ok, w_ok, *ref.as_args(), 4)
     check_ffn(y, y_ref, "given ids")
+
+
+def test_tiny_epoch_wrap():
+    """Calls across the wrap of the epoch (65535 -> 1): the call at the last epoch clears
+    every tagged value, so values left with tag 1 from long ago are never taken as new.
+    Words carrying epoch 1 are planted before two one-token calls (which write rows 0-7
+    only); the two-token call after the wrap reads rows 8-15 and must not take them."""
+    E, H, I, k = 16, 256, 128, 8
+    routed = gpu_layer(34, 0, E, H, I, 4)
+    ref = OracleExperts(34, 0, H, I, 4)
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(2, H, I, E, k), DEV)
+    # stale values tagged with epoch 1 in every tag word (value bits: bf16 1.0)
+    stale = np.full(((HEAD_BYTES - SYNC_BYTES) // 4,), (1 << 16) | 0x3F80, dtype=np.uint32)
+    _set_epoch_word(ws, EPOCHS - 3)                 # next calls: epochs 65533, 65534, 65535, 1, 2
+    for i, T in enumerate((2, 1, 1, 2, 1)):
+        say(f"tiny epoch wrap call {i}: T={T} epoch word {_epoch_word(ws)}")
+        if i == 1:
+            ws[SYNC_BYTES:HEAD_BYTES] = torch.from_numpy(stale.view(np.uint8)).to(DEV)
+        x = synth.activations_bf16(600 + i, T, H)
+        logits = synth.router_logits(600 + i, T, E)
+        y = w4.moe_w4a16_forward(bf16_to_dev(x), *routed, top_k=k, router_logits=f32_to_dev(logits), workspace=ws)
+        torch.cuda.synchronize()
+        y_ref, _ = oracle.moe_layer(x, logits, k, *ref.as_args(), 4)
+        check_ffn(y, y_ref, f"wrap call {i}")
+        assert _counters_reset(ws)
+        assert _epoch_word(ws) == (EPOCHS - 3 + i + 1) % EPOCHS
+        if i == 2:   # the call at epoch 65535 cleared the tag area on its way out
+            assert not ws[SYNC_BYTES:HEAD_BYTES].cpu().numpy().any()

@@ -139,7 +139,8 @@ def moe_w4a16_workspace_init(workspace, stream=None):
 def new_workspace(nbytes: int, device):
     """A device workspace of ``nbytes`` bytes ready for :func:`moe_w4a16_forward`."""
     torch = _torch()
-    return moe_w4a16_workspace_init(torch.empty((max(int(nbytes), 16384),), dtype=torch.uint8, device=device))
+    return moe_w4a16_workspace_init(torch.empty((max(int(nbytes), _lib.WORKSPACE_HEAD_BYTES),), dtype=torch.uint8,
+                                                device=device))
 
 
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,

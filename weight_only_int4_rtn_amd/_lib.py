@@ -12,7 +12,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
+WORKSPACE_HEAD_BYTES = 147456   # W4A16_WORKSPACE_HEAD_BYTES
 
 W4A16_OK = 0
 W4A16_ERR_INVALID_ARG = 1

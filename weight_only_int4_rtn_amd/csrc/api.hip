@@ -74,7 +74,7 @@ WsLayout layout(const moe_w4a16_args* a) {
         off = align_up(off + bytes);
         return o;
     };
-    L.sync = take(kSyncBytes);
+    L.sync = take(kHeadBytes);
     L.ids = take(P * 4);
     L.wts = take(P * 4);
     L.counts = take(E * 4);
@@ -156,7 +156,14 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits};
     uint16_t* abuf = static_cast<uint16_t*>(at(L.abuf));
 
-    if (a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH) {
+    // single launch for tiny batches when the tagged a words fit the workspace head, the
+    // down workgroups' LDS (y accumulators, every a row padded, a zero block, group sums) stays
+    // small enough for two workgroups per CU, and the spinning down workgroups leave room
+    const size_t tag_bytes = (size_t)L.rows_a * L.width_a * 4;
+    const size_t tiny_lds = 8 * (size_t)a->T * 16 * 4 + (size_t)L.rows_a * (L.width_a + kTinyPad) * 2 + 1024 +
+                            (size_t)L.rows_a * (L.width_a / kGroup) * 4;
+    if (a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes && tiny_lds <= kTinyMaxLds &&
+        a->H / 16 <= tiny_max_down_workgroups(a->bits, a->shared_bits)) {
         TinyArgs d{};
         d.x = a->x;
         d.T = (int)a->T;
@@ -171,22 +178,17 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.counts = r.counts;
         d.offsets = r.offsets;
         d.sorted = r.sorted;
-        d.abuf = abuf;
-        d.width_a = L.width_a;
-        d.abuf_bytes = (uint32_t)(L.rows_a * L.width_a * 2);
         d.sync = static_cast<uint32_t*>(at(L.sync));
+        d.tags = d.sync + kSyncBytes / 4;
+        d.width_a = L.width_a;
+        d.rows_a = (int)L.rows_a;
+        d.tag_bytes = (uint32_t)tag_bytes;
         d.residual = a->residual;
         d.y = a->y;
         const int64_t slots = std::min(a->E, a->T * a->top_k) + (a->shared_bits ? 1 : 0);
         d.n_rb = (int)(L.width_a / 16);
         d.n_gk = (int)(slots * d.n_rb);
-        // down workgroups: per-wave y accumulators, then (when they fit) every a row in LDS
-        const size_t red = 8 * 8 * 64 * 4, yacc = 8 * (size_t)a->T * 16 * 4;
-        const size_t stage = (d.abuf_bytes + 1023) / 1024 * 1024;   // whole a buffer, 1 KiB copies
-        const bool dense = L.width_a == a->I && (!a->shared_bits || L.width_a == a->shared_I);
-        d.stage_a = (dense && yacc + stage + (size_t)L.rows_a * (L.width_a / kGroup) * 4 <= 56 * 1024) ? 1 : 0;
-        const size_t xsums = (size_t)L.rows_a * (L.width_a / kGroup) * 4;   // group sums of the staged rows
-        d.lds_bytes = (uint32_t)std::max(red, yacc + (d.stage_a ? stage + xsums : 0));
+        d.lds_bytes = (uint32_t)std::max<size_t>(8 * 8 * 64 * 4, tiny_lds);   // gate/up: partial sums
         return hip_status(launch_tiny(d, s, timer), "decode launch");
     }
     if (a->T <= kSmallT) {
@@ -302,10 +304,10 @@ int moe_w4a16_workspace_init(void* workspace, size_t workspace_bytes, void* stre
     g_last_error.clear();
     if (!workspace) return fail(W4A16_ERR_INVALID_ARG, "NULL workspace");
     if (!aligned16(workspace)) return fail(W4A16_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    if (workspace_bytes < kSyncBytes)
+    if (workspace_bytes < kHeadBytes)
         return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the smallest layout (%zu)",
-                    workspace_bytes, kSyncBytes);
-    return hip_status(launch_sync_init(static_cast<uint32_t*>(workspace), static_cast<hipStream_t>(stream)),
+                    workspace_bytes, kHeadBytes);
+    return hip_status(launch_head_init(static_cast<uint32_t*>(workspace), static_cast<hipStream_t>(stream)),
                       "workspace init launch");
 }
 

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
+#include "w4a16.h"
 #include <stddef.h>
 
 #include <algorithm>
@@ -154,13 +155,17 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g * __built
 
 // ------------------------------------------------------------ workspace layout
 
-// Head of every workspace: counters of the single-launch tiny-batch path.  They must be
-// zero before a workspace's first use (moe_w4a16_workspace_init) and every forward leaves
-// them zero.  One counter per 128-byte line (index * 32 words): [0, 64) routed expert
-// slots, 64 the shared expert, [80, 96) down-workgroup groups, 100 the group total,
-// 101 a sticky error word (a wait that timed out).
+// Head of every workspace: the state of the single-launch tiny-batch path, kept across
+// calls.  It must be zero before a workspace's first use (moe_w4a16_workspace_init).
+// kSyncBytes of counters, one per 128-byte line (index * 32 words): [80, 96) exit counts
+// of down-workgroup groups and 100 their total (zero between calls), 101 a sticky error
+// word (a wait that timed out), 102 the epoch word (epoch - 1 of the next call).  Then
+// kTagBytes of tagged a words (bf16 value | epoch << 16), rows of width max(I, shared I).
 constexpr size_t kSyncBytes = 16384;
-constexpr int kSyncShared = 64, kSyncGroup = 80, kSyncTop = 100, kSyncError = 101;
+constexpr size_t kTagBytes = 131072;
+constexpr size_t kHeadBytes = kSyncBytes + kTagBytes;
+static_assert(kHeadBytes == W4A16_WORKSPACE_HEAD_BYTES, "workspace head size");
+constexpr int kSyncGroup = 80, kSyncTop = 100, kSyncError = 101, kSyncEpoch = 102;
 __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return sync + i * 32; }
 
 struct WsLayout {
@@ -174,8 +179,15 @@ struct WsLayout {
 };
 
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
+// A small-path slot record carries its expert's first kRecTokens tokens (ascending,
+// kRecTokBits bits each) so gate/up can fetch activations without reading the row list.
+constexpr int kRecTokBits = 6;
+constexpr int kRecTokens = 5;
+static_assert(kSmallT <= (1 << kRecTokBits) && kRecTokens * kRecTokBits <= 31, "record token packing");
 constexpr int kTinyP = 16;       // T * k up to this (and H <= kTinyMaxH) take the single-launch path
 constexpr int kTinyMaxH = 4096;
+constexpr size_t kTinyMaxLds = 64 * 1024;   // LDS of a single-launch down workgroup at most
+constexpr int kTinyPad = 8;   // bf16 padding of an a row staged in LDS: 16 rows start in 16 different bank quads
 constexpr int kRouteBlockT = 32; // tokens per routing block on the large-batch path
 constexpr int kPrefillMT = 128;  // tokens per M-tile of the large-batch grouped GEMM
 
@@ -227,7 +239,7 @@ struct RouteArgs {
     uint16_t* xp;         // large path: [T, H] activations with each 8-column block reordered
     int2* tokw;           // [T*k] (token, weight bits) of each pair, in sorted order
     int32_t* inv;         // large path: [T*k] sorted position of each pair, -1 when dropped
-    int4* rec;            // small path: [max_slots] (expert, first sorted row, count, 0);
+    int4* rec;            // small path: [max_slots] (expert, first sorted row, count, first tokens);
                           // count 0 marks a slot beyond the active experts
     int max_slots;
     int64_t H;
@@ -257,7 +269,7 @@ struct DecodeArgs {
     const int32_t* sorted;
     const int32_t* active;
     const int32_t* meta;
-    const int4* rec;            // per active-expert slot: (expert, first sorted row, count, 0)
+    const int4* rec;            // per active-expert slot: (expert, first sorted row, count, first tokens)
     const int2* tokw;           // per sorted row: (token, weight bits)
     uint16_t* abuf;             // [rows_a, width_a]
     int64_t width_a;
@@ -283,19 +295,22 @@ struct TinyArgs {
     int32_t* counts;            // [E] out
     int32_t* offsets;           // [E + 1] out
     int32_t* sorted;            // [T * k] out
-    uint16_t* abuf;             // [rows_a, width_a]
+    uint32_t* sync;             // workspace head: counters (kSyncBytes) ...
+    uint32_t* tags;             // ... then tagged a words [rows_a, width_a] (tag_bytes <= kTagBytes)
     int64_t width_a;
-    uint32_t abuf_bytes;
-    uint32_t* sync;             // workspace head (kSyncBytes), zero on entry and exit
+    int rows_a;                 // T * k routed rows, then T shared rows
+    uint32_t tag_bytes;
     const uint16_t* residual;
     uint16_t* y;
     int n_gk;                   // gate/up workgroups: (slots + shared) * n_rb
     int n_rb;                   // 16-row blocks per slot: max(I, shared I) / 16
-    int stage_a;                // down workgroups stage every a row in LDS first
     uint32_t lds_bytes;         // dynamic LDS per workgroup
 };
 hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t = nullptr);
-hipError_t launch_sync_init(uint32_t* sync, hipStream_t s);
+// Down workgroups the single-launch path may use on the current device: half of the
+// workgroups of its kernel that the device holds at once (0 when unknown).
+int tiny_max_down_workgroups(int bits, int sbits);
+hipError_t launch_head_init(uint32_t* head, hipStream_t s);
 
 struct PrefillArgs {
     const uint16_t* x;

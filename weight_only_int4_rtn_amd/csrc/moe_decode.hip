@@ -93,10 +93,15 @@ constexpr float code_offset() { return BITS == 4 ? 136.f : 2304.f; }
 // split K: wave w takes groups w, w+8, ...; two groups per pass, every load of a pass
 // issued before its MFMAs.  (Two groups keep the activation operand, which is K/8
 // registers per lane however few tokens there are, at 32 registers.)
-template <int BITS, bool WT = false>
+// The a row is stored with every 8 columns in MFMA operand order (column j at
+// perm_pos(j)), so the down projection reads its A fragments as they lie.  TAGGED: one
+// 32-bit word per value, bf16 in the low half and `tag` in the high half, written through
+// to memory (sc1) for a reader on another XCD in the same launch; else plain bf16.
+template <int BITS, bool TAGGED = false>
 __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, const int32_t* __restrict__ w13e,
                         const uint16_t* __restrict__ s13e, int n0, int tok, bool xok, int row_base, int rows,
-                        uint16_t* __restrict__ abuf, int64_t width_a, float* s_red, uint32_t abuf_bytes = 0) {
+                        void* __restrict__ abuf, int64_t width_a, float* s_red, uint32_t abuf_bytes = 0,
+                        uint32_t tag = 0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int G = (int)(H / kGroup);
@@ -158,14 +163,14 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
             us += s_red[(w * 8 + 4 + r) * 64 + lane];
         }
         const int m = 4 * q + r;
-        const int64_t idx = (int64_t)(row_base + m) * width_a + n0 + ml;
+        const int64_t idx = (int64_t)(row_base + m) * width_a + perm_pos(n0 + ml);
         const uint32_t v = cvt_bf16(silu_mul(gs, us));
-        if constexpr (WT) {   // write-through to memory (sc1): another XCD reads it in this launch
+        if constexpr (TAGGED) {
             if (m < rows)
-                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, make_rsrc(abuf, abuf_bytes),
-                                                      (uint32_t)(idx * 2), 0, kSc1);
+                __builtin_amdgcn_raw_buffer_store_b32(v | tag, make_rsrc(abuf, abuf_bytes), (uint32_t)(idx * 4), 0,
+                                                      kSc1);
         } else {
-            if (m < rows) abuf[idx] = (uint16_t)v;
+            if (m < rows) static_cast<uint16_t*>(abuf)[idx] = (uint16_t)v;
         }
     }
     __syncthreads();
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(64 * kGkWaves) void gk_decode_kernel(DecodeArgs a) 
     const bool shared = SBITS != 0 && slot == (int)gridDim.y - 1;
     const int n0 = blockIdx.x * 16;
     const int ml = threadIdx.x & 15;
-    int count, pos0, e = 0;
+    int count, pos0, e = 0, toks = 0;
     int64_t I_e;
     if (shared) {
         I_e = a.shared.I;
@@ -191,6 +196,7 @@ __global__ __launch_bounds__(64 * kGkWaves) void gk_decode_kernel(DecodeArgs a) 
         e = r.x;
         pos0 = r.y;
         count = r.z;
+        toks = r.w;
         I_e = a.routed.I;
     }
     if (count == 0 || n0 >= I_e) return;
@@ -203,7 +209,9 @@ __global__ __launch_bounds__(64 * kGkWaves) void gk_decode_kernel(DecodeArgs a) 
                 gk_tile<SBITS>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? m : mt, ok, pos0 + mt, rows,
                                a.abuf, a.width_a, s_red);
         } else {
-            const int tok = a.tokw[pos0 + (ok ? m : mt)].x;
+            const int mm = ok ? m : mt;
+            const int tok = mm < kRecTokens ? (toks >> (kRecTokBits * mm)) & ((1 << kRecTokBits) - 1)
+                                            : a.tokw[pos0 + mm].x;
             const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
             gk_tile<BITS>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
                           a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, tok, ok, pos0 + mt, rows,
@@ -282,7 +290,7 @@ __device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], TokW 
             const bool okj = aok && j < u.ngroups;
             const int cj = col + (j < u.ngroups ? j : 0) * kGroup;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) av[j][i] = perm_act(afetch(okj, pos, cj + 8 * i));
+            for (int i = 0; i < 4; ++i) av[j][i] = afetch(okj, pos, cj + 8 * i);
         }
         f32x4_t t[kDkChunk];
 #pragma unroll
@@ -429,25 +437,35 @@ __global__ __launch_bounds__(256) void dk_combine_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ tiny batches
 //
-// T * k <= kTinyP pairs (one or two tokens at top-8):
-// one launch.  Every workgroup routes the batch itself from the logits (a few KB, served
-// by L2 after the first reads), so no workgroup waits on a routing kernel.  Workgroups
-// [0, n_gk) own one 16-row block of one active expert's gate/up bank (as gk_decode) and
-// write their a rows through to memory, then add 1 to that expert slot's counter.
-// The remaining workgroups own 16 output rows each: they issue the loads of their first
-// down-projection codes, wait until every active slot's counter is complete, read a past
-// the caches and finish as dk_decode (one split, so the sum over experts stays in one
-// workgroup and in a fixed order).  Down workgroups count their exits in groups of 16;
-// the last one to leave returns every counter to zero for the next launch.
+// T * k <= kTinyP pairs (one or two tokens at top-8): one launch.  Every workgroup routes
+// the batch itself from the logits (a few KB), so no workgroup waits on a routing kernel.
+// Workgroups [0, H / 16) own 16 output rows each: they issue the loads of their first
+// down-projection codes, then read every a word this launch produces, past the caches,
+// until each carries the current epoch; the values go to LDS and the workgroup finishes
+// the down projection of all active experts for its rows (the sum over experts stays in
+// one workgroup and in a fixed order).  The workgroups after them own one 16-row block of
+// one active expert's gate/up bank (as gk_decode) and write their a values through to
+// memory, into the tag area of the workspace head: one 32-bit word per value, the bf16
+// value in the low half and this launch's epoch in the high half.  A value carries its own
+// readiness: no counter is raised between the two halves.  The down workgroups come first
+// so that they are resident, with their codes in flight, while gate/up runs.
 //
-// Progress: gate/up workgroups never wait, and at most kTinyMaxH / 16 = 256 down
-// workgroups spin, far fewer than the workgroups the GPU holds at once, so a gate/up
-// workgroup always finds room.  A wait is still bounded: on time-out the workgroup
-// raises the sticky error word and continues.
+// Epochs run 1..65535 (the epoch word holds epoch - 1).  Down workgroups count their
+// exits in groups of 16; the last one to leave resets those counters and advances the
+// epoch word, and when the epoch wraps to 1 it also clears the tag area, so a word left by
+// an earlier launch never carries the current epoch.
+//
+// Progress: gate/up workgroups never wait, and the host takes this path only when the
+// down workgroups fill at most half of the workgroups the GPU holds at once
+// (tiny_max_down_workgroups), so gate/up workgroups always find room, in whatever order
+// workgroups are dispatched.  A wait is still bounded: on time-out the workgroup raises
+// the sticky error word and continues.
 
 namespace {
 
 constexpr int kTinySpinLimit = 1 << 22;
+constexpr uint32_t kTinyEpochs = 65535;
+constexpr int kTinyPoll = 4;   // 16-byte chunks of a words each thread keeps in flight
 
 struct TinyRoute {
     int ids[kTinyP];          // per pair (token * k + slot): expert, -1 when dropped
@@ -527,8 +545,9 @@ __device__ void tiny_route(const TinyArgs& a, TinyRoute& r, bool writer) {
 }
 
 template <int BITS, int SBITS>
-__device__ void tiny_gate_up(const TinyArgs& a, const TinyRoute& r, float* s_red) {
-    const int slot = blockIdx.x / a.n_rb, rb = blockIdx.x % a.n_rb;
+__device__ void tiny_gate_up(const TinyArgs& a, const TinyRoute& r, float* s_red, uint32_t tag) {
+    const int b = blockIdx.x - (int)(a.H / 16);   // down workgroups come first in the grid
+    const int slot = b / a.n_rb, rb = b % a.n_rb;
     const int P = min(a.E, a.T * a.k);
     const bool shared = SBITS != 0 && slot == P;
     const int n0 = rb * 16;
@@ -555,96 +574,223 @@ __device__ void tiny_gate_up(const TinyArgs& a, const TinyRoute& r, float* s_red
         if (shared) {
             if constexpr (SBITS != 0)
                 gk_tile<SBITS, true>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? m : mt, ok, pos0 + mt, rows,
-                                     a.abuf, a.width_a, s_red, a.abuf_bytes);
+                                     a.tags, a.width_a, s_red, a.tag_bytes, tag);
         } else {
             const int tok = r.tw[pos0 + (ok ? m : mt)].x;
             const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
             gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
                                 a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, tok, ok, pos0 + mt, rows,
-                                a.abuf, a.width_a, s_red, a.abuf_bytes);
+                                a.tags, a.width_a, s_red, a.tag_bytes, tag);
         }
     }
-    // every wave's write-through stores have completed before the block is counted
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-    __syncthreads();
-    if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(sync_word(a.sync, shared ? kSyncShared : slot), 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int SBITS>
-__device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int d = blockIdx.x - a.n_gk, n_dk = gridDim.x - a.n_gk;
-    const int h0 = d * 16;
-    const int T = a.T;
-    float* yacc = s_dyn + wave * T * 16;                                   // [waves][T][16]
-    uint16_t* stage = reinterpret_cast<uint16_t*>(s_dyn + kDkWaves * T * 16);   // staged a rows
-    float* xs = reinterpret_cast<float*>(stage + (a.abuf_bytes + 1023) / 1024 * 512);   // their group sums
-    for (int i = lane; i < T * 16; i += 64) yacc[i] = 0.f;
-
-    const int n_active = r.n_active;
-    const int nch = (int)((a.routed.I / kGroup + kDkChunk - 1) / kDkChunk);
-    const int nch_s = SBITS != 0 ? (int)((a.shared.I / kGroup + kDkChunk - 1) / kDkChunk) : 0;
-    const int n_routed_units = n_active * nch;
-    const int n_units = n_routed_units + nch_s;
-    auto recf = [&r](int slot) { return r.slot[slot]; };
-    auto tw = [&r](int pos) { return r.tw[pos]; };
-    const int V = kDkWaves;
-    int u = wave;
-    u32x4_t cur[kDkChunk][2], nxt[kDkChunk][2];
-    int bits = BITS, nbits = BITS;
-    DkUnit cu, nu;
-    // the first two units' codes go out before the wait
-    if (u < n_units) {
-        cu = dk_make_unit(a.routed, a.shared, a.H, T, a.k, recf, u, n_routed_units, nch, nch_s, h0, &bits);
-        if (bits == BITS) dk_load_codes<BITS>(cu, cur);
-        else if constexpr (SBITS != 0) dk_load_codes<SBITS>(cu, cur);
-    }
-    if (u + V < n_units) {
-        nu = dk_make_unit(a.routed, a.shared, a.H, T, a.k, recf, u + V, n_routed_units, nch, nch_s, h0, &nbits);
-        if (nbits == BITS) dk_load_codes<BITS>(nu, nxt);
-        else if constexpr (SBITS != 0) dk_load_codes<SBITS>(nu, nxt);
-    }
-    if (wave == 0) {   // wait until every active slot (and the shared expert) is complete
-        const uint32_t need = (uint32_t)(a.routed.I / 16);
-        const uint32_t need_s = SBITS != 0 ? (uint32_t)(a.shared.I / 16) : 0u;
-        for (int spins = 0;; ++spins) {
-            bool ok = true;
-            if (lane < n_active)
-                ok = __hip_atomic_load(sync_word(a.sync, lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
-            if (SBITS != 0)
-                ok = ok && __hip_atomic_load(sync_word(a.sync, kSyncShared), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) >= need_s;
-            if (__all(ok)) break;
+// Copies every a value of this launch from the tag area ([rows_a, W] words) into `stage`
+// ([rows_a, Ws] bf16), waiting for each 16-byte chunk until all four of its words carry
+// `tag`.  Routed rows [0, n_valid) hold I_r values, shared rows [T*k, T*k + T) hold I_s.
+__device__ void tiny_collect_a(const TinyArgs& a, int n_valid, uint32_t tag, uint16_t* stage, int Ws) {
+    const int W = (int)a.width_a, Tk = a.T * a.k;
+    const int cr = (int)(a.routed.I / 4), cs = (int)(a.shared.I / 4);   // chunks per row
+    const int n_rc = n_valid * cr;
+    const int n_c = n_rc + (a.shared.bits ? a.T * cs : 0);
+    const __amdgpu_buffer_rsrc_t tr = make_rsrc(a.tags, a.tag_bytes);
+    bool timed_out = false;
+    for (int c0 = threadIdx.x; c0 < n_c; c0 += kTinyPoll * (int)blockDim.x) {
+        uint32_t off[kTinyPoll];
+        int soff[kTinyPoll];
+        uint32_t pending = 0;
+#pragma unroll
+        for (int i = 0; i < kTinyPoll; ++i) {
+            const int c = c0 + i * (int)blockDim.x;
+            const int row = c < n_rc ? c / cr : Tk + (c - n_rc) / cs;
+            const int col = 4 * (c < n_rc ? c % cr : (c - n_rc) % cs);
+            off[i] = c < n_c ? (uint32_t)(row * W + col) * 4 : 0xfffffff0u;   // beyond the buffer: reads zeros
+            soff[i] = row * Ws + col;
+            if (c < n_c) pending |= 1u << i;
+        }
+        for (int spins = 0; pending; ++spins) {
+            u32x4_t v[kTinyPoll];
+#pragma unroll
+            for (int i = 0; i < kTinyPoll; ++i)
+                v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tr, off[i], 0, kSc1));
+#pragma unroll
+            for (int i = 0; i < kTinyPoll; ++i) {
+                // all four high halves equal to the tag <=> the OR of the XORs is below 2^16
+                const uint32_t diff = (v[i][0] ^ tag) | (v[i][1] ^ tag) | (v[i][2] ^ tag) | (v[i][3] ^ tag);
+                if ((pending >> i & 1u) && diff < 0x10000u) {
+                    const uint32_t lo = (v[i][0] & 0xffffu) | (v[i][1] << 16);
+                    const uint32_t hi = (v[i][2] & 0xffffu) | (v[i][3] << 16);
+                    *reinterpret_cast<uint2*>(stage + soff[i]) = make_uint2(lo, hi);
+                    pending &= ~(1u << i);
+                }
+            }
+            if (!pending) break;
             if (spins >= kTinySpinLimit) {
-                if (lane == 0)
-                    __hip_atomic_store(sync_word(a.sync, kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                timed_out = true;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    __syncthreads();
+    if (timed_out) __hip_atomic_store(sync_word(a.sync, kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-    // a rows: written in this launch by other workgroups, so read past the caches (sc1).
-    // When the whole a buffer fits in LDS (and its rows have no padding), it is copied
-    // there first by direct-to-LDS loads, all in flight at once; the units then read LDS
-    // at the same offsets.  Otherwise each unit loads its rows itself.
-    const int Tk = T * a.k;
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.abuf, a.abuf_bytes);
-    if (a.stage_a) {
-        const int n_chunks = (int)((a.abuf_bytes + 1023) / 1024);   // 64 lanes x 16 bytes
-        for (int c = wave; c < n_chunks; c += kDkWaves)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, stage + c * 512, 16, (uint32_t)(c * 1024 + lane * 16), 0, 0,
-                                                     kSc1);
-        __syncthreads();   // waits for this wave's loads, then for every wave
-        // sum of every staged row's 128-column groups (16 lanes per row and group)
-        const int G = (int)(a.width_a / kGroup);
-        const int n_pairs = (int)(a.abuf_bytes / (uint32_t)(a.width_a * 2)) * G;
+// A unit of the single-launch down projection: kTinyCh<BITS> groups of one slot's a rows
+// (a slot holds at most 16 rows here: T <= 16) against the workgroup's 16 output rows.
+// Groups beyond the expert's last re-read its last group with scale 0.
+template <int BITS>
+constexpr int kTinyCh = BITS == 4 ? 4 : 2;
+
+struct TinyUnit {
+    const uint8_t* wrow;    // this lane's code bytes: row h0 + ml, the unit's first group, quarter q
+    const uint16_t* srow;   // scales of row h0 + ml from the unit's first group
+    int pos0, count;        // a rows pos0 .. pos0 + count - 1
+    int g0, ngroups;        // first group, groups present
+    int shared;
+};
+
+template <int BITS>
+struct TinyCodes {
+    u32x4_t w[kTinyCh<BITS>][BITS / 4];
+    uint32_t s[kTinyCh<BITS>];   // raw bf16 scales, 0 for an absent group
+};
+
+// Unit `u` of this workgroup: routed slots (kTinyCh-group chunks) first, then the shared
+// expert's chunks.  Returns the unit's code width.
+__device__ __forceinline__ int tiny_make_unit(const TinyArgs& a, const TinyRoute& r, int u, int nch, int h0,
+                                              TinyUnit& t) {
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const int n_routed = r.n_active * nch;
+    const ExpertSet& es = u < n_routed ? a.routed : a.shared;
+    int64_t e = 0;
+    int chunk;
+    if (u < n_routed) {
+        const int4 sl = r.slot[u / nch];
+        e = sl.x;
+        t.pos0 = sl.y;
+        t.count = sl.z;
+        t.shared = 0;
+        chunk = u % nch;
+    } else {
+        t.pos0 = a.T * a.k;
+        t.count = a.T;
+        t.shared = 1;
+        chunk = u - n_routed;
+    }
+    const int ch = es.bits == 4 ? kTinyCh<4> : kTinyCh<8>;
+    const int G = (int)(es.I / kGroup);
+    t.g0 = chunk * ch;
+    t.ngroups = min(ch, G - t.g0);
+    const int64_t row_bytes = es.I * es.bits / 8;
+    t.wrow = reinterpret_cast<const uint8_t*>(es.w2) + e * a.H * row_bytes + (int64_t)(h0 + ml) * row_bytes +
+             (int64_t)t.g0 * (kGroup * es.bits / 8) + q * (32 * es.bits / 8);
+    t.srow = es.s2 + e * a.H * G + (int64_t)(h0 + ml) * G + t.g0;
+    return es.bits;
+}
+
+// Issues the unit's code and scale loads; nothing waits for them here.
+template <int BITS>
+__device__ __forceinline__ void tiny_load_unit(const TinyUnit& t, TinyCodes<BITS>& c) {
+    constexpr int kGroupBytes = kGroup * BITS / 8;
+#pragma unroll
+    for (int j = 0; j < kTinyCh<BITS>; ++j) {
+        const int jj = min(j, t.ngroups - 1);
+#pragma unroll
+        for (int v = 0; v < BITS / 4; ++v) c.w[j][v] = load_stream16(t.wrow + (int64_t)jj * kGroupBytes + 16 * v);
+        c.s[j] = t.srow[jj];
+    }
+}
+
+// y[token][h0 + ml] += router weight * sum over the unit's groups of
+// scale * (sum_k a_k (q_k + OFF) - OFF * sum_k a_k), added into this wave's yacc with LDS
+// adds (one wave owns its yacc, so the additions keep program order: deterministic).
+// A fragments come from the staged rows (stride Ws, padded so that the 16 rows of an
+// M-tile fall in different LDS banks); a padding lane reads its own 16 bytes of the zero
+// block `zb` instead, so no two lanes of a read share an address.
+template <int BITS>
+__device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BITS>& c, const uint16_t* stage,
+                                          const float* xs, int Ws, int G, const uint16_t* zb, const TinyRoute& r,
+                                          float* yacc) {
+    constexpr int CH = kTinyCh<BITS>;
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const bool real = ml < t.count;
+    const uint16_t* arow = stage + (int64_t)(t.pos0 + ml) * Ws + 32 * q;
+    const uint16_t* zl = zb + 8 * lane;
+    f32x4_t d[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int g = t.g0 + min(j, t.ngroups - 1);
+        u32x4_t av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            av[i] = *reinterpret_cast<const u32x4_t*>(real ? arow + g * kGroup + 8 * i : zl);
+        d[j] = group_dot<BITS>(av, c.w[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int m = 4 * q + rr;
+        const int p = t.pos0 + min(m, t.count - 1);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int g = t.g0 + min(j, t.ngroups - 1);
+            const float sc = j < t.ngroups ? bf16_to_f32(c.s[j]) : 0.f;
+            acc += sc * (d[j][rr] - code_offset<BITS>() * xs[p * G + g]);
+        }
+        if (m < t.count) {
+            const int2 tw = t.shared ? int2{m, __float_as_int(1.0f)} : r.tw[p];
+            atomicAdd(&yacc[tw.x * 16 + ml], __int_as_float(tw.y) * acc);
+        }
+    }
+}
+
+template <int BITS, int SBITS>
+__device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, uint32_t epoch_word) {
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int d = blockIdx.x, n_dk = (int)(a.H / 16);
+    const int h0 = d * 16;
+    const int T = a.T, Tk = T * a.k;
+    const int W = (int)a.width_a, G = W / kGroup, Ws = W + kTinyPad;
+    float* yacc = s_dyn + wave * T * 16;                                       // [waves][T][16]
+    uint16_t* stage = reinterpret_cast<uint16_t*>(s_dyn + kDkWaves * T * 16);   // [rows_a][Ws] a rows
+    uint16_t* zb = stage + (int64_t)a.rows_a * Ws;                              // 1 KiB of zeros
+    float* xs = reinterpret_cast<float*>(zb + 512);                            // [rows_a][G] group sums
+    for (int i = lane; i < T * 16; i += 64) yacc[i] = 0.f;
+    if (threadIdx.x < 64) *reinterpret_cast<u32x4_t*>(zb + 8 * threadIdx.x) = u32x4_t{0u, 0u, 0u, 0u};
+
+    // units: kTinyCh-group chunks of every active slot, then of the shared expert
+    const int nch = (int)((a.routed.I / kGroup + kTinyCh<BITS> - 1) / kTinyCh<BITS>);
+    const int nch_s = SBITS != 0 ? (int)((a.shared.I / kGroup + kTinyCh<SBITS> - 1) / kTinyCh<SBITS>) : 0;
+    const int n_units = r.n_active * nch + nch_s;
+    const int V = kDkWaves;
+    int u = wave;
+    TinyUnit cu, nu;
+    TinyCodes<BITS> cc, nc;
+    TinyCodes<SBITS ? SBITS : 4> cs, ns;   // shared-expert codes when their width differs
+    int cbits = BITS, nbits = BITS;
+    // the first two units' codes go out before the wait for the a rows
+    if (u < n_units) {
+        cbits = tiny_make_unit(a, r, u, nch, h0, cu);
+        if (cbits == BITS) tiny_load_unit<BITS>(cu, cc);
+        else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(cu, cs);
+    }
+    if (u + V < n_units) {
+        nbits = tiny_make_unit(a, r, u + V, nch, h0, nu);
+        if (nbits == BITS) tiny_load_unit<BITS>(nu, nc);
+        else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
+    }
+
+    tiny_collect_a(a, r.n_valid, (epoch_word + 1) << 16, stage, Ws);
+    __syncthreads();
+    {   // sum of every 128-column group of every row in use (16 lanes per row and group)
+        const int Gr = (int)(a.routed.I / kGroup), Gs = (int)(a.shared.I / kGroup);
+        const int n_rp = r.n_valid * Gr;
+        const int n_pairs = n_rp + (SBITS != 0 ? T * Gs : 0);
         for (int p = (int)threadIdx.x >> 4; p < n_pairs; p += (int)blockDim.x >> 4) {
-            const int row = p / G, g = p % G;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (int64_t)row * a.width_a + g * kGroup +
+            const int row = p < n_rp ? p / Gr : Tk + (p - n_rp) / Gs;
+            const int g = p < n_rp ? p % Gr : (p - n_rp) % Gs;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (int64_t)row * Ws + g * kGroup +
                                                                (threadIdx.x & 15) * 8);
             float sum = 0.f;
 #pragma unroll
@@ -653,46 +799,24 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn) {
             sum += __shfl_xor(sum, 4, 16);
             sum += __shfl_xor(sum, 2, 16);
             sum += __shfl_xor(sum, 1, 16);
-            if ((threadIdx.x & 15) == 0) xs[p] = sum;
+            if ((threadIdx.x & 15) == 0) xs[row * G + g] = sum;
         }
-        __syncthreads();
     }
-    const int64_t width_a = a.width_a;
-    const bool staged = a.stage_a != 0;
-    auto af = [stage, ar, staged, width_a](bool ok, int pos, int col) {
-        if (staged) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + pos * width_a + col);
-            const uint32_t m = ok ? 0xffffffffu : 0u;
-            return u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
-        }
-        // a padded row reads beyond the buffer, which returns zeros
-        const uint32_t off = ok ? (uint32_t)(((int64_t)pos * width_a + col) * 2) : 0xfffff000u;
-        return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, kSc1));
-    };
+    __syncthreads();
 
     while (u < n_units) {
-        const int G = (int)(a.width_a / kGroup);
-        auto xsf = [xs, G](int pos, int g) { return xs[pos * G + g]; };
-        if (staged) {
-            if (bits == BITS) dk_unit<BITS, true>(cu, cur, tw, af, xsf, yacc);
-            else if constexpr (SBITS != 0) dk_unit<SBITS, true>(cu, cur, tw, af, xsf, yacc);
-        } else {
-            if (bits == BITS) dk_unit<BITS, false>(cu, cur, tw, af, xsf, yacc);
-            else if constexpr (SBITS != 0) dk_unit<SBITS, false>(cu, cur, tw, af, xsf, yacc);
-        }
+        if (cbits == BITS) tiny_unit<BITS>(cu, cc, stage, xs, Ws, G, zb, r, yacc);
+        else if constexpr (SBITS != 0 && SBITS != BITS) tiny_unit<SBITS>(cu, cs, stage, xs, Ws, G, zb, r, yacc);
         u += V;
         if (u >= n_units) break;
-#pragma unroll
-        for (int j = 0; j < kDkChunk; ++j) {
-            cur[j][0] = nxt[j][0];
-            cur[j][1] = nxt[j][1];
-        }
         cu = nu;
-        bits = nbits;
+        cc = nc;
+        if constexpr (SBITS != 0 && SBITS != BITS) cs = ns;
+        cbits = nbits;
         if (u + V < n_units) {
-            nu = dk_make_unit(a.routed, a.shared, a.H, T, a.k, recf, u + V, n_routed_units, nch, nch_s, h0, &nbits);
-            if (nbits == BITS) dk_load_codes<BITS>(nu, nxt);
-            else if constexpr (SBITS != 0) dk_load_codes<SBITS>(nu, nxt);
+            nbits = tiny_make_unit(a, r, u + V, nch, h0, nu);
+            if (nbits == BITS) tiny_load_unit<BITS>(nu, nc);
+            else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
         }
     }
     __syncthreads();
@@ -705,17 +829,30 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn) {
         const float res = a.residual ? bf16_to_f32(a.residual[o]) : 0.f;
         a.y[o] = (uint16_t)cvt_bf16(s + res);
     }
-    if (threadIdx.x == 0) {   // exit count; the last down workgroup resets every counter
-        const int g = d >> 4, gsz = min(16, n_dk - (g << 4)), ng = (n_dk + 15) >> 4;
-        if (__hip_atomic_fetch_add(sync_word(a.sync, kSyncGroup + g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)gsz - 1 &&
-            __hip_atomic_fetch_add(sync_word(a.sync, kSyncTop), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)ng - 1) {
-            for (int i = 0; i <= kSyncShared; ++i)
-                __hip_atomic_store(sync_word(a.sync, i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // exit count in groups of 16; the last down workgroup resets the counters and
+    // advances the epoch (clearing the tag area when it wraps)
+    const int ng = (n_dk + 15) >> 4;
+    if (threadIdx.x == 0) {
+        const int g = d >> 4, gsz = min(16, n_dk - (g << 4));
+        s_last = __hip_atomic_fetch_add(sync_word(a.sync, kSyncGroup + g), 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)gsz - 1 &&
+                 __hip_atomic_fetch_add(sync_word(a.sync, kSyncTop), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)ng - 1;
+    }
+    __syncthreads();
+    if (s_last) {
+        const uint32_t next = (epoch_word + 1) % kTinyEpochs;
+        if (next == 0) {   // the whole area: earlier calls may have used more rows than this one
+            const __amdgpu_buffer_rsrc_t tr = make_rsrc(a.tags, (uint32_t)kTagBytes);
+            for (uint32_t o = threadIdx.x * 16; o < (uint32_t)kTagBytes; o += blockDim.x * 16)
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, tr, o, 0, kSc1);
+        }
+        if (threadIdx.x == 0) {
             for (int i = 0; i < ng; ++i)
                 __hip_atomic_store(sync_word(a.sync, kSyncGroup + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync_word(a.sync, kSyncTop), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync_word(a.sync, kSyncEpoch), next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -723,10 +860,14 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn) {
 template <int BITS, int SBITS>
 __device__ __forceinline__ void tiny_decode_body(const TinyArgs& a) {
     __shared__ TinyRoute route;
-    extern __shared__ float s_dyn[];   // gate/up: [waves * 8][64] partial sums; down: y, then a rows
+    // 16-byte aligned: the static route table before it would leave it at a 4-byte boundary
+    extern __shared__ __attribute__((aligned(16))) float s_dyn[];   // gate/up: partial sums; down: y, a rows, group sums
+    // epoch - 1 of this launch (written by the previous launch's last workgroup)
+    const uint32_t epoch_word =
+        __hip_atomic_load(sync_word(a.sync, kSyncEpoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     tiny_route(a, route, blockIdx.x == 0);
-    if ((int)blockIdx.x < a.n_gk) tiny_gate_up<BITS, SBITS>(a, route, s_dyn);
-    else tiny_down<BITS, SBITS>(a, route, s_dyn);
+    if ((int)blockIdx.x >= (int)(a.H / 16)) tiny_gate_up<BITS, SBITS>(a, route, s_dyn, (epoch_word + 1) << 16);
+    else tiny_down<BITS, SBITS>(a, route, s_dyn, epoch_word);
 }
 
 // Two workgroups per CU where the registers allow it without spilling (4-bit codes with
@@ -741,8 +882,9 @@ __global__ __launch_bounds__(64 * kDkWaves) void tiny_decode_wide_kernel(TinyArg
     tiny_decode_body<BITS, SBITS>(a);
 }
 
-__global__ void sync_init_kernel(uint32_t* sync) {
-    for (int i = threadIdx.x; i < (int)(kSyncBytes / 4); i += blockDim.x) sync[i] = 0u;
+__global__ __launch_bounds__(256) void head_init_kernel(uint32_t* head) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < (int)(kHeadBytes / 16); i += gridDim.x * blockDim.x)
+        reinterpret_cast<u32x4_t*>(head)[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
 }  // namespace
@@ -797,6 +939,39 @@ hipError_t launch_tiny_t(const TinyArgs& a, hipStream_t s, StageTimer* t) {
 }
 }  // namespace
 
+namespace {
+// Workgroups of the single-launch kernel that the current device holds at once (CUs times
+// the occupancy at the largest dynamic LDS the path allows), cached per device.
+template <int BITS, int SBITS>
+int tiny_capacity_t() {
+    static int cache[64];   // 0: not yet known, -1: query failed
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int cus = 0, nb = 0;
+        hipError_t st = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (st == hipSuccess) {
+            if constexpr (BITS == 4 && SBITS != 8)
+                st = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &nb, reinterpret_cast<const void*>(tiny_decode_kernel<BITS, SBITS>), 64 * kDkWaves, kTinyMaxLds);
+            else
+                st = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &nb, reinterpret_cast<const void*>(tiny_decode_wide_kernel<BITS, SBITS>), 64 * kDkWaves,
+                    kTinyMaxLds);
+        }
+        cache[dev] = (st == hipSuccess && cus > 0 && nb > 0) ? cus * nb : -1;
+    }
+    return cache[dev] > 0 ? cache[dev] : 0;
+}
+}  // namespace
+
+int tiny_max_down_workgroups(int bits, int sbits) {
+    int cap;
+    if (bits == 4) cap = sbits == 0 ? tiny_capacity_t<4, 0>() : sbits == 4 ? tiny_capacity_t<4, 4>() : tiny_capacity_t<4, 8>();
+    else cap = sbits == 0 ? tiny_capacity_t<8, 0>() : sbits == 4 ? tiny_capacity_t<8, 4>() : tiny_capacity_t<8, 8>();
+    return cap / 2;
+}
+
 hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t) {
     const int sb = a.shared.bits;
     if (a.routed.bits == 4) {
@@ -809,8 +984,8 @@ hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t) {
     return launch_tiny_t<8, 8>(a, s, t);
 }
 
-hipError_t launch_sync_init(uint32_t* sync, hipStream_t s) {
-    hipLaunchKernelGGL(sync_init_kernel, dim3(1), dim3(256), 0, s, sync);
+hipError_t launch_head_init(uint32_t* head, hipStream_t s) {
+    hipLaunchKernelGGL(head_init_kernel, dim3(16), dim3(256), 0, s, head);
     return hipGetLastError();
 }
 

@@ -107,8 +107,15 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
         a.offsets[tid] = off;
         a.counts[tid] = c;
         if (c > 0) {
+            // the first kRecTokens tokens of the expert, ascending, kRecTokBits bits each
+            uint64_t m = (uint64_t)s_mhi[tid] << 32 | s_mlo[tid];
+            int toks = 0;
+            for (int j = 0; j < kRecTokens && m; ++j) {
+                toks |= __builtin_ctzll(m) << (kRecTokBits * j);
+                m &= m - 1;
+            }
             a.active[act] = tid;
-            a.rec[act] = int4{tid, off, c, 0};
+            a.rec[act] = int4{tid, off, c, toks};
         }
     }
     for (int sl = n_active + tid; sl < a.max_slots; sl += blockDim.x) a.rec[sl] = int4{0, 0, 0, 0};
