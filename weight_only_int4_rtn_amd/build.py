@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "quant.hip", "route.hip", "moe_decode.hip", "moe_prefill.hip"]
+SOURCES = ["api.hip", "quant.hip", "route.hip", "moe_decode.hip", "decode_stream.hip", "moe_prefill.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -84,6 +84,7 @@ WsLayout layout(const moe_w4a16_args* a) {
     L.meta = take(64);
     L.tokw = take(P * 8);
     L.rec = take(std::min(E, P) * 16);
+    L.trec = take((std::min(E, P) + P / 16 + 1) * 32);
     L.rows_a = P + (shared ? T : 0);
     L.width_a = std::max(a->I, shared ? a->shared_I : (int64_t)0);
     L.abuf = take((size_t)L.rows_a * L.width_a * 2);
@@ -150,6 +151,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     r.H = a->H;
     r.tokw = static_cast<int2*>(at(L.tokw));
     r.rec = static_cast<int4*>(at(L.rec));
+    r.trec = static_cast<int4*>(at(L.trec));
     r.max_slots = (int)std::min(a->E, a->T * a->top_k);
 
     ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits};
@@ -208,6 +210,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.active = r.active;
         d.meta = r.meta;
         d.rec = r.rec;
+        d.trec = r.trec;
         d.tokw = r.tokw;
         d.abuf = abuf;
         d.width_a = L.width_a;

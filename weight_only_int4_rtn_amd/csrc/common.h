@@ -170,7 +170,7 @@ __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return s
 
 struct WsLayout {
     size_t sync, ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
-        ystage, inv, asum, tokw, rec, xp, total;
+        ystage, inv, asum, tokw, rec, trec, xp, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
     int nblk;           // routing blocks of the large-batch path
@@ -183,7 +183,8 @@ constexpr int kSmallT = 64;      // batches up to this size take the small-batch
 // kRecTokBits bits each) so gate/up can fetch activations without reading the row list.
 constexpr int kRecTokBits = 6;
 constexpr int kRecTokens = 5;
-static_assert(kSmallT <= (1 << kRecTokBits) && kRecTokens * kRecTokBits <= 31, "record token packing");
+static_assert(kSmallT <= (1 << kRecTokBits) && kRecTokens * kRecTokBits <= 31 && 16 * kRecTokBits <= 96,
+              "record token packing");
 constexpr int kTinyP = 16;       // T * k up to this (and H <= kTinyMaxH) take the single-launch path
 constexpr int kTinyMaxH = 4096;
 constexpr size_t kTinyMaxLds = 64 * 1024;   // LDS of a single-launch down workgroup at most
@@ -230,7 +231,7 @@ struct RouteArgs {
     int32_t* offsets;
     int32_t* sorted;
     int32_t* active;
-    int32_t* meta;        // [0] active experts, [1] M-tiles
+    int32_t* meta;        // [0] active experts, [1] M-tiles (routed)
     int32_t* hist;        // large path: [nblk, E]
     int32_t* lrank;       // large path: [T*k]
     int32_t* tiles;       // large path: [max_tiles, 2] (expert, first row)
@@ -241,6 +242,8 @@ struct RouteArgs {
     int32_t* inv;         // large path: [T*k] sorted position of each pair, -1 when dropped
     int4* rec;            // small path: [max_slots] (expert, first sorted row, count, first tokens);
                           // count 0 marks a slot beyond the active experts
+    int4* trec;           // small path: [max_slots + T*k/16][2] M-tiles of <= 16 rows: (expert,
+                          // first sorted row, count, 0), (96 bits of tokens: m at bit 6m, 0)
     int max_slots;
     int64_t H;
     int nblk;
@@ -270,6 +273,7 @@ struct DecodeArgs {
     const int32_t* active;
     const int32_t* meta;
     const int4* rec;            // per active-expert slot: (expert, first sorted row, count, first tokens)
+    const int4* trec;           // per routed M-tile: two int4 (see RouteArgs::trec)
     const int2* tokw;           // per sorted row: (token, weight bits)
     uint16_t* abuf;             // [rows_a, width_a]
     int64_t width_a;
@@ -279,6 +283,12 @@ struct DecodeArgs {
     uint16_t* y;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
+// Workgroups of the streaming gate/up kernel (one per CU of the current device, 0 when
+// unknown) and whether it can take a batch of these shapes (H <= 2048 and a bounded
+// number of M-tiles per workgroup); otherwise launch_decode uses one workgroup per tile.
+int stream_workgroups();
+bool stream_fits(const DecodeArgs& a, int max_tiles);
+hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 // Single-launch path for tiny batches (T * k <= kTinyP): every workgroup routes the batch
 // itself; workgroups [0, n_gk) compute gate/up row blocks and count each finished block

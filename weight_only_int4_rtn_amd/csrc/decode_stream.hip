@@ -1,0 +1,504 @@
+// Gate/up projection of the small-batch path (2 < T <= 64 tokens) as one persistent
+// stream per CU.
+//
+// Work is a flat list of items: (M-tile of <= 16 rows of one expert, 16-row block of its
+// gate/up bank, 8-group K chunk) for the routed tiles (built by the routing kernel), then
+// the shared expert's tiles of 16 tokens.  A 4-bit item carries the 16 gate rows and the
+// 16 up rows of its K chunk, an 8-bit item one of the two halves; either way 16 KiB of
+// codes.  Each workgroup (one per CU) walks a contiguous range of the list, so an
+// M-tile's activations are fetched once and serve every row block of its expert.
+//
+// Every item's codes and scales reach LDS by direct-to-LDS buffer loads into a ring of
+// kSStages stages: while item s computes, items s+1 .. s+kSStages-2 are in flight, which
+// keeps about 85 KiB of weights in flight per CU without spending registers on them.  A
+// tile's activation rows (at most kSARows of them) are copied the same way, together with
+// the tile's first item, into one of two LDS buffers, and moved into registers when that
+// item computes; larger tiles (rare at decode) load their rows straight into registers.
+//
+// Within an item, wave w computes K group 8 * kh + w of the item's rows with 16x16x32 bf16
+// MFMAs (codes as exact bf16 integers, offset removed by the seed, see dq4 / dq8 in
+// common.h); the fp32 partial sums of the 8 waves meet in LDS after the row block's last
+// K chunk, and the epilogue stores a = SiLU(g) * u as bf16 in MFMA operand order.
+#include "common.h"
+#include "decode_dev.h"
+#include "dma.h"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kSWaves = 8;                         // compute waves
+constexpr int kSIssuers = 2;                       // producer waves: they only issue the copies
+constexpr int kSThreads = 64 * (kSWaves + kSIssuers);
+constexpr int kSStages = 6;
+constexpr int kSCodeBytes = 16384;                 // one item: 16 blocks of 64 lanes x 16 B
+constexpr int kSStageBytes = kSCodeBytes + 1024;   // + one block of scales
+constexpr int kSARows = 4;                         // activation rows an A buffer holds
+constexpr int kSARowBytes = 4096 + 16;             // one row (H <= 2048), padded against bank conflicts
+constexpr int kSABytes = kSARows * kSARowBytes;
+constexpr int kSMaxTiles = 8;                      // routed M-tiles one workgroup's range may touch
+constexpr int kSMaxH = 2048;
+constexpr int kSKH = kSMaxH / kGroup / 8;          // 8-group K chunks at the largest H: 2
+// dynamic LDS: stages | two A buffers | zero block | partial sums | tile records
+constexpr int kSOffA = kSStages * kSStageBytes;
+constexpr int kSOffZero = kSOffA + 2 * kSABytes;
+constexpr int kSOffRed = kSOffZero + 1024;
+constexpr int kSOffTiles = kSOffRed + kSWaves * 8 * 64 * 4;
+constexpr int kSLdsBytes = kSOffTiles + kSMaxTiles * 32;
+static_assert(kSLdsBytes <= 160 * 1024, "streaming gate/up LDS");
+
+// One M-tile: expert, first row of the a buffer, rows, and how to find each row's token.
+struct STile {
+    int e;          // expert (routed)
+    int row0;       // first row in the a buffer
+    int count;      // rows (1..16)
+    int shared;     // 1: the shared expert, token of row m is tbase + m
+    int tbase;
+    uint32_t tk0, tk1, tk2;   // routed: token m in bits [6m, 6m + 6) of tk2:tk1:tk0
+};
+
+__device__ __forceinline__ int stile_token(const STile& t, int m) {
+    if (t.shared) return t.tbase + m;
+    // one 96-bit shift (no indexed array: that would live in scratch memory, and a scratch
+    // load makes the compiler wait for every copy in flight)
+    const unsigned __int128 v = (unsigned __int128)t.tk0 | ((unsigned __int128)t.tk1 << 32) |
+                                ((unsigned __int128)t.tk2 << 64);
+    return (int)(uint32_t)(v >> (kRecTokBits * m)) & ((1 << kRecTokBits) - 1);
+}
+
+struct SLayout {    // per-launch constants, wave-uniform
+    int G, T, Tk;
+    int n_rb_r, n_rb_s, sub_r, sub_s, n_tiles_r;
+    int t_lo;       // first routed tile of this workgroup's range
+};
+
+// A position in the item list: tile, row block, K chunk.  Advanced one item at a time
+// with compares only (the scalar unit is the scarce resource of this loop: one per CU,
+// shared by its eight waves), and the current tile's record kept at hand.
+struct SCursor {
+    int tile;       // global tile id: routed tiles first, then shared tiles
+    int rb, sub;    // row block; K chunk (4-bit) or K chunk * 2 + half (8-bit)
+    int n_rb, n_sub, bits;
+    STile tl;
+};
+
+template <int BITS, int SBITS>
+__device__ __forceinline__ void s_set_tile(SCursor& c, const SLayout& L, const int* s_tiles) {
+    const bool shared = c.tile >= L.n_tiles_r;
+    c.n_rb = shared ? L.n_rb_s : L.n_rb_r;
+    c.n_sub = shared ? L.sub_s : L.sub_r;
+    c.bits = shared ? SBITS : BITS;
+    if (!shared) {
+        // (a cursor stepping past the range end lands on a record it never uses)
+        const int* r = s_tiles + 8 * min(c.tile - L.t_lo, kSMaxTiles - 1);
+        c.tl.e = __builtin_amdgcn_readfirstlane(r[0]);   // wave-uniform: keep it in scalar registers
+        c.tl.row0 = __builtin_amdgcn_readfirstlane(r[1]);
+        c.tl.count = __builtin_amdgcn_readfirstlane(r[2]);
+        c.tl.tk0 = __builtin_amdgcn_readfirstlane(r[4]);
+        c.tl.tk1 = __builtin_amdgcn_readfirstlane(r[5]);
+        c.tl.tk2 = __builtin_amdgcn_readfirstlane(r[6]);
+        c.tl.shared = 0;
+        c.tl.tbase = 0;
+    } else {
+        const int ts = c.tile - L.n_tiles_r;
+        c.tl.e = 0;
+        c.tl.tbase = 16 * ts;
+        c.tl.row0 = L.Tk + 16 * ts;
+        c.tl.count = min(16, L.T - 16 * ts);
+        c.tl.shared = 1;
+        c.tl.tk0 = c.tl.tk1 = c.tl.tk2 = 0u;
+    }
+}
+
+// Every field is wave-uniform; saying so keeps the cursor in scalar registers and its
+// tests as scalar branches (the compiler cannot prove it through the loop).
+__device__ __forceinline__ void s_uniform(SCursor& c) {
+    c.tile = __builtin_amdgcn_readfirstlane(c.tile);
+    c.rb = __builtin_amdgcn_readfirstlane(c.rb);
+    c.sub = __builtin_amdgcn_readfirstlane(c.sub);
+    c.n_rb = __builtin_amdgcn_readfirstlane(c.n_rb);
+    c.n_sub = __builtin_amdgcn_readfirstlane(c.n_sub);
+    c.bits = __builtin_amdgcn_readfirstlane(c.bits);
+    c.tl.e = __builtin_amdgcn_readfirstlane(c.tl.e);
+    c.tl.row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
+    c.tl.count = __builtin_amdgcn_readfirstlane(c.tl.count);
+    c.tl.shared = __builtin_amdgcn_readfirstlane(c.tl.shared);
+    c.tl.tbase = __builtin_amdgcn_readfirstlane(c.tl.tbase);
+    c.tl.tk0 = __builtin_amdgcn_readfirstlane(c.tl.tk0);
+    c.tl.tk1 = __builtin_amdgcn_readfirstlane(c.tl.tk1);
+    c.tl.tk2 = __builtin_amdgcn_readfirstlane(c.tl.tk2);
+}
+
+// Moves to the next item; true when it starts a new tile.
+template <int BITS, int SBITS>
+__device__ __forceinline__ bool s_advance(SCursor& c, const SLayout& L, const int* s_tiles) {
+    bool start = false;
+    if (++c.sub >= c.n_sub) {
+        c.sub = 0;
+        if (++c.rb >= c.n_rb) {
+            c.rb = 0;
+            ++c.tile;
+            s_set_tile<BITS, SBITS>(c, L, s_tiles);
+            start = true;
+        }
+    }
+    s_uniform(c);
+    return start;
+}
+
+// What the issuing side keeps per tile: buffer descriptors and this lane's offsets.
+struct SIssueTile {
+    i32x4_t wr, sr;        // codes and scales of the tile's expert
+    int64_t I_e, row_bytes;
+    uint32_t v_code;       // lane part of a code copy offset
+    uint32_t v_scale;      // lane part of the scale copy offset (kOob: idle lane)
+};
+
+__device__ __forceinline__ void s_issue_tile(const DecodeArgs& a, const SLayout& L, const SCursor& c,
+                                             SIssueTile& st) {
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const ExpertSet& es = c.tl.shared ? a.shared : a.routed;
+    st.I_e = es.I;
+    st.row_bytes = a.H * c.bits / 8;
+    const int64_t e = c.tl.e;
+    st.wr = uniform_rsrc(dma_rsrc(reinterpret_cast<const uint8_t*>(es.w13) + e * 2 * st.I_e * st.row_bytes,
+                                  (uint32_t)(2 * st.I_e * st.row_bytes)));
+    st.sr = uniform_rsrc(dma_rsrc(es.s13 + e * 2 * st.I_e * L.G, (uint32_t)(2 * st.I_e * L.G * 2)));
+    st.v_code = (uint32_t)(ml * st.row_bytes + q * (c.bits == 4 ? 16 : 32));
+    if (c.bits == 4) st.v_scale = lane < 32 ? (uint32_t)((((lane >> 4) * st.I_e + ml) * L.G) * 2) : kOob;
+    else st.v_scale = lane < 16 ? (uint32_t)(lane * L.G * 2) : kOob;
+}
+
+// Issues producer wave w's copies of the cursor's item into `stage`: code blocks
+// 8w .. 8w + 7 (producer 0 also the scales) and, at a tile start whose rows fit an A
+// buffer, its share of the tile's activation rows into `abuf_lds`.  Returns the copies
+// issued.  The producers do nothing else: an issue stalls while the memory system is
+// saturated, and that stall must not hold up the MFMAs (nor should all waves repeat the
+// per-item scalar work on the CU's one scalar unit).
+__device__ __forceinline__ int s_issue(const DecodeArgs& a, const SLayout& L, const SCursor& c,
+                                       const SIssueTile& st, uint32_t stage, bool tile_start, uint32_t abuf_lds) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) - kSWaves);   // producer index
+    const int n0 = c.rb * 16;
+    const int kh = c.bits == 4 ? c.sub : c.sub >> 1, half = c.bits == 4 ? 0 : c.sub & 1;
+    const i32x4_t wr = uniform_rsrc(st.wr);   // in scalar registers whatever the compiler kept
+    // groups past the last (a hidden size that is not a multiple of 1024) read other rows
+    // or past the buffer (zeros); no wave computes them
+    uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + wave * 8 * 1024);
+    if (c.bits == 4) {   // blocks 8w + j: half w (gate, up), group 8 kh + j
+        int soff = __builtin_amdgcn_readfirstlane((int)((wave * st.I_e + n0) * st.row_bytes) + 8 * kh * 64);
+#pragma unroll
+        for (int j = 0; j < 8; ++j, soff += 64, m0 += 1024) dma16(wr, m0, st.v_code, soff);
+    } else {             // blocks 8w + i: group 8 kh + 4w + i / 2, 16-byte half i % 2
+        const int soff =
+            __builtin_amdgcn_readfirstlane((int)((half * st.I_e + n0) * st.row_bytes) + (8 * kh + 4 * wave) * 128);
+#pragma unroll
+        for (int i = 0; i < 8; ++i, m0 += 1024) dma16(wr, m0, st.v_code, soff + (i >> 1) * 128 + (i & 1) * 16);
+    }
+    int n = 8;
+    if (wave == 0) {   // scales: 8 groups (16 B) of each row this item needs
+        const int soff = c.bits == 4 ? (n0 * L.G + 8 * kh) * 2 : (int)(((half * st.I_e + n0) * L.G + 8 * kh) * 2);
+        dma16(uniform_rsrc(st.sr), __builtin_amdgcn_readfirstlane(stage + kSCodeBytes), st.v_scale,
+              __builtin_amdgcn_readfirstlane(soff));
+        ++n;
+    }
+    if (tile_start && c.tl.count <= kSARows) {   // the tile's activation rows, 1 KiB per copy
+        const int row_b = (int)(a.H * 2);
+        const int cpr = (row_b + 1023) / 1024;
+        const int n_dma = c.tl.count * cpr;
+        const i32x4_t xr = uniform_rsrc(dma_rsrc(a.x, (uint32_t)((int64_t)a.T * row_b)));
+        for (int d = wave; d < n_dma; d += kSIssuers) {
+            const int r = d / cpr, cc = d - r * cpr;
+            const int b = cc * 1024 + lane * 16;
+            const uint32_t off = b < row_b ? (uint32_t)(stile_token(c.tl, r) * row_b + b) : kOob;
+            dma16(xr, __builtin_amdgcn_readfirstlane(abuf_lds + r * kSARowBytes + cc * 1024), off, 0);
+            ++n;
+        }
+    }
+    return n;
+}
+
+// This wave's activation fragments of K groups w and w + 8 for the tile's 16 rows
+// (padding rows zero), and their MFMA offset seeds.
+template <int BITS>
+__device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, const STile& tl, const uint8_t* smem,
+                                         const uint8_t* abuf, u32x4_t (&A)[kSKH][4], f32x4_t (&seed)[kSKH]) {
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool real = ml < tl.count;
+    if (tl.count <= kSARows) {
+        const uint8_t* row = abuf + ml * kSARowBytes + 64 * q;
+        const uint8_t* zl = smem + kSOffZero + 16 * lane;
+#pragma unroll
+        for (int kh = 0; kh < kSKH; ++kh) {
+            const int g = 8 * kh + wave;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint8_t* p = (real && g < L.G) ? row + g * 256 + 16 * i : zl;
+                A[kh][i] = perm_act(*reinterpret_cast<const u32x4_t*>(p));
+            }
+        }
+    } else {   // more rows than an A buffer holds: straight from memory into registers
+        const uint16_t* xr = a.x + (int64_t)stile_token(tl, real ? ml : 0) * a.H + 32 * q;
+#pragma unroll
+        for (int kh = 0; kh < kSKH; ++kh) {
+            const int g = min(8 * kh + wave, L.G - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) A[kh][i] = load_act<BITS>(xr, real && 8 * kh + wave < L.G, g * kGroup + 8 * i);
+        }
+    }
+#pragma unroll
+    for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<BITS>(A[kh]);
+}
+
+// One item's MFMAs for this wave: K group 8 * kh + wave of the item's rows.
+template <int BITS>
+__device__ __forceinline__ void s_compute(const SLayout& L, int kh, int half, const uint8_t* stage,
+                                          const u32x4_t (&A)[4], f32x4_t seed, f32x4_t& accg, f32x4_t& accu) {
+    const int lane = threadIdx.x & 63, ml = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (8 * kh + wave >= L.G) return;
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(stage + kSCodeBytes);
+    if constexpr (BITS == 4) {
+        const u32x4_t bg[1] = {*reinterpret_cast<const u32x4_t*>(stage + wave * 1024 + lane * 16)};
+        const u32x4_t bu[1] = {*reinterpret_cast<const u32x4_t*>(stage + (8 + wave) * 1024 + lane * 16)};
+        const float sg = bf16_to_f32(sc[ml * 8 + wave]), su = bf16_to_f32(sc[(16 + ml) * 8 + wave]);
+        const f32x4_t tg = group_dot<4>(A, bg, seed);
+        const f32x4_t tu = group_dot<4>(A, bu, seed);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            accg[r] += sg * tg[r];
+            accu[r] += su * tu[r];
+        }
+    } else {
+        const u32x4_t bw[2] = {*reinterpret_cast<const u32x4_t*>(stage + (2 * wave) * 1024 + lane * 16),
+                               *reinterpret_cast<const u32x4_t*>(stage + (2 * wave + 1) * 1024 + lane * 16)};
+        const float s = bf16_to_f32(sc[ml * 8 + wave]);
+        const float sg = half == 0 ? s : 0.f, su = half == 0 ? 0.f : s;   // selects, no branch
+        const f32x4_t t = group_dot<8>(A, bw, seed);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            accg[r] += sg * t[r];
+            accu[r] += su * t[r];
+        }
+    }
+}
+
+template <int BITS, int SBITS>
+// One workgroup of ten waves per CU (its LDS ring takes the CU): three waves share a SIMD at most.
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) void gk_stream_kernel(
+    DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, ml = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    SLayout L;
+    L.G = (int)(a.H / kGroup);
+    const int KH = (L.G + 7) / 8;
+    L.T = a.T;
+    L.Tk = a.T * a.k;
+    L.n_rb_r = (int)(a.routed.I / 16);
+    L.n_rb_s = SBITS != 0 ? (int)(a.shared.I / 16) : 0;
+    L.sub_r = BITS == 4 ? KH : 2 * KH;
+    L.sub_s = SBITS == 4 ? KH : 2 * KH;
+    L.n_tiles_r = __builtin_amdgcn_readfirstlane(a.meta[1]);
+    // ranges are cut between row blocks (units), never inside one: a row block's K chunks
+    // are summed in one workgroup's registers
+    const int U_r = L.n_tiles_r * L.n_rb_r;
+    const int U = U_r + (SBITS != 0 ? ((a.T + 15) / 16) * L.n_rb_s : 0);
+    const int u0 = (int)((int64_t)U * blockIdx.x / gridDim.x);
+    const int u1 = (int)((int64_t)U * (blockIdx.x + 1) / gridDim.x);
+    const int nI = (min(u1, U_r) - min(u0, U_r)) * L.sub_r + (max(u1, U_r) - max(u0, U_r)) * L.sub_s;
+    if (nI <= 0) return;
+
+    // routed tile records of this range into LDS
+    int* s_tiles = reinterpret_cast<int*>(smem + kSOffTiles);
+    L.t_lo = u0 < U_r ? u0 / L.n_rb_r : L.n_tiles_r;
+    const int t_hi = u0 < U_r ? (min(u1, U_r) - 1) / L.n_rb_r : L.n_tiles_r - 1;
+    if (t_hi - L.t_lo + 1 > kSMaxTiles) return;   // excluded on the host (stream_fits)
+    if (tid < 2 * (t_hi - L.t_lo + 1))
+        reinterpret_cast<int4*>(s_tiles)[tid] = a.trec[2 * L.t_lo + tid];
+    if (tid < 64) *reinterpret_cast<u32x4_t*>(smem + kSOffZero + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    // two cursors over the range: copies run kSStages - 1 items ahead of the MFMAs
+    SCursor ic;
+    ic.tile = u0 < U_r ? u0 / L.n_rb_r : L.n_tiles_r + (u0 - U_r) / L.n_rb_s;
+    ic.rb = u0 < U_r ? u0 % L.n_rb_r : (u0 - U_r) % L.n_rb_s;
+    ic.sub = 0;
+    s_set_tile<BITS, SBITS>(ic, L, s_tiles);
+    s_uniform(ic);
+    SCursor cc = ic;
+    const int first_tile = ic.tile;
+
+    const uint32_t lds0 = lds_offset(smem);
+    const bool issuer = wave >= kSWaves;
+    const int base_ops = wave == kSWaves ? 9 : 8;   // copies per item of a producer wave
+    // copies of the two most recent tile starts (by A buffer): relative item, this wave's count
+    int a_rel0 = -1, a_cnt0 = 0, a_rel1 = -1, a_cnt1 = 0;
+    SIssueTile st;
+    s_issue_tile(a, L, ic, st);
+    int i_stage = 0;
+    bool i_start = true;
+
+    auto issue = [&](int rel) {
+        const int b = (ic.tile - first_tile) & 1;
+        const int n = __builtin_amdgcn_readfirstlane(
+            s_issue(a, L, ic, st, lds0 + i_stage * kSStageBytes, i_start, lds0 + kSOffA + b * kSABytes));
+        if (i_start) {
+            if (b == 0) { a_rel0 = rel; a_cnt0 = n - base_ops; }
+            else { a_rel1 = rel; a_cnt1 = n - base_ops; }
+        }
+        i_stage = i_stage + 1 == kSStages ? 0 : i_stage + 1;
+        i_start = s_advance<BITS, SBITS>(ic, L, s_tiles);
+        if (i_start && rel + 1 < nI) s_issue_tile(a, L, ic, st);
+    };
+
+    if (issuer) {   // ---- producer waves: copies only, kSStages - 1 items ahead
+        for (int rel = 0; rel < kSStages - 1 && rel < nI; ++rel) issue(rel);
+        for (int rel = 0; rel < nI; ++rel) {
+            // this wave's copies of item rel have landed once only the later items' remain
+            const int later = min(nI - 1 - rel, kSStages - 2);
+            int n = later * base_ops;
+            if (a_rel0 > rel && a_rel0 <= rel + later) n += a_cnt0;
+            if (a_rel1 > rel && a_rel1 <= rel + later) n += a_cnt1;
+            n = __builtin_amdgcn_readfirstlane(n);
+            if (n == (kSStages - 2) * 8) wait_vmcnt<(kSStages - 2) * 8>();
+            else if (n == (kSStages - 2) * 9) wait_vmcnt<(kSStages - 2) * 9>();
+            else wait_vmcnt_dyn(n);
+            bar();   // item rel is in LDS; every compute wave is done with item rel - 1's stage
+            if (rel + kSStages - 1 < nI) issue(rel + kSStages - 1);
+        }
+        bar();   // matches the compute waves' final barrier
+        return;
+    }
+
+    // ---- compute waves
+    u32x4_t A[kSKH][4];
+    f32x4_t seed[kSKH];
+    f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+    bool c_start = true;
+    int c_stage = 0;
+    int ep_row0 = 0, ep_count = 0, ep_n0 = 0, ep_pending = 0;
+    float* s_red = reinterpret_cast<float*>(smem + kSOffRed);
+
+    // waves 4..7: element r = wave - 4 of every lane (D row 4q + r, column ml)
+    auto epilogue = [&]() {
+        if (wave >= 4) {
+            const int r = wave - 4;
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int w = 0; w < kSWaves; ++w) {
+                gs += s_red[(w * 8 + r) * 64 + lane];
+                us += s_red[(w * 8 + 4 + r) * 64 + lane];
+            }
+            const int m = 4 * q + r;
+            if (m < ep_count)
+                a.abuf[(int64_t)(ep_row0 + m) * a.width_a + perm_pos(ep_n0 + ml)] = (uint16_t)cvt_bf16(silu_mul(gs, us));
+        }
+    };
+
+    for (int rel = 0; rel < nI; ++rel) {
+        wait_lgkm0();   // this wave's partial sums are in LDS before the barrier
+        bar();          // item rel is in LDS (the producers waited); the partial sums are complete
+        if (ep_pending) {
+            epilogue();
+            ep_pending = 0;
+        }
+        if (c_start) {
+            const uint8_t* abuf = smem + kSOffA + ((cc.tile - first_tile) & 1) * kSABytes;
+            if (cc.bits == BITS) s_load_a<BITS>(a, L, cc.tl, smem, abuf, A, seed);
+            else if constexpr (SBITS != 0 && SBITS != BITS) s_load_a<SBITS>(a, L, cc.tl, smem, abuf, A, seed);
+        }
+        const uint8_t* stage = smem + c_stage * kSStageBytes;
+        const int kh = cc.bits == 4 ? cc.sub : cc.sub >> 1, half = cc.bits == 4 ? 0 : cc.sub & 1;
+        if (cc.bits == BITS) {
+            if (kh == 0) s_compute<BITS>(L, kh, half, stage, A[0], seed[0], accg, accu);
+            else s_compute<BITS>(L, kh, half, stage, A[1], seed[1], accg, accu);
+        } else if constexpr (SBITS != 0 && SBITS != BITS) {
+            if (kh == 0) s_compute<SBITS>(L, kh, half, stage, A[0], seed[0], accg, accu);
+            else s_compute<SBITS>(L, kh, half, stage, A[1], seed[1], accg, accu);
+        }
+        if (cc.sub == cc.n_sub - 1) {   // the row block's last K chunk
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s_red[(wave * 8 + r) * 64 + lane] = accg[r];
+                s_red[(wave * 8 + 4 + r) * 64 + lane] = accu[r];
+                accg[r] = 0.f;
+                accu[r] = 0.f;
+            }
+            ep_row0 = cc.tl.row0;
+            ep_count = cc.tl.count;
+            ep_n0 = cc.rb * 16;
+            ep_pending = 1;
+        }
+        c_stage = c_stage + 1 == kSStages ? 0 : c_stage + 1;
+        c_start = s_advance<BITS, SBITS>(cc, L, s_tiles);
+    }
+    wait_lgkm0();
+    bar();
+    if (ep_pending) epilogue();
+}
+
+int g_stream_wgs[64];   // per device: CUs (0: not yet known, -1: query failed)
+
+template <int BITS, int SBITS>
+hipError_t launch_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(gk_stream_kernel<BITS, SBITS>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kSLdsBytes);
+        if (st != hipSuccess) return st;
+        attr_set = true;
+    }
+    launch(t, "gk_stream", gk_stream_kernel<BITS, SBITS>, dim3((unsigned)stream_workgroups()), dim3(kSThreads), s,
+           (uint32_t)kSLdsBytes, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int stream_workgroups() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (g_stream_wgs[dev] == 0) {
+        int cus = 0;
+        g_stream_wgs[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                                    cus > 0
+                                ? cus
+                                : -1;
+    }
+    return g_stream_wgs[dev] > 0 ? g_stream_wgs[dev] : 0;
+}
+
+bool stream_fits(const DecodeArgs& a, int max_tiles) {
+    const int nwg = stream_workgroups();
+    if (nwg <= 0 || a.H > kSMaxH || a.T > kSmallT) return false;
+    const int64_t G = a.H / kGroup, KH = (G + 7) / 8;
+    // the scale copies read 16 bytes from each row's first group of a K chunk: with an
+    // even group count every such address is 4-byte aligned
+    if (G % 2 != 0) return false;
+    // a 4-bit row block must span two K chunks: its partial sums are read back one item
+    // after they are written and rewritten no sooner than two items later
+    if (KH < 2 && (a.routed.bits == 4 || a.shared.bits == 4)) return false;
+    const int64_t ipt_r = (a.routed.I / 16) * (a.routed.bits == 4 ? KH : 2 * KH);
+    const int64_t ipt_s = a.shared.bits ? (a.shared.I / 16) * (a.shared.bits == 4 ? KH : 2 * KH) : 0;
+    const int64_t n_rb_r = a.routed.I / 16;
+    const int64_t u_max = max_tiles * n_rb_r + (a.shared.bits ? ((a.T + 15) / 16) * (a.shared.I / 16) : 0);
+    const int64_t range = (u_max + nwg - 1) / nwg + 1;   // row blocks per workgroup, at most
+    // routed tiles a range can touch, whatever the device-side tile count
+    return (ipt_r > 0 && ipt_s >= 0) && (range + n_rb_r - 1) / n_rb_r + 1 <= kSMaxTiles;
+}
+
+hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (a.routed.bits == 4) {
+        if (sb == 0) return launch_stream_t<4, 0>(a, s, t);
+        if (sb == 4) return launch_stream_t<4, 4>(a, s, t);
+        return launch_stream_t<4, 8>(a, s, t);
+    }
+    if (sb == 0) return launch_stream_t<8, 0>(a, s, t);
+    if (sb == 4) return launch_stream_t<8, 4>(a, s, t);
+    return launch_stream_t<8, 8>(a, s, t);
+}
+
+}  // namespace w4a16

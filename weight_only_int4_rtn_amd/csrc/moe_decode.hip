@@ -15,6 +15,7 @@
 //   w[t,j] * (W2_e a) per token in LDS.  Waves, then splits, are summed in a fixed
 //   order, so the result is bitwise reproducible.
 #include "common.h"
+#include "decode_dev.h"
 #include "route_dev.h"
 
 namespace w4a16 {
@@ -25,44 +26,6 @@ constexpr int kDkWaves = 8;   // waves per down workgroup
 constexpr int kDkChunk = 2;   // groups of K per down work unit (group_dot2 assumes 2)
 
 namespace {
-
-// 16 bytes of one activation row (8 bf16) at column c, reordered for a BITS-wide code;
-// zero when the row is padding (`ok` false; `row` then points at any valid row).
-template <int BITS>
-__device__ __forceinline__ u32x4_t load_act(const uint16_t* row, bool ok, int64_t c) {
-    return perm_act(load16_or_zero(row + c, ok, row));
-}
-
-// One 128-column group: seed with -OFF * sum(x), then add sum_k x_k * (q_k + OFF) for the
-// lane's four 8-column slices.  bw holds the lane's 32 codes (16 B for INT4, 32 B INT8).
-template <int BITS>
-__device__ __forceinline__ f32x4_t group_dot(const u32x4_t (&av)[4], const u32x4_t (&bw)[BITS / 4],
-                                             f32x4_t seed) {
-    f32x4_t t = seed;
-    const uint32_t M = nibble_mask();
-    if constexpr (BITS == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t = mfma16(av[i], dq4(bw[0][i], M), t);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            u32x4_t lo, hi;
-            dq8(bw[i >> 1][(2 * i) & 3], bw[i >> 1][(2 * i + 1) & 3], lo, hi, M);
-            t = mfma16(av[i], lo, t);
-            t = mfma16(av[i], hi, t);
-        }
-    }
-    return t;
-}
-
-template <int BITS>
-__device__ __forceinline__ f32x4_t offset_seed(const u32x4_t (&av)[4]) {
-    const u32x4_t neg = neg_offset_operand<BITS>();
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c = mfma16(av[i], neg, c);
-    return c;
-}
 
 // Two groups at once (two independent MFMA chains, interleaved), each started from `t`.
 template <int BITS>
@@ -83,10 +46,6 @@ __device__ __forceinline__ void group_dot2(const u32x4_t (&av)[kDkChunk][4], con
             }
         }
 }
-
-// The code offset OFF of a BITS-wide code (see neg_offset_operand).
-template <int BITS>
-constexpr float code_offset() { return BITS == 4 ? 136.f : 2304.f; }
 
 // Gate/up of one M-tile (this lane's activation row: token `tok`, zero when !xok) against rows n0..n0+15 of the
 // gate half and the same rows of the up half of one expert's [2I, H] bank.  The 8 waves
@@ -894,9 +853,13 @@ namespace {
 template <int BITS, int SBITS>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
-    const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
-    const dim3 gk_grid((unsigned)(Imax / 16), (unsigned)(max_active + (SBITS ? 1 : 0)));
-    launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, 0u, a);
+    if (stream_fits(a, max_active + a.T * a.k / 16)) {
+        if (hipError_t st = launch_gk_stream(a, s, t)) return st;
+    } else {
+        const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
+        const dim3 gk_grid((unsigned)(Imax / 16), (unsigned)(max_active + (SBITS ? 1 : 0)));
+        launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, 0u, a);
+    }
     const dim3 dk_grid((unsigned)(a.H / 16), (unsigned)a.splits);
     launch(t, "dk_decode", dk_decode_kernel<BITS, SBITS>, dk_grid, dim3(64 * kDkWaves), s, 0u, a);
     if (a.splits > 1) {

@@ -28,6 +28,7 @@
 // Routed items (code width BITS) and the shared expert's items (SBITS) are walked as two
 // separate streams by every workgroup.
 #include "common.h"
+#include "dma.h"
 
 namespace w4a16 {
 
@@ -85,45 +86,6 @@ __device__ Item make_item(const PrefillArgs& a, int L, int nb) {
     return it;
 }
 
-// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-// Workgroup barrier that orders the compiler's memory accesses but waits for nothing
-// (the waits are explicit).
-__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
-
-// Direct global -> LDS copies (buffer_load ... lds: lane l's 16 or 4 bytes land at the
-// wave-uniform LDS address + 16 l or + 4 l).  Issued from inline asm so that the compiler,
-// which cannot tell the stages apart, does not wait for every copy in flight before each
-// LDS read; the step waits above carry the ordering instead.  The copies write no
-// registers.  Buffer descriptor: base, num_records = bytes, gfx9-family word 3.
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_t dma_rsrc(const void* p, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    return i32x4_t{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), (int32_t)bytes, 0x00020000};
-}
-// LDS byte address of a pointer into shared memory (wave-uniform).
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is set here, on purpose
-__device__ __forceinline__ void dma16(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every staged array: reads zero
 
 // ------------------------------------------------------------- operand layouts
 //

@@ -119,10 +119,29 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
         }
     }
     for (int sl = n_active + tid; sl < a.max_slots; sl += blockDim.x) a.rec[sl] = int4{0, 0, 0, 0};
+    // M-tiles of at most 16 rows, in slot order, each with all of its tokens (token m in
+    // bits [6m, 6m + 6) of the 96 bits .x, .y, .z of the second int4)
+    int n_tiles = 0;
+    const int nmt = (c + 15) >> 4;
+    const int t0 = block_exclusive_scan(nmt, s_tmp, &n_tiles);
+    if (tid < E && c > 0) {
+        uint64_t m = (uint64_t)s_mhi[tid] << 32 | s_mlo[tid];
+        for (int j = 0; j < nmt; ++j) {
+            const int cnt = min(16, c - 16 * j);
+            unsigned __int128 toks = 0;
+            for (int i = 0; i < cnt; ++i) {
+                const int t = __builtin_ctzll(m);
+                m &= m - 1;
+                toks |= (unsigned __int128)t << (kRecTokBits * i);
+            }
+            a.trec[2 * (t0 + j)] = int4{tid, off + 16 * j, cnt, 0};
+            a.trec[2 * (t0 + j) + 1] = int4{(int)(uint32_t)toks, (int)(uint32_t)(toks >> 32), (int)(uint32_t)(toks >> 64), 0};
+        }
+    }
     if (tid == 0) {
         a.offsets[E] = total;
         a.meta[0] = n_active;
-        a.meta[1] = 0;
+        a.meta[1] = n_tiles;
     }
     __syncthreads();
 
