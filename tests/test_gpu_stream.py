@@ -1,12 +1,12 @@
-"""The streaming gate/up kernel of the small-batch path (T <= 64 tokens outside the
+"""The streaming gate/up and down kernels of the small-batch path (T <= 64 tokens outside the
 single-launch path, hidden size an even number of 128-column groups from 1280 to 2048), against the CPU oracle through the C ABI.
 
 The cases cover M-tiles whose activation rows go through LDS (at most 4 rows) and larger
 ones loaded straight into registers, experts with more than 16 rows (several M-tiles),
 a hidden size whose second K chunk holds two groups, a small intermediate size,
 8-bit routed experts, and a shared expert of either width (16-token tiles plus a ragged
-one).  Each case also checks that the streaming kernel is the one that ran and that two
-calls agree bitwise.
+one).  Each case also checks that the streaming kernels are the ones that ran and that
+two calls agree bitwise.
 """
 
 import pytest
@@ -46,7 +46,8 @@ def test_stream_gate_up(T, E, H, I, k, bits, sbits):
     logits = synth.router_logits(500 + T, T, E)
     y, timings = w4.moe_w4a16_forward_timed(bf16_to_dev(x), *routed, top_k=k, bits=bits,
                                             router_logits=f32_to_dev(logits), shared=sh_gpu)
-    assert "gk_stream" in [name for name, _ in timings], timings
+    names = [name for name, _ in timings]
+    assert "gk_stream" in names and "dk_stream" in names, timings
     y_ref, _ = oracle.moe_layer(x, logits, k, *ref.as_args(), bits, shared=sh_ref)
     check_ffn(y, y_ref, f"stream T={T}")
     y2 = w4.moe_w4a16_forward(bf16_to_dev(x), *routed, top_k=k, bits=bits, router_logits=f32_to_dev(logits),

@@ -94,6 +94,8 @@ WsLayout layout(const moe_w4a16_args* a) {
         const int64_t units = std::min(E, P) * chunks(a->I) + (shared ? chunks(a->shared_I) : 0);
         L.splits = (int)std::min<int64_t>(16, std::max<int64_t>(1, (units + 15) / 16));
         if (L.splits > 1) L.part = take((size_t)L.splits * T * H * 4);
+        L.ystage = take((size_t)L.rows_a * H * 4);   // streaming down projection: fp32 rows
+        L.inv = take(P * 4);
     } else {
         L.splits = 1;
         L.nblk = (int)((T + kRouteBlockT - 1) / kRouteBlockT);
@@ -150,6 +152,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     r.x = a->x;
     r.H = a->H;
     r.tokw = static_cast<int2*>(at(L.tokw));
+    r.inv = L.inv ? static_cast<int32_t*>(at(L.inv)) : nullptr;
     r.rec = static_cast<int4*>(at(L.rec));
     r.trec = static_cast<int4*>(at(L.trec));
     r.max_slots = (int)std::min(a->E, a->T * a->top_k);
@@ -216,6 +219,9 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.width_a = L.width_a;
         d.part = L.splits > 1 ? static_cast<float*>(at(L.part)) : nullptr;
         d.splits = L.splits;
+        d.inv = r.inv;
+        d.ystage = static_cast<float*>(at(L.ystage));
+        d.rows_a = L.rows_a;
         d.residual = a->residual;
         d.y = a->y;
         return hip_status(launch_decode(d, s, timer), "decode launch");
@@ -226,7 +232,6 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     r.tiles = static_cast<int32_t*>(at(L.tiles));
     r.xsum = static_cast<float*>(at(L.xsum));
     r.xp = static_cast<uint16_t*>(at(L.xp));
-    r.inv = static_cast<int32_t*>(at(L.inv));
     r.nblk = L.nblk;
     r.max_tiles = L.max_tiles;
     if (int st = hip_status(launch_route_large(r, s, timer), "routing launch")) return st;

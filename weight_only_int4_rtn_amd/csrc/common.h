@@ -239,7 +239,7 @@ struct RouteArgs {
     float* xsum;          // large path: [T, H/128] sums of bf16 activations per group
     uint16_t* xp;         // large path: [T, H] activations with each 8-column block reordered
     int2* tokw;           // [T*k] (token, weight bits) of each pair, in sorted order
-    int32_t* inv;         // large path: [T*k] sorted position of each pair, -1 when dropped
+    int32_t* inv;         // [T*k] sorted position of each pair, -1 when dropped
     int4* rec;            // small path: [max_slots] (expert, first sorted row, count, first tokens);
                           // count 0 marks a slot beyond the active experts
     int4* trec;           // small path: [max_slots + T*k/16][2] M-tiles of <= 16 rows: (expert,
@@ -279,6 +279,9 @@ struct DecodeArgs {
     int64_t width_a;
     float* part;                // [splits, T, H]
     int splits;
+    const int32_t* inv;         // [T*k] sorted position of each pair (-1: dropped)
+    float* ystage;              // [rows_a, H] unweighted down-projection rows (streaming path)
+    int64_t rows_a;             // rows of abuf and ystage: T * k routed, then T shared
     const uint16_t* residual;
     uint16_t* y;
 };
@@ -289,6 +292,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nul
 int stream_workgroups();
 bool stream_fits(const DecodeArgs& a, int max_tiles);
 hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
+// The streaming down projection (intermediate sizes up to 512) and the kernel that sums
+// each token's rows in slot order; otherwise launch_decode splits experts over workgroups.
+bool dk_stream_fits(const DecodeArgs& a);
+hipError_t launch_dk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 // Single-launch path for tiny batches (T * k <= kTinyP): every workgroup routes the batch
 // itself; workgroups [0, n_gk) compute gate/up row blocks and count each finished block

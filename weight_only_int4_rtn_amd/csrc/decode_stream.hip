@@ -284,6 +284,14 @@ __device__ __forceinline__ void s_compute(const SLayout& L, int kh, int half, co
     }
 }
 
+// The first unit (row block) of range b of n when ranges are cut by items, rounded up to a
+// unit boundary: units [0, U_r) hold sub_r items each, units [U_r, U) sub_s.
+__device__ __forceinline__ int s_unit_at(int N_items, int b, int n, int U_r, int U, int sub_r, int sub_s) {
+    const int i = (int)((int64_t)N_items * b / n);
+    if (i <= U_r * sub_r) return (i + sub_r - 1) / sub_r;
+    return min(U, U_r + (i - U_r * sub_r + sub_s - 1) / sub_s);
+}
+
 template <int BITS, int SBITS>
 // One workgroup of ten waves per CU (its LDS ring takes the CU): three waves share a SIMD at most.
 __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) void gk_stream_kernel(
@@ -305,8 +313,9 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     // are summed in one workgroup's registers
     const int U_r = L.n_tiles_r * L.n_rb_r;
     const int U = U_r + (SBITS != 0 ? ((a.T + 15) / 16) * L.n_rb_s : 0);
-    const int u0 = (int)((int64_t)U * blockIdx.x / gridDim.x);
-    const int u1 = (int)((int64_t)U * (blockIdx.x + 1) / gridDim.x);
+    const int N_items = U_r * L.sub_r + (U - U_r) * L.sub_s;
+    const int u0 = s_unit_at(N_items, blockIdx.x, gridDim.x, U_r, U, L.sub_r, L.sub_s);
+    const int u1 = s_unit_at(N_items, blockIdx.x + 1, gridDim.x, U_r, U, L.sub_r, L.sub_s);
     const int nI = (min(u1, U_r) - min(u0, U_r)) * L.sub_r + (max(u1, U_r) - max(u0, U_r)) * L.sub_s;
     if (nI <= 0) return;
 
@@ -439,6 +448,302 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     if (ep_pending) epilogue();
 }
 
+// ------------------------------------------------------------ down projection
+//
+// Items: (M-tile, 16-row block of the output, K half for 8-bit codes).  Every wave streams
+// its own contiguous range of items through a private ring of kDStages LDS stages (no
+// barriers): per item 4 code blocks of 1 KiB (all K <= 512 of 16 rows for 4-bit codes,
+// half of it for 8-bit codes) and the 16 rows' scales.  The M-tile's a rows, stored by
+// gate/up in MFMA operand order, stay in registers while the range stays on that tile.
+// Each finished row block is written unweighted in fp32 to its sorted rows of ystage;
+// dk_finalize_kernel applies the router weights and sums each token's rows in slot order.
+
+constexpr int kDStages = 4;
+constexpr int kDCodeBytes = 4096;                  // 4 blocks of 64 lanes x 16 B
+constexpr int kDStageBytes = kDCodeBytes + 256;    // + scales (64 lanes x 4 B)
+constexpr int kDWaveBytes = kDStages * kDStageBytes;
+constexpr int kDLdsBytes = kSWaves * kDWaveBytes;
+constexpr int kDMaxI = 512;
+constexpr int kDOps = 5;                           // copies per item
+constexpr uint32_t kDSkip = 0x40000000u;           // scalar offset that puts a copy past its buffer
+
+struct DCursor {
+    int tile, hb, kh;
+    int n_kh, bits, G2;
+    STile tl;
+};
+
+__device__ __forceinline__ void d_uniform(DCursor& c) {
+    c.tile = __builtin_amdgcn_readfirstlane(c.tile);
+    c.hb = __builtin_amdgcn_readfirstlane(c.hb);
+    c.kh = __builtin_amdgcn_readfirstlane(c.kh);
+    c.n_kh = __builtin_amdgcn_readfirstlane(c.n_kh);
+    c.bits = __builtin_amdgcn_readfirstlane(c.bits);
+    c.G2 = __builtin_amdgcn_readfirstlane(c.G2);
+    c.tl.e = __builtin_amdgcn_readfirstlane(c.tl.e);
+    c.tl.row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
+    c.tl.count = __builtin_amdgcn_readfirstlane(c.tl.count);
+    c.tl.shared = __builtin_amdgcn_readfirstlane(c.tl.shared);
+}
+
+template <int BITS, int SBITS>
+__device__ __forceinline__ void d_set_tile(const DecodeArgs& a, DCursor& c, int n_tiles_r) {
+    const bool shared = c.tile >= n_tiles_r;
+    const ExpertSet& es = shared ? a.shared : a.routed;
+    c.bits = shared ? SBITS : BITS;
+    c.G2 = (int)(es.I / kGroup);
+    c.n_kh = c.bits == 4 ? 1 : (c.G2 + 1) / 2;
+    if (!shared) {
+        const int4 r = a.trec[2 * c.tile];
+        c.tl.e = r.x;
+        c.tl.row0 = r.y;
+        c.tl.count = r.z;
+        c.tl.shared = 0;
+    } else {
+        const int ts = c.tile - n_tiles_r;
+        c.tl.e = 0;
+        c.tl.row0 = a.T * a.k + 16 * ts;
+        c.tl.count = min(16, a.T - 16 * ts);
+        c.tl.shared = 1;
+    }
+    d_uniform(c);
+}
+
+// This wave's copies of the cursor's item into `stage` (kDOps of them).
+__device__ __forceinline__ void d_issue(const DecodeArgs& a, const DCursor& c, uint32_t stage) {
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const ExpertSet& es = c.tl.shared ? a.shared : a.routed;
+    const int64_t row_bytes = es.I * c.bits / 8;
+    const int64_t e = c.tl.e;
+    const i32x4_t wr = uniform_rsrc(dma_rsrc(reinterpret_cast<const uint8_t*>(es.w2) + e * a.H * row_bytes,
+                                             (uint32_t)(a.H * row_bytes)));
+    const i32x4_t sr = uniform_rsrc(dma_rsrc(es.s2 + e * a.H * c.G2, (uint32_t)(a.H * c.G2 * 2)));
+    const int h0 = c.hb * 16;
+    const uint32_t v = (uint32_t)(ml * row_bytes + q * (c.bits == 4 ? 16 : 32));
+    const int base = __builtin_amdgcn_readfirstlane((int)(h0 * row_bytes));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {   // 4-bit: block b = group b; 8-bit: group 2 kh + b / 2, 16-byte half b % 2
+        const int g = c.bits == 4 ? b : 2 * c.kh + (b >> 1);
+        const int off = c.bits == 4 ? g * 64 : g * 128 + (b & 1) * 16;
+        dma16(wr, stage + b * 1024, v, g < c.G2 ? base + off : (int)kDSkip);
+    }
+    // the 16 rows' scales are contiguous: 16 * G2 bf16 = 32 * G2 bytes, 4 per lane
+    dma4(sr, stage + kDCodeBytes, lane < 8 * c.G2 ? (uint32_t)(lane * 4) : kOob,
+         __builtin_amdgcn_readfirstlane(h0 * c.G2 * 2));
+}
+
+// The tile's a rows as MFMA A fragments (groups 0..3, padding rows zero) and their seeds.
+template <int BITS>
+__device__ __forceinline__ void d_load_a(const DecodeArgs& a, const DCursor& c, u32x4_t (&A)[4][4],
+                                         f32x4_t (&seed)[4]) {
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const bool real = ml < c.tl.count;
+    const uint16_t* row = a.abuf + (int64_t)(c.tl.row0 + (real ? ml : 0)) * a.width_a + 32 * q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gg = min(g, c.G2 - 1);
+            A[g][i] = load16_or_zero(row + gg * kGroup + 8 * i, real && g < c.G2, row);
+        }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) seed[g] = offset_seed<BITS>(A[g]);
+}
+
+// One item's MFMAs: groups of this K part, partial sums (rows 4q + r, column ml) into acc.
+template <int BITS>
+__device__ __forceinline__ void d_compute(const DCursor& c, const uint8_t* stage, const u32x4_t (&A)[4][4],
+                                          const f32x4_t (&seed)[4], f32x4_t& acc) {
+    const int lane = threadIdx.x & 63, ml = lane & 15;
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(stage + kDCodeBytes) + ml * c.G2;
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if (g < c.G2) {
+                const u32x4_t bw[1] = {*reinterpret_cast<const u32x4_t*>(stage + g * 1024 + lane * 16)};
+                const float s = bf16_to_f32(sc[g]);
+                const f32x4_t t = group_dot<4>(A[g], bw, seed[g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += s * t[r];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int g = 2 * c.kh + j;
+            if (g < c.G2) {
+                const u32x4_t bw[2] = {*reinterpret_cast<const u32x4_t*>(stage + (2 * j) * 1024 + lane * 16),
+                                       *reinterpret_cast<const u32x4_t*>(stage + (2 * j + 1) * 1024 + lane * 16)};
+                const float s = bf16_to_f32(sc[g]);
+                const f32x4_t t = c.kh == 0 ? group_dot<8>(A[j], bw, seed[j]) : group_dot<8>(A[2 + j], bw, seed[2 + j]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += s * t[r];
+            }
+        }
+    }
+}
+
+template <int BITS, int SBITS>
+__global__ __launch_bounds__(64 * kSWaves) void dk_stream_kernel(DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_hb = (int)(a.H / 16);
+    const int n_tiles_r = __builtin_amdgcn_readfirstlane(a.meta[1]);
+    const int n_tiles_s = SBITS != 0 ? (a.T + 15) / 16 : 0;
+    const int kh_r = BITS == 4 ? 1 : (int)(a.routed.I / kGroup + 1) / 2;
+    const int kh_s = SBITS == 0 ? 0 : SBITS == 4 ? 1 : (int)(a.shared.I / kGroup + 1) / 2;
+    // ranges are cut between row blocks, never inside one (8-bit codes take two items per
+    // row block, summed in one wave's registers)
+    const int U_r = n_tiles_r * n_hb, U = U_r + n_tiles_s * n_hb;
+    const int nw = gridDim.x * kSWaves, gw = blockIdx.x * kSWaves + wave;
+    const int N_items = U_r * kh_r + (U - U_r) * kh_s;
+    const int u0 = s_unit_at(N_items, gw, nw, U_r, U, kh_r, max(kh_s, 1));
+    const int u1 = s_unit_at(N_items, gw + 1, nw, U_r, U, kh_r, max(kh_s, 1));
+    const int nI = (min(u1, U_r) - min(u0, U_r)) * kh_r + (max(u1, U_r) - max(u0, U_r)) * kh_s;
+    if (nI <= 0) return;
+
+    DCursor ic;
+    ic.tile = u0 / n_hb;   // routed and shared tiles have n_hb row blocks alike
+    ic.hb = u0 - ic.tile * n_hb;
+    ic.kh = 0;
+    d_set_tile<BITS, SBITS>(a, ic, n_tiles_r);
+    DCursor cc = ic;
+    auto advance = [&](DCursor& c) {   // true when a new tile starts
+        bool start = false;
+        if (++c.kh >= c.n_kh) {
+            c.kh = 0;
+            if (++c.hb >= n_hb) {
+                c.hb = 0;
+                ++c.tile;
+                if (c.tile < n_tiles_r + n_tiles_s) d_set_tile<BITS, SBITS>(a, c, n_tiles_r);
+                start = true;
+            }
+        }
+        d_uniform(c);
+        return start;
+    };
+
+    const uint32_t ring = lds_offset(smem) + wave * kDWaveBytes;
+    const uint8_t* ring_p = smem + wave * kDWaveBytes;
+    for (int rel = 0; rel < kDStages - 1 && rel < nI; ++rel) {
+        d_issue(a, ic, ring + rel * kDStageBytes);
+        advance(ic);
+    }
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.ystage, (uint32_t)((int64_t)a.rows_a * a.H * 4));
+    u32x4_t A[4][4];
+    f32x4_t seed[4];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    bool c_start = true;
+    int st_hist = 0;   // store instructions of the last three items, 3 bits each
+    for (int rel = 0; rel < nI; ++rel) {
+        // copies after item rel's: the later items' (at most kDStages - 2 of them) and the
+        // stores of the three items before it
+        const int later = min(nI - 1 - rel, kDStages - 2);
+        const int n = __builtin_amdgcn_readfirstlane(later * kDOps + (st_hist & 7) + ((st_hist >> 3) & 7) +
+                                                     ((st_hist >> 6) & 7));
+        wait_vmcnt_dyn(n);
+        asm volatile("" ::: "memory");
+        if (rel + kDStages - 1 < nI) {
+            d_issue(a, ic, ring + ((rel + kDStages - 1) % kDStages) * kDStageBytes);
+            advance(ic);
+        }
+        if (c_start) {
+            if (cc.bits == BITS) d_load_a<BITS>(a, cc, A, seed);
+            else if constexpr (SBITS != 0 && SBITS != BITS) d_load_a<SBITS>(a, cc, A, seed);
+        }
+        const uint8_t* stage = ring_p + (rel % kDStages) * kDStageBytes;
+        if (cc.bits == BITS) d_compute<BITS>(cc, stage, A, seed, acc);
+        else if constexpr (SBITS != 0 && SBITS != BITS) d_compute<SBITS>(cc, stage, A, seed, acc);
+        int nst = 0;
+        if (cc.kh == cc.n_kh - 1) {   // the row block is complete: rows 4q + r, column ml
+            const int h = cc.hb * 16 + ml;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * q + r;
+                const uint32_t off = m < cc.tl.count ? (uint32_t)(((int64_t)(cc.tl.row0 + m) * a.H + h) * 4) : kOob;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), yr, off, 0, 0);
+                acc[r] = 0.f;
+            }
+            nst = 4;
+        }
+        st_hist = ((st_hist << 3) | nst) & 0x1ff;
+        c_start = advance(cc);
+    }
+}
+
+// y[t] = residual[t] + sum over slots j of w[t, j] * ystage[position of (t, j)] (+ the
+// shared expert's row), in slot order.  Workgroup (t, c) covers 512 columns of token t, so
+// the token's positions and weights are wave-uniform loads and every row read is issued
+// at once.
+constexpr int kFinCols = 512;
+template <int KMAX>   // KMAX == 8 == k, or KMAX = 16 >= k: every load is issued before the first use
+__global__ __launch_bounds__(256) void dk_finalize_kernel(DecodeArgs a) {
+    const int nc = (int)((a.H + kFinCols - 1) / kFinCols);
+    const int t = blockIdx.x / nc;
+    const int64_t h = (int64_t)(blockIdx.x - t * nc) * kFinCols + 2 * threadIdx.x;
+    if (h >= a.H) return;
+    const int k = a.k;
+    int pos[KMAX];
+    float w[KMAX];
+    if constexpr (KMAX == 8) {   // k == 8: two 16-byte loads of each (the token's row starts 32-byte aligned)
+        const int4 p0 = *reinterpret_cast<const int4*>(a.inv + t * 8), p1 = *reinterpret_cast<const int4*>(a.inv + t * 8 + 4);
+        const float4 w0 = *reinterpret_cast<const float4*>(a.wts + t * 8), w1 = *reinterpret_cast<const float4*>(a.wts + t * 8 + 4);
+        const int pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pos[j] = max(pp[j], 0);
+            w[j] = pp[j] >= 0 ? ww[j] : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {   // slots past k repeat slot k - 1 with weight 0
+            const int idx = t * k + min(j, k - 1);
+            const int p = a.inv[idx];
+            pos[j] = max(p, 0);
+            w[j] = (j < k && p >= 0) ? a.wts[idx] : 0.f;
+        }
+    }
+    float2 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) v[j] = *reinterpret_cast<const float2*>(a.ystage + (int64_t)pos[j] * a.H + h);
+    float2 sh = {0.f, 0.f};
+    if (a.shared.bits) sh = *reinterpret_cast<const float2*>(a.ystage + (int64_t)(a.T * k + t) * a.H + h);
+    const int64_t o = (int64_t)t * a.H + h;
+    const uint32_t res = a.residual ? *reinterpret_cast<const uint32_t*>(a.residual + o) : 0u;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        s0 += w[j] * v[j].x;
+        s1 += w[j] * v[j].y;
+    }
+    s0 += sh.x;
+    s1 += sh.y;
+    if (a.residual) {
+        s0 += bf16_to_f32(res & 0xffffu);
+        s1 += bf16_to_f32(res >> 16);
+    }
+    *reinterpret_cast<uint32_t*>(a.y + o) = cvt_bf16x2(s0, s1);
+}
+
+template <int BITS, int SBITS>
+hipError_t launch_dk_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(dk_stream_kernel<BITS, SBITS>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kDLdsBytes);
+        if (st != hipSuccess) return st;
+        attr_set = true;
+    }
+    launch(t, "dk_stream", dk_stream_kernel<BITS, SBITS>, dim3((unsigned)stream_workgroups()),
+           dim3(64 * kSWaves), s, (uint32_t)kDLdsBytes, a);
+    const int64_t nb = (int64_t)a.T * ((a.H + kFinCols - 1) / kFinCols);
+    if (a.k == 8) launch(t, "dk_finalize", dk_finalize_kernel<8>, dim3((unsigned)nb), dim3(256), s, 0u, a);
+    else launch(t, "dk_finalize", dk_finalize_kernel<16>, dim3((unsigned)nb), dim3(256), s, 0u, a);
+    return hipGetLastError();
+}
+
 int g_stream_wgs[64];   // per device: CUs (0: not yet known, -1: query failed)
 
 template <int BITS, int SBITS>
@@ -499,6 +804,24 @@ hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     if (sb == 0) return launch_stream_t<8, 0>(a, s, t);
     if (sb == 4) return launch_stream_t<8, 4>(a, s, t);
     return launch_stream_t<8, 8>(a, s, t);
+}
+
+bool dk_stream_fits(const DecodeArgs& a) {
+    if (stream_workgroups() <= 0) return false;
+    if (a.routed.I > kDMaxI || (a.shared.bits && a.shared.I > kDMaxI)) return false;
+    return a.H % 32 == 0 && a.rows_a * a.H * 4 < (int64_t)kDSkip;
+}
+
+hipError_t launch_dk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (a.routed.bits == 4) {
+        if (sb == 0) return launch_dk_stream_t<4, 0>(a, s, t);
+        if (sb == 4) return launch_dk_stream_t<4, 4>(a, s, t);
+        return launch_dk_stream_t<4, 8>(a, s, t);
+    }
+    if (sb == 0) return launch_dk_stream_t<8, 0>(a, s, t);
+    if (sb == 4) return launch_dk_stream_t<8, 4>(a, s, t);
+    return launch_dk_stream_t<8, 8>(a, s, t);
 }
 
 }  // namespace w4a16

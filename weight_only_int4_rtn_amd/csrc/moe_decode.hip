@@ -860,6 +860,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
         const dim3 gk_grid((unsigned)(Imax / 16), (unsigned)(max_active + (SBITS ? 1 : 0)));
         launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, 0u, a);
     }
+    if (dk_stream_fits(a)) return launch_dk_stream(a, s, t);
     const dim3 dk_grid((unsigned)(a.H / 16), (unsigned)a.splits);
     launch(t, "dk_decode", dk_decode_kernel<BITS, SBITS>, dk_grid, dim3(64 * kDkWaves), s, 0u, a);
     if (a.splits > 1) {

@@ -155,6 +155,9 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
             a.sorted[s_off[e] + rank] = p;
             a.tokw[s_off[e] + rank] = int2{t, __float_as_int(s_w[p])};
         }
+        a.inv[p] = e >= 0 ? s_off[e] + (int)__popcll(((uint64_t)s_mhi[e] << 32 | s_mlo[e]) &
+                                                     ((1ull << (p / k)) - 1ull))
+                          : -1;
     }
 }
 
