@@ -183,7 +183,9 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
 
 
 KERNEL_SOURCES = {"tiny_decode": "moe_decode.hip", "gk_decode": "moe_decode.hip", "dk_decode": "moe_decode.hip",
+                  "gk_stream": "decode_stream.hip", "dk_stream": "decode_stream.hip",
                   "gk_prefill": "moe_prefill.hip", "dk_prefill": "moe_prefill.hip"}
+KERNEL_HEADERS = ("common.h", "route_dev.h", "dma.h", "decode_dev.h")
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.txt")
 
 
@@ -192,7 +194,7 @@ def kernel_source_digest(kernel):
     import hashlib
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_int4_rtn_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "common.h", "route_dev.h"):
+    for f in (KERNEL_SOURCES[kernel],) + KERNEL_HEADERS:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -51,16 +51,25 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 // lane keeps them sorted (larger first, lower index first on equal values) so its best
 // is its first register; with more, the lane scans them each round.
 // Lane j < k returns slot j's expert and its softmax weight over the chosen logits.
+// This lane's logits of one token (experts lane, lane + 64, ...): unconditional (clamped)
+// loads, all in flight together.
+template <int NV>
+__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E, float (&raw)[NV]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) raw[i] = row[min(lane + 64 * i, E - 1)];
+}
+
 template <int NV>   // logits per lane: E <= 64 * NV
-__device__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_id, float* my_w) {
+__device__ void wave_topk_from(const float (&raw)[NV], int E, int k, int* my_id, float* my_w) {
     constexpr bool kSorted = NV <= 4;
     const int lane = threadIdx.x & 63;
     float hv[NV];
     int he[kSorted ? NV : 1];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {   // unconditional (clamped) loads: all in flight together
+    for (int i = 0; i < NV; ++i) {
         const int e = lane + 64 * i;
-        const float v = row[min(e, E - 1)];
+        const float v = raw[i];
         hv[i] = (e < E && !__builtin_isnan(v)) ? v : -__builtin_inff();
         if constexpr (kSorted) he[i] = e < E ? e : 0x7fffffff;
     }
@@ -132,6 +141,13 @@ __device__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_i
     }
     *my_id = lane < k ? id : -1;
     *my_w = lane < k ? mine / den : 0.f;
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_id, float* my_w) {
+    float raw[NV];
+    wave_topk_load<NV>(row, E, raw);
+    wave_topk_from<NV>(raw, E, k, my_id, my_w);
 }
 
 __device__ __forceinline__ void wave_topk_any(const float* __restrict__ row, int E, int k, int* my_id,
