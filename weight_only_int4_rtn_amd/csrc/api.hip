@@ -197,7 +197,6 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         return hip_status(launch_tiny(d, s, timer), "decode launch");
     }
     if (a->T <= kSmallT) {
-        if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
         DecodeArgs d{};
         d.x = a->x;
         d.T = (int)a->T;
@@ -222,6 +221,10 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.inv = r.inv;
         d.ystage = static_cast<float*>(at(L.ystage));
         d.rows_a = L.rows_a;
+        d.route = r;
+        d.fused_route = stream_fits(d, (int)(std::min(a->E, a->T * a->top_k) + a->T * a->top_k / 16)) ? 1 : 0;
+        if (!d.fused_route)
+            if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
         d.residual = a->residual;
         d.y = a->y;
         return hip_status(launch_decode(d, s, timer), "decode launch");

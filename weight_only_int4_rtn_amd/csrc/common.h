@@ -284,6 +284,8 @@ struct DecodeArgs {
     int64_t rows_a;             // rows of abuf and ystage: T * k routed, then T shared
     const uint16_t* residual;
     uint16_t* y;
+    int fused_route;            // 1: the streaming gate/up kernel routes the batch itself
+    RouteArgs route;            // ... with these outputs (its workgroup 0 writes them)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 // Workgroups of the streaming gate/up kernel (one per CU of the current device, 0 when

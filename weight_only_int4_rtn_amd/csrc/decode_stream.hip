@@ -22,6 +22,7 @@
 #include "common.h"
 #include "decode_dev.h"
 #include "dma.h"
+#include "route_small.h"
 
 namespace w4a16 {
 
@@ -308,7 +309,16 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     L.n_rb_s = SBITS != 0 ? (int)(a.shared.I / 16) : 0;
     L.sub_r = BITS == 4 ? KH : 2 * KH;
     L.sub_s = SBITS == 4 ? KH : 2 * KH;
-    L.n_tiles_r = __builtin_amdgcn_readfirstlane(a.meta[1]);
+    // the batch's routing: done here by every workgroup (in the LDS the ring will reuse,
+    // workgroup 0 also writing it out), or read from the routing kernel's outputs
+    SmallRouteLds& rl = *reinterpret_cast<SmallRouteLds*>(smem);
+    static_assert(sizeof(SmallRouteLds) <= kSOffA, "routing scratch inside the stage ring");
+    if (a.fused_route) {
+        route_small_wg(a.route, rl, blockIdx.x == 0);
+        L.n_tiles_r = __builtin_amdgcn_readfirstlane(rl.n_tiles);
+    } else {
+        L.n_tiles_r = __builtin_amdgcn_readfirstlane(a.meta[1]);
+    }
     // ranges are cut between row blocks (units), never inside one: a row block's K chunks
     // are summed in one workgroup's registers
     const int U_r = L.n_tiles_r * L.n_rb_r;
@@ -324,8 +334,16 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     L.t_lo = u0 < U_r ? u0 / L.n_rb_r : L.n_tiles_r;
     const int t_hi = u0 < U_r ? (min(u1, U_r) - 1) / L.n_rb_r : L.n_tiles_r - 1;
     if (t_hi - L.t_lo + 1 > kSMaxTiles) return;   // excluded on the host (stream_fits)
-    if (tid < 2 * (t_hi - L.t_lo + 1))
+    if (a.fused_route) {
+        if (tid < t_hi - L.t_lo + 1) {
+            int4 r0, r1;
+            small_tile_record(rl, a.E, L.t_lo + tid, r0, r1);
+            reinterpret_cast<int4*>(s_tiles)[2 * tid] = r0;
+            reinterpret_cast<int4*>(s_tiles)[2 * tid + 1] = r1;
+        }
+    } else if (tid < 2 * (t_hi - L.t_lo + 1)) {
         reinterpret_cast<int4*>(s_tiles)[tid] = a.trec[2 * L.t_lo + tid];
+    }
     if (tid < 64) *reinterpret_cast<u32x4_t*>(smem + kSOffZero + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
 

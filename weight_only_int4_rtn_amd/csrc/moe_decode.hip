@@ -853,7 +853,7 @@ namespace {
 template <int BITS, int SBITS>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
-    if (stream_fits(a, max_active + a.T * a.k / 16)) {
+    if (a.fused_route) {   // stream_fits holds: routing runs inside the streaming gate/up kernel
         if (hipError_t st = launch_gk_stream(a, s, t)) return st;
     } else {
         const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);

@@ -16,175 +16,15 @@
 // route_scatter_kernel (sorted pair list).
 #include "common.h"
 #include "route_dev.h"
+#include "route_small.h"
 
 namespace w4a16 {
-
-namespace {
-
-// Block-wide exclusive scan of one value per thread (blockDim.x <= 1024, multiple of 64);
-// s_tmp holds 64 values.
-template <typename V>
-__device__ V block_exclusive_scan(V v, V* s_tmp, V* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    V incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const V o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) s_tmp[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        V t = lane < nw ? s_tmp[lane] : V(0);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const V o = __shfl_up(t, off);
-            if (lane >= off) t += o;
-        }
-        if (lane < nw) s_tmp[32 + lane] = t;   // inclusive wave prefix
-    }
-    __syncthreads();
-    const V base = wave ? s_tmp[32 + wave - 1] : V(0);
-    *total = s_tmp[32 + nw - 1];
-    __syncthreads();
-    return base + incl - v;
-}
-
-}  // namespace
 
 // ------------------------------------------------------------------ small batch
 
 __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
-    __shared__ int s_ids[kSmallT * kMaxK];
-    __shared__ float s_w[kSmallT * kMaxK];
-    __shared__ int s_cnt[kMaxE];
-    __shared__ uint32_t s_mlo[kMaxE], s_mhi[kMaxE];
-    __shared__ int s_off[kMaxE];
-    __shared__ uint64_t s_tmp64[64];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T, E = a.E, k = a.k, P = T * k;
-    for (int e = tid; e < E; e += blockDim.x) { s_cnt[e] = 0; s_mlo[e] = 0; s_mhi[e] = 0; }
-
-    if (a.logits) {
-        const int nw = blockDim.x >> 6;
-        auto emit = [&](int t, int my_id, float my_w) {
-            if (lane < k) {
-                a.ids[t * k + lane] = my_id;
-                a.wts[t * k + lane] = my_w;
-                s_ids[t * k + lane] = my_id;
-                s_w[t * k + lane] = my_w;
-            }
-        };
-        if (E <= 256) {   // every token of this wave (at most kSmallT / 16) loaded before the first top-k
-            constexpr int kTok = kSmallT / 16;
-            float raw[kTok][4];
-#pragma unroll
-            for (int j = 0; j < kTok; ++j)
-                wave_topk_load<4>(a.logits + (int64_t)min(wave + j * nw, T - 1) * E, E, raw[j]);
-#pragma unroll
-            for (int j = 0; j < kTok; ++j) {
-                const int t = wave + j * nw;
-                if (t < T) {
-                    int my_id;
-                    float my_w;
-                    wave_topk_from<4>(raw[j], E, k, &my_id, &my_w);
-                    emit(t, my_id, my_w);
-                }
-            }
-        } else {
-            for (int t = wave; t < T; t += nw) {
-                int my_id;
-                float my_w;
-                wave_topk_any(a.logits + (int64_t)t * E, E, k, &my_id, &my_w);
-                emit(t, my_id, my_w);
-            }
-        }
-    } else {
-        for (int p = tid; p < P; p += blockDim.x) {
-            s_ids[p] = checked_id(a.ids + (p / k) * k, p % k, E);
-            s_w[p] = a.wts[p];
-        }
-    }
-    __syncthreads();
-
-    for (int p = tid; p < P; p += blockDim.x) {
-        const int e = s_ids[p];
-        if (e >= 0) {
-            const int t = p / k;
-            atomicAdd(&s_cnt[e], 1);
-            if (t < 32) atomicOr(&s_mlo[e], 1u << t);
-            else atomicOr(&s_mhi[e], 1u << (t - 32));
-        }
-    }
-    __syncthreads();
-
-    // offsets (exclusive scan of counts), the ascending list of active experts and the first
-    // M-tile of each, from one scan of count << 42 | M-tiles << 21 | (count > 0) (every sum
-    // stays below 2^21 for T * k <= 1024)
-    uint64_t packed_total = 0;
-    const int c = tid < E ? s_cnt[tid] : 0;
-    const int nmt = (c + 15) >> 4;
-    const uint64_t packed = block_exclusive_scan<uint64_t>(
-        (uint64_t)c << 42 | (uint64_t)nmt << 21 | (uint64_t)(c > 0), s_tmp64, &packed_total);
-    constexpr uint64_t kF = (1u << 21) - 1;
-    const int off = (int)(packed >> 42), t0 = (int)((packed >> 21) & kF), act = (int)(packed & kF);
-    const int total = (int)(packed_total >> 42), n_tiles = (int)((packed_total >> 21) & kF),
-              n_active = (int)(packed_total & kF);
-    if (tid < E) {
-        s_off[tid] = off;
-        a.offsets[tid] = off;
-        a.counts[tid] = c;
-        if (c > 0) {
-            // the first kRecTokens tokens of the expert, ascending, kRecTokBits bits each
-            uint64_t m = (uint64_t)s_mhi[tid] << 32 | s_mlo[tid];
-            int toks = 0;
-            for (int j = 0; j < kRecTokens && m; ++j) {
-                toks |= __builtin_ctzll(m) << (kRecTokBits * j);
-                m &= m - 1;
-            }
-            a.active[act] = tid;
-            a.rec[act] = int4{tid, off, c, toks};
-        }
-    }
-    for (int sl = n_active + tid; sl < a.max_slots; sl += blockDim.x) a.rec[sl] = int4{0, 0, 0, 0};
-    // M-tiles of at most 16 rows, in slot order, each with all of its tokens (token m in
-    // bits [6m, 6m + 6) of the 96 bits .x, .y, .z of the second int4)
-    if (tid < E && c > 0) {
-        uint64_t m = (uint64_t)s_mhi[tid] << 32 | s_mlo[tid];
-        for (int j = 0; j < nmt; ++j) {
-            const int cnt = min(16, c - 16 * j);
-            unsigned __int128 toks = 0;
-            for (int i = 0; i < cnt; ++i) {
-                const int t = __builtin_ctzll(m);
-                m &= m - 1;
-                toks |= (unsigned __int128)t << (kRecTokBits * i);
-            }
-            a.trec[2 * (t0 + j)] = int4{tid, off + 16 * j, cnt, 0};
-            a.trec[2 * (t0 + j) + 1] = int4{(int)(uint32_t)toks, (int)(uint32_t)(toks >> 32), (int)(uint32_t)(toks >> 64), 0};
-        }
-    }
-    if (tid == 0) {
-        a.offsets[E] = total;
-        a.meta[0] = n_active;
-        a.meta[1] = n_tiles;
-    }
-    __syncthreads();
-
-    for (int p = tid; p < P; p += blockDim.x) {
-        const int e = s_ids[p];
-        if (e >= 0) {
-            const int t = p / k;
-            const uint32_t lo = s_mlo[e], hi = s_mhi[e];
-            const int rank = t < 32 ? __popc(lo & ((1u << t) - 1u))
-                                    : __popc(lo) + __popc(hi & ((1u << (t - 32)) - 1u));
-            a.sorted[s_off[e] + rank] = p;
-            a.tokw[s_off[e] + rank] = int2{t, __float_as_int(s_w[p])};
-        }
-        a.inv[p] = e >= 0 ? s_off[e] + (int)__popcll(((uint64_t)s_mhi[e] << 32 | s_mlo[e]) &
-                                                     ((1ull << (p / k)) - 1ull))
-                          : -1;
-    }
+    __shared__ SmallRouteLds lds;
+    route_small_wg(a, lds, true);
 }
 
 // ------------------------------------------------------------------ large batch
