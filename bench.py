@@ -185,18 +185,22 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
 KERNEL_SOURCES = {"tiny_decode": "moe_decode.hip", "gk_decode": "moe_decode.hip", "dk_decode": "moe_decode.hip",
                   "gk_stream": "decode_stream.hip", "dk_stream": "decode_stream.hip",
                   "gk_prefill": "moe_prefill.hip", "dk_prefill": "moe_prefill.hip"}
-KERNEL_HEADERS = ("common.h", "route_dev.h", "dma.h", "decode_dev.h")
+KERNEL_HEADERS = ("common.h", "route_dev.h", "route_small.h", "dma.h", "decode_dev.h")
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.txt")
 
 
 def kernel_source_digest(kernel):
-    """Digest of the sources a kernel is built from (its .hip file and the shared headers)."""
+    """Digest of the code a kernel is built from (its .hip file and the shared headers), with
+    comments and blank space removed so that a change to the text alone keeps the digest."""
     import hashlib
+    import re
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "weight_only_int4_rtn_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[kernel],) + KERNEL_HEADERS:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

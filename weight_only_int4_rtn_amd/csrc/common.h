@@ -300,9 +300,9 @@ bool dk_stream_fits(const DecodeArgs& a);
 hipError_t launch_dk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 // Single-launch path for tiny batches (T * k <= kTinyP): every workgroup routes the batch
-// itself; workgroups [0, n_gk) compute gate/up row blocks and count each finished block
-// on its expert slot's counter; the others compute 16 output rows of the down projection
-// once every active slot is complete.
+// itself; workgroups [0, H / 16) compute 16 output rows of the down projection each, from
+// a values they read back as soon as every word carries this launch's epoch; the n_gk
+// workgroups after them compute gate/up row blocks and write those tagged words.
 struct TinyArgs {
     const uint16_t* x;
     int T, E, k;

@@ -7,13 +7,17 @@
 // holds the (at most 16) tokens routed to that expert.  The MFMA does the K reduction,
 // so no cross-lane sums are needed; zero-padded token rows cost nothing in HBM bytes.
 //
+// tiny_decode_kernel (T * k <= 16 pairs): routing, gate/up and down in one launch; see
+//   the tiny-batch section below.
 // gk_decode_kernel: one workgroup per (active expert, 16 gate + 16 matching up rows);
-//   its 4 waves split the 128-column groups of K and meet in LDS.  Writes
-//   a = SiLU(g) * u as bf16 in sorted-pair order.
+//   its 8 waves split the 128-column groups of K and meet in LDS.  Writes
+//   a = SiLU(g) * u as bf16 in sorted-pair order.  Used when the streaming gate/up kernel
+//   (decode_stream.hip) does not fit the shape.
 // dk_decode_kernel: one 8-wave workgroup per (16 output rows, expert split); each wave walks a
 //   strided subset of the active experts in ascending order and accumulates
 //   w[t,j] * (W2_e a) per token in LDS.  Waves, then splits, are summed in a fixed
-//   order, so the result is bitwise reproducible.
+//   order, so the result is bitwise reproducible.  Used when the streaming down kernel
+//   does not fit the shape (intermediate size above 512).
 #include "common.h"
 #include "decode_dev.h"
 #include "route_dev.h"
