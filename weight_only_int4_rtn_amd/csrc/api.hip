@@ -190,7 +190,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.tag_bytes = (uint32_t)tag_bytes;
         d.residual = a->residual;
         d.y = a->y;
-        const int64_t slots = std::min(a->E, a->T * a->top_k) + (a->shared_bits ? 1 : 0);
+        const int64_t slots = a->T * a->top_k + (a->shared_bits ? 1 : 0);   // one per pair, + the shared expert
         d.n_rb = (int)(L.width_a / 16);
         d.n_gk = (int)(slots * d.n_rb);
         d.lds_bytes = (uint32_t)std::max<size_t>(8 * 8 * 64 * 4, tiny_lds);   // gate/up: partial sums

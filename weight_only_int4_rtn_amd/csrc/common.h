@@ -302,7 +302,8 @@ hipError_t launch_dk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = 
 // Single-launch path for tiny batches (T * k <= kTinyP): every workgroup routes the batch
 // itself; workgroups [0, H / 16) compute 16 output rows of the down projection each, from
 // a values they read back as soon as every word carries this launch's epoch; the n_gk
-// workgroups after them compute gate/up row blocks and write those tagged words.
+// workgroups after them compute gate/up row blocks of one (token, rank) pair each, or of
+// the shared expert, and write those tagged words.
 struct TinyArgs {
     const uint16_t* x;
     int T, E, k;
@@ -321,7 +322,7 @@ struct TinyArgs {
     uint32_t tag_bytes;
     const uint16_t* residual;
     uint16_t* y;
-    int n_gk;                   // gate/up workgroups: (slots + shared) * n_rb
+    int n_gk;                   // gate/up workgroups: (T * k pairs + shared) * n_rb
     int n_rb;                   // 16-row blocks per slot: max(I, shared I) / 16
     uint32_t lds_bytes;         // dynamic LDS per workgroup
 };

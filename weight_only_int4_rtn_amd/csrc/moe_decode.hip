@@ -402,16 +402,19 @@ __global__ __launch_bounds__(256) void dk_combine_kernel(const float* __restrict
 //
 // T * k <= kTinyP pairs (one or two tokens at top-8): one launch.  Every workgroup routes
 // the batch itself from the logits (a few KB), so no workgroup waits on a routing kernel.
-// Workgroups [0, H / 16) own 16 output rows each: they issue the loads of their first
-// down-projection codes, then read every a word this launch produces, past the caches,
-// until each carries the current epoch; the values go to LDS and the workgroup finishes
-// the down projection of all active experts for its rows (the sum over experts stays in
-// one workgroup and in a fixed order).  The workgroups after them own one 16-row block of
-// one active expert's gate/up bank (as gk_decode) and write their a values through to
-// memory, into the tag area of the workspace head: one 32-bit word per value, the bf16
-// value in the low half and this launch's epoch in the high half.  A value carries its own
-// readiness: no counter is raised between the two halves.  The down workgroups come first
-// so that they are resident, with their codes in flight, while gate/up runs.
+// Workgroups [0, H / 16) own 16 output rows each: they route the whole batch, issue the
+// loads of their first down-projection codes, then read every a word this launch
+// produces, past the caches, until each carries the current epoch; the values go to LDS
+// and the workgroup finishes the down projection of all active experts for its rows (the
+// sum over experts stays in one workgroup and in a fixed order).  The workgroups after
+// them each own one 16-row block of the gate/up bank of one (token, rank) pair: they run
+// the top-k of that token only up to that rank, so the first ranks start streaming their
+// weights while later ones are still being chosen, and the shared expert's row blocks
+// start at once.  They write their a values through to memory, row p of the tag area in
+// the workspace head for pair p: one 32-bit word per value, the bf16 value in the low half
+// and this launch's epoch in the high half.  A value carries its own readiness: no counter
+// is raised between the two halves.  The down workgroups come first so that they are
+// resident, with their codes in flight, while gate/up runs.
 //
 // Epochs run 1..65535 (the epoch word holds epoch - 1).  Down workgroups count their
 // exits in groups of 16; the last one to leave resets those counters and advances the
@@ -507,51 +510,67 @@ __device__ void tiny_route(const TinyArgs& a, TinyRoute& r, bool writer) {
     }
 }
 
-template <int BITS, int SBITS>
-__device__ void tiny_gate_up(const TinyArgs& a, const TinyRoute& r, float* s_red, uint32_t tag) {
-    const int b = blockIdx.x - (int)(a.H / 16);   // down workgroups come first in the grid
-    const int slot = b / a.n_rb, rb = b % a.n_rb;
-    const int P = min(a.E, a.T * a.k);
-    const bool shared = SBITS != 0 && slot == P;
-    const int n0 = rb * 16;
-    int count, pos0, e = 0;
-    int64_t I_e;
-    if (shared) {
-        I_e = a.shared.I;
-        count = a.T;
-        pos0 = a.T * a.k;
+// Expert of pair (token t, top-k rank j), the same in every lane.  From logits the wave
+// runs the top-k only up to round j (the rounds are those of the full routing, so the
+// winner is the same), which lets the workgroup of an early rank start loading its
+// weights before the whole batch is routed.
+__device__ __forceinline__ int tiny_pair_expert(const TinyArgs& a, int t, int j) {
+    const int E = a.E, k = a.k;
+    if (!a.logits) return checked_id(a.ids + t * k, j, E);
+    const float* row = a.logits + (int64_t)t * E;
+    int id;
+    float w;
+    if (E <= 256) {
+        float raw[4];
+        wave_topk_load<4>(row, E, raw);
+        wave_topk_from<4>(raw, E, j + 1, &id, &w);
+    } else if (E <= 512) {
+        float raw[8];
+        wave_topk_load<8>(row, E, raw);
+        wave_topk_from<8>(raw, E, j + 1, &id, &w);
     } else {
-        if (slot >= r.n_active) return;
-        const int4 sl = r.slot[slot];
-        e = sl.x;
-        pos0 = sl.y;
-        count = sl.z;
-        I_e = a.routed.I;
+        float raw[16];
+        wave_topk_load<16>(row, E, raw);
+        wave_topk_from<16>(raw, E, j + 1, &id, &w);
     }
-    if (n0 >= I_e) return;
+    return __builtin_amdgcn_readlane(id, j);
+}
+
+// Gate/up workgroup b: pair p = b / n_rb (token p / k, rank p % k) and its 16-row block
+// b % n_rb, writing row p of the tag area; or, after the pairs, a row block of the shared
+// expert for every token (rows T * k + t).
+template <int BITS, int SBITS>
+__device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
+    const int b = blockIdx.x - (int)(a.H / 16);   // down workgroups come first in the grid
+    const int Tk = a.T * a.k;
+    const int p = b / a.n_rb, rb = b % a.n_rb;
+    const int n0 = rb * 16;
     const int ml = threadIdx.x & 15;
-    for (int mt = 0; mt < count; mt += 16) {
-        const int m = mt + ml;
-        const bool ok = m < count;
-        const int rows = min(16, count - mt);
-        if (shared) {
-            if constexpr (SBITS != 0)
-                gk_tile<SBITS, true>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? m : mt, ok, pos0 + mt, rows,
-                                     a.tags, a.width_a, s_red, a.tag_bytes, tag);
-        } else {
-            const int tok = r.tw[pos0 + (ok ? m : mt)].x;
-            const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
-            gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
-                                a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, tok, ok, pos0 + mt, rows,
-                                a.tags, a.width_a, s_red, a.tag_bytes, tag);
-        }
+    if (p < Tk) {
+        const int64_t I_e = a.routed.I;
+        if (n0 >= I_e) return;
+        const int t = p / a.k;
+        const int e = tiny_pair_expert(a, t, p % a.k);
+        if (e < 0) return;   // dropped pair: the down workgroups skip its row
+        const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
+        gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
+                            a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, t, ml == 0, p, 1, a.tags,
+                            a.width_a, s_red, a.tag_bytes, tag);
+    } else if constexpr (SBITS != 0) {
+        const int64_t I_e = a.shared.I;
+        if (p > Tk || n0 >= I_e) return;
+        const bool ok = ml < a.T;
+        gk_tile<SBITS, true>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? ml : 0, ok, Tk, a.T, a.tags,
+                             a.width_a, s_red, a.tag_bytes, tag);
     }
 }
 
 // Copies every a value of this launch from the tag area ([rows_a, W] words) into `stage`
 // ([rows_a, Ws] bf16), waiting for each 16-byte chunk until all four of its words carry
-// `tag`.  Routed rows [0, n_valid) hold I_r values, shared rows [T*k, T*k + T) hold I_s.
-__device__ void tiny_collect_a(const TinyArgs& a, int n_valid, uint32_t tag, uint16_t* stage, int Ws) {
+// `tag`.  Routed rows are those of the n_valid pairs pair_at[0 .. n_valid) (I_r values
+// each), shared rows [T*k, T*k + T) hold I_s.
+__device__ void tiny_collect_a(const TinyArgs& a, const TinyRoute& r, uint32_t tag, uint16_t* stage, int Ws) {
+    const int n_valid = r.n_valid;
     const int W = (int)a.width_a, Tk = a.T * a.k;
     const int cr = (int)(a.routed.I / 4), cs = (int)(a.shared.I / 4);   // chunks per row
     const int n_rc = n_valid * cr;
@@ -565,7 +584,7 @@ __device__ void tiny_collect_a(const TinyArgs& a, int n_valid, uint32_t tag, uin
 #pragma unroll
         for (int i = 0; i < kTinyPoll; ++i) {
             const int c = c0 + i * (int)blockDim.x;
-            const int row = c < n_rc ? c / cr : Tk + (c - n_rc) / cs;
+            const int row = c < n_rc ? r.pair_at[c / cr] : Tk + (c - n_rc) / cs;
             const int col = 4 * (c < n_rc ? c % cr : (c - n_rc) % cs);
             off[i] = c < n_c ? (uint32_t)(row * W + col) * 4 : 0xfffffff0u;   // beyond the buffer: reads zeros
             soff[i] = row * Ws + col;
@@ -677,7 +696,9 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
     constexpr int CH = kTinyCh<BITS>;
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const bool real = ml < t.count;
-    const uint16_t* arow = stage + (int64_t)(t.pos0 + ml) * Ws + 32 * q;
+    // stage rows: routed a rows sit at their pair index, shared rows at T * k + token
+    const int srow = t.shared ? t.pos0 + ml : r.pair_at[t.pos0 + min(ml, t.count - 1)];
+    const uint16_t* arow = stage + (int64_t)srow * Ws + 32 * q;
     const uint16_t* zl = zb + 8 * lane;
     f32x4_t d[CH];
 #pragma unroll
@@ -693,12 +714,13 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
     for (int rr = 0; rr < 4; ++rr) {
         const int m = 4 * q + rr;
         const int p = t.pos0 + min(m, t.count - 1);
+        const int xr = t.shared ? p : r.pair_at[p];   // stage row of D row m
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int g = t.g0 + min(j, t.ngroups - 1);
             const float sc = j < t.ngroups ? bf16_to_f32(c.s[j]) : 0.f;
-            acc += sc * (d[j][rr] - code_offset<BITS>() * xs[p * G + g]);
+            acc += sc * (d[j][rr] - code_offset<BITS>() * xs[xr * G + g]);
         }
         if (m < t.count) {
             const int2 tw = t.shared ? int2{m, __float_as_int(1.0f)} : r.tw[p];
@@ -744,14 +766,14 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
         else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
     }
 
-    tiny_collect_a(a, r.n_valid, (epoch_word + 1) << 16, stage, Ws);
+    tiny_collect_a(a, r, (epoch_word + 1) << 16, stage, Ws);
     __syncthreads();
     {   // sum of every 128-column group of every row in use (16 lanes per row and group)
         const int Gr = (int)(a.routed.I / kGroup), Gs = (int)(a.shared.I / kGroup);
         const int n_rp = r.n_valid * Gr;
         const int n_pairs = n_rp + (SBITS != 0 ? T * Gs : 0);
         for (int p = (int)threadIdx.x >> 4; p < n_pairs; p += (int)blockDim.x >> 4) {
-            const int row = p < n_rp ? p / Gr : Tk + (p - n_rp) / Gs;
+            const int row = p < n_rp ? r.pair_at[p / Gr] : Tk + (p - n_rp) / Gs;
             const int g = p < n_rp ? p % Gr : (p - n_rp) % Gs;
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (int64_t)row * Ws + g * kGroup +
                                                                (threadIdx.x & 15) * 8);
@@ -828,9 +850,12 @@ __device__ __forceinline__ void tiny_decode_body(const TinyArgs& a) {
     // epoch - 1 of this launch (written by the previous launch's last workgroup)
     const uint32_t epoch_word =
         __hip_atomic_load(sync_word(a.sync, kSyncEpoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tiny_route(a, route, blockIdx.x == 0);
-    if ((int)blockIdx.x >= (int)(a.H / 16)) tiny_gate_up<BITS, SBITS>(a, route, s_dyn, (epoch_word + 1) << 16);
-    else tiny_down<BITS, SBITS>(a, route, s_dyn, epoch_word);
+    if ((int)blockIdx.x >= (int)(a.H / 16)) {
+        tiny_gate_up<BITS, SBITS>(a, s_dyn, (epoch_word + 1) << 16);
+    } else {
+        tiny_route(a, route, blockIdx.x == 0);
+        tiny_down<BITS, SBITS>(a, route, s_dyn, epoch_word);
+    }
 }
 
 // Two workgroups per CU where the registers allow it without spilling (4-bit codes with
