@@ -565,58 +565,6 @@ __device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
     }
 }
 
-// Copies every a value of this launch from the tag area ([rows_a, W] words) into `stage`
-// ([rows_a, Ws] bf16), waiting for each 16-byte chunk until all four of its words carry
-// `tag`.  Routed rows are those of the n_valid pairs pair_at[0 .. n_valid) (I_r values
-// each), shared rows [T*k, T*k + T) hold I_s.
-__device__ void tiny_collect_a(const TinyArgs& a, const TinyRoute& r, uint32_t tag, uint16_t* stage, int Ws) {
-    const int n_valid = r.n_valid;
-    const int W = (int)a.width_a, Tk = a.T * a.k;
-    const int cr = (int)(a.routed.I / 4), cs = (int)(a.shared.I / 4);   // chunks per row
-    const int n_rc = n_valid * cr;
-    const int n_c = n_rc + (a.shared.bits ? a.T * cs : 0);
-    const __amdgpu_buffer_rsrc_t tr = make_rsrc(a.tags, a.tag_bytes);
-    bool timed_out = false;
-    for (int c0 = threadIdx.x; c0 < n_c; c0 += kTinyPoll * (int)blockDim.x) {
-        uint32_t off[kTinyPoll];
-        int soff[kTinyPoll];
-        uint32_t pending = 0;
-#pragma unroll
-        for (int i = 0; i < kTinyPoll; ++i) {
-            const int c = c0 + i * (int)blockDim.x;
-            const int row = c < n_rc ? r.pair_at[c / cr] : Tk + (c - n_rc) / cs;
-            const int col = 4 * (c < n_rc ? c % cr : (c - n_rc) % cs);
-            off[i] = c < n_c ? (uint32_t)(row * W + col) * 4 : 0xfffffff0u;   // beyond the buffer: reads zeros
-            soff[i] = row * Ws + col;
-            if (c < n_c) pending |= 1u << i;
-        }
-        for (int spins = 0; pending; ++spins) {
-            u32x4_t v[kTinyPoll];
-#pragma unroll
-            for (int i = 0; i < kTinyPoll; ++i)
-                v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tr, off[i], 0, kSc1));
-#pragma unroll
-            for (int i = 0; i < kTinyPoll; ++i) {
-                // all four high halves equal to the tag <=> the OR of the XORs is below 2^16
-                const uint32_t diff = (v[i][0] ^ tag) | (v[i][1] ^ tag) | (v[i][2] ^ tag) | (v[i][3] ^ tag);
-                if ((pending >> i & 1u) && diff < 0x10000u) {
-                    const uint32_t lo = (v[i][0] & 0xffffu) | (v[i][1] << 16);
-                    const uint32_t hi = (v[i][2] & 0xffffu) | (v[i][3] << 16);
-                    *reinterpret_cast<uint2*>(stage + soff[i]) = make_uint2(lo, hi);
-                    pending &= ~(1u << i);
-                }
-            }
-            if (!pending) break;
-            if (spins >= kTinySpinLimit) {
-                timed_out = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    if (timed_out) __hip_atomic_store(sync_word(a.sync, kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // A unit of the single-launch down projection: kTinyCh<BITS> groups of one slot's a rows
 // (a slot holds at most 16 rows here: T <= 16) against the workgroup's 16 output rows.
 // Groups beyond the expert's last re-read its last group with scale 0.
@@ -729,6 +677,75 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
     }
 }
 
+// One wave gathers the a values its unit reads from the tag area ([rows_a, W] words): the
+// unit's groups of each of its rows (routed rows at their pair index, shared rows at
+// T * k + token), waiting for every 16-byte chunk until all four of its words carry `tag`,
+// and stages them in `stage` ([rows_a, Ws] bf16); then the sum of each (row, group) into
+// xs.  Units cover disjoint (row, group) ranges, so no other wave touches them.
+__device__ void tiny_collect_unit(const TinyArgs& a, const TinyRoute& r, const TinyUnit& t, uint32_t tag,
+                                  uint16_t* stage, int Ws, float* xs, int G) {
+    const int lane = threadIdx.x & 63;
+    const int W = (int)a.width_a;
+    const int cg = t.ngroups * (kGroup / 4);   // chunks of 4 values per row in the unit's groups
+    const int n_c = t.count * cg;
+    const __amdgpu_buffer_rsrc_t tr = make_rsrc(a.tags, a.tag_bytes);
+    auto row_of = [&](int m) { return t.shared ? t.pos0 + m : r.pair_at[t.pos0 + m]; };
+    bool timed_out = false;
+    for (int c0 = lane; c0 < n_c; c0 += kTinyPoll * 64) {
+        uint32_t off[kTinyPoll];
+        int soff[kTinyPoll];
+        uint32_t pending = 0;
+#pragma unroll
+        for (int i = 0; i < kTinyPoll; ++i) {
+            const int c = c0 + i * 64;
+            const int row = c < n_c ? row_of(c / cg) : 0;
+            const int col = t.g0 * kGroup + 4 * (c % cg);
+            off[i] = c < n_c ? (uint32_t)(row * W + col) * 4 : 0xfffffff0u;   // beyond the buffer: reads zeros
+            soff[i] = row * Ws + col;
+            if (c < n_c) pending |= 1u << i;
+        }
+        for (int spins = 0; pending; ++spins) {
+            u32x4_t v[kTinyPoll];
+#pragma unroll
+            for (int i = 0; i < kTinyPoll; ++i)
+                v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(tr, off[i], 0, kSc1));
+#pragma unroll
+            for (int i = 0; i < kTinyPoll; ++i) {
+                const uint32_t diff = (v[i][0] ^ tag) | (v[i][1] ^ tag) | (v[i][2] ^ tag) | (v[i][3] ^ tag);
+                if ((pending >> i & 1u) && diff < 0x10000u) {
+                    const uint32_t lo = (v[i][0] & 0xffffu) | (v[i][1] << 16);
+                    const uint32_t hi = (v[i][2] & 0xffffu) | (v[i][3] << 16);
+                    *reinterpret_cast<uint2*>(stage + soff[i]) = make_uint2(lo, hi);
+                    pending &= ~(1u << i);
+                }
+            }
+            if (!pending) break;
+            if (spins >= kTinySpinLimit) {
+                timed_out = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    if (timed_out) __hip_atomic_store(sync_word(a.sync, kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (row, group) sums: 16 lanes per pair, 8 values each (this wave's own LDS writes above
+    // are complete before its reads: one wave's LDS accesses stay in order)
+    const int n_pairs = t.count * t.ngroups;
+    for (int p = lane >> 4; p < n_pairs; p += 4) {
+        const int row = row_of(p / t.ngroups);
+        const int g = t.g0 + p % t.ngroups;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (int64_t)row * Ws + g * kGroup + (lane & 15) * 8);
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += bf16_to_f32(v[e] & 0xffffu) + bf16_to_f32(v[e] >> 16);
+        sum += __shfl_xor(sum, 8, 16);
+        sum += __shfl_xor(sum, 4, 16);
+        sum += __shfl_xor(sum, 2, 16);
+        sum += __shfl_xor(sum, 1, 16);
+        if ((lane & 15) == 0) xs[row * G + g] = sum;
+    }
+}
+
 template <int BITS, int SBITS>
 __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, uint32_t epoch_word) {
     __shared__ int s_last;
@@ -743,6 +760,7 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     float* xs = reinterpret_cast<float*>(zb + 512);                            // [rows_a][G] group sums
     for (int i = lane; i < T * 16; i += 64) yacc[i] = 0.f;
     if (threadIdx.x < 64) *reinterpret_cast<u32x4_t*>(zb + 8 * threadIdx.x) = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();   // the zero block is read by every wave
 
     // units: kTinyCh-group chunks of every active slot, then of the shared expert
     const int nch = (int)((a.routed.I / kGroup + kTinyCh<BITS> - 1) / kTinyCh<BITS>);
@@ -766,30 +784,11 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
         else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
     }
 
-    tiny_collect_a(a, r, (epoch_word + 1) << 16, stage, Ws);
-    __syncthreads();
-    {   // sum of every 128-column group of every row in use (16 lanes per row and group)
-        const int Gr = (int)(a.routed.I / kGroup), Gs = (int)(a.shared.I / kGroup);
-        const int n_rp = r.n_valid * Gr;
-        const int n_pairs = n_rp + (SBITS != 0 ? T * Gs : 0);
-        for (int p = (int)threadIdx.x >> 4; p < n_pairs; p += (int)blockDim.x >> 4) {
-            const int row = p < n_rp ? r.pair_at[p / Gr] : Tk + (p - n_rp) / Gs;
-            const int g = p < n_rp ? p % Gr : (p - n_rp) % Gs;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (int64_t)row * Ws + g * kGroup +
-                                                               (threadIdx.x & 15) * 8);
-            float sum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sum += bf16_to_f32(v[e] & 0xffffu) + bf16_to_f32(v[e] >> 16);
-            sum += __shfl_xor(sum, 8, 16);
-            sum += __shfl_xor(sum, 4, 16);
-            sum += __shfl_xor(sum, 2, 16);
-            sum += __shfl_xor(sum, 1, 16);
-            if ((threadIdx.x & 15) == 0) xs[row * G + g] = sum;
-        }
-    }
-    __syncthreads();
-
+    // each wave waits for the a values of its own units only, unit by unit, so a wave whose
+    // experts are done early computes while later ranks are still in flight
+    const uint32_t tag = (epoch_word + 1) << 16;
     while (u < n_units) {
+        tiny_collect_unit(a, r, cu, tag, stage, Ws, xs, G);
         if (cbits == BITS) tiny_unit<BITS>(cu, cc, stage, xs, Ws, G, zb, r, yacc);
         else if constexpr (SBITS != 0 && SBITS != BITS) tiny_unit<SBITS>(cu, cs, stage, xs, Ws, G, zb, r, yacc);
         u += V;
