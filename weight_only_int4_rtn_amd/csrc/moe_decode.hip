@@ -136,7 +136,7 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
             if (m < rows) static_cast<uint16_t*>(abuf)[idx] = (uint16_t)v;
         }
     }
-    __syncthreads();
+    if constexpr (!TAGGED) __syncthreads();   // s_red is reused by the caller's next tile (tagged: one tile)
 }
 
 }  // namespace
@@ -760,6 +760,10 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     float* xs = reinterpret_cast<float*>(zb + 512);                            // [rows_a][G] group sums
     for (int i = lane; i < T * 16; i += 64) yacc[i] = 0.f;
     if (threadIdx.x < 64) *reinterpret_cast<u32x4_t*>(zb + 8 * threadIdx.x) = u32x4_t{0u, 0u, 0u, 0u};
+    // the residual of this thread's output (T * 16 <= blockDim.x), loaded now, off the tail
+    float res_pre = 0.f;
+    if (a.residual && (int)threadIdx.x < T * 16)
+        res_pre = bf16_to_f32(a.residual[(int64_t)(threadIdx.x >> 4) * a.H + h0 + (threadIdx.x & 15)]);
     __syncthreads();   // the zero block is read by every wave
 
     // units: kTinyCh-group chunks of every active slot, then of the shared expert
@@ -804,18 +808,9 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kDkWaves; ++w) s += s_dyn[w * T * 16 + i];
-        const int t = i >> 4, n = i & 15;
-        const int64_t o = (int64_t)t * a.H + h0 + n;
-        const float res = a.residual ? bf16_to_f32(a.residual[o]) : 0.f;
-        a.y[o] = (uint16_t)cvt_bf16(s + res);
-    }
-
-    // exit count in groups of 16; the last down workgroup resets the counters and
-    // advances the epoch (clearing the tag area when it wraps)
+    // every wave is done with the tag area: count this workgroup's exit now, so that the
+    // atomic's round trip overlaps the sum below (groups of 16; the last workgroup resets
+    // the counters and advances the epoch, clearing the tag area when it wraps)
     const int ng = (n_dk + 15) >> 4;
     if (threadIdx.x == 0) {
         const int g = d >> 4, gsz = min(16, n_dk - (g << 4));
@@ -823,6 +818,13 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
                                         __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)gsz - 1 &&
                  __hip_atomic_fetch_add(sync_word(a.sync, kSyncTop), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      (uint32_t)ng - 1;
+    }
+    for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
+        float s = res_pre;
+#pragma unroll
+        for (int w = 0; w < kDkWaves; ++w) s += s_dyn[w * T * 16 + i];
+        const int t = i >> 4, n = i & 15;
+        a.y[(int64_t)t * a.H + h0 + n] = (uint16_t)cvt_bf16(s);
     }
     __syncthreads();
     if (s_last) {
