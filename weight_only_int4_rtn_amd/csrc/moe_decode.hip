@@ -648,15 +648,33 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
     const int srow = t.shared ? t.pos0 + ml : r.pair_at[t.pos0 + min(ml, t.count - 1)];
     const uint16_t* arow = stage + (int64_t)srow * Ws + 32 * q;
     const uint16_t* zl = zb + 8 * lane;
+    // two groups at a time: both groups' A fragments first, then their MFMA chains side by side
+    const uint32_t M = nibble_mask();
     f32x4_t d[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        const int g = t.g0 + min(j, t.ngroups - 1);
-        u32x4_t av[4];
+    for (int j0 = 0; j0 < CH; j0 += 2) {
+        u32x4_t av[2][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int g = t.g0 + min(j0 + jj, t.ngroups - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                av[jj][i] = *reinterpret_cast<const u32x4_t*>(real ? arow + g * kGroup + 8 * i : zl);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            av[i] = *reinterpret_cast<const u32x4_t*>(real ? arow + g * kGroup + 8 * i : zl);
-        d[j] = group_dot<BITS>(av, c.w[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = j0 + jj;
+                const f32x4_t c0 = i == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : d[j];
+                if constexpr (BITS == 4) {
+                    d[j] = mfma16(av[jj][i], dq4(c.w[j][0][i], M), c0);
+                } else {
+                    u32x4_t lo, hi;
+                    dq8(c.w[j][i >> 1][(2 * i) & 3], c.w[j][i >> 1][(2 * i + 1) & 3], lo, hi, M);
+                    d[j] = mfma16(av[jj][i], hi, mfma16(av[jj][i], lo, c0));
+                }
+            }
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
