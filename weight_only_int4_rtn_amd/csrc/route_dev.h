@@ -143,6 +143,99 @@ __device__ void wave_topk_from(const float (&raw)[NV], int E, int k, int* my_id,
     *my_w = lane < k ? mine / den : 0.f;
 }
 
+// NT tokens of one wave at once (E <= 256: four logits per lane and token): the same
+// rounds, tie rule and weights as wave_topk_from<4>, with the tokens' independent
+// reduction chains interleaved so that their latencies overlap.
+template <int NT>
+__device__ void wave_topk_multi(const float (&raw)[NT][4], int E, int k, int (&my_id)[NT], float (&my_w)[NT]) {
+    const int lane = threadIdx.x & 63;
+    float hv[NT][4];
+    int he[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            hv[t][i] = (e < E && !__builtin_isnan(raw[t][i])) ? raw[t][i] : -__builtin_inff();
+            he[t][i] = e < E ? e : 0x7fffffff;
+        }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 1; i < 4; ++i)   // stable insertion sort, larger value first
+#pragma unroll
+            for (int j = i; j > 0; --j) {
+                const bool sw = hv[t][j] > hv[t][j - 1];
+                const float tv = hv[t][j];
+                const int te = he[t][j];
+                hv[t][j] = sw ? hv[t][j - 1] : hv[t][j];
+                he[t][j] = sw ? he[t][j - 1] : he[t][j];
+                hv[t][j - 1] = sw ? tv : hv[t][j - 1];
+                he[t][j - 1] = sw ? te : he[t][j - 1];
+            }
+    float v0[NT], den[NT], mine[NT];
+    int id[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        v0[t] = 0.f;
+        den[t] = 0.f;
+        mine[t] = 0.f;
+        id[t] = -1;
+    }
+    for (int j = 0; j < k; ++j) {
+        float v[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = hv[t][0];
+        // the wave maxima, one DPP stage at a time over the tokens (as wave_max_f32)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0xb1, 0xf>(__float_as_int(v[t])));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x4e, 0xf>(__float_as_int(v[t])));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x141, 0xf>(__float_as_int(v[t])));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x140, 0xf>(__float_as_int(v[t])));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x142, 0xa>(__float_as_int(v[t])));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x143, 0xc>(__float_as_int(v[t])));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[t]), 63));
+            const bool at_max = hv[t][0] == m;
+            const uint64_t cand = __ballot(at_max);
+            int wl;
+            if (__popcll(cand) == 1) {
+                wl = (int)__ffsll((long long)cand) - 1;
+            } else {   // equal logits: the lowest expert index among the tied lanes
+                const int emin = wave_min_i32(at_max ? he[t][0] : 0x7fffffff);
+                wl = (int)__ffsll((long long)__ballot(at_max && he[t][0] == emin)) - 1;
+            }
+            const int widx = __builtin_amdgcn_readlane(he[t][0], wl);
+            const bool pop = lane == wl;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                hv[t][i] = pop ? hv[t][i + 1] : hv[t][i];
+                he[t][i] = pop ? he[t][i + 1] : he[t][i];
+            }
+            hv[t][3] = pop ? -__builtin_inff() : hv[t][3];
+            he[t][3] = pop ? 0x7fffffff : he[t][3];
+            if (j == 0) v0[t] = m;
+            const float ex = __expf(m - v0[t]);
+            den[t] += ex;
+            if (lane == j) {
+                id[t] = widx;
+                mine[t] = ex;
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        my_id[t] = lane < k ? id[t] : -1;
+        my_w[t] = lane < k ? mine[t] / den[t] : 0.f;
+    }
+}
+
 template <int NV>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int* my_id, float* my_w) {
     float raw[NV];

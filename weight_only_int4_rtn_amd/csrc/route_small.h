@@ -90,7 +90,19 @@ __device__ void route_small_wg(const RouteArgs& a, SmallRouteLds& s, bool writer
                 s.w[t * k + lane] = my_w;
             }
         };
-        if (E <= 256) {   // up to four tokens of this wave loaded before their top-k
+        if (E <= 256 && T <= 2 * nw) {   // at most two tokens per wave: their rounds interleaved
+            const int t0 = wave, t1 = wave + nw;
+            if (t0 < T) {
+                float raw[2][4];
+                wave_topk_load<4>(a.logits + (int64_t)t0 * E, E, raw[0]);
+                wave_topk_load<4>(a.logits + (int64_t)min(t1, T - 1) * E, E, raw[1]);
+                int my_id[2];
+                float my_w[2];
+                wave_topk_multi<2>(raw, E, k, my_id, my_w);
+                emit(t0, my_id[0], my_w[0]);
+                if (t1 < T) emit(t1, my_id[1], my_w[1]);
+            }
+        } else if (E <= 256) {   // up to four tokens of this wave loaded before their top-k, one after another
             for (int t0 = wave; t0 < T; t0 += 4 * nw) {
                 float raw[4][4];
 #pragma unroll
