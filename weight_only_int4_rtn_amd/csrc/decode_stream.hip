@@ -476,11 +476,12 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
 // Each finished row block is written unweighted in fp32 to its sorted rows of ystage;
 // dk_finalize_kernel applies the router weights and sums each token's rows in slot order.
 
+constexpr int kDWaves = 8;                         // waves per workgroup, one ring each
 constexpr int kDStages = 4;
 constexpr int kDCodeBytes = 4096;                  // 4 blocks of 64 lanes x 16 B
 constexpr int kDStageBytes = kDCodeBytes + 256;    // + scales (64 lanes x 4 B)
 constexpr int kDWaveBytes = kDStages * kDStageBytes;
-constexpr int kDLdsBytes = kSWaves * kDWaveBytes;
+constexpr int kDLdsBytes = kDWaves * kDWaveBytes;
 constexpr int kDMaxI = 512;
 constexpr int kDOps = 5;                           // copies per item
 constexpr uint32_t kDSkip = 0x40000000u;           // scalar offset that puts a copy past its buffer
@@ -602,7 +603,7 @@ __device__ __forceinline__ void d_compute(const DCursor& c, const uint8_t* stage
 }
 
 template <int BITS, int SBITS>
-__global__ __launch_bounds__(64 * kSWaves) void dk_stream_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDWaves) void dk_stream_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(64 * kSWaves) void dk_stream_kernel(DecodeArgs a) {
     // ranges are cut between row blocks, never inside one (8-bit codes take two items per
     // row block, summed in one wave's registers)
     const int U_r = n_tiles_r * n_hb, U = U_r + n_tiles_s * n_hb;
-    const int nw = gridDim.x * kSWaves, gw = blockIdx.x * kSWaves + wave;
+    const int nw = gridDim.x * kDWaves, gw = blockIdx.x * kDWaves + wave;
     const int N_items = U_r * kh_r + (U - U_r) * kh_s;
     const int u0 = s_unit_at(N_items, gw, nw, U_r, U, kh_r, max(kh_s, 1));
     const int u1 = s_unit_at(N_items, gw + 1, nw, U_r, U, kh_r, max(kh_s, 1));
@@ -755,7 +756,7 @@ hipError_t launch_dk_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t)
         attr_set = true;
     }
     launch(t, "dk_stream", dk_stream_kernel<BITS, SBITS>, dim3((unsigned)stream_workgroups()),
-           dim3(64 * kSWaves), s, (uint32_t)kDLdsBytes, a);
+           dim3(64 * kDWaves), s, (uint32_t)kDLdsBytes, a);
     const int64_t nb = (int64_t)a.T * ((a.H + kFinCols - 1) / kFinCols);
     if (a.k == 8) launch(t, "dk_finalize", dk_finalize_kernel<8>, dim3((unsigned)nb), dim3(256), s, 0u, a);
     else launch(t, "dk_finalize", dk_finalize_kernel<16>, dim3((unsigned)nb), dim3(256), s, 0u, a);
