@@ -523,15 +523,15 @@ __device__ __forceinline__ int tiny_pair_expert(const TinyArgs& a, int t, int j)
     if (E <= 256) {
         float raw[4];
         wave_topk_load<4>(row, E, raw);
-        wave_topk_from<4>(raw, E, j + 1, &id, &w);
+        wave_topk_from<4, false>(raw, E, j + 1, &id, &w);
     } else if (E <= 512) {
         float raw[8];
         wave_topk_load<8>(row, E, raw);
-        wave_topk_from<8>(raw, E, j + 1, &id, &w);
+        wave_topk_from<8, false>(raw, E, j + 1, &id, &w);
     } else {
         float raw[16];
         wave_topk_load<16>(row, E, raw);
-        wave_topk_from<16>(raw, E, j + 1, &id, &w);
+        wave_topk_from<16, false>(raw, E, j + 1, &id, &w);
     }
     return __builtin_amdgcn_readlane(id, j);
 }

@@ -60,7 +60,9 @@ __device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, in
     for (int i = 0; i < NV; ++i) raw[i] = row[min(lane + 64 * i, E - 1)];
 }
 
-template <int NV>   // logits per lane: E <= 64 * NV
+// WEIGHTS false: only the experts (my_w untouched), for callers that need just a rank's
+// winner; the rounds are the same.
+template <int NV, bool WEIGHTS = true>   // logits per lane: E <= 64 * NV
 __device__ void wave_topk_from(const float (&raw)[NV], int E, int k, int* my_id, float* my_w) {
     constexpr bool kSorted = NV <= 4;
     const int lane = threadIdx.x & 63;
@@ -131,16 +133,20 @@ __device__ void wave_topk_from(const float (&raw)[NV], int E, int k, int* my_id,
 #pragma unroll
             for (int i = 0; i < NV; ++i) hv[i] = (pop && lane + 64 * i == widx) ? -__builtin_inff() : hv[i];
         }
-        if (j == 0) v0 = m;
-        const float ex = __expf(m - v0);
-        den += ex;
-        if (lane == j) {
-            id = widx;
-            mine = ex;
+        if constexpr (WEIGHTS) {
+            if (j == 0) v0 = m;
+            const float ex = __expf(m - v0);
+            den += ex;
+            if (lane == j) {
+                id = widx;
+                mine = ex;
+            }
+        } else {
+            if (lane == j) id = widx;
         }
     }
     *my_id = lane < k ? id : -1;
-    *my_w = lane < k ? mine / den : 0.f;
+    if constexpr (WEIGHTS) *my_w = lane < k ? mine / den : 0.f;
 }
 
 // NT tokens of one wave at once (E <= 256: four logits per lane and token): the same
