@@ -442,26 +442,36 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         return p;
     };
     uint32_t cpar = row_parity(s_items[0]);
+    // An item's epilogue runs after the next step's wait and barrier, before that step's
+    // copies go out: its stores are then older than every copy batch still awaited, so
+    // the in-order vmcnt waits never hold a batch back behind them.
+    bool epi = false;
+    auto finish_item = [&]() {   // the item before ci (its record stays in LDS)
+        const Item eit = s_items[ci - 1];
+        if constexpr (GATE_UP) gk_epilogue(a, eit, acc, s_asum);
+        else dk_epilogue(a, eit, acc);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        epi = false;
+    };
     for (int s = 0; s < total_steps; ++s) {
         // step s's loads are this wave's oldest outstanding ones; at most the later steps'
         // (kLoadsPerStep each) may still be out
         if (issued - s - 1 >= 1) wait_vmcnt<P::kLoadsPerStep>();
         else wait_vmcnt<0>();
         bar();   // every wave's step-s data is in LDS, and stage (s - 1) is no longer read
+        if (epi) finish_item();
         if (issued < total_steps) issue_next();
         compute_step<BITS>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc);
         if (++gc == G) {
-            const Item cit = s_items[ci];
-            if constexpr (GATE_UP) gk_epilogue(a, cit, acc, s_asum);
-            else dk_epilogue(a, cit, acc);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[mi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            epi = true;
             gc = 0;
             if (++ci < n_items) cpar = row_parity(s_items[ci]);
         }
     }
+    if (epi) finish_item();
 }
 
 template <int BITS>
