@@ -183,6 +183,7 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
 
 
 KERNEL_SOURCES = {"tiny_decode": "moe_decode.hip", "gk_decode": "moe_decode.hip", "dk_decode": "moe_decode.hip",
+                  "gk_pair_stream": "decode_stream.hip",
                   "gk_stream": "decode_stream.hip", "dk_stream": "decode_stream.hip",
                   "gk_prefill": "moe_prefill.hip", "dk_prefill": "moe_prefill.hip"}
 KERNEL_HEADERS = ("common.h", "route_dev.h", "route_small.h", "dma.h", "decode_dev.h")

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # T, E, H, I, k, routed bits, shared bits
-    (3, 64, 2048, 512, 8, 4, 0),
+    (3, 32, 2048, 512, 8, 4, 0),
     (17, 32, 2048, 384, 4, 4, 0),
     (64, 8, 2048, 256, 4, 4, 0),
     (40, 16, 1280, 128, 2, 4, 0),

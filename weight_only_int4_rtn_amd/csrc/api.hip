@@ -222,9 +222,14 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.ystage = static_cast<float*>(at(L.ystage));
         d.rows_a = L.rows_a;
         d.route = r;
-        d.fused_route = stream_fits(d, (int)(std::min(a->E, a->T * a->top_k) + a->T * a->top_k / 16)) ? 1 : 0;
-        if (!d.fused_route)
-            if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
+        if (pair_fits(d)) {   // the gate/up kernel's workgroup 0 routes; a rows in pair order
+            d.a_by_pair = 1;
+            d.route.pair_rows = 1;
+        } else {
+            d.fused_route = stream_fits(d, (int)(std::min(a->E, a->T * a->top_k) + a->T * a->top_k / 16)) ? 1 : 0;
+            if (!d.fused_route)
+                if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
+        }
         d.residual = a->residual;
         d.y = a->y;
         return hip_status(launch_decode(d, s, timer), "decode launch");

@@ -179,11 +179,12 @@ struct WsLayout {
 };
 
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
+constexpr int kPairP = 64;       // T * k up to this may take the pair-mapped gate/up (pair < 2^kRecTokBits)
 // A small-path slot record carries its expert's first kRecTokens tokens (ascending,
 // kRecTokBits bits each) so gate/up can fetch activations without reading the row list.
 constexpr int kRecTokBits = 6;
 constexpr int kRecTokens = 5;
-static_assert(kSmallT <= (1 << kRecTokBits) && kRecTokens * kRecTokBits <= 31 && 16 * kRecTokBits <= 96,
+static_assert(kSmallT <= (1 << kRecTokBits) && kPairP <= (1 << kRecTokBits) && kRecTokens * kRecTokBits <= 31 && 16 * kRecTokBits <= 96,
               "record token packing");
 constexpr int kTinyP = 16;       // T * k up to this (and H <= kTinyMaxH) take the single-launch path
 constexpr int kTinyMaxH = 4096;
@@ -244,6 +245,7 @@ struct RouteArgs {
                           // count 0 marks a slot beyond the active experts
     int4* trec;           // small path: [max_slots + T*k/16][2] M-tiles of <= 16 rows: (expert,
                           // first sorted row, count, 0), (96 bits of tokens: m at bit 6m, 0)
+    int pair_rows;        // 1 (T*k <= kPairP): trec's 96 bits hold each row's pair t*k + j, not its token
     int max_slots;
     int64_t H;
     int nblk;
@@ -285,7 +287,8 @@ struct DecodeArgs {
     const uint16_t* residual;
     uint16_t* y;
     int fused_route;            // 1: the streaming gate/up kernel routes the batch itself
-    RouteArgs route;            // ... with these outputs (its workgroup 0 writes them)
+    int a_by_pair;              // 1: pair mode (pair_fits); routed a rows lie in pair order (row t*k + j)
+    RouteArgs route;            // ... with these outputs (workgroup 0 of either kernel writes them)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 // Workgroups of the streaming gate/up kernel (one per CU of the current device, 0 when
@@ -297,6 +300,10 @@ hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = 
 // The streaming down projection (intermediate sizes up to 512) and the kernel that sums
 // each token's rows in slot order; otherwise launch_decode splits experts over workgroups.
 bool dk_stream_fits(const DecodeArgs& a);
+// Pair mode of the streaming gate/up (T * k <= kPairP, at least twice as many experts as
+// pairs): its routed tiles are the pairs themselves, each workgroup finds the experts of
+// its own pairs with a top-k that stops at their ranks, and workgroup 0 routes the batch.
+bool pair_fits(const DecodeArgs& a);
 hipError_t launch_dk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 // Single-launch path for tiny batches (T * k <= kTinyP): every workgroup routes the batch

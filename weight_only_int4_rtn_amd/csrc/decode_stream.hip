@@ -313,7 +313,16 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     // workgroup 0 also writing it out), or read from the routing kernel's outputs
     SmallRouteLds& rl = *reinterpret_cast<SmallRouteLds*>(smem);
     static_assert(sizeof(SmallRouteLds) <= kSOffA, "routing scratch inside the stage ring");
-    if (a.fused_route) {
+    int wg = blockIdx.x, n_wg = gridDim.x;
+    if (a.a_by_pair) {   // workgroup 0 routes the batch for the down kernels; routed tiles are the pairs
+        if (blockIdx.x == 0) {
+            route_small_wg(a.route, rl, true);
+            return;
+        }
+        --wg;
+        --n_wg;
+        L.n_tiles_r = L.Tk;
+    } else if (a.fused_route) {
         route_small_wg(a.route, rl, blockIdx.x == 0);
         L.n_tiles_r = __builtin_amdgcn_readfirstlane(rl.n_tiles);
     } else {
@@ -324,8 +333,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     const int U_r = L.n_tiles_r * L.n_rb_r;
     const int U = U_r + (SBITS != 0 ? ((a.T + 15) / 16) * L.n_rb_s : 0);
     const int N_items = U_r * L.sub_r + (U - U_r) * L.sub_s;
-    const int u0 = s_unit_at(N_items, blockIdx.x, gridDim.x, U_r, U, L.sub_r, L.sub_s);
-    const int u1 = s_unit_at(N_items, blockIdx.x + 1, gridDim.x, U_r, U, L.sub_r, L.sub_s);
+    const int u0 = s_unit_at(N_items, wg, n_wg, U_r, U, L.sub_r, L.sub_s);
+    const int u1 = s_unit_at(N_items, wg + 1, n_wg, U_r, U, L.sub_r, L.sub_s);
     const int nI = (min(u1, U_r) - min(u0, U_r)) * L.sub_r + (max(u1, U_r) - max(u0, U_r)) * L.sub_s;
     if (nI <= 0) return;
 
@@ -334,7 +343,18 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     L.t_lo = u0 < U_r ? u0 / L.n_rb_r : L.n_tiles_r;
     const int t_hi = u0 < U_r ? (min(u1, U_r) - 1) / L.n_rb_r : L.n_tiles_r - 1;
     if (t_hi - L.t_lo + 1 > kSMaxTiles) return;   // excluded on the host (stream_fits)
-    if (a.fused_route) {
+    if (a.a_by_pair) {
+        // wave w finds the expert of pair t_lo + w (token p / k, rank p % k) with a top-k that
+        // stops at that rank; a dropped pair keeps its items (expert 0's rows, no row written)
+        static_assert(kSMaxTiles <= kSWaves + kSIssuers, "one wave per routed tile of a range");
+        if (wave <= t_hi - L.t_lo) {
+            const int p = L.t_lo + wave, t = p / a.k;
+            const int e = pair_expert(a.route.logits, a.route.ids, a.E, a.k, t, p - t * a.k);
+            if (lane < 8)
+                s_tiles[8 * wave + lane] = lane == 0 ? max(e, 0) : lane == 1 ? p : lane == 2 ? (e >= 0 ? 1 : 0)
+                                                                                 : lane == 4 ? t : 0;
+        }
+    } else if (a.fused_route) {
         if (tid < t_hi - L.t_lo + 1) {
             int4 r0, r1;
             small_tile_record(rl, a.E, L.t_lo + tid, r0, r1);
@@ -518,6 +538,12 @@ __device__ __forceinline__ void d_set_tile(const DecodeArgs& a, DCursor& c, int 
         c.tl.row0 = r.y;
         c.tl.count = r.z;
         c.tl.shared = 0;
+        if (a.a_by_pair) {   // the rows' pair indices (their a rows), 6 bits each
+            const int4 r1 = a.trec[2 * c.tile + 1];
+            c.tl.tk0 = __builtin_amdgcn_readfirstlane((uint32_t)r1.x);
+            c.tl.tk1 = __builtin_amdgcn_readfirstlane((uint32_t)r1.y);
+            c.tl.tk2 = __builtin_amdgcn_readfirstlane((uint32_t)r1.z);
+        }
     } else {
         const int ts = c.tile - n_tiles_r;
         c.tl.e = 0;
@@ -557,7 +583,9 @@ __device__ __forceinline__ void d_load_a(const DecodeArgs& a, const DCursor& c, 
                                          f32x4_t (&seed)[4]) {
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const bool real = ml < c.tl.count;
-    const uint16_t* row = a.abuf + (int64_t)(c.tl.row0 + (real ? ml : 0)) * a.width_a + 32 * q;
+    // a rows in sorted order, or (pair-mapped gate/up) routed rows at their pair index
+    const int r = !real ? c.tl.row0 : (a.a_by_pair && !c.tl.shared) ? stile_token(c.tl, ml) : c.tl.row0 + ml;
+    const uint16_t* row = a.abuf + (int64_t)r * a.width_a + 32 * q;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -774,8 +802,8 @@ hipError_t launch_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
         if (st != hipSuccess) return st;
         attr_set = true;
     }
-    launch(t, "gk_stream", gk_stream_kernel<BITS, SBITS>, dim3((unsigned)stream_workgroups()), dim3(kSThreads), s,
-           (uint32_t)kSLdsBytes, a);
+    launch(t, a.a_by_pair ? "gk_pair_stream" : "gk_stream", gk_stream_kernel<BITS, SBITS>,
+           dim3((unsigned)stream_workgroups()), dim3(kSThreads), s, (uint32_t)kSLdsBytes, a);
     return hipGetLastError();
 }
 
@@ -795,7 +823,7 @@ int stream_workgroups() {
 }
 
 bool stream_fits(const DecodeArgs& a, int max_tiles) {
-    const int nwg = stream_workgroups();
+    const int nwg = stream_workgroups() - (a.a_by_pair ? 1 : 0);   // pair mode: workgroup 0 only routes
     if (nwg <= 0 || a.H > kSMaxH || a.T > kSmallT) return false;
     const int64_t G = a.H / kGroup, KH = (G + 7) / 8;
     // the scale copies read 16 bytes from each row's first group of a K chunk: with an
@@ -823,6 +851,15 @@ hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     if (sb == 0) return launch_stream_t<8, 0>(a, s, t);
     if (sb == 4) return launch_stream_t<8, 4>(a, s, t);
     return launch_stream_t<8, 8>(a, s, t);
+}
+
+bool pair_fits(const DecodeArgs& a) {
+    const int64_t Tk = (int64_t)a.T * a.k;
+    // every pair reads its own expert's rows: only for batches whose pairs rarely share one
+    if (Tk > kPairP || 2 * Tk > a.E || a.E > kMaxE || a.k > kMaxK || !dk_stream_fits(a)) return false;
+    DecodeArgs p = a;
+    p.a_by_pair = 1;
+    return stream_fits(p, (int)Tk);
 }
 
 bool dk_stream_fits(const DecodeArgs& a) {

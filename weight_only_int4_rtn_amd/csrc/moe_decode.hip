@@ -510,32 +510,6 @@ __device__ void tiny_route(const TinyArgs& a, TinyRoute& r, bool writer) {
     }
 }
 
-// Expert of pair (token t, top-k rank j), the same in every lane.  From logits the wave
-// runs the top-k only up to round j (the rounds are those of the full routing, so the
-// winner is the same), which lets the workgroup of an early rank start loading its
-// weights before the whole batch is routed.
-__device__ __forceinline__ int tiny_pair_expert(const TinyArgs& a, int t, int j) {
-    const int E = a.E, k = a.k;
-    if (!a.logits) return checked_id(a.ids + t * k, j, E);
-    const float* row = a.logits + (int64_t)t * E;
-    int id;
-    float w;
-    if (E <= 256) {
-        float raw[4];
-        wave_topk_load<4>(row, E, raw);
-        wave_topk_from<4, false>(raw, E, j + 1, &id, &w);
-    } else if (E <= 512) {
-        float raw[8];
-        wave_topk_load<8>(row, E, raw);
-        wave_topk_from<8, false>(raw, E, j + 1, &id, &w);
-    } else {
-        float raw[16];
-        wave_topk_load<16>(row, E, raw);
-        wave_topk_from<16, false>(raw, E, j + 1, &id, &w);
-    }
-    return __builtin_amdgcn_readlane(id, j);
-}
-
 // Gate/up workgroup b: pair p = b / n_rb (token p / k, rank p % k) and its 16-row block
 // b % n_rb, writing row p of the tag area; or, after the pairs, a row block of the shared
 // expert for every token (rows T * k + t).
@@ -550,7 +524,7 @@ __device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
         const int64_t I_e = a.routed.I;
         if (n0 >= I_e) return;
         const int t = p / a.k;
-        const int e = tiny_pair_expert(a, t, p % a.k);
+        const int e = pair_expert(a.logits, a.ids, a.E, a.k, t, p % a.k);
         if (e < 0) return;   // dropped pair: the down workgroups skip its row
         const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
         gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
@@ -901,7 +875,7 @@ namespace {
 template <int BITS, int SBITS>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
-    if (a.fused_route) {   // stream_fits holds: routing runs inside the streaming gate/up kernel
+    if (a.a_by_pair || a.fused_route) {   // pair_fits or stream_fits holds: routing inside the streaming gate/up kernel
         if (hipError_t st = launch_gk_stream(a, s, t)) return st;
     } else {
         const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);

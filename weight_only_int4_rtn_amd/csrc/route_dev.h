@@ -15,170 +15,79 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 
 
-// Wave-wide maximum / minimum by DPP moves (quad permutes, row mirrors, then row
-// broadcasts of lanes 15 and 31): the full result lands in lane 63 and is read back as a
-// scalar, so every lane gets it without LDS.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_i32(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+// Logits are compared as ordered integer keys: signed comparison of two keys is the
+// float comparison of the logits, -0 and +0 get the same key (0) and so tie, and a NaN
+// logit takes the key of -inf, below every other value.  kKeyNone, below every logit's
+// key, marks a slot with no expert.
+constexpr int kKeyNone = (int)0x80000000;
+__device__ __forceinline__ int logit_key(float v) {
+    const int b = __float_as_int(__builtin_isnan(v) ? -__builtin_inff() : v + 0.0f);
+    return b >= 0 ? b : b ^ 0x7fffffff;
 }
-__device__ __forceinline__ float fdpp_max(float v, int o) { return fmaxf(v, __int_as_float(o)); }
+__device__ __forceinline__ float key_logit(int key) { return __int_as_float(key >= 0 ? key : key ^ 0x7fffffff); }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-    v = fdpp_max(v, dpp_i32<0xb1, 0xf>(__float_as_int(v)));    // quad_perm [1,0,3,2]
-    v = fdpp_max(v, dpp_i32<0x4e, 0xf>(__float_as_int(v)));    // quad_perm [2,3,0,1]
-    v = fdpp_max(v, dpp_i32<0x141, 0xf>(__float_as_int(v)));   // row_half_mirror
-    v = fdpp_max(v, dpp_i32<0x140, 0xf>(__float_as_int(v)));   // row_mirror: every row holds its max
-    v = fdpp_max(v, dpp_i32<0x142, 0xa>(__float_as_int(v)));   // row_bcast:15 into rows 1 and 3
-    v = fdpp_max(v, dpp_i32<0x143, 0xc>(__float_as_int(v)));   // row_bcast:31 into rows 2 and 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+// One DPP stage of a wave-wide reduction: lanes outside ROW_MASK's rows read IDENT, the
+// identity of the reduction, so the move folds into the max / min instruction itself.
+template <int CTRL, int ROW_MASK, int IDENT>
+__device__ __forceinline__ int dpp_in(int v) {
+    return __builtin_amdgcn_update_dpp(IDENT, v, CTRL, ROW_MASK, 0xf, false);
+}
+// Stage s of the wave-wide maximum / minimum (quad permutes, row mirrors, then row
+// broadcasts of lanes 15 and 31): after the sixth, lane 63 holds the result.
+template <int S, bool MAX>
+__device__ __forceinline__ int wave_stage(int v) {
+    constexpr int I = MAX ? (int)0x80000000 : 0x7fffffff;
+    constexpr int C = S == 0 ? 0xb1 : S == 1 ? 0x4e : S == 2 ? 0x141 : S == 3 ? 0x140 : S == 4 ? 0x142 : 0x143;
+    constexpr int R = S == 4 ? 0xa : S == 5 ? 0xc : 0xf;
+    const int o = dpp_in<C, R, I>(v);
+    return MAX ? max(v, o) : min(v, o);
 }
 __device__ __forceinline__ int wave_min_i32(int v) {
-    v = min(v, dpp_i32<0xb1, 0xf>(v));
-    v = min(v, dpp_i32<0x4e, 0xf>(v));
-    v = min(v, dpp_i32<0x141, 0xf>(v));
-    v = min(v, dpp_i32<0x140, 0xf>(v));
-    v = min(v, dpp_i32<0x142, 0xa>(v));
-    v = min(v, dpp_i32<0x143, 0xc>(v));
+    v = wave_stage<0, false>(v);
+    v = wave_stage<1, false>(v);
+    v = wave_stage<2, false>(v);
+    v = wave_stage<3, false>(v);
+    v = wave_stage<4, false>(v);
+    v = wave_stage<5, false>(v);
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-k of one token by one wave.  Lane l holds the logits of experts l, l + 64, ...
-// Each of the k rounds takes the wave-wide maximum of the lanes' best remaining logits;
-// when several lanes tie on it, the lowest expert index among them wins (a second,
-// rarely taken reduction).  The winner's lane removes it.  -0 and +0 compare equal, so
-// they tie; NaN logits rank below every other value.  With NV <= 4 logits per lane the
-// lane keeps them sorted (larger first, lower index first on equal values) so its best
-// is its first register; with more, the lane scans them each round.
-// Lane j < k returns slot j's expert and its softmax weight over the chosen logits.
-// This lane's logits of one token (experts lane, lane + 64, ...): unconditional (clamped)
-// loads, all in flight together.
-template <int NV>
-__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E, float (&raw)[NV]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) raw[i] = row[min(lane + 64 * i, E - 1)];
-}
-
-// WEIGHTS false: only the experts (my_w untouched), for callers that need just a rank's
-// winner; the rounds are the same.
-template <int NV, bool WEIGHTS = true>   // logits per lane: E <= 64 * NV
-__device__ void wave_topk_from(const float (&raw)[NV], int E, int k, int* my_id, float* my_w) {
+// Top-k of NT tokens by one wave, their rounds interleaved so that the latencies of the
+// tokens' reduction chains overlap.  Lane l holds the logits of experts l, l + 64, ... of
+// each token.  Each of the k rounds takes the wave-wide maximum of the lanes' best
+// remaining keys; when several lanes tie on it, the lowest expert index among them wins (a
+// second, rarely taken reduction).  The winner's lane removes it.  With NV <= 4 logits per
+// lane the lane keeps its keys sorted (larger first, lower expert first on equal keys, the
+// experts' positions packed 2 bits each) so its best is its first register; with more, the
+// lane scans them each round.  Lane j < k returns slot j's expert and, with WEIGHTS, its
+// softmax weight over the chosen logits.
+template <int NT, int NV, bool WEIGHTS>
+__device__ void wave_topk_core(const float (&raw)[NT][NV], int E, int k, int (&my_id)[NT], float (&my_w)[NT]) {
     constexpr bool kSorted = NV <= 4;
     const int lane = threadIdx.x & 63;
-    float hv[NV];
-    int he[kSorted ? NV : 1];
+    int hk[NT][NV];
+    uint32_t perm[NT];   // sorted: slot s holds the lane's logit i = (perm >> 2s) & 3
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        const float v = raw[i];
-        hv[i] = (e < E && !__builtin_isnan(v)) ? v : -__builtin_inff();
-        if constexpr (kSorted) he[i] = e < E ? e : 0x7fffffff;
-    }
-    if constexpr (kSorted) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int i = 1; i < NV; ++i)     // stable insertion sort, larger value first
-#pragma unroll
-            for (int j = i; j > 0; --j) {
-                const bool sw = hv[j] > hv[j - 1];
-                const float tv = hv[j];
-                const int te = he[j];
-                hv[j] = sw ? hv[j - 1] : hv[j];
-                he[j] = sw ? he[j - 1] : he[j];
-                hv[j - 1] = sw ? tv : hv[j - 1];
-                he[j - 1] = sw ? te : he[j - 1];
-            }
-    }
-    float v0 = 0.f, den = 0.f, mine = 0.f;
-    int id = -1;
-    for (int j = 0; j < k; ++j) {
-        float best;
-        int best_e;
-        if constexpr (kSorted) {
-            best = hv[0];
-            best_e = he[0];
-        } else {   // the lane's largest remaining value, lowest index first on ties
-            best = hv[0];
-            int bi = 0;
-#pragma unroll
-            for (int i = 1; i < NV; ++i) {
-                const bool gt = hv[i] > best;
-                best = gt ? hv[i] : best;
-                bi = gt ? i : bi;
-            }
-            const int e = lane + 64 * bi;
-            best_e = e < E ? e : 0x7fffffff;
-        }
-        const float m = wave_max_f32(best);
-        const bool at_max = best == m;
-        const uint64_t cand = __ballot(at_max);
-        int wl;
-        if (__popcll(cand) == 1) {
-            wl = (int)__ffsll((long long)cand) - 1;
-        } else {   // equal logits: the lowest expert index among the tied lanes
-            const int emin = wave_min_i32(at_max ? best_e : 0x7fffffff);
-            wl = (int)__ffsll((long long)__ballot(at_max && best_e == emin)) - 1;
-        }
-        const int widx = __builtin_amdgcn_readlane(best_e, wl);
-        const bool pop = lane == wl;
+        for (int i = 0; i < NV; ++i) hk[t][i] = lane + 64 * i < E ? logit_key(raw[t][i]) : kKeyNone;
+        perm[t] = 0xe4u;   // identity: 0, 1, 2, 3
         if constexpr (kSorted) {
 #pragma unroll
-            for (int i = 0; i + 1 < NV; ++i) {
-                hv[i] = pop ? hv[i + 1] : hv[i];
-                he[i] = pop ? he[i + 1] : he[i];
-            }
-            hv[NV - 1] = pop ? -__builtin_inff() : hv[NV - 1];
-            he[NV - 1] = pop ? 0x7fffffff : he[NV - 1];
-        } else {
+            for (int i = 1; i < NV; ++i)     // stable insertion sort, larger key first
 #pragma unroll
-            for (int i = 0; i < NV; ++i) hv[i] = (pop && lane + 64 * i == widx) ? -__builtin_inff() : hv[i];
-        }
-        if constexpr (WEIGHTS) {
-            if (j == 0) v0 = m;
-            const float ex = __expf(m - v0);
-            den += ex;
-            if (lane == j) {
-                id = widx;
-                mine = ex;
-            }
-        } else {
-            if (lane == j) id = widx;
+                for (int j = i; j > 0; --j) {
+                    const bool sw = hk[t][j] > hk[t][j - 1];
+                    const int tk = hk[t][j];
+                    hk[t][j] = sw ? hk[t][j - 1] : hk[t][j];
+                    hk[t][j - 1] = sw ? tk : hk[t][j - 1];
+                    // swap the 2-bit fields of slots j - 1 and j
+                    const uint32_t a = (perm[t] >> (2 * j - 2)) & 3u, b = (perm[t] >> (2 * j)) & 3u;
+                    const uint32_t swapped = (perm[t] & ~(0xfu << (2 * j - 2))) | (b << (2 * j - 2)) | (a << (2 * j));
+                    perm[t] = sw ? swapped : perm[t];
+                }
         }
     }
-    *my_id = lane < k ? id : -1;
-    if constexpr (WEIGHTS) *my_w = lane < k ? mine / den : 0.f;
-}
-
-// NT tokens of one wave at once (E <= 256: four logits per lane and token): the same
-// rounds, tie rule and weights as wave_topk_from<4>, with the tokens' independent
-// reduction chains interleaved so that their latencies overlap.
-template <int NT>
-__device__ void wave_topk_multi(const float (&raw)[NT][4], int E, int k, int (&my_id)[NT], float (&my_w)[NT]) {
-    const int lane = threadIdx.x & 63;
-    float hv[NT][4];
-    int he[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            hv[t][i] = (e < E && !__builtin_isnan(raw[t][i])) ? raw[t][i] : -__builtin_inff();
-            he[t][i] = e < E ? e : 0x7fffffff;
-        }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 1; i < 4; ++i)   // stable insertion sort, larger value first
-#pragma unroll
-            for (int j = i; j > 0; --j) {
-                const bool sw = hv[t][j] > hv[t][j - 1];
-                const float tv = hv[t][j];
-                const int te = he[t][j];
-                hv[t][j] = sw ? hv[t][j - 1] : hv[t][j];
-                he[t][j] = sw ? he[t][j - 1] : he[t][j];
-                hv[t][j - 1] = sw ? tv : hv[t][j - 1];
-                he[t][j - 1] = sw ? te : he[t][j - 1];
-            }
     float v0[NT], den[NT], mine[NT];
     int id[NT];
 #pragma unroll
@@ -189,57 +98,107 @@ __device__ void wave_topk_multi(const float (&raw)[NT][4], int E, int k, int (&m
         id[t] = -1;
     }
     for (int j = 0; j < k; ++j) {
-        float v[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = hv[t][0];
-        // the wave maxima, one DPP stage at a time over the tokens (as wave_max_f32)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0xb1, 0xf>(__float_as_int(v[t])));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x4e, 0xf>(__float_as_int(v[t])));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x141, 0xf>(__float_as_int(v[t])));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x140, 0xf>(__float_as_int(v[t])));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x142, 0xa>(__float_as_int(v[t])));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = fdpp_max(v[t], dpp_i32<0x143, 0xc>(__float_as_int(v[t])));
+        int best[NT], bi[NT], v[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[t]), 63));
-            const bool at_max = hv[t][0] == m;
+            if constexpr (kSorted) {
+                best[t] = hk[t][0];
+                bi[t] = (int)(perm[t] & 3u);
+            } else {   // the lane's largest remaining key, lowest position first on ties
+                best[t] = hk[t][0];
+                bi[t] = 0;
+#pragma unroll
+                for (int i = 1; i < NV; ++i) {
+                    const bool gt = hk[t][i] > best[t];
+                    best[t] = gt ? hk[t][i] : best[t];
+                    bi[t] = gt ? i : bi[t];
+                }
+            }
+            v[t] = best[t];
+        }
+        // the wave maxima, one DPP stage at a time over the tokens
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = wave_stage<0, true>(v[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = wave_stage<1, true>(v[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = wave_stage<2, true>(v[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = wave_stage<3, true>(v[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = wave_stage<4, true>(v[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = wave_stage<5, true>(v[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int m = __builtin_amdgcn_readlane(v[t], 63);
+            const bool at_max = best[t] == m;
+            const int be = best[t] == kKeyNone ? 0x7fffffff : lane + 64 * bi[t];
             const uint64_t cand = __ballot(at_max);
             int wl;
             if (__popcll(cand) == 1) {
                 wl = (int)__ffsll((long long)cand) - 1;
             } else {   // equal logits: the lowest expert index among the tied lanes
-                const int emin = wave_min_i32(at_max ? he[t][0] : 0x7fffffff);
-                wl = (int)__ffsll((long long)__ballot(at_max && he[t][0] == emin)) - 1;
+                const int emin = wave_min_i32(at_max ? be : 0x7fffffff);
+                wl = (int)__ffsll((long long)__ballot(at_max && be == emin)) - 1;
             }
-            const int widx = __builtin_amdgcn_readlane(he[t][0], wl);
+            const int widx = __builtin_amdgcn_readlane(be, wl);
             const bool pop = lane == wl;
+            if constexpr (kSorted) {
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                hv[t][i] = pop ? hv[t][i + 1] : hv[t][i];
-                he[t][i] = pop ? he[t][i + 1] : he[t][i];
+                for (int i = 0; i + 1 < NV; ++i) hk[t][i] = pop ? hk[t][i + 1] : hk[t][i];
+                hk[t][NV - 1] = pop ? kKeyNone : hk[t][NV - 1];
+                perm[t] = pop ? perm[t] >> 2 : perm[t];
+            } else {
+#pragma unroll
+                for (int i = 0; i < NV; ++i) hk[t][i] = (pop && i == bi[t]) ? kKeyNone : hk[t][i];
             }
-            hv[t][3] = pop ? -__builtin_inff() : hv[t][3];
-            he[t][3] = pop ? 0x7fffffff : he[t][3];
-            if (j == 0) v0[t] = m;
-            const float ex = __expf(m - v0[t]);
-            den[t] += ex;
-            if (lane == j) {
-                id[t] = widx;
-                mine[t] = ex;
+            if constexpr (WEIGHTS) {
+                const float mf = key_logit(m);
+                if (j == 0) v0[t] = mf;
+                const float ex = __expf(mf - v0[t]);
+                den[t] += ex;
+                if (lane == j) {
+                    id[t] = widx;
+                    mine[t] = ex;
+                }
+            } else {
+                if (lane == j) id[t] = widx;
             }
         }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         my_id[t] = lane < k ? id[t] : -1;
-        my_w[t] = lane < k ? mine[t] / den[t] : 0.f;
+        if constexpr (WEIGHTS) my_w[t] = lane < k ? mine[t] / den[t] : 0.f;
     }
+}
+
+// This lane's logits of one token (experts lane, lane + 64, ...): unconditional (clamped)
+// loads, all in flight together.
+template <int NV>
+__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E, float (&raw)[NV]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) raw[i] = row[min(lane + 64 * i, E - 1)];
+}
+
+// One token (WEIGHTS false: only the experts, my_w untouched, for callers that need just a
+// rank's winner; the rounds are the same).
+template <int NV, bool WEIGHTS = true>   // logits per lane: E <= 64 * NV
+__device__ __forceinline__ void wave_topk_from(const float (&raw)[NV], int E, int k, int* my_id, float* my_w) {
+    int id[1];
+    float w[1];
+    wave_topk_core<1, NV, WEIGHTS>(reinterpret_cast<const float(&)[1][NV]>(raw), E, k, id, w);
+    *my_id = id[0];
+    if constexpr (WEIGHTS) *my_w = w[0];
+}
+
+// NT tokens of one wave at once (E <= 256: four logits per lane and token).
+template <int NT>
+__device__ __forceinline__ void wave_topk_multi(const float (&raw)[NT][4], int E, int k, int (&my_id)[NT],
+                                                float (&my_w)[NT]) {
+    wave_topk_core<NT, 4, true>(raw, E, k, my_id, my_w);
 }
 
 template <int NV>
@@ -263,6 +222,31 @@ __device__ __forceinline__ int checked_id(const int32_t* tok_ids, int j, int E) 
     for (int jj = 0; jj < j; ++jj)
         if (tok_ids[jj] == e) return -1;
     return e;
+}
+
+// Expert of pair (token t, top-k rank j), the same in every lane (-1: dropped).  From
+// logits the wave runs the top-k only up to round j (the rounds are those of the full
+// routing, so the winner is the same), which lets a workgroup that serves one pair start
+// loading its weights before the whole batch is routed.
+__device__ __forceinline__ int pair_expert(const float* logits, const int32_t* ids, int E, int k, int t, int j) {
+    if (!logits) return checked_id(ids + t * k, j, E);
+    const float* row = logits + (int64_t)t * E;
+    int id;
+    float w;
+    if (E <= 256) {
+        float raw[4];
+        wave_topk_load<4>(row, E, raw);
+        wave_topk_from<4, false>(raw, E, j + 1, &id, &w);
+    } else if (E <= 512) {
+        float raw[8];
+        wave_topk_load<8>(row, E, raw);
+        wave_topk_from<8, false>(raw, E, j + 1, &id, &w);
+    } else {
+        float raw[16];
+        wave_topk_load<16>(row, E, raw);
+        wave_topk_from<16, false>(raw, E, j + 1, &id, &w);
+    }
+    return __builtin_amdgcn_readlane(id, j);
 }
 
 }  // namespace

@@ -52,7 +52,9 @@ struct SmallRouteLds {
 };
 
 // Record of routed M-tile t (two int4, see RouteArgs::trec) from the workgroup's routing.
-__device__ __forceinline__ void small_tile_record(const SmallRouteLds& s, int E, int t, int4& r0, int4& r1) {
+// pair_k > 0: each row's pair index t * pair_k + j in place of its token t.
+__device__ __forceinline__ void small_tile_record(const SmallRouteLds& s, int E, int t, int4& r0, int4& r1,
+                                                  int pair_k = 0) {
     int lo = 0, hi = E - 1;   // the last expert whose first tile is <= t owns tile t
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -65,7 +67,13 @@ __device__ __forceinline__ void small_tile_record(const SmallRouteLds& s, int E,
     for (int i = 0; i < 16 * j; ++i) m &= m - 1;
     unsigned __int128 toks = 0;
     for (int i = 0; i < cnt; ++i) {
-        toks |= (unsigned __int128)__builtin_ctzll(m) << (kRecTokBits * i);
+        int v = __builtin_ctzll(m);
+        if (pair_k > 0) {   // the token's rank of expert e (ids are distinct within a token)
+            int j = 0;
+            while (j < pair_k - 1 && s.ids[v * pair_k + j] != e) ++j;
+            v = v * pair_k + j;
+        }
+        toks |= (unsigned __int128)v << (kRecTokBits * i);
         m &= m - 1;
     }
     r0 = int4{e, s.off[e] + 16 * j, cnt, 0};
@@ -205,7 +213,7 @@ __device__ void route_small_wg(const RouteArgs& a, SmallRouteLds& s, bool writer
     for (int sl = s.n_active + tid; sl < a.max_slots; sl += blockDim.x) a.rec[sl] = int4{0, 0, 0, 0};
     for (int t = tid; t < s.n_tiles; t += blockDim.x) {   // M-tiles in slot order, with all their tokens
         int4 r0, r1;
-        small_tile_record(s, E, t, r0, r1);
+        small_tile_record(s, E, t, r0, r1, a.pair_rows ? k : 0);
         a.trec[2 * t] = r0;
         a.trec[2 * t + 1] = r1;
     }
