@@ -577,10 +577,9 @@ __device__ __forceinline__ void d_issue(const DecodeArgs& a, const DCursor& c, u
          __builtin_amdgcn_readfirstlane(h0 * c.G2 * 2));
 }
 
-// The tile's a rows as MFMA A fragments (groups 0..3, padding rows zero) and their seeds.
-template <int BITS>
-__device__ __forceinline__ void d_load_a(const DecodeArgs& a, const DCursor& c, u32x4_t (&A)[4][4],
-                                         f32x4_t (&seed)[4]) {
+// The tile's a rows as MFMA A fragments (groups 0..3, padding rows zero); d_seed gives
+// their seeds once they have landed.
+__device__ __forceinline__ void d_load_a(const DecodeArgs& a, const DCursor& c, u32x4_t (&A)[4][4]) {
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const bool real = ml < c.tl.count;
     // a rows in sorted order, or (pair-mapped gate/up) routed rows at their pair index
@@ -593,6 +592,9 @@ __device__ __forceinline__ void d_load_a(const DecodeArgs& a, const DCursor& c, 
             const int gg = min(g, c.G2 - 1);
             A[g][i] = load16_or_zero(row + gg * kGroup + 8 * i, real && g < c.G2, row);
         }
+}
+template <int BITS>
+__device__ __forceinline__ void d_seed(const u32x4_t (&A)[4][4], f32x4_t (&seed)[4]) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) seed[g] = offset_seed<BITS>(A[g]);
 }
@@ -673,13 +675,16 @@ __global__ __launch_bounds__(64 * kDWaves) void dk_stream_kernel(DecodeArgs a) {
 
     const uint32_t ring = lds_offset(smem) + wave * kDWaveBytes;
     const uint8_t* ring_p = smem + wave * kDWaveBytes;
+    // the first tile's a rows go out before the ring's copies: the wait for the first item
+    // then covers them (a later tile's rows are loaded when the tile starts)
+    u32x4_t A[4][4];
+    f32x4_t seed[4];
+    d_load_a(a, cc, A);
     for (int rel = 0; rel < kDStages - 1 && rel < nI; ++rel) {
         d_issue(a, ic, ring + rel * kDStageBytes);
         advance(ic);
     }
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.ystage, (uint32_t)((int64_t)a.rows_a * a.H * 4));
-    u32x4_t A[4][4];
-    f32x4_t seed[4];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     bool c_start = true;
     int st_hist = 0;   // store instructions of the last three items, 3 bits each
@@ -696,8 +701,9 @@ __global__ __launch_bounds__(64 * kDWaves) void dk_stream_kernel(DecodeArgs a) {
             advance(ic);
         }
         if (c_start) {
-            if (cc.bits == BITS) d_load_a<BITS>(a, cc, A, seed);
-            else if constexpr (SBITS != 0 && SBITS != BITS) d_load_a<SBITS>(a, cc, A, seed);
+            if (rel > 0) d_load_a(a, cc, A);
+            if (cc.bits == BITS) d_seed<BITS>(A, seed);
+            else if constexpr (SBITS != 0 && SBITS != BITS) d_seed<SBITS>(A, seed);
         }
         const uint8_t* stage = ring_p + (rel % kDStages) * kDStageBytes;
         if (cc.bits == BITS) d_compute<BITS>(cc, stage, A, seed, acc);
@@ -832,13 +838,16 @@ bool stream_fits(const DecodeArgs& a, int max_tiles) {
     // a 4-bit row block must span two K chunks: its partial sums are read back one item
     // after they are written and rewritten no sooner than two items later
     if (KH < 2 && (a.routed.bits == 4 || a.shared.bits == 4)) return false;
-    const int64_t ipt_r = (a.routed.I / 16) * (a.routed.bits == 4 ? KH : 2 * KH);
-    const int64_t ipt_s = a.shared.bits ? (a.shared.I / 16) * (a.shared.bits == 4 ? KH : 2 * KH) : 0;
     const int64_t n_rb_r = a.routed.I / 16;
-    const int64_t u_max = max_tiles * n_rb_r + (a.shared.bits ? ((a.T + 15) / 16) * (a.shared.I / 16) : 0);
-    const int64_t range = (u_max + nwg - 1) / nwg + 1;   // row blocks per workgroup, at most
-    // routed tiles a range can touch, whatever the device-side tile count
-    return (ipt_r > 0 && ipt_s >= 0) && (range + n_rb_r - 1) / n_rb_r + 1 <= kSMaxTiles;
+    if (n_rb_r <= 0) return false;
+    const int U_s = a.shared.bits ? (int)(((a.T + 15) / 16) * (a.shared.I / 16)) : 0;
+    // routed units of a range at most: a cut by items, each end rounded up to a unit,
+    // whatever the device-side tile count
+    const int64_t sub_r = a.routed.bits == 4 ? KH : 2 * KH, sub_s = a.shared.bits == 4 ? KH : 2 * KH;
+    const int64_t N = max_tiles * n_rb_r * sub_r + U_s * sub_s;
+    const int64_t cap_r = ((N + nwg - 1) / nwg + 2 * sub_r) / sub_r;
+    // routed tiles a range can touch
+    return (cap_r + n_rb_r - 1) / n_rb_r + 1 <= kSMaxTiles;
 }
 
 hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
