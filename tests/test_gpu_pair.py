@@ -98,3 +98,39 @@ def test_pair_given_ids_with_dropped_pairs():
     w_ok = np.where(keep, w, 0.0).astype(np.float32)
     y_ref = oracle.moe_ffn(x, ids_ok, w_ok, *ref.as_args(), 4)
     check_ffn(y, y_ref, "pair given ids")
+
+
+def _tied_logits(seed, T, E):
+    """Router logits whose top ranks are full of exact ties: the 12 largest of each token
+    take only three distinct values, one token's top values are +0 and -0 among negatives,
+    and some logits are -inf."""
+    logits = synth.router_logits(seed, T, E)
+    for t in range(T):
+        top = np.argsort(-logits[t], kind="stable")[:12]
+        logits[t, top] = np.array([3.0, 3.0, 3.0, 2.5, 2.5, 2.5, 2.5, 2.5, 1.0, 1.0, 1.0, 1.0],
+                                  dtype=np.float32)[np.arange(12) % 12]
+    t = T - 1
+    logits[t] = -np.abs(logits[t]) - 1.0
+    logits[t, [5, 9, 40, 41, 200]] = np.array([0.0, -0.0, 0.0, -0.0, -0.0], dtype=np.float32)
+    logits[t, [1, 2]] = -np.inf
+    return logits
+
+
+@pytest.mark.parametrize("T,path", [(1, "tiny_decode"), (2, "tiny_decode"), (4, "gk_pair_stream")])
+def test_rank_expert_with_ties(T, path):
+    """Each gate/up workgroup runs its pair's top-k only up to the pair's rank; with exact
+    ties, signed zeros and -inf among the top ranks the experts it finds (and so y) must
+    still be those of the oracle's order (larger logit first, lower index first)."""
+    E, H, I, k = 256, 2048, 512, 8
+    say(f"rank ties T={T}")
+    routed = gpu_layer(81, 0, E, H, I, 4)
+    ref = OracleExperts(81, 0, H, I, 4)
+    x = synth.activations_bf16(810 + T, T, H)
+    logits = _tied_logits(820 + T, T, E)
+    (y, r), timings = w4.moe_w4a16_forward_timed(bf16_to_dev(x), *routed, top_k=k,
+                                                 router_logits=f32_to_dev(logits), routing_out=True)
+    assert path in _names(timings), timings
+    ids, w, _, _, _ = oracle.route(logits, k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    y_ref, _ = oracle.moe_layer(x, logits, k, *ref.as_args(), 4)
+    check_ffn(y, y_ref, f"rank ties T={T}")
