@@ -224,9 +224,18 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
         d.route = r;
         if (pair_fits(d)) {   // the gate/up kernel's workgroup 0 routes; a rows in pair order
             d.a_by_pair = 1;
+            d.gk_stream = 1;
             d.route.pair_rows = 1;
+        } else if (a->router_logits && a->T > kSplitRouteT) {
+            // routing spread over waves (one token each) in its own launch; the streaming
+            // gate/up kernel, if it takes the shapes, then reads the tile records
+            r.sync = static_cast<uint32_t*>(at(L.sync));
+            d.route = r;
+            d.gk_stream = stream_fits(d, (int)(std::min(a->E, a->T * a->top_k) + a->T * a->top_k / 16)) ? 1 : 0;
+            if (int st = hip_status(launch_route_split(r, s, timer), "routing launch")) return st;
         } else {
             d.fused_route = stream_fits(d, (int)(std::min(a->E, a->T * a->top_k) + a->T * a->top_k / 16)) ? 1 : 0;
+            d.gk_stream = d.fused_route;
             if (!d.fused_route)
                 if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
         }

@@ -159,13 +159,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g * __built
 // calls.  It must be zero before a workspace's first use (moe_w4a16_workspace_init).
 // kSyncBytes of counters, one per 128-byte line (index * 32 words): [80, 96) exit counts
 // of down-workgroup groups and 100 their total (zero between calls), 101 a sticky error
-// word (a wait that timed out), 102 the epoch word (epoch - 1 of the next call).  Then
+// word (a wait that timed out), 102 the epoch word (epoch - 1 of the next call), 103 the
+// arrivals of the split routing kernel's workgroups (zero between calls).  Then
 // kTagBytes of tagged a words (bf16 value | epoch << 16), rows of width max(I, shared I).
 constexpr size_t kSyncBytes = 16384;
 constexpr size_t kTagBytes = 131072;
 constexpr size_t kHeadBytes = kSyncBytes + kTagBytes;
 static_assert(kHeadBytes == W4A16_WORKSPACE_HEAD_BYTES, "workspace head size");
-constexpr int kSyncGroup = 80, kSyncTop = 100, kSyncError = 101, kSyncEpoch = 102;
+constexpr int kSyncGroup = 80, kSyncTop = 100, kSyncError = 101, kSyncEpoch = 102, kSyncRoute = 103;
 __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return sync + i * 32; }
 
 struct WsLayout {
@@ -179,6 +180,7 @@ struct WsLayout {
 };
 
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
+constexpr int kSplitRouteT = 16;  // above this many tokens (from logits, not pair mode) routing takes its own launch
 constexpr int kPairP = 64;       // T * k up to this may take the pair-mapped gate/up (pair < 2^kRecTokBits)
 // A small-path slot record carries its expert's first kRecTokens tokens (ascending,
 // kRecTokBits bits each) so gate/up can fetch activations without reading the row list.
@@ -246,12 +248,15 @@ struct RouteArgs {
     int4* trec;           // small path: [max_slots + T*k/16][2] M-tiles of <= 16 rows: (expert,
                           // first sorted row, count, 0), (96 bits of tokens: m at bit 6m, 0)
     int pair_rows;        // 1 (T*k <= kPairP): trec's 96 bits hold each row's pair t*k + j, not its token
+    uint32_t* sync;       // workspace head counters (route_split_kernel's arrivals)
     int max_slots;
     int64_t H;
     int nblk;
     int64_t max_tiles;
 };
 hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
+// Small batch from logits over ceil(T / 8) workgroups, one token per wave (see route.hip).
+hipError_t launch_route_split(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 struct ExpertSet {       // one family of experts sharing a code width
@@ -286,6 +291,7 @@ struct DecodeArgs {
     int64_t rows_a;             // rows of abuf and ystage: T * k routed, then T shared
     const uint16_t* residual;
     uint16_t* y;
+    int gk_stream;              // 1: gate/up by the streaming kernel (stream_fits), else one workgroup per tile
     int fused_route;            // 1: the streaming gate/up kernel routes the batch itself
     int a_by_pair;              // 1: pair mode (pair_fits); routed a rows lie in pair order (row t*k + j)
     RouteArgs route;            // ... with these outputs (workgroup 0 of either kernel writes them)

@@ -875,7 +875,7 @@ namespace {
 template <int BITS, int SBITS>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
-    if (a.a_by_pair || a.fused_route) {   // pair_fits or stream_fits holds: routing inside the streaming gate/up kernel
+    if (a.gk_stream) {   // stream_fits (or pair_fits) holds
         if (hipError_t st = launch_gk_stream(a, s, t)) return st;
     } else {
         const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);

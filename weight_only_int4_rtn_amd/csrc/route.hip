@@ -10,7 +10,9 @@
 // computed with per-expert token bitmasks (a token picks an expert at most once), never
 // from the order in which atomics land.
 //
-// Small batches (T <= 64): one 1024-thread workgroup does everything in one launch.
+// Small batches (T <= 64): one 1024-thread workgroup does everything in one launch; or,
+// from logits, route_split_kernel: one token per wave over ceil(T / 8) workgroups, and the
+// last workgroup to arrive finishes the routing of the whole batch.
 // Large batches: route_block_kernel (top-k, block histogram, in-block ranks, activation
 // group sums) -> route_scan_kernel (offsets, active experts, GEMM tile list) ->
 // route_scatter_kernel (sorted pair list).
@@ -25,6 +27,44 @@ namespace w4a16 {
 __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
     __shared__ SmallRouteLds lds;
     route_small_wg(a, lds, true);
+}
+
+// Wave w of workgroup b runs the top-k of token 8 b + w and writes its experts and weights
+// through to memory; the workgroup then counts its arrival (the atomic releases its
+// writes), and the last one to arrive reads every pair back past the caches, resets the
+// counter for the next call and finishes the routing alone.  A wave's top-k is a chain of
+// dependent reductions (about 2 us for k = 8), so spreading the tokens over waves instead
+// of queueing several per wave shortens the launch by the difference.
+constexpr int kSplitWaves = 8;
+__global__ __launch_bounds__(64 * kSplitWaves) void route_split_kernel(RouteArgs a) {
+    __shared__ SmallRouteLds lds;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, k = a.k, P = a.T * k;
+    const int t = blockIdx.x * kSplitWaves + wave;
+    const __amdgpu_buffer_rsrc_t ir = make_rsrc(a.ids, (uint32_t)(P * 4));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wts, (uint32_t)(P * 4));
+    if (t < a.T) {
+        int my_id;
+        float my_w;
+        wave_topk_any(a.logits + (int64_t)t * E, E, k, &my_id, &my_w);
+        if (lane < k) {
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)my_id, ir, (uint32_t)((t * k + lane) * 4), 0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_w), wr, (uint32_t)((t * k + lane) * 4), 0, kSc1);
+        }
+    }
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(sync_word(a.sync, kSyncRoute), 1u, __ATOMIC_ACQ_REL,
+                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) __hip_atomic_store(sync_word(a.sync, kSyncRoute), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int p = tid; p < P; p += blockDim.x) {
+        lds.ids[p] = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, (uint32_t)(p * 4), 0, kSc1);
+        lds.w[p] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wr, (uint32_t)(p * 4), 0, kSc1));
+    }
+    route_small_finish(a, lds, true);
 }
 
 // ------------------------------------------------------------------ large batch
@@ -191,6 +231,12 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
 
 hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t) {
     launch(t, "route_small", route_small_kernel, dim3(1), dim3(1024), s, 0u, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_split(const RouteArgs& a, hipStream_t s, StageTimer* t) {
+    launch(t, "route_split", route_split_kernel, dim3((unsigned)((a.T + kSplitWaves - 1) / kSplitWaves)),
+           dim3(64 * kSplitWaves), s, 0u, a);
     return hipGetLastError();
 }
 

@@ -80,12 +80,13 @@ __device__ __forceinline__ void small_tile_record(const SmallRouteLds& s, int E,
     r1 = int4{(int)(uint32_t)toks, (int)(uint32_t)(toks >> 32), (int)(uint32_t)(toks >> 64), 0};
 }
 
+__device__ void route_small_finish(const RouteArgs& a, SmallRouteLds& s, bool writer);
+
 // Routes the batch into `s` (all threads of the workgroup take part; E <= 2 * blockDim.x).
 // `writer`: also stores every routing output of RouteArgs.
 __device__ void route_small_wg(const RouteArgs& a, SmallRouteLds& s, bool writer) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int T = a.T, E = a.E, k = a.k, P = T * k;
-    for (int e = tid; e < E; e += blockDim.x) { s.cnt[e] = 0; s.mlo[e] = 0; s.mhi[e] = 0; }
 
     if (a.logits) {
         auto emit = [&](int t, int my_id, float my_w) {
@@ -141,6 +142,16 @@ __device__ void route_small_wg(const RouteArgs& a, SmallRouteLds& s, bool writer
             s.w[p] = a.wts[p];
         }
     }
+    route_small_finish(a, s, writer);
+}
+
+// The rest of the routing once s.ids and s.w hold every pair (the workgroup's own writes
+// to them need no barrier before the call): counts, offsets, tiles, and with `writer` every
+// output of RouteArgs but ids and wts.
+__device__ void route_small_finish(const RouteArgs& a, SmallRouteLds& s, bool writer) {
+    const int tid = threadIdx.x;
+    const int T = a.T, E = a.E, k = a.k, P = T * k;
+    for (int e = tid; e < E; e += blockDim.x) { s.cnt[e] = 0; s.mlo[e] = 0; s.mhi[e] = 0; }
     __syncthreads();
 
     for (int p = tid; p < P; p += blockDim.x) {
