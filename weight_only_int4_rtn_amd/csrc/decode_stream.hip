@@ -220,7 +220,9 @@ __device__ __forceinline__ int s_issue(const DecodeArgs& a, const SLayout& L, co
 }
 
 // This wave's activation fragments of K groups w and w + 8 for the tile's 16 rows
-// (padding rows zero), and their MFMA offset seeds.
+// (padding rows zero), and their MFMA offset seeds.  Each branch computes the seeds
+// itself: the register path's loads are then complete before the branches join, so the
+// compiler puts no wait for them (a wait for every copy in flight) on the LDS path.
 template <int BITS>
 __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, const STile& tl, const uint8_t* smem,
                                          const uint8_t* abuf, u32x4_t (&A)[kSKH][4], f32x4_t (&seed)[kSKH]) {
@@ -239,6 +241,8 @@ __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, 
                 A[kh][i] = perm_act(*reinterpret_cast<const u32x4_t*>(p));
             }
         }
+#pragma unroll
+        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<BITS>(A[kh]);
     } else {   // more rows than an A buffer holds: straight from memory into registers
         const uint16_t* xr = a.x + (int64_t)stile_token(tl, real ? ml : 0) * a.H + 32 * q;
 #pragma unroll
@@ -247,9 +251,9 @@ __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) A[kh][i] = load_act<BITS>(xr, real && 8 * kh + wave < L.G, g * kGroup + 8 * i);
         }
-    }
 #pragma unroll
-    for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<BITS>(A[kh]);
+        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<BITS>(A[kh]);
+    }
 }
 
 // One item's MFMAs for this wave: K group 8 * kh + wave of the item's rows.

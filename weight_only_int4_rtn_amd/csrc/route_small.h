@@ -205,6 +205,28 @@ __device__ void route_small_finish(const RouteArgs& a, SmallRouteLds& s, bool wr
                     }
                     a.active[act] = e;
                     a.rec[act] = int4{e, off, c, toks};
+                    // the expert's M-tiles (tiles t0, t0 + 1, ...): every row's token (or
+                    // pair), kRecTokBits bits each, in three words per tile
+                    m = (uint64_t)s.mhi[e] << 32 | s.mlo[e];
+                    for (int j0 = 0; j0 < c; j0 += 16) {
+                        const int cnt = min(16, c - j0);
+                        uint32_t w[3] = {0u, 0u, 0u};
+                        for (int i = 0; i < cnt; ++i) {
+                            int v = __builtin_ctzll(m);
+                            m &= m - 1;
+                            if (a.pair_rows) {   // the token's rank of expert e (ids are distinct within a token)
+                                int jj = 0;
+                                while (jj < k - 1 && s.ids[v * k + jj] != e) ++jj;
+                                v = v * k + jj;
+                            }
+                            const int b = kRecTokBits * i;
+                            w[b >> 5] |= (uint32_t)v << (b & 31);
+                            if ((b & 31) + kRecTokBits > 32) w[(b >> 5) + 1] |= (uint32_t)v >> (32 - (b & 31));
+                        }
+                        const int tile = t0 + j0 / 16;
+                        a.trec[2 * tile] = int4{e, off + j0, cnt, 0};
+                        a.trec[2 * tile + 1] = int4{(int)w[0], (int)w[1], (int)w[2], 0};
+                    }
                 }
             }
             packed += mine[j];
@@ -222,12 +244,6 @@ __device__ void route_small_finish(const RouteArgs& a, SmallRouteLds& s, bool wr
     __syncthreads();
     if (!writer) return;
     for (int sl = s.n_active + tid; sl < a.max_slots; sl += blockDim.x) a.rec[sl] = int4{0, 0, 0, 0};
-    for (int t = tid; t < s.n_tiles; t += blockDim.x) {   // M-tiles in slot order, with all their tokens
-        int4 r0, r1;
-        small_tile_record(s, E, t, r0, r1, a.pair_rows ? k : 0);
-        a.trec[2 * t] = r0;
-        a.trec[2 * t + 1] = r1;
-    }
     for (int p = tid; p < P; p += blockDim.x) {
         const int e = s.ids[p];
         if (e >= 0) {
