@@ -193,9 +193,23 @@ __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const Expert
     }
 }
 
+// The tokens of a routed gate/up item's MT rows (the token half of tokw), copied into an
+// LDS buffer by wave 0 one item ahead: two direct copies of 64 words.  A load the compiler
+// sees would make it wait, where the tokens are used, for every copy in flight.
+__device__ __forceinline__ void copy_item_tokens(const PrefillArgs& a, const Item& it, uint32_t lds_buf) {
+    const int lane = threadIdx.x & 63;
+    const i32x4_t tr = uniform_rsrc(dma_rsrc(a.tokw, (uint32_t)((int64_t)a.T * a.k * 8)));
+#pragma unroll
+    for (int h = 0; h < MT / 64; ++h) {
+        const int row = it.row0 + 64 * h + lane;
+        dma4(tr, __builtin_amdgcn_readfirstlane(lds_buf + 256 * h),
+             it.e >= 0 && 64 * h + lane < it.count ? (uint32_t)(row * 8) : kOob, 0);
+    }
+}
+
 // The tokens of the rows a lane's A and row-sum loads read for a gate/up item (padding
-// rows repeat the last real row).
-__device__ __forceinline__ void item_tokens(const PrefillArgs& a, const Item& it, int (&tok)[5]) {
+// rows repeat the last real row), from the item's token buffer.
+__device__ __forceinline__ void item_tokens(const Item& it, const int* s_tok, int (&tok)[5]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
@@ -207,7 +221,7 @@ __device__ __forceinline__ void item_tokens(const PrefillArgs& a, const Item& it
             r = 16 * wave + (lane & 15);
         }
         r = min(r, it.count - 1);
-        tok[j] = it.e < 0 ? it.row0 + r : a.tokw[it.row0 + r].x;
+        tok[j] = it.e < 0 ? it.row0 + r : s_tok[r];
     }
 }
 
@@ -364,7 +378,7 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
 // one pipelined stream.
 template <int BITS, bool GATE_UP, bool SHARED>
 __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int total, uint8_t* smem,
-                          Item* s_items, float* s_asum, int* s_cnt) {
+                          Item* s_items, float* s_asum, int* s_cnt, int* s_tok) {
     using P = Pipe<BITS>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = (total + 7) / 8;
@@ -394,12 +408,20 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
     const int G = (int)((GATE_UP ? a.H : es.I) / kGroup);   // groups of K per item
     const int total_steps = n_items * G;
 
-    // issue side: item ii, group gi; the tokens of the item after it are prefetched
+    // issue side: item ii, group gi.  Gate/up: item i's tokens sit in token buffer i & 1,
+    // copied when item i - 1 starts issuing; the copy is older than every step wait from
+    // then on, and a barrier follows wave 0's next wait before any wave reads it.
     int ii = 0, gi = 0, issued = 0;
-    int tok[5] = {0, 0, 0, 0, 0}, tok_next[5] = {0, 0, 0, 0, 0};
+    int tok[5] = {0, 0, 0, 0, 0};
+    const uint32_t lds_tok = lds_offset(s_tok);
     if constexpr (GATE_UP) {
-        item_tokens(a, s_items[0], tok);
-        if (n_items > 1) item_tokens(a, s_items[1], tok_next);
+        if (__builtin_amdgcn_readfirstlane(wave) == 0) {   // (wave-uniform branch)
+            copy_item_tokens(a, s_items[0], lds_tok);
+            if (n_items > 1) copy_item_tokens(a, s_items[1], lds_tok + MT * 4);
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        item_tokens(s_items[0], s_tok, tok);
     }
     IssueState st;
     prepare_issue<BITS, GATE_UP>(a, s_items[0], es, tok, st);
@@ -411,9 +433,9 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
             ++ii;
             gi = 0;
             if constexpr (GATE_UP) {
-#pragma unroll
-                for (int j = 0; j < 5; ++j) tok[j] = tok_next[j];
-                if (ii + 1 < n_items) item_tokens(a, s_items[ii + 1], tok_next);
+                item_tokens(s_items[ii], s_tok + (ii & 1) * MT, tok);
+                if (__builtin_amdgcn_readfirstlane(wave) == 0 && ii + 1 < n_items)
+                    copy_item_tokens(a, s_items[ii + 1], lds_tok + ((ii + 1) & 1) * MT * 4);
             }
             prepare_issue<BITS, GATE_UP>(a, s_items[ii], es, tok, st);
         }
@@ -489,12 +511,14 @@ __global__ __launch_bounds__(kPThreads) void gk_prefill_kernel(PrefillArgs a) {
     constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
     Item* s_items = reinterpret_cast<Item*>(smem + kPipe);
     float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
+    int* s_tok = reinterpret_cast<int*>(s_asum + 4 * MT);   // two items' tokens
     __shared__ int s_cnt[kPWaves];
     const int nb = (int)(a.routed.I / kGroup);
-    run_items<BITS, true, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt);
+    run_items<BITS, true, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, s_tok);
     if constexpr (SBITS != 0) {
         const int nbs = (int)(a.shared.I / kGroup);
-        run_items<SBITS, true, true>(a, a.shared, nbs, ((a.T + MT - 1) / MT) * nbs, smem, s_items, s_asum, s_cnt);
+        run_items<SBITS, true, true>(a, a.shared, nbs, ((a.T + MT - 1) / MT) * nbs, smem, s_items, s_asum, s_cnt,
+                                     s_tok);
     }
 }
 
@@ -506,9 +530,10 @@ __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
     float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
     __shared__ int s_cnt[kPWaves];
     const int nb = (int)((a.H + NT - 1) / NT);
-    run_items<BITS, false, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt);
+    run_items<BITS, false, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, nullptr);
     if constexpr (SBITS != 0)
-        run_items<SBITS, false, true>(a, a.shared, nb, ((a.T + MT - 1) / MT) * nb, smem, s_items, s_asum, s_cnt);
+        run_items<SBITS, false, true>(a, a.shared, nb, ((a.T + MT - 1) / MT) * nb, smem, s_items, s_asum, s_cnt,
+                                      nullptr);
 }
 
 // y[t] = sum over slots j in order of w[t, j] times the staged row of pair (t, j), then
@@ -560,7 +585,7 @@ unsigned prefill_grid(int64_t max_items) {
 template <int BITS, int SBITS>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
     constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
-    constexpr uint32_t lds = kPipe + kMaxItems * sizeof(Item) + 4 * MT * 4;
+    constexpr uint32_t lds = kPipe + kMaxItems * sizeof(Item) + 4 * MT * 4 + 2 * MT * 4;
     static_assert(lds + 64 <= 160 * 1024, "LDS budget of one workgroup");
     static const bool attr = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gk_prefill_kernel<BITS, SBITS>),
