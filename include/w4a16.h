@@ -142,7 +142,9 @@ typedef struct moe_w4a16_args {
     void* workspace;               /* device scratch, >= moe_w4a16_workspace_size(args);    */
                                    /* its first W4A16_WORKSPACE_HEAD_BYTES must be zero     */
                                    /* before the first call (moe_w4a16_workspace_init) and  */
-                                   /* then stay owned by the library across calls           */
+                                   /* then stay owned by the library across calls; calls    */
+                                   /* that may overlap on the GPU need workspaces of their  */
+                                   /* own                                                    */
     size_t workspace_bytes;
 } moe_w4a16_args;
 

@@ -2,11 +2,15 @@
 // stream per CU.
 //
 // Work is a flat list of items: (M-tile of <= 16 rows of one expert, 16-row block of its
-// gate/up bank, 8-group K chunk) for the routed tiles (built by the routing kernel), then
-// the shared expert's tiles of 16 tokens.  A 4-bit item carries the 16 gate rows and the
-// 16 up rows of its K chunk, an 8-bit item one of the two halves; either way 16 KiB of
-// codes.  Each workgroup (one per CU) walks a contiguous range of the list, so an
-// M-tile's activations are fetched once and serve every row block of its expert.
+// gate/up bank, 8-group K chunk) for the routed tiles, then the shared expert's tiles of 16
+// tokens.  The routed tiles come from the routing kernel's tile records, or from the batch
+// routed again by every workgroup (fused_route), or, in pair mode, are the (token, rank)
+// pairs themselves: one row each, whose experts each workgroup finds for its own range
+// with a top-k that stops at the pair's rank (workgroup 0 then only routes the batch for
+// the down kernels).  A 4-bit item carries the 16 gate rows and the 16 up rows of its K
+// chunk, an 8-bit item one of the two halves; either way 16 KiB of codes.  Each workgroup
+// (one per CU) walks a contiguous range of the list, so an M-tile's activations are
+// fetched once and serve every row block of its expert.
 //
 // Every item's codes and scales reach LDS by direct-to-LDS buffer loads into a ring of
 // kSStages stages: while item s computes, items s+1 .. s+kSStages-2 are in flight, which
