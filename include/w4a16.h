@@ -162,7 +162,7 @@ size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
  * gate/up workgroups hand their results to the down-projection workgroups of the same
  * kernel: exit counters (zero between calls), an epoch number that each call advances, and
  * the handed-over values, each tagged with the epoch of the call that wrote it; and to the
- * small-batch routing from logits over several workgroups (17..64 tokens), whose last
+ * small-batch routing from logits over several workgroups (25..64 tokens), whose last
  * workgroup to arrive finishes the routing: its arrival counter (zero between calls).  A
  * workspace needs this once, not per call (a zero-filled allocation needs none).
  * Enqueued on `stream` as a small fill kernel (no memset node, so it may be captured in a

@@ -108,9 +108,9 @@ def _run_route(logits, k, E, H=256, I=128):
 
 @pytest.mark.parametrize("T,E,k", [(4, 8, 2), (1, 256, 8), (32, 256, 8), (64, 256, 8), (65, 256, 8),
                                    (300, 64, 6), (8192, 256, 8), (7, 1024, 16), (5, 3, 3),
-                                   # the split routing launch (17..64 tokens): its smallest and
+                                   # the split routing launch (25..64 tokens): its smallest and
                                    # largest workgroup counts, 8 and 16 logits per lane
-                                   (17, 512, 4), (40, 1024, 16), (64, 128, 1)])
+                                   (25, 512, 4), (40, 1024, 16), (64, 128, 1)])
 def test_route_bitexact(T, E, k):
     say(f"route T={T} E={E} k={k}")
     logits = synth.router_logits(50 + T, T, E)

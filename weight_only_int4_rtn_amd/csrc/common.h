@@ -180,7 +180,7 @@ struct WsLayout {
 };
 
 constexpr int kSmallT = 64;      // batches up to this size take the small-batch path
-constexpr int kSplitRouteT = 16;  // above this many tokens (from logits, not pair mode) routing takes its own launch
+constexpr int kSplitRouteT = 24;  // above this many tokens (from logits, not pair mode) routing takes its own launch
 constexpr int kPairP = 64;       // T * k up to this may take the pair-mapped gate/up (pair < 2^kRecTokBits)
 // A small-path slot record carries its expert's first kRecTokens tokens (ascending,
 // kRecTokBits bits each) so gate/up can fetch activations without reading the row list.
