@@ -13,10 +13,13 @@ from gpu_util import DEV, bf16_to_dev, f32_to_dev, gpu_layer, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [1, 32, 300])
-def test_graph_replay_matches_eager(T):
-    say(f"graph replay T={T}")
-    E, H, I, k = 64, 512, 256, 8
+@pytest.mark.parametrize("T,E,H,I", [(1, 64, 512, 256), (32, 64, 512, 256), (300, 64, 512, 256),
+                                     # pair mode of the stream; the split routing launch (its
+                                     # arrival counter resets on every replay) and the stream
+                                     (4, 256, 2048, 512), (32, 256, 2048, 512)])
+def test_graph_replay_matches_eager(T, E, H, I):
+    say(f"graph replay T={T} E={E} H={H}")
+    k = 8
     w13, s13, w2, s2 = gpu_layer(21, 0, E, H, I, 4)
     x = bf16_to_dev(synth.activations_bf16(70 + T, T, H))
     logits = f32_to_dev(synth.router_logits(70 + T, T, E))
