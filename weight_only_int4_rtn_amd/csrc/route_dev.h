@@ -228,6 +228,91 @@ __device__ __forceinline__ int checked_id(const int32_t* tok_ids, int j, int E) 
 // logits the wave runs the top-k only up to round j (the rounds are those of the full
 // routing, so the winner is the same), which lets a workgroup that serves one pair start
 // loading its weights before the whole batch is routed.
+// Rank j's expert of one token (E <= 256, four logits per lane), up to two winners per
+// round: one reduction gives the two largest lane-best keys M1 > M2 (a max / second-max
+// pair per DPP stage); the lane holding M1 wins first, and the second winner is that lane's
+// next key when it is larger than M2, else the lane holding M2.  Any equal keys among these
+// candidates (where the lower expert index decides) take a round of one winner with the
+// tie rule of wave_topk_core instead.  Same winners, in the same order, as wave_topk_core.
+__device__ int wave_rank_expert2(const float (&raw)[4], int E, int j) {
+    const int lane = threadIdx.x & 63;
+    int hk[4];
+    uint32_t perm = 0xe4u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hk[i] = lane + 64 * i < E ? logit_key(raw[i]) : kKeyNone;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)   // stable insertion sort, larger key first
+#pragma unroll
+        for (int jj = i; jj > 0; --jj) {
+            const bool sw = hk[jj] > hk[jj - 1];
+            const int tk = hk[jj];
+            hk[jj] = sw ? hk[jj - 1] : hk[jj];
+            hk[jj - 1] = sw ? tk : hk[jj - 1];
+            const uint32_t a = (perm >> (2 * jj - 2)) & 3u, b = (perm >> (2 * jj)) & 3u;
+            const uint32_t swapped = (perm & ~(0xfu << (2 * jj - 2))) | (b << (2 * jj - 2)) | (a << (2 * jj));
+            perm = sw ? swapped : perm;
+        }
+    auto pop = [&](bool me) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) hk[i] = me ? hk[i + 1] : hk[i];
+        hk[3] = me ? kKeyNone : hk[3];
+        perm = me ? perm >> 2 : perm;
+    };
+    for (int r = 0;;) {
+        // the two largest lane-best keys: (first, second) pairs merged stage by stage
+        int a1 = hk[0], a2 = kKeyNone;
+#pragma unroll
+        for (int st = 0; st < 6; ++st) {
+            const int b1 = st == 0 ? dpp_in<0xb1, 0xf, (int)0x80000000>(a1)
+                         : st == 1 ? dpp_in<0x4e, 0xf, (int)0x80000000>(a1)
+                         : st == 2 ? dpp_in<0x141, 0xf, (int)0x80000000>(a1)
+                         : st == 3 ? dpp_in<0x140, 0xf, (int)0x80000000>(a1)
+                         : st == 4 ? dpp_in<0x142, 0xa, (int)0x80000000>(a1)
+                                   : dpp_in<0x143, 0xc, (int)0x80000000>(a1);
+            const int b2 = st == 0 ? dpp_in<0xb1, 0xf, (int)0x80000000>(a2)
+                         : st == 1 ? dpp_in<0x4e, 0xf, (int)0x80000000>(a2)
+                         : st == 2 ? dpp_in<0x141, 0xf, (int)0x80000000>(a2)
+                         : st == 3 ? dpp_in<0x140, 0xf, (int)0x80000000>(a2)
+                         : st == 4 ? dpp_in<0x142, 0xa, (int)0x80000000>(a2)
+                                   : dpp_in<0x143, 0xc, (int)0x80000000>(a2);
+            a2 = max(min(a1, b1), max(a2, b2));
+            a1 = max(a1, b1);
+        }
+        const int M1 = __builtin_amdgcn_readlane(a1, 63), M2 = __builtin_amdgcn_readlane(a2, 63);
+        const int be = hk[0] == kKeyNone ? 0x7fffffff : lane + 64 * (int)(perm & 3u);
+        const uint64_t c1 = __ballot(hk[0] == M1);
+        if (__popcll(c1) == 1) {
+            const int w1 = (int)__ffsll((long long)c1) - 1;
+            if (r == j) return __builtin_amdgcn_readlane(be, w1);
+            const int s = __builtin_amdgcn_readlane(hk[1], w1);
+            if (s > M2) {   // the winner lane's next key is second
+                if (r + 1 == j) return __builtin_amdgcn_readlane(lane + 64 * (int)((perm >> 2) & 3u), w1);
+                pop(lane == w1);
+                pop(lane == w1);
+                r += 2;
+                continue;
+            }
+            const uint64_t c2 = __ballot(hk[0] == M2);
+            if (s < M2 && __popcll(c2) == 1) {   // another lane's best is second
+                const int w2 = (int)__ffsll((long long)c2) - 1;
+                if (r + 1 == j) return __builtin_amdgcn_readlane(be, w2);
+                pop(lane == w1 || lane == w2);
+                r += 2;
+                continue;
+            }
+            pop(lane == w1);   // equal keys behind the first: one winner this round
+            r += 1;
+            continue;
+        }
+        // equal keys on top: the lowest expert index among the tied lanes, one winner
+        const int emin = wave_min_i32(hk[0] == M1 ? be : 0x7fffffff);
+        const int wl = (int)__ffsll((long long)__ballot(hk[0] == M1 && be == emin)) - 1;
+        if (r == j) return emin;
+        pop(lane == wl);
+        r += 1;
+    }
+}
+
 __device__ __forceinline__ int pair_expert(const float* logits, const int32_t* ids, int E, int k, int t, int j) {
     if (!logits) return checked_id(ids + t * k, j, E);
     const float* row = logits + (int64_t)t * E;
@@ -236,7 +321,7 @@ __device__ __forceinline__ int pair_expert(const float* logits, const int32_t* i
     if (E <= 256) {
         float raw[4];
         wave_topk_load<4>(row, E, raw);
-        wave_topk_from<4, false>(raw, E, j + 1, &id, &w);
+        return __builtin_amdgcn_readfirstlane(wave_rank_expert2(raw, E, j));
     } else if (E <= 512) {
         float raw[8];
         wave_topk_load<8>(row, E, raw);
