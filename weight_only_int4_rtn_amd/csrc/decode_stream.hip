@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
         static_assert(kSMaxTiles <= kSWaves + kSIssuers, "one wave per routed tile of a range");
         if (wave <= t_hi - L.t_lo) {
             const int p = L.t_lo + wave, t = p / a.k;
-            const int e = pair_expert(a.route.logits, a.route.ids, a.E, a.k, t, p - t * a.k);
+            const int e = pair_expert<false>(a.route.logits, a.route.ids, a.E, a.k, t, p - t * a.k);
             if (lane < 8)
                 s_tiles[8 * wave + lane] = lane == 0 ? max(e, 0) : lane == 1 ? p : lane == 2 ? (e >= 0 ? 1 : 0)
                                                                                  : lane == 4 ? t : 0;

@@ -524,7 +524,7 @@ __device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
         const int64_t I_e = a.routed.I;
         if (n0 >= I_e) return;
         const int t = p / a.k;
-        const int e = pair_expert(a.logits, a.ids, a.E, a.k, t, p % a.k);
+        const int e = pair_expert<true>(a.logits, a.ids, a.E, a.k, t, p % a.k);
         if (e < 0) return;   // dropped pair: the down workgroups skip its row
         const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
         gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,

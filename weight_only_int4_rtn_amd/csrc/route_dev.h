@@ -313,6 +313,9 @@ __device__ int wave_rank_expert2(const float (&raw)[4], int E, int j) {
     }
 }
 
+// TWO: the two-winner rounds (E <= 256); measured faster in the single-launch kernel and
+// slightly slower inside the streaming kernel, whose code around it it changes.
+template <bool TWO>
 __device__ __forceinline__ int pair_expert(const float* logits, const int32_t* ids, int E, int k, int t, int j) {
     if (!logits) return checked_id(ids + t * k, j, E);
     const float* row = logits + (int64_t)t * E;
@@ -321,7 +324,8 @@ __device__ __forceinline__ int pair_expert(const float* logits, const int32_t* i
     if (E <= 256) {
         float raw[4];
         wave_topk_load<4>(row, E, raw);
-        return __builtin_amdgcn_readfirstlane(wave_rank_expert2(raw, E, j));
+        if constexpr (TWO) return __builtin_amdgcn_readfirstlane(wave_rank_expert2(raw, E, j));
+        wave_topk_from<4, false>(raw, E, j + 1, &id, &w);
     } else if (E <= 512) {
         float raw[8];
         wave_topk_load<8>(row, E, raw);
