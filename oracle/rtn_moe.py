@@ -217,7 +217,8 @@ def expert_ffn(x, w13, w2):
     section describes); ``w2`` is ``[H, I]``.
 
     ``a = SiLU(Wg x) * (Wu x)`` with ``SiLU(z) = z / (1 + exp(-z))``; returns
-    ``W2 a``.
+    ``W2 a``.  ``x`` may also be ``[H, n]``: n tokens as columns, each evaluated
+    independently (the same products, as a matrix instead of n vectors).
     """
     I = w13.shape[0] // 2
     g = w13[:I] @ x
@@ -256,8 +257,12 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
     for e in sorted(by_expert):
         W13 = dequantize(w13[e], s13[e], bits).astype(np.float64)
         W2 = dequantize(w2[e], s2[e], bits).astype(np.float64)
-        for ti, j in by_expert[e]:
-            out[ti, j] = expert_ffn(x[tokens[ti]], W13, W2)
+        rows = by_expert[e]
+        # every (token, slot) routed to e at once: token activations as the columns
+        X = x[[tokens[ti] for ti, _ in rows]].T
+        O = expert_ffn(X, W13, W2).T
+        for r, (ti, j) in enumerate(rows):
+            out[ti, j] = O[r]
 
     y = np.zeros((len(tokens), H))
     wsel = np.asarray(w, dtype=np.float32).astype(np.float64)[tokens]
@@ -266,8 +271,7 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
     if shared is not None:
         S13 = dequantize(shared["w13"], shared["s13"], shared["bits"]).astype(np.float64)
         S2 = dequantize(shared["w2"], shared["s2"], shared["bits"]).astype(np.float64)
-        for ti, t in enumerate(tokens):
-            y[ti] += expert_ffn(x[t], S13, S2)
+        y += expert_ffn(x[tokens].T, S13, S2).T
     if residual_bits is not None:
         y += f32_from_bf16_bits(residual_bits).astype(np.float64)[tokens]
     return y

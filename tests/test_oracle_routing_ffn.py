@@ -130,31 +130,56 @@ def test_ffn_invariants():
     assert np.all(oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, np.zeros_like(s2), 4) == 0)
     s2x2 = oracle.bf16_bits_from_f32(2 * oracle.f32_from_bf16_bits(s2))
     assert np.allclose(oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2x2, 4), 2 * y, rtol=1e-12, atol=0)
-    # batch invariance: a token alone gives the same row
+    # batch invariance: a token alone gives the same row (up to the fp64 summation order
+    # of a matrix product against a vector product)
     for t in range(cfg.T):
         yt = oracle.moe_ffn(x_bits[t:t + 1], ids[t:t + 1], w[t:t + 1], p13, s13, p2, s2, 4)
-        assert np.array_equal(yt[0], y[t])
+        assert np.allclose(yt[0], y[t], rtol=1e-12, atol=1e-15)
     # token permutation equivariance, and the token-subset argument
     perm = np.array([2, 0, 3, 1])
     yp = oracle.moe_ffn(x_bits[perm], ids[perm], w[perm], p13, s13, p2, s2, 4)
-    assert np.array_equal(yp, y[perm])
-    assert np.array_equal(oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2, 4, tokens=[3, 1]), y[[3, 1]])
+    assert np.allclose(yp, y[perm], rtol=1e-12, atol=1e-15)
+    ys = oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2, 4, tokens=[3, 1])
+    assert np.allclose(ys, y[[3, 1]], rtol=1e-12, atol=1e-15)
 
 
-def test_shared_expert_and_residual_add():
+@pytest.mark.parametrize("shared_bits", [4, 8])
+def test_shared_expert_and_residual_against_torch_functional(shared_bits):
+    """The shared expert (weight 1) and the bf16 residual, pinned by an independent
+    evaluation: torch.nn.functional's linear and silu in fp64 on the dequantized shared
+    weights, the routed experts as a dense mixture over every expert (no routing code),
+    and the residual widened by torch's own bf16 -> fp64 conversion."""
     cfg = synth.CONFIGS["tiny"]
+    H, I = cfg.H, cfg.I
     p13, s13, p2, s2 = _tiny_layer()
-    sp13, ss13 = oracle.quantize_pack(synth.expert_w13(0, 0, 0, 256, 128, shared=True), 8)
-    sp2, ss2 = oracle.quantize_pack(synth.expert_w2(0, 0, 0, 256, 128, shared=True), 8)
-    shared = dict(w13=sp13, s13=ss13, w2=sp2, s2=ss2, bits=8)
-    x_bits = synth.activations_bf16(0, cfg.T, cfg.H)
-    res_bits = synth.activations_bf16(0, cfg.T, cfg.H, stream=12)
+    sp13, ss13 = oracle.quantize_pack(synth.expert_w13(0, 0, 0, H, I, shared=True), shared_bits)
+    sp2, ss2 = oracle.quantize_pack(synth.expert_w2(0, 0, 0, H, I, shared=True), shared_bits)
+    shared = dict(w13=sp13, s13=ss13, w2=sp2, s2=ss2, bits=shared_bits)
+    x_bits = synth.activations_bf16(0, cfg.T, H)
+    res_bits = synth.activations_bf16(0, cfg.T, H, stream=12)
     ids, w, *_ = oracle.route(synth.router_logits(0, cfg.T, cfg.E), cfg.k)
-    y = oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2, 4)
     ys = oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2, 4, shared=shared, residual_bits=res_bits)
-    x = oracle.f32_from_bf16_bits(x_bits).astype(np.float64)
-    S13 = oracle.dequantize(sp13, ss13, 8).astype(np.float64)
-    S2 = oracle.dequantize(sp2, ss2, 8).astype(np.float64)
-    extra = np.stack([oracle.expert_ffn(x[t], S13, S2) for t in range(cfg.T)])
-    extra += oracle.f32_from_bf16_bits(res_bits).astype(np.float64)
-    assert np.allclose(ys, y + extra, rtol=1e-12, atol=1e-12)
+
+    def as_torch_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double()
+
+    def mlp(x, W13, W2):
+        W13 = torch.from_numpy(W13).double()
+        W2 = torch.from_numpy(W2).double()
+        return F.linear(F.silu(F.linear(x, W13[:I])) * F.linear(x, W13[I:]), W2)
+
+    x = as_torch_bf16(x_bits)
+    ref = torch.zeros((cfg.T, H), dtype=torch.float64)
+    for e in range(cfg.E):   # dense mixture: weight of e for each token, 0 when not chosen
+        ge = torch.zeros(cfg.T, dtype=torch.float64)
+        for t in range(cfg.T):
+            hit = np.nonzero(ids[t] == e)[0]
+            if len(hit):
+                ge[t] = float(w[t, hit[0]])
+        ref += ge[:, None] * mlp(x, oracle.dequantize(p13[e], s13[e], 4), oracle.dequantize(p2[e], s2[e], 4))
+    ref += mlp(x, oracle.dequantize(sp13, ss13, shared_bits), oracle.dequantize(sp2, ss2, shared_bits))
+    ref += as_torch_bf16(res_bits)
+    assert np.allclose(ys, ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the shared term is really there: dropping it moves the result by far more than rounding
+    no_shared = oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2, 4, residual_bits=res_bits)
+    assert np.abs(no_shared - ys).max() > 1e-3
