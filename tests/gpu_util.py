@@ -67,6 +67,13 @@ class OracleExperts:
             self.cache[e] = (p13, s13, p2, s2)
         return self.cache[e]
 
+    def prefetch(self, experts, threads=8):
+        """Quantize these experts ahead, on a thread pool (NumPy releases the GIL)."""
+        from concurrent.futures import ThreadPoolExecutor
+        todo = [int(e) for e in experts if int(e) not in self.cache]
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(self.get, todo))
+
     def view(self, i):
         parent = self
 

@@ -4,7 +4,7 @@ Bar: packed codes, scales and routing (ids, counts, offsets, sorted pairs) bit-e
 routing weights within 1e-6; FFN outputs within the acceptance tolerance of
 ``gpu_util.check_ffn``.  Sizes span several tiles and ragged tails; the full layer
 shape (256 experts, top-8, hidden 2048, intermediate 512) runs at 1, 32 and 8192
-tokens, the last one checked on sampled tokens the oracle evaluates one by one.
+tokens, the last one checked on every token routed to any of 16 experts.
 """
 
 import numpy as np
@@ -229,20 +229,26 @@ def test_ffn_full_layer_decode(full_layer, cfg_name):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "decode result not bitwise reproducible"
 
 
-def test_ffn_full_layer_prefill_sampled(full_layer):
+def test_ffn_full_layer_prefill_sixteen_experts(full_layer):
+    """8192 tokens over the full layer: every output row of every token routed to any of
+    16 experts spread over the bank (about 40 % of the tokens), so each of those experts'
+    M-tiles, the ragged last one included, is compared in full."""
     cfg = synth.CONFIGS["prefill8192"]
-    say("ffn prefill8192 (sampled tokens)")
+    say("ffn prefill8192 (all tokens of 16 experts)")
     w13, s13, w2, s2 = full_layer
     ref = OracleExperts(FULL.group, 0, FULL.H, FULL.I, 4)
     x = synth.activations_bf16(3, cfg.T, cfg.H)
     logits = synth.router_logits(3, cfg.T, cfg.E)
     y = w4.moe_w4a16_forward(bf16_to_dev(x), w13, s13, w2, s2, top_k=cfg.k, router_logits=f32_to_dev(logits))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(8192)
-    tokens = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 8191], rng.choice(cfg.T, 26, replace=False)]))
-    ids, wts, *_ = oracle.route(logits, cfg.k)
+    ids, wts, counts, *_ = oracle.route(logits, cfg.k)
+    chosen = np.arange(0, 256, 17)
+    assert len(chosen) == 16 and np.any(counts[chosen] % 128 != 0)
+    tokens = np.nonzero(np.isin(ids, chosen).any(axis=1))[0]
+    say(f"  {len(tokens)} tokens")
+    ref.prefetch(np.unique(ids[tokens]))
     y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), 4, tokens=tokens)
-    check_ffn(y[torch.from_numpy(tokens).to(DEV)], y_ref, "prefill8192 sampled")
+    check_ffn(y[torch.from_numpy(tokens).to(DEV)], y_ref, "prefill8192, 16 experts' tokens")
     y2 = w4.moe_w4a16_forward(bf16_to_dev(x), w13, s13, w2, s2, top_k=cfg.k, router_logits=f32_to_dev(logits))
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "prefill result not bitwise reproducible"
