@@ -18,8 +18,13 @@
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major, contiguous.  Device pointers must be 16-byte
  *     aligned.  bf16 values travel as uint16_t bit patterns.
- *   - The caller owns every buffer.  The library allocates no device memory and keeps
- *     no state between calls except a per-thread error message.
+ *   - The caller owns every buffer.  The library allocates no device memory.  Host-side it
+ *     keeps a per-thread error message and a few per-device launch facts (CU count,
+ *     occupancy) read once from the runtime.  Device-side state lives only in the head of
+ *     a caller's workspace (W4A16_WORKSPACE_HEAD_BYTES): a launch epoch, counters that
+ *     are zero between calls, a sticky time-out word and epoch-tagged hand-off values,
+ *     carried from one forward to the next on that workspace (see
+ *     moe_w4a16_workspace_init and moe_w4a16_workspace_check).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and
  *     runs asynchronously; no entry point synchronises.  A fault inside a kernel shows
  *     up at the caller's next synchronisation.
@@ -38,14 +43,15 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 3
+#define W4A16_ABI_VERSION 4
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
     W4A16_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misaligned pointer, k > E, ...    */
     W4A16_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement          */
     W4A16_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_w4a16_workspace_size() */
-    W4A16_ERR_HIP = 4          /* a HIP launch reported an error                            */
+    W4A16_ERR_HIP = 4,         /* a HIP launch reported an error                            */
+    W4A16_ERR_TIMEOUT = 5      /* a bounded in-kernel wait timed out (workspace_check)      */
 } w4a16_status;
 
 typedef enum w4a16_dtype {
@@ -106,7 +112,9 @@ int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, 
  * the softmax over all E logits renormalised over the chosen ones.  With
  * router_logits == NULL, topk_ids / topk_w are read as inputs instead (ids must be in
  * [0, E) and distinct within a token; an id outside [0, E) or a repeat of an earlier
- * slot's id contributes nothing).
+ * slot's id contributes nothing).  Logits must not be NaN: a NaN logit is outside the
+ * contract (the kernels rank it like -inf, the oracle below every number), and so is a
+ * row whose logits are all -inf (its weights are not defined).
  *
  * Output: y[t] = residual[t] + sum_j w[t,j] * down_e( SiLU(gate_e x_t) * up_e x_t )
  *              + shared( x_t )                        (e = topk_ids[t,j])
@@ -139,7 +147,7 @@ typedef struct moe_w4a16_args {
     int32_t* expert_offsets;       /* optional out, int32 [E+1]: exclusive prefix of counts */
     int32_t* sorted_pairs;         /* optional out, int32 [T*top_k]: pair ids t*top_k+j by   */
                                    /* (expert, token) ascending                              */
-    void* workspace;               /* device scratch, >= moe_w4a16_workspace_size(args);    */
+    void* workspace;               /* device scratch, >= moe_w4a16_workspace_size(...);     */
                                    /* its first W4A16_WORKSPACE_HEAD_BYTES must be zero     */
                                    /* before the first call (moe_w4a16_workspace_init) and  */
                                    /* then stay owned by the library across calls; calls    */
@@ -148,12 +156,16 @@ typedef struct moe_w4a16_args {
     size_t workspace_bytes;
 } moe_w4a16_args;
 
-/* Device workspace bytes moe_w4a16_forward needs for these shapes (reads T, H, I, E,
- * top_k, shared_bits and shared_I only).  Returns 0 when the shapes are invalid. */
-size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
+/* Device workspace bytes moe_w4a16_forward needs for T tokens, hidden H, intermediate I,
+ * E experts, top_k, and a shared expert of intermediate size shared_I (0: none).  The
+ * size does not depend on the code widths.  Returns 0 when the shapes are invalid (the
+ * same checks as moe_w4a16_forward; w4a16_last_error() says which). */
+size_t moe_w4a16_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t shared_I);
 
 /* Bytes at the start of every workspace that carry state from one forward to the next. */
 #define W4A16_WORKSPACE_HEAD_BYTES 147456
+/* Byte offset, inside the head, of the sticky time-out word (uint32, 0 = no time-out). */
+#define W4A16_WORKSPACE_ERROR_OFFSET 12928
 
 /*
  * moe_w4a16_workspace_init - zero the head of a new workspace (its first
@@ -170,6 +182,26 @@ size_t moe_w4a16_workspace_size(const moe_w4a16_args* args);
  * W4A16_ERR_WORKSPACE when workspace_bytes < W4A16_WORKSPACE_HEAD_BYTES.
  */
 int moe_w4a16_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_w4a16_workspace_check - surface a time-out of the single-launch path.
+ *
+ * The single-launch path (T * top_k <= 16) hands values from its gate/up workgroups to
+ * its down workgroups inside one kernel, relying on both being resident together.  Each
+ * wait is bounded: when one times out (the GPU was shared so that the producers could
+ * not run), the kernel sets the workspace's sticky time-out word, and from then on every
+ * single-launch forward on that workspace writes quiet NaN (bf16 0x7FC0) to the output
+ * rows it owns instead of waiting, so a wrong result is never silent.  The rows of the
+ * call that timed out that depend on the missing values are NaN as well.
+ *
+ * This call synchronises `stream` (so every forward enqueued on it has finished), reads
+ * the word, and when it is set clears the whole head (epoch, counters, tagged values and
+ * the word itself, as moe_w4a16_workspace_init does) and returns W4A16_ERR_TIMEOUT;
+ * otherwise W4A16_OK.  Forwards after it run normally again.  Errors:
+ * W4A16_ERR_INVALID_ARG (NULL or misaligned workspace), W4A16_ERR_WORKSPACE (smaller
+ * than the head), W4A16_ERR_HIP.
+ */
+int moe_w4a16_workspace_check(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_w4a16_forward - routing, fused dequant gate/up + SiLU(gate)*up, fused dequant down

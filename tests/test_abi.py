@@ -47,9 +47,10 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 3
+    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 4
     assert _lib.status_string(0) == "W4A16_OK"
     assert _lib.status_string(3) == "W4A16_ERR_WORKSPACE"
+    assert _lib.status_string(5) == "W4A16_ERR_TIMEOUT"
     assert _lib.status_string(99) == "W4A16_UNKNOWN_STATUS"
 
 
@@ -110,7 +111,7 @@ def test_forward_rejects_missing_ids_and_small_workspace(L):
     a.router_logits = None
     assert forward_status(L, a) == _lib.W4A16_ERR_INVALID_ARG
     a = base_args()
-    need = L.moe_w4a16_workspace_size(C.byref(a))
+    need = L.moe_w4a16_workspace_size(a.T, a.H, a.I, a.E, a.top_k, 0)
     assert need > 0
     a.workspace, a.workspace_bytes = FAKE + 0x10000, need - 1
     assert forward_status(L, a) == _lib.W4A16_ERR_WORKSPACE
@@ -149,17 +150,31 @@ def test_workspace_head_size_matches_header():
 def test_workspace_size(L):
     sizes = {}
     for T in (1, 32, 64, 65, 8192):
-        sizes[T] = L.moe_w4a16_workspace_size(C.byref(base_args(T=T)))
+        sizes[T] = L.moe_w4a16_workspace_size(T, 2048, 512, 256, 8, 0)
         assert sizes[T] > 0 and sizes[T] % 256 == 0
     assert sizes[1] < sizes[32] < sizes[8192]
     # the gate/up output of 8192 x 8 pairs alone is 64 MiB of bf16
     assert sizes[8192] >= 8192 * 8 * 512 * 2
-    bad = base_args()
-    bad.bits = 3
-    assert L.moe_w4a16_workspace_size(C.byref(bad)) == 0
-    sh = base_args(T=4)
-    sh.shared_bits, sh.shared_I = 8, 512
-    assert L.moe_w4a16_workspace_size(C.byref(sh)) > L.moe_w4a16_workspace_size(C.byref(base_args(T=4)))
+    for bad in ((1, 2000, 512, 256, 8, 0), (1, 2048, 100, 256, 8, 0), (1, 2048, 512, 256, 0, 0),
+                (1, 2048, 512, 8, 9, 0), (-1, 2048, 512, 256, 8, 0), (1, 2048, 512, 256, 8, 100),
+                (1, 2048, 512, 256, 8, -128)):
+        assert L.moe_w4a16_workspace_size(*bad) == 0, bad
+        assert _lib.last_error()
+    assert L.moe_w4a16_workspace_size(4, 2048, 512, 256, 8, 512) > L.moe_w4a16_workspace_size(4, 2048, 512, 256, 8, 0)
+
+
+def test_workspace_check_validation(L):
+    """Host-side rejections of the time-out check (no GPU call is reached)."""
+    assert L.moe_w4a16_workspace_check(None, 1 << 20, None) == _lib.W4A16_ERR_INVALID_ARG
+    assert L.moe_w4a16_workspace_check(C.c_void_p(MISALIGNED), 1 << 20, None) == _lib.W4A16_ERR_INVALID_ARG
+    assert L.moe_w4a16_workspace_check(C.c_void_p(FAKE), 100, None) == _lib.W4A16_ERR_WORKSPACE
+
+
+def test_error_offset_matches_header():
+    hdr = open(HEADER).read()
+    m = re.search(r"#define W4A16_WORKSPACE_ERROR_OFFSET (\d+)", hdr)
+    assert m and int(m.group(1)) == _lib.WORKSPACE_ERROR_OFFSET
+    assert _lib.WORKSPACE_ERROR_OFFSET + 4 <= _lib.WORKSPACE_HEAD_BYTES
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -177,3 +192,26 @@ def test_quantize_validation(L, args, expect):
     packed = None if w is None else FAKE
     st = L.rtn_quantize_pack(w, dt, n, r, c, bits, group, packed, packed, None)
     assert st == expect
+
+
+def test_binding_shape_checks_on_the_host():
+    """The binding's shape rules (run before any call into the library), on meta tensors."""
+    import torch
+    import weight_only_int4_rtn_amd as w4
+    m = dict(device="meta")
+    E, H, I = 8, 256, 128
+    good = (torch.empty((E, 2 * I, H // 8), dtype=torch.int32, **m), torch.empty((E, 2 * I, H // 128), **m),
+            torch.empty((E, H, I // 8), dtype=torch.int32, **m), torch.empty((E, H, I // 128), **m))
+    assert w4._check_experts(*good, 4, H) == (E, I)
+    with pytest.raises(ValueError):
+        w4._check_experts(*good, 8, H)                     # 8-bit codes need twice the words
+    with pytest.raises(ValueError):
+        w4._check_experts(*good, 4, H + 128)               # another hidden size
+    with pytest.raises(ValueError):
+        w4._check_experts(*good, 3, H)
+    bad_s2 = torch.empty((E, H, 2), **m)
+    with pytest.raises(ValueError):
+        w4._check_experts(good[0], good[1], good[2], bad_s2, 4, H)
+    with pytest.raises(ValueError):
+        w4._shape(torch.empty((3, H), **m), "out", (4, H))
+    w4._shape(None, "residual", (4, H))                  # absent optional tensors pass

@@ -4,18 +4,25 @@ The functions here only marshal torch tensors into the C ABI of
 ``include/w4a16.h`` (pointers, sizes, the current HIP stream); every step of the
 computation runs in the library's HIP kernels.  Tensors must be contiguous and on
 the GPU.  bf16 data is passed as ``torch.bfloat16`` (or its bit pattern as
-``torch.int16`` / ``torch.uint16``).
+``torch.int16`` / ``torch.uint16``).  Every tensor's shape is checked against the
+others before anything is enqueued (the C ABI sees raw pointers and cannot); a
+mismatch raises ``ValueError``.
+
+Streams: with ``stream=s`` every tensor the binding allocates (outputs, routing
+tensors, a temporary workspace) is allocated and initialised on ``s`` itself, so it is
+ordered before the kernels and returns to the caching allocator on that stream.
 """
 
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 
 from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
 __all__ = ["rtn_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
-           "moe_w4a16_workspace_init", "new_workspace",
+           "moe_w4a16_workspace_init", "moe_w4a16_workspace_check", "new_workspace",
            "MoeCall", "w4a16_abi_version", "W4A16Error", "library_path"]
 
 GROUP = 128
@@ -66,6 +73,59 @@ def _stream(device, stream):
     return C.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which allocations and torch work go to ``stream`` (None: unchanged)."""
+    return _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_bits(bits, name="bits"):
+    if bits not in (4, 8):
+        raise ValueError(f"{name} = {bits}, must be 4 or 8")
+
+
+def _check_experts(w13, s13, w2, s2, bits, H):
+    """Shapes of a routed-expert bank for code width ``bits`` and hidden size ``H``:
+    returns (E, I)."""
+    _check_bits(bits)
+    if w13.dim() != 3 or w2.dim() != 3:
+        raise ValueError("w13 and w2 must be 3-D")
+    E, twoI = w13.shape[0], w13.shape[1]
+    if twoI % 2 or H % GROUP or (twoI // 2) % GROUP:
+        raise ValueError(f"H = {H} and I = {twoI / 2} must be multiples of {GROUP}")
+    I = twoI // 2
+    _shape(w13, "w13", (E, 2 * I, H * bits // 32))
+    _shape(s13, "s13", (E, 2 * I, H // GROUP))
+    _shape(w2, "w2", (E, H, I * bits // 32))
+    _shape(s2, "s2", (E, H, I // GROUP))
+    return E, I
+
+
+def _check_shared(shared, H, dev):
+    """Validates the shared-expert dict; returns (bits, intermediate size)."""
+    torch = _torch()
+    bf = _bf16_types()
+    for name in ("w13", "s13", "w2", "s2", "bits"):
+        if name not in shared:
+            raise ValueError(f"shared.{name} is required")
+    for name in ("w13", "s13", "w2", "s2"):
+        _need(shared[name], "shared." + name, (torch.int32,) if name[0] == "w" else bf, dev)
+    sb = shared["bits"]
+    _check_bits(sb, "shared.bits")
+    if shared["w13"].dim() != 2 or shared["w13"].shape[0] % (2 * GROUP):
+        raise ValueError("shared.w13 must be [2 * shared_I, H * bits / 32] with shared_I a multiple of 128")
+    sI = shared["w13"].shape[0] // 2
+    _shape(shared["w13"], "shared.w13", (2 * sI, H * sb // 32))
+    _shape(shared["s13"], "shared.s13", (2 * sI, H // GROUP))
+    _shape(shared["w2"], "shared.w2", (H, sI * sb // 32))
+    _shape(shared["s2"], "shared.s2", (H, sI // GROUP))
+    return sb, sI
+
+
 def rtn_quantize_pack(w, bits: int = 4, group: int = GROUP, packed=None, scales=None, stream=None):
     """Quantize ``w[..., rows, cols]`` (fp32 or bf16, on the GPU) with symmetric RTN.
 
@@ -75,15 +135,23 @@ def rtn_quantize_pack(w, bits: int = 4, group: int = GROUP, packed=None, scales=
     _need(w, "w", (torch.float32, torch.bfloat16))
     if w.dim() < 2:
         raise ValueError("w must have at least 2 dims")
+    _check_bits(bits)
+    if group != GROUP:
+        raise ValueError(f"group = {group}, only {GROUP} is supported")
     rows, cols = w.shape[-2], w.shape[-1]
+    if cols % GROUP:
+        raise ValueError(f"cols = {cols} is not a multiple of {GROUP}")
     n_mats = w.numel() // max(1, rows * cols) if rows * cols else 0
     lead = tuple(w.shape[:-1])
-    if packed is None:
-        packed = torch.empty(lead + (cols * bits // 32,), dtype=torch.int32, device=w.device)
-    if scales is None:
-        scales = torch.empty(lead + (cols // group if group else 0,), dtype=torch.bfloat16, device=w.device)
+    with _on(stream):
+        if packed is None:
+            packed = torch.empty(lead + (cols * bits // 32,), dtype=torch.int32, device=w.device)
+        if scales is None:
+            scales = torch.empty(lead + (cols // group,), dtype=torch.bfloat16, device=w.device)
     _need(packed, "packed", (torch.int32,), w.device)
     _need(scales, "scales", _bf16_types(), w.device)
+    _shape(packed, "packed", lead + (cols * bits // 32,))
+    _shape(scales, "scales", lead + (cols // group,))
     dt = _lib.W4A16_F32 if w.dtype == torch.float32 else _lib.W4A16_BF16
     st = _lib.lib().rtn_quantize_pack(_ptr(w), dt, n_mats, rows, cols, bits, group, _ptr(packed), _ptr(scales),
                                       _stream(w.device, stream))
@@ -115,11 +183,9 @@ def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, sha
 
 def moe_w4a16_workspace_size(T: int, H: int, I: int, E: int, top_k: int, shared_bits: int = 0,
                              shared_I: int = 0) -> int:
-    """Bytes of device workspace :func:`moe_w4a16_forward` needs for these shapes."""
-    a = MoeArgs()
-    a.T, a.H, a.I, a.E, a.top_k, a.bits, a.group = T, H, I, E, top_k, 4, GROUP
-    a.shared_bits, a.shared_I = shared_bits, shared_I
-    n = _lib.lib().moe_w4a16_workspace_size(C.byref(a))
+    """Bytes of device workspace :func:`moe_w4a16_forward` needs for these shapes
+    (``shared_I`` counts only when ``shared_bits`` is non-zero)."""
+    n = _lib.lib().moe_w4a16_workspace_size(T, H, I, E, top_k, shared_I if shared_bits else 0)
     if n == 0:
         raise W4A16Error(_lib.W4A16_ERR_INVALID_ARG, "moe_w4a16_workspace_size", _lib.last_error())
     return n
@@ -136,11 +202,27 @@ def moe_w4a16_workspace_init(workspace, stream=None):
     return workspace
 
 
-def new_workspace(nbytes: int, device):
-    """A device workspace of ``nbytes`` bytes ready for :func:`moe_w4a16_forward`."""
+def moe_w4a16_workspace_check(workspace, stream=None) -> bool:
+    """Synchronise ``stream`` and report whether a single-launch wait timed out on this
+    workspace since the last check (True: it did, and the head has been reset; the
+    outputs of the forwards since then hold NaN rows).  Never raises for a time-out."""
     torch = _torch()
-    return moe_w4a16_workspace_init(torch.empty((max(int(nbytes), _lib.WORKSPACE_HEAD_BYTES),), dtype=torch.uint8,
-                                                device=device))
+    _need(workspace, "workspace", (torch.uint8,))
+    st = _lib.lib().moe_w4a16_workspace_check(C.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                              _stream(workspace.device, stream))
+    if st == _lib.W4A16_ERR_TIMEOUT:
+        return True
+    _lib.check(st, "moe_w4a16_workspace_check")
+    return False
+
+
+def new_workspace(nbytes: int, device, stream=None):
+    """A device workspace of ``nbytes`` bytes ready for :func:`moe_w4a16_forward`,
+    allocated and initialised on ``stream`` (default: the current stream)."""
+    torch = _torch()
+    with _on(stream):
+        ws = torch.empty((max(int(nbytes), _lib.WORKSPACE_HEAD_BYTES),), dtype=torch.uint8, device=device)
+        return moe_w4a16_workspace_init(ws)
 
 
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,
@@ -163,53 +245,61 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
     for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, bf), ("w2", w2, (torch.int32,)),
                         ("s2", s2, bf)):
         _need(t, name, dt, dev)
-    if x.dim() != 2 or w13.dim() != 3 or w2.dim() != 3:
-        raise ValueError("x must be 2-D and w13, w2 3-D")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [T, H]")
     T, H = x.shape
-    E = w13.shape[0]
-    I = w13.shape[1] // 2
+    E, I = _check_experts(w13, s13, w2, s2, bits, H)
+    if not 1 <= top_k <= E:
+        raise ValueError(f"top_k = {top_k} not in [1, E = {E}]")
     if router_logits is not None:
         _need(router_logits, "router_logits", (torch.float32,), dev)
-        if tuple(router_logits.shape) != (T, E):
-            raise ValueError("router_logits must be [T, E]")
+        _shape(router_logits, "router_logits", (T, E))
     else:
         _need(topk_ids, "topk_ids", (torch.int32,), dev)
         _need(topk_w, "topk_w", (torch.float32,), dev)
+        _shape(topk_ids, "topk_ids", (T, top_k))
+        _shape(topk_w, "topk_w", (T, top_k))
+    sb = sI = 0
     if shared is not None:
-        for name in ("w13", "s13", "w2", "s2"):
-            _need(shared[name], "shared." + name, (torch.int32,) if name[0] == "w" else bf, dev)
+        sb, sI = _check_shared(shared, H, dev)
     if residual is not None:
         _need(residual, "residual", bf, dev)
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    _need(out, "out", bf, dev)
+        _shape(residual, "residual", (T, H))
+    if out is not None:
+        _need(out, "out", bf, dev)
+        _shape(out, "out", (T, H))
+    need = moe_w4a16_workspace_size(T, H, I, E, top_k, sb, sI) if T > 0 else 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     routing = {}
     counts = offsets = sorted_pairs = None
-    if routing_out:
-        if router_logits is not None:
-            topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-            topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-        counts = torch.empty((E,), dtype=torch.int32, device=dev)
-        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-        sorted_pairs = torch.empty((T * top_k,), dtype=torch.int32, device=dev)
-        routing = dict(ids=topk_ids, w=topk_w, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
-    if workspace is None:
-        sb = shared["bits"] if shared is not None else 0
-        sI = shared["w13"].shape[0] // 2 if shared is not None else 0
-        n = moe_w4a16_workspace_size(T, H, I, E, top_k, sb, sI) if T > 0 else 0
-        workspace = torch.zeros((max(n, 1),), dtype=torch.uint8, device=dev)   # zero head: see workspace_init
-    a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
-              counts, offsets, sorted_pairs, workspace)
-    if _timed is None:
-        st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, stream))
-        _lib.check(st, "moe_w4a16_forward")
-    else:
-        n = C.c_int(0)
-        ms = (C.c_float * 16)()
-        names = (C.c_char_p * 16)()
-        st = _lib.lib().moe_w4a16_forward_timed(C.byref(a), _stream(dev, stream), 16, ms, names, C.byref(n))
-        _lib.check(st, "moe_w4a16_forward_timed")
-        _timed.extend((names[i].decode(), float(ms[i])) for i in range(n.value))
+    with _on(stream):   # everything allocated here is ordered before the kernels on `stream`
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        if routing_out:
+            if router_logits is not None:
+                topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+                topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+            counts = torch.empty((E,), dtype=torch.int32, device=dev)
+            offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+            sorted_pairs = torch.empty((T * top_k,), dtype=torch.int32, device=dev)
+            routing = dict(ids=topk_ids, w=topk_w, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
+        if workspace is None:
+            workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)   # zero head: see workspace_init
+        a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
+                  counts, offsets, sorted_pairs, workspace)
+        if _timed is None:
+            st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, None))
+            _lib.check(st, "moe_w4a16_forward")
+        else:
+            n = C.c_int(0)
+            ms = (C.c_float * 16)()
+            names = (C.c_char_p * 16)()
+            st = _lib.lib().moe_w4a16_forward_timed(C.byref(a), _stream(dev, None), 16, ms, names, C.byref(n))
+            _lib.check(st, "moe_w4a16_forward_timed")
+            _timed.extend((names[i].decode(), float(ms[i])) for i in range(n.value))
     return (out, routing) if routing_out else out
 
 
@@ -224,9 +314,8 @@ def moe_w4a16_forward_timed(*args, **kwargs):
 class MoeCall:
     """A prepared :func:`moe_w4a16_forward` for repeated calls with fixed shapes, weights
     and workspace (a decode loop): everything is validated once here, and each call
-    only sets the per-call pointers (activations, logits, residual, output) before
-    calling the library.  Tensors passed per call must have the shapes, dtypes and
-    device given at construction.
+    checks only the per-call tensors' shapes and sets their pointers (activations,
+    logits or ids, residual, output) before calling the library.
     """
 
     def __init__(self, x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, shared=None, workspace=None,
@@ -238,28 +327,47 @@ class MoeCall:
         for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, bf), ("w2", w2, (torch.int32,)),
                             ("s2", s2, bf)):
             _need(t, name, dt, dev)
+        if x.dim() != 2:
+            raise ValueError("x must be 2-D [T, H]")
         self.T, self.H = x.shape
-        self.E, self.top_k = w13.shape[0], top_k
-        sb = shared["bits"] if shared is not None else 0
-        sI = shared["w13"].shape[0] // 2 if shared is not None else 0
+        self.E, I = _check_experts(w13, s13, w2, s2, bits, self.H)
+        if not 1 <= top_k <= self.E:
+            raise ValueError(f"top_k = {top_k} not in [1, E = {self.E}]")
+        self.top_k = top_k
+        sb = sI = 0
         if shared is not None:
-            for name in ("w13", "s13", "w2", "s2"):
-                _need(shared[name], "shared." + name, (torch.int32,) if name[0] == "w" else bf, dev)
-        need = moe_w4a16_workspace_size(self.T, self.H, w13.shape[1] // 2, self.E, top_k, sb, sI)
+            sb, sI = _check_shared(shared, self.H, dev)
+        need = moe_w4a16_workspace_size(self.T, self.H, I, self.E, top_k, sb, sI)
         if workspace is None:
-            workspace = new_workspace(need, dev)
+            workspace = new_workspace(need, dev, stream)
         _need(workspace, "workspace", (torch.uint8,), dev)
         if workspace.numel() < need:
             raise ValueError(f"workspace needs {need} bytes")
         self._keep = (w13, s13, w2, s2, shared, workspace)
+        self.workspace = workspace
         self.args = _args(x, w13, s13, w2, s2, top_k, bits, None, None, None, shared, None, None, None, None, None,
                           workspace)
         self.device = dev
         self.stream = None if stream is None else _stream(dev, stream)   # None: the current stream per call
         self._fn = _lib.lib().moe_w4a16_forward
         self._ref = C.byref(self.args)
+        self._th = (self.T, self.H)
+        self._tk = (self.T, self.top_k)
+        self._te = (self.T, self.E)
 
     def __call__(self, x, out, router_logits=None, topk_ids=None, topk_w=None, residual=None):
+        torch = _torch()
+        if (x.shape != self._th or out.shape != self._th or x.element_size() != 2 or out.element_size() != 2
+                or not (x.is_contiguous() and out.is_contiguous())):
+            raise ValueError(f"x and out must be contiguous 16-bit {self._th}")
+        if router_logits is not None:
+            if router_logits.shape != self._te or router_logits.dtype != torch.float32:
+                raise ValueError(f"router_logits must be fp32 {self._te}")
+        elif (topk_ids is None or topk_w is None or topk_ids.shape != self._tk or topk_w.shape != self._tk
+              or topk_ids.dtype != torch.int32 or topk_w.dtype != torch.float32):
+            raise ValueError(f"topk_ids (int32) and topk_w (fp32) must be {self._tk} when router_logits is None")
+        if residual is not None and (residual.shape != self._th or residual.element_size() != 2):
+            raise ValueError(f"residual must be 16-bit {self._th}")
         a = self.args
         a.x = x.data_ptr()
         a.y = out.data_ptr()

@@ -12,14 +12,16 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 WORKSPACE_HEAD_BYTES = 147456   # W4A16_WORKSPACE_HEAD_BYTES
+WORKSPACE_ERROR_OFFSET = 12928  # W4A16_WORKSPACE_ERROR_OFFSET
 
 W4A16_OK = 0
 W4A16_ERR_INVALID_ARG = 1
 W4A16_ERR_UNSUPPORTED = 2
 W4A16_ERR_WORKSPACE = 3
 W4A16_ERR_HIP = 4
+W4A16_ERR_TIMEOUT = 5
 
 W4A16_F32 = 0
 W4A16_BF16 = 1
@@ -31,6 +33,7 @@ EXPORTED = (
     "rtn_quantize_pack",
     "moe_w4a16_workspace_size",
     "moe_w4a16_workspace_init",
+    "moe_w4a16_workspace_check",
     "moe_w4a16_forward",
     "moe_w4a16_forward_timed",
 )
@@ -83,9 +86,11 @@ def lib():
     L.rtn_quantize_pack.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int,
                                     C.c_void_p, C.c_void_p, C.c_void_p]
     L.moe_w4a16_workspace_size.restype = C.c_size_t
-    L.moe_w4a16_workspace_size.argtypes = [C.POINTER(MoeArgs)]
+    L.moe_w4a16_workspace_size.argtypes = [C.c_int64] * 6
     L.moe_w4a16_workspace_init.restype = C.c_int
     L.moe_w4a16_workspace_init.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p]
+    L.moe_w4a16_workspace_check.restype = C.c_int
+    L.moe_w4a16_workspace_check.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p]
     L.moe_w4a16_forward.restype = C.c_int
     L.moe_w4a16_forward.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
     L.moe_w4a16_forward_timed.restype = C.c_int

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/w4a16.h: argument validation, workspace
-// layout and kernel dispatch.  Nothing here allocates device memory or synchronises.
+// layout and kernel dispatch.  Nothing here allocates device memory; only the timed forward
+// and the workspace check synchronise (both documented as doing so).
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -294,6 +295,7 @@ const char* w4a16_status_string(int status) {
         case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED";
         case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE";
         case W4A16_ERR_HIP: return "W4A16_ERR_HIP";
+        case W4A16_ERR_TIMEOUT: return "W4A16_ERR_TIMEOUT";
         default: return "W4A16_UNKNOWN_STATUS";
     }
 }
@@ -320,9 +322,37 @@ int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, 
                       "rtn_quantize_pack launch");
 }
 
-size_t moe_w4a16_workspace_size(const moe_w4a16_args* args) {
-    if (check_shapes(args) != W4A16_OK) return 0;
-    return layout(args).total;
+size_t moe_w4a16_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t shared_I) {
+    g_last_error.clear();
+    if (shared_I < 0) {
+        fail(W4A16_ERR_INVALID_ARG, "shared_I = %lld < 0", (long long)shared_I);
+        return 0;
+    }
+    moe_w4a16_args a{};
+    a.T = T, a.H = H, a.I = I, a.E = E, a.top_k = top_k;
+    a.bits = 4, a.group = kGroup;
+    a.shared_bits = shared_I ? 8 : 0, a.shared_I = shared_I;
+    if (check_shapes(&a) != W4A16_OK) return 0;
+    return layout(&a).total;
+}
+
+int moe_w4a16_workspace_check(void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (!workspace) return fail(W4A16_ERR_INVALID_ARG, "NULL workspace");
+    if (!aligned16(workspace)) return fail(W4A16_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (workspace_bytes < kHeadBytes)
+        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes is smaller than its head (%zu)", workspace_bytes,
+                    kHeadBytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize")) return st;
+    uint32_t word = 0;
+    const char* p = static_cast<const char*>(workspace) + W4A16_WORKSPACE_ERROR_OFFSET;
+    if (int st = hip_status(hipMemcpy(&word, p, sizeof(word), hipMemcpyDeviceToHost), "reading the time-out word"))
+        return st;
+    if (word == 0) return W4A16_OK;
+    if (int st = hip_status(launch_head_init(static_cast<uint32_t*>(workspace), s), "workspace head reset")) return st;
+    if (int st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize")) return st;
+    return fail(W4A16_ERR_TIMEOUT, "a single-launch wait timed out on this workspace; its head has been reset");
 }
 
 int moe_w4a16_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -340,6 +370,7 @@ int moe_w4a16_forward(const moe_w4a16_args* a, void* stream) {
     g_last_error.clear();
     return forward_impl(a, stream, nullptr);
 }
+
 
 int moe_w4a16_forward_timed(const moe_w4a16_args* a, void* stream, int max_kernels, float* kernel_ms,
                             const char** kernel_names, int* n_kernels) {

@@ -167,6 +167,7 @@ constexpr size_t kTagBytes = 131072;
 constexpr size_t kHeadBytes = kSyncBytes + kTagBytes;
 static_assert(kHeadBytes == W4A16_WORKSPACE_HEAD_BYTES, "workspace head size");
 constexpr int kSyncGroup = 80, kSyncTop = 100, kSyncError = 101, kSyncEpoch = 102, kSyncRoute = 103;
+static_assert(kSyncError * 32 * 4 == W4A16_WORKSPACE_ERROR_OFFSET, "time-out word offset");
 __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return sync + i * 32; }
 
 struct WsLayout {

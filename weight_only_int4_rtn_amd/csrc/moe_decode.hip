@@ -674,8 +674,8 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
 // T * k + token), waiting for every 16-byte chunk until all four of its words carry `tag`,
 // and stages them in `stage` ([rows_a, Ws] bf16); then the sum of each (row, group) into
 // xs.  Units cover disjoint (row, group) ranges, so no other wave touches them.
-__device__ void tiny_collect_unit(const TinyArgs& a, const TinyRoute& r, const TinyUnit& t, uint32_t tag,
-                                  uint16_t* stage, int Ws, float* xs, int G) {
+__device__ bool tiny_collect_unit(const TinyArgs& a, const TinyRoute& r, const TinyUnit& t, uint32_t tag,
+                                  uint16_t* stage, int Ws, float* xs, int G, int spin_limit) {
     const int lane = threadIdx.x & 63;
     const int W = (int)a.width_a;
     const int cg = t.ngroups * (kGroup / 4);   // chunks of 4 values per row in the unit's groups
@@ -712,7 +712,7 @@ __device__ void tiny_collect_unit(const TinyArgs& a, const TinyRoute& r, const T
                 }
             }
             if (!pending) break;
-            if (spins >= kTinySpinLimit) {
+            if (spins >= spin_limit) {
                 timed_out = true;
                 break;
             }
@@ -736,15 +736,17 @@ __device__ void tiny_collect_unit(const TinyArgs& a, const TinyRoute& r, const T
         sum += __shfl_xor(sum, 1, 16);
         if ((lane & 15) == 0) xs[row * G + g] = sum;
     }
+    return timed_out;
 }
 
 template <int BITS, int SBITS>
 __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, uint32_t epoch_word) {
     __shared__ int s_last;
+    __shared__ int s_bad;   // a wait of this workgroup timed out, or an earlier call's did
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int d = blockIdx.x, n_dk = (int)(a.H / 16);
     const int h0 = d * 16;
-    const int T = a.T, Tk = T * a.k;
+    const int T = a.T;
     const int W = (int)a.width_a, G = W / kGroup, Ws = W + kTinyPad;
     float* yacc = s_dyn + wave * T * 16;                                       // [waves][T][16]
     uint16_t* stage = reinterpret_cast<uint16_t*>(s_dyn + kDkWaves * T * 16);   // [rows_a][Ws] a rows
@@ -752,6 +754,9 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     float* xs = reinterpret_cast<float*>(zb + 512);                            // [rows_a][G] group sums
     for (int i = lane; i < T * 16; i += 64) yacc[i] = 0.f;
     if (threadIdx.x < 64) *reinterpret_cast<u32x4_t*>(zb + 8 * threadIdx.x) = u32x4_t{0u, 0u, 0u, 0u};
+    // a set time-out word (this workspace's earlier call): no waiting, NaN rows out
+    if (threadIdx.x == 0)
+        s_bad = __hip_atomic_load(sync_word(a.sync, kSyncError), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
     // the residual of this thread's output (T * 16 <= blockDim.x), loaded now, off the tail
     float res_pre = 0.f;
     if (a.residual && (int)threadIdx.x < T * 16)
@@ -783,8 +788,10 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     // each wave waits for the a values of its own units only, unit by unit, so a wave whose
     // experts are done early computes while later ranks are still in flight
     const uint32_t tag = (epoch_word + 1) << 16;
+    const int spin_limit = s_bad ? 0 : kTinySpinLimit;   // (s_bad is read after the barrier above)
+    bool bad = false;
     while (u < n_units) {
-        tiny_collect_unit(a, r, cu, tag, stage, Ws, xs, G);
+        bad |= tiny_collect_unit(a, r, cu, tag, stage, Ws, xs, G, spin_limit);
         if (cbits == BITS) tiny_unit<BITS>(cu, cc, stage, xs, Ws, G, zb, r, yacc);
         else if constexpr (SBITS != 0 && SBITS != BITS) tiny_unit<SBITS>(cu, cs, stage, xs, Ws, G, zb, r, yacc);
         u += V;
@@ -799,6 +806,7 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
             else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
         }
     }
+    if (bad) s_bad = 1;   // (benign race: every writer stores 1)
     __syncthreads();
     // every wave is done with the tag area: count this workgroup's exit now, so that the
     // atomic's round trip overlaps the sum below (groups of 16; the last workgroup resets
@@ -811,12 +819,13 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
                  __hip_atomic_fetch_add(sync_word(a.sync, kSyncTop), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      (uint32_t)ng - 1;
     }
+    const bool poison = s_bad != 0;
     for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
         float s = res_pre;
 #pragma unroll
         for (int w = 0; w < kDkWaves; ++w) s += s_dyn[w * T * 16 + i];
         const int t = i >> 4, n = i & 15;
-        a.y[(int64_t)t * a.H + h0 + n] = (uint16_t)cvt_bf16(s);
+        a.y[(int64_t)t * a.H + h0 + n] = poison ? (uint16_t)0x7fc0u : (uint16_t)cvt_bf16(s);
     }
     __syncthreads();
     if (s_last) {
