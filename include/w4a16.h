@@ -213,6 +213,32 @@ int moe_w4a16_workspace_check(void* workspace, size_t workspace_bytes, void* str
 int moe_w4a16_forward(const moe_w4a16_args* args, void* stream);
 
 /*
+ * moe_w4a16_forward_noalloc - moe_w4a16_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): it allocates nothing, directly or through any library.
+ *
+ * args->workspace and args->workspace_bytes are ignored.  The scratch is instead one
+ * static device array of W4A16_NOALLOC_SCRATCH_BYTES per GPU, in the library's code
+ * object, held by each GPU the library runs on until the process ends.  Its address is
+ * taken on the first call on each device, which also zeroes its head with a small fill
+ * kernel on `stream` (as moe_w4a16_workspace_init does for a caller's workspace).
+ * Shapes whose moe_w4a16_workspace_size exceeds that size return W4A16_ERR_UNSUPPORTED
+ * before anything is enqueued (64 MiB holds the full 256-expert, hidden-2048 layer up to
+ * 64 decode tokens, or about 1000 prefill tokens, with a shared expert).
+ *
+ * Every call on one GPU shares that GPU's array and finds the previous call's contents
+ * in it: calls that may overlap on one GPU (different streams, no ordering between them)
+ * race and must not be made.  This entry point never takes the single-launch path of
+ * tiny batches (whose workgroups wait on each other), so no time-out state can arise in
+ * the shared array; tiny batches run on the streaming decode kernels instead, and the
+ * output agrees with moe_w4a16_forward's to the tolerance of the path, bit for bit
+ * whenever both take the same kernels (T * top_k > 16).  Other arguments, results and
+ * errors are those of moe_w4a16_forward.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_w4a16_forward_noalloc(const moe_w4a16_args* args, void* stream);
+
+/*
  * moe_w4a16_forward_timed - the same work as moe_w4a16_forward, each kernel launched with
  * a start and a stop HIP event bound to its own dispatch (hipExtLaunchKernelGGL), then a
  * wait for the last stop event (this call synchronises with the stream's work up to that

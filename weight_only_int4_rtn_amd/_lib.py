@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 ABI_VERSION = 4
 WORKSPACE_HEAD_BYTES = 147456   # W4A16_WORKSPACE_HEAD_BYTES
 WORKSPACE_ERROR_OFFSET = 12928  # W4A16_WORKSPACE_ERROR_OFFSET
+NOALLOC_SCRATCH_BYTES = 64 << 20  # W4A16_NOALLOC_SCRATCH_BYTES
 
 W4A16_OK = 0
 W4A16_ERR_INVALID_ARG = 1
@@ -36,6 +37,7 @@ EXPORTED = (
     "moe_w4a16_workspace_check",
     "moe_w4a16_forward",
     "moe_w4a16_forward_timed",
+    "moe_w4a16_forward_noalloc",
 )
 
 
@@ -93,6 +95,8 @@ def lib():
     L.moe_w4a16_workspace_check.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p]
     L.moe_w4a16_forward.restype = C.c_int
     L.moe_w4a16_forward.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
+    L.moe_w4a16_forward_noalloc.restype = C.c_int
+    L.moe_w4a16_forward_noalloc.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
     L.moe_w4a16_forward_timed.restype = C.c_int
     L.moe_w4a16_forward_timed.argtypes = [C.POINTER(MoeArgs), C.c_void_p, C.c_int, C.POINTER(C.c_float),
                                           C.POINTER(C.c_char_p), C.POINTER(C.c_int)]

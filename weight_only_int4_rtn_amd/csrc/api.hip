@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -114,7 +115,7 @@ WsLayout layout(const moe_w4a16_args* a) {
     return L;
 }
 
-int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
+int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool allow_single_launch = true) {
     if (int st = check_shapes(a)) return st;
     if (a->T == 0) return W4A16_OK;
     if (!a->x || !a->w13 || !a->s13 || !a->w2 || !a->s2 || !a->y)
@@ -168,7 +169,8 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     const size_t tag_bytes = (size_t)L.rows_a * L.width_a * 4;
     const size_t tiny_lds = 8 * (size_t)a->T * 16 * 4 + (size_t)L.rows_a * (L.width_a + kTinyPad) * 2 + 1024 +
                             (size_t)L.rows_a * (L.width_a / kGroup) * 4;
-    if (a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes && tiny_lds <= kTinyMaxLds &&
+    if (allow_single_launch && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
+        tiny_lds <= kTinyMaxLds &&
         a->H / 16 <= tiny_max_down_workgroups(a->bits, a->shared_bits)) {
         TinyArgs d{};
         d.x = a->x;
@@ -282,6 +284,38 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer) {
     return hip_status(launch_prefill(p, s, timer), "prefill launch");
 }
 
+// ------------------------------------------------------------ allocation-free entry point
+//
+// The scratch of moe_w4a16_forward_noalloc: one array per GPU, in the code object, held
+// until the process ends.  Host code never passes `scratch` itself (on the host it names a
+// stand-in, not device memory): each device's address comes from hipGetSymbolAddress,
+// taken once with that device current, and only that address reaches kernels.
+static __device__ __align__(256) char scratch[W4A16_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's scratch address; on first use per device also zeroes its workspace
+// head on `s` (a fill kernel, so a captured first call stays valid on replay).
+int scratch_for_current_device(hipStream_t s, void** out) {
+    int dev = -1;
+    if (int st = hip_status(hipGetDevice(&dev), "hipGetDevice")) return st;
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4A16_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    std::call_once(g_scratch_once[dev], [&] {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e == hipSuccess) e = launch_head_init(static_cast<uint32_t*>(p), s);
+        g_scratch_err[dev] = e;
+        g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return hip_status(g_scratch_err[dev], "setting up the static scratch");
+    *out = g_scratch_ptr[dev];
+    return W4A16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +405,21 @@ int moe_w4a16_forward(const moe_w4a16_args* a, void* stream) {
     return forward_impl(a, stream, nullptr);
 }
 
+int moe_w4a16_forward_noalloc(const moe_w4a16_args* a, void* stream) {
+    g_last_error.clear();
+    if (int st = check_shapes(a)) return st;
+    if (a->T == 0) return W4A16_OK;
+    const size_t need = layout(a).total;
+    if (need > (size_t)W4A16_NOALLOC_SCRATCH_BYTES)
+        return fail(W4A16_ERR_UNSUPPORTED, "these shapes need %zu bytes of scratch, the static scratch holds %zu", need,
+                    (size_t)W4A16_NOALLOC_SCRATCH_BYTES);
+    void* ptr = nullptr;
+    if (int st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ptr)) return st;
+    moe_w4a16_args b = *a;
+    b.workspace = ptr;
+    b.workspace_bytes = W4A16_NOALLOC_SCRATCH_BYTES;
+    return forward_impl(&b, stream, nullptr, /*allow_single_launch=*/false);
+}
 
 int moe_w4a16_forward_timed(const moe_w4a16_args* a, void* stream, int max_kernels, float* kernel_ms,
                             const char** kernel_names, int* n_kernels) {
