@@ -15,7 +15,8 @@ computes, written from the model-card pages this project follows:
 * page "Nex-N2.5-mini FP8 W8A8 with Calibrated FP8 KV Scales", section Artifact
   summary: 256 routed experts, 8 active per token;
 * the same Int4-Int8Mix page, Recipe table: each routed expert is a
-  gate_proj / up_proj / down_proj triple (a SwiGLU MLP).
+  gate_proj / up_proj / down_proj triple (a SwiGLU MLP); the router
+  (``mlp.gate``) and the ``shared_expert_gate`` stay BF16.
 
 Where the pages leave a step open, the reading taken is stated at the function.
 """
@@ -31,6 +32,8 @@ from .rtn_moe import (  # noqa: F401
     quantize_pack,
     dequantize,
     route,
+    router_logits,
+    shared_gate,
     expert_ffn,
     moe_ffn,
     moe_layer,

@@ -205,6 +205,45 @@ def route(logits, k: int):
 
 
 # ---------------------------------------------------------------------------
+# Router and shared-expert gate (kept in BF16)
+# ---------------------------------------------------------------------------
+
+def router_logits(x_bits, wr_bits):
+    """Router logits ``l[t, e] = sum_h x[t, h] * Wr[e, h]``, fp64.
+
+    Page "Nex-N2.5-mini Int4-Int8Mix", Recipe table: the routers (``mlp.gate``)
+    are left in BF16; page "Nex-N2.5-mini FP8 W8A8 with Calibrated FP8 KV Scales",
+    "Components retained at source precision": MoE routers.  So the router is a
+    plain bf16 linear map ``[E, H]`` applied to the bf16 activation; both are
+    widened exactly and the sum is taken in fp64.
+
+    ``x_bits`` uint16 bf16 ``[T, H]``; ``wr_bits`` uint16 bf16 ``[E, H]``.
+    Returns fp64 ``[T, E]``.
+    """
+    x = f32_from_bf16_bits(x_bits).astype(np.float64)
+    wr = f32_from_bf16_bits(wr_bits).astype(np.float64)
+    return x @ wr.T
+
+
+def shared_gate(x_bits, wg_bits):
+    """Shared-expert gate ``g[t] = sigmoid(sum_h x[t, h] * wg[h])``, fp64.
+
+    The same two pages keep ``shared_expert_gate`` in BF16 next to the router.
+    The pages name the gate but not its function; the reading taken is the
+    plainest one for a single-output gate on a residual branch: a bf16 linear
+    map ``[1, H]`` followed by the logistic sigmoid ``1 / (1 + exp(-z))``, whose
+    value scales the shared expert's output for that token.
+
+    ``x_bits`` uint16 bf16 ``[T, H]``; ``wg_bits`` uint16 bf16 ``[H]``.
+    Returns fp64 ``[T]``.
+    """
+    x = f32_from_bf16_bits(x_bits).astype(np.float64)
+    wg = f32_from_bf16_bits(wg_bits).astype(np.float64)
+    z = x @ wg
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# ---------------------------------------------------------------------------
 # Expert MLP and the routed sum
 # ---------------------------------------------------------------------------
 
@@ -229,7 +268,7 @@ def expert_ffn(x, w13, w2):
 
 
 def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
-            shared=None, residual_bits=None):
+            shared=None, residual_bits=None, shared_gate=None):
     """Router-weighted sum of the selected W4A16 experts, fp64.
 
     ``y_t = sum_j w[t,j] * FFN_{ids[t,j]}(x_t)`` over the slots in order, then
@@ -242,7 +281,9 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
     ``w2`` int32 ``[E, H, I*bits/32]`` with scales ``s2`` ``[E, H, I/128]``.
     ``tokens`` restricts the output to those token indices (default: all).
     ``shared`` is a dict with keys ``w13, s13, w2, s2, bits`` (one expert,
-    leading axis absent).  Returns fp64 ``[len(tokens), H]``.
+    leading axis absent); ``shared_gate`` (``[T]``, see :func:`shared_gate`)
+    scales its output per token instead of the weight 1.  Returns fp64
+    ``[len(tokens), H]``.
     """
     x = f32_from_bf16_bits(x_bits).astype(np.float64)
     T, k = ids.shape
@@ -271,16 +312,19 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
     if shared is not None:
         S13 = dequantize(shared["w13"], shared["s13"], shared["bits"]).astype(np.float64)
         S2 = dequantize(shared["w2"], shared["s2"], shared["bits"]).astype(np.float64)
-        y += expert_ffn(x[tokens].T, S13, S2).T
+        ys = expert_ffn(x[tokens].T, S13, S2).T
+        if shared_gate is not None:
+            ys = np.asarray(shared_gate, dtype=np.float64)[tokens][:, None] * ys
+        y += ys
     if residual_bits is not None:
         y += f32_from_bf16_bits(residual_bits).astype(np.float64)[tokens]
     return y
 
 
 def moe_layer(x_bits, logits, k: int, w13, s13, w2, s2, bits: int, tokens=None,
-              shared=None, residual_bits=None):
+              shared=None, residual_bits=None, shared_gate=None):
     """Routing followed by the routed sum: ``(y fp64, route outputs)``."""
     r = route(logits, k)
     y = moe_ffn(x_bits, r[0], r[1], w13, s13, w2, s2, bits, tokens=tokens,
-                shared=shared, residual_bits=residual_bits)
+                shared=shared, residual_bits=residual_bits, shared_gate=shared_gate)
     return y, r

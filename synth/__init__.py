@@ -14,7 +14,9 @@ Seeds are tuples fed to ``numpy.random.default_rng``:
 
 * weights ``(2026, group, layer, expert, tensor)`` with tensor 0 = gate,
   1 = up, 2 = down, 3/4/5 = shared gate/up/down, so one expert can be
-  regenerated without the rest of the layer;
+  regenerated without the rest of the layer; 6 = the router ``[E, H]`` and
+  7 = the shared-expert gate ``[H]`` (expert 0), both N(0, 1/H) so that the
+  logits of N(0, 1) activations are about N(0, 1), rounded to bf16;
 * activations ``(2026, cfg, 10)``;
 * logits ``(2026, cfg, 11, layer, iteration)``.
 
@@ -32,7 +34,7 @@ import numpy as np
 SEED = 2026
 WEIGHT_STD = 0.02
 
-GATE, UP, DOWN, SHARED_GATE, SHARED_UP, SHARED_DOWN = range(6)
+GATE, UP, DOWN, SHARED_GATE, SHARED_UP, SHARED_DOWN, ROUTER, SHARED_GATE_W = range(8)
 
 
 @dataclass(frozen=True)
@@ -95,6 +97,21 @@ def layer_weights(group: int, layer: int, E: int, H: int, I: int):
     w13 = np.stack([expert_w13(group, layer, e, H, I) for e in range(E)])
     w2 = np.stack([expert_w2(group, layer, e, H, I) for e in range(E)])
     return w13, w2
+
+
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def router_weight_bf16(group: int, layer: int, E: int, H: int) -> np.ndarray:
+    """Router ``[E, H]``, N(0, 1/H) fp32 rounded to bf16 (uint16 bit patterns)."""
+    return _bf16_bits(_normal((SEED, group, layer, 0, ROUTER), (E, H), float(H) ** -0.5))
+
+
+def shared_gate_weight_bf16(group: int, layer: int, H: int) -> np.ndarray:
+    """Shared-expert gate ``[H]``, N(0, 1/H) fp32 rounded to bf16 (uint16 bit patterns)."""
+    return _bf16_bits(_normal((SEED, group, layer, 0, SHARED_GATE_W), (H,), float(H) ** -0.5))
 
 
 def activations_f32(cfg: int, T: int, H: int, stream: int = 10) -> np.ndarray:
