@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 4
+#define W4A16_ABI_VERSION 5
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -107,7 +107,8 @@ int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, 
  * The gate/up bank of expert e is one [2I, H] matrix: rows [0, I) are gate_proj, rows
  * [I, 2I) up_proj (the split of the fused gate_up_proj bank in the Int4-Int8Mix Recipe).
  *
- * Routing (router_logits != NULL): for each token the top_k largest fp32 logits are
+ * Routing (router_logits != NULL, or router_w != NULL and the logits computed from x,
+ * see the last fields): for each token the top_k largest fp32 logits are
  * chosen (equal logits: lower expert index first; slot j = j-th chosen) and weighted by
  * the softmax over all E logits renormalised over the chosen ones.  With
  * router_logits == NULL, topk_ids / topk_w are read as inputs instead (ids must be in
@@ -117,7 +118,8 @@ int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, 
  * row whose logits are all -inf (its weights are not defined).
  *
  * Output: y[t] = residual[t] + sum_j w[t,j] * down_e( SiLU(gate_e x_t) * up_e x_t )
- *              + shared( x_t )                        (e = topk_ids[t,j])
+ *              + g[t] * shared( x_t )                 (e = topk_ids[t,j]; g = 1 without
+ *                                                       shared_gate_w)
  * accumulated in fp32 and rounded once to bf16 (residual and shared terms only when
  * given).  The shared expert, when shared_bits != 0, is one always-on expert of
  * intermediate size shared_I with weight 1 (the Int4-Int8Mix Recipe keeps one shared
@@ -154,6 +156,16 @@ typedef struct moe_w4a16_args {
                                    /* that may overlap on the GPU need workspaces of their  */
                                    /* own                                                    */
     size_t workspace_bytes;
+    /* Router and shared-expert gate in bf16 (Int4-Int8Mix Recipe table: routers and
+     * shared_expert_gate stay BF16).  With router_w the logits are computed from x,
+     * logit[t, e] = sum_h x[t, h] * router_w[e, h] (fp32 accumulation), and router_logits
+     * must be NULL; the routing then proceeds as above.  With shared_gate_w the shared
+     * expert's output for token t is scaled by g[t] = 1 / (1 + exp(-sum_h x[t, h] *
+     * shared_gate_w[h])) instead of 1 (needs shared_bits != 0). */
+    const uint16_t* router_w;      /* bf16 [E, H], or NULL                                  */
+    const uint16_t* shared_gate_w; /* bf16 [H], or NULL                                     */
+    float* logits_out;             /* optional out, fp32 [T, E]: logits from router_w       */
+    float* shared_gate_out;        /* optional out, fp32 [T]: g from shared_gate_w          */
 } moe_w4a16_args;
 
 /* Device workspace bytes moe_w4a16_forward needs for T tokens, hidden H, intermediate I,

@@ -160,7 +160,8 @@ def rtn_quantize_pack(w, bits: int = 4, group: int = GROUP, packed=None, scales=
 
 
 def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
-          counts, offsets, sorted_pairs, workspace):
+          counts, offsets, sorted_pairs, workspace, router_w=None, shared_gate_w=None, logits_out=None,
+          gate_out=None):
     a = MoeArgs()
     T, H = x.shape
     E, twoI = w13.shape[0], w13.shape[1]
@@ -178,6 +179,8 @@ def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, sha
     a.expert_counts, a.expert_offsets, a.sorted_pairs = _ptr(counts), _ptr(offsets), _ptr(sorted_pairs)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.router_w, a.shared_gate_w = _ptr(router_w), _ptr(shared_gate_w)
+    a.logits_out, a.shared_gate_out = _ptr(logits_out), _ptr(gate_out)
     return a
 
 
@@ -227,7 +230,7 @@ def new_workspace(nbytes: int, device, stream=None):
 
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,
                       topk_ids=None, topk_w=None, shared=None, residual=None, out=None, workspace=None,
-                      routing_out: bool = False, stream=None, _timed=None):
+                      routing_out: bool = False, stream=None, router_w=None, shared_gate_w=None, _timed=None):
     """One routed-expert MoE FFN on the GPU.
 
     ``x`` bf16 ``[T, H]``; ``w13`` int32 ``[E, 2I, H*bits/32]`` and ``s13`` bf16
@@ -237,6 +240,11 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
     ``{w13, s13, w2, s2, bits}`` of one always-on expert.  Returns ``y`` bf16 ``[T, H]``,
     and with ``routing_out`` also a dict of the routing outputs (ids, w, counts, offsets,
     sorted_pairs).
+
+    ``router_w`` bf16 ``[E, H]`` computes the logits from ``x`` (then ``router_logits``
+    must be None); ``shared_gate_w`` bf16 ``[H]`` scales the shared expert's output per
+    token by ``sigmoid(x . shared_gate_w)``.  With ``routing_out`` the routing dict then
+    also holds ``logits`` fp32 ``[T, E]`` and ``shared_gate`` fp32 ``[T]``.
     """
     torch = _torch()
     bf = _bf16_types()
@@ -251,7 +259,12 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
     E, I = _check_experts(w13, s13, w2, s2, bits, H)
     if not 1 <= top_k <= E:
         raise ValueError(f"top_k = {top_k} not in [1, E = {E}]")
-    if router_logits is not None:
+    if router_w is not None:
+        if router_logits is not None:
+            raise ValueError("router_w and router_logits are exclusive")
+        _need(router_w, "router_w", bf, dev)
+        _shape(router_w, "router_w", (E, H))
+    elif router_logits is not None:
         _need(router_logits, "router_logits", (torch.float32,), dev)
         _shape(router_logits, "router_logits", (T, E))
     else:
@@ -262,6 +275,11 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
     sb = sI = 0
     if shared is not None:
         sb, sI = _check_shared(shared, H, dev)
+    if shared_gate_w is not None:
+        if shared is None:
+            raise ValueError("shared_gate_w needs a shared expert")
+        _need(shared_gate_w, "shared_gate_w", bf, dev)
+        _shape(shared_gate_w, "shared_gate_w", (H,))
     if residual is not None:
         _need(residual, "residual", bf, dev)
         _shape(residual, "residual", (T, H))
@@ -274,22 +292,30 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
         if workspace.numel() < need:
             raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     routing = {}
-    counts = offsets = sorted_pairs = None
+    counts = offsets = sorted_pairs = logits_out = gate_out = None
     with _on(stream):   # everything allocated here is ordered before the kernels on `stream`
         if out is None:
             out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         if routing_out:
-            if router_logits is not None:
+            if router_w is not None:
+                logits_out = torch.empty((T, E), dtype=torch.float32, device=dev)
+            if shared_gate_w is not None:
+                gate_out = torch.empty((T,), dtype=torch.float32, device=dev)
+            if router_logits is not None or router_w is not None:
                 topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
                 topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
             counts = torch.empty((E,), dtype=torch.int32, device=dev)
             offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
             sorted_pairs = torch.empty((T * top_k,), dtype=torch.int32, device=dev)
             routing = dict(ids=topk_ids, w=topk_w, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
+            if logits_out is not None:
+                routing["logits"] = logits_out
+            if gate_out is not None:
+                routing["shared_gate"] = gate_out
         if workspace is None:
             workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)   # zero head: see workspace_init
         a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
-                  counts, offsets, sorted_pairs, workspace)
+                  counts, offsets, sorted_pairs, workspace, router_w, shared_gate_w, logits_out, gate_out)
         if _timed is None:
             st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, None))
             _lib.check(st, "moe_w4a16_forward")
@@ -319,7 +345,7 @@ class MoeCall:
     """
 
     def __init__(self, x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, shared=None, workspace=None,
-                 stream=None):
+                 stream=None, router_w=None, shared_gate_w=None):
         torch = _torch()
         bf = _bf16_types()
         _need(x, "x", bf)
@@ -337,16 +363,25 @@ class MoeCall:
         sb = sI = 0
         if shared is not None:
             sb, sI = _check_shared(shared, self.H, dev)
+        if router_w is not None:
+            _need(router_w, "router_w", bf, dev)
+            _shape(router_w, "router_w", (self.E, self.H))
+        if shared_gate_w is not None:
+            if shared is None:
+                raise ValueError("shared_gate_w needs a shared expert")
+            _need(shared_gate_w, "shared_gate_w", bf, dev)
+            _shape(shared_gate_w, "shared_gate_w", (self.H,))
+        self.self_routed = router_w is not None
         need = moe_w4a16_workspace_size(self.T, self.H, I, self.E, top_k, sb, sI)
         if workspace is None:
             workspace = new_workspace(need, dev, stream)
         _need(workspace, "workspace", (torch.uint8,), dev)
         if workspace.numel() < need:
             raise ValueError(f"workspace needs {need} bytes")
-        self._keep = (w13, s13, w2, s2, shared, workspace)
+        self._keep = (w13, s13, w2, s2, shared, workspace, router_w, shared_gate_w)
         self.workspace = workspace
         self.args = _args(x, w13, s13, w2, s2, top_k, bits, None, None, None, shared, None, None, None, None, None,
-                          workspace)
+                          workspace, router_w, shared_gate_w)
         self.device = dev
         self.stream = None if stream is None else _stream(dev, stream)   # None: the current stream per call
         self._fn = _lib.lib().moe_w4a16_forward
@@ -360,7 +395,10 @@ class MoeCall:
         if (x.shape != self._th or out.shape != self._th or x.element_size() != 2 or out.element_size() != 2
                 or not (x.is_contiguous() and out.is_contiguous())):
             raise ValueError(f"x and out must be contiguous 16-bit {self._th}")
-        if router_logits is not None:
+        if self.self_routed:
+            if router_logits is not None or topk_ids is not None:
+                raise ValueError("this call computes its logits from x (router_w): pass no logits or ids")
+        elif router_logits is not None:
             if router_logits.shape != self._te or router_logits.dtype != torch.float32:
                 raise ValueError(f"router_logits must be fp32 {self._te}")
         elif (topk_ids is None or topk_w is None or topk_ids.shape != self._tk or topk_w.shape != self._tk

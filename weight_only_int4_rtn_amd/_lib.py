@@ -12,7 +12,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 WORKSPACE_HEAD_BYTES = 147456   # W4A16_WORKSPACE_HEAD_BYTES
 WORKSPACE_ERROR_OFFSET = 12928  # W4A16_WORKSPACE_ERROR_OFFSET
 NOALLOC_SCRATCH_BYTES = 64 << 20  # W4A16_NOALLOC_SCRATCH_BYTES
@@ -58,6 +58,8 @@ class MoeArgs(C.Structure):
         ("topk_ids", C.c_void_p), ("topk_w", C.c_void_p),
         ("expert_counts", C.c_void_p), ("expert_offsets", C.c_void_p), ("sorted_pairs", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+        ("router_w", C.c_void_p), ("shared_gate_w", C.c_void_p),
+        ("logits_out", C.c_void_p), ("shared_gate_out", C.c_void_p),
     ]
 
 

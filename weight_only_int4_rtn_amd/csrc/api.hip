@@ -90,6 +90,8 @@ WsLayout layout(const moe_w4a16_args* a) {
     L.rows_a = P + (shared ? T : 0);
     L.width_a = std::max(a->I, shared ? a->shared_I : (int64_t)0);
     L.abuf = take((size_t)L.rows_a * L.width_a * 2);
+    L.logits = take((size_t)T * E * 4);   // router logits computed from x
+    L.gate = take((size_t)T * 4);         // shared-expert gate values
     if (T <= kSmallT) {
         // down-kernel work units: 2-group K chunks of every expert that can be active
         auto chunks = [](int64_t I_e) { return (I_e / kGroup + 1) / 2; };
@@ -120,13 +122,18 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     if (a->T == 0) return W4A16_OK;
     if (!a->x || !a->w13 || !a->s13 || !a->w2 || !a->s2 || !a->y)
         return fail(W4A16_ERR_INVALID_ARG, "NULL x, w13, s13, w2, s2 or y");
-    if (!a->router_logits && (!a->topk_ids || !a->topk_w))
-        return fail(W4A16_ERR_INVALID_ARG, "router_logits is NULL, so topk_ids and topk_w must be given");
+    if (a->router_w && a->router_logits)
+        return fail(W4A16_ERR_INVALID_ARG, "router_w and router_logits are exclusive");
+    if (!a->router_logits && !a->router_w && (!a->topk_ids || !a->topk_w))
+        return fail(W4A16_ERR_INVALID_ARG, "no router_logits or router_w, so topk_ids and topk_w must be given");
+    if (a->shared_gate_w && !a->shared_bits)
+        return fail(W4A16_ERR_INVALID_ARG, "shared_gate_w needs a shared expert");
     if (a->shared_bits && (!a->shared_w13 || !a->shared_s13 || !a->shared_w2 || !a->shared_s2))
         return fail(W4A16_ERR_INVALID_ARG, "NULL shared expert pointer");
     const void* ptrs[] = {a->x, a->router_logits, a->w13, a->s13, a->w2, a->s2, a->shared_w13, a->shared_s13,
                           a->shared_w2, a->shared_s2, a->residual, a->y, a->topk_ids, a->topk_w,
-                          a->expert_counts, a->expert_offsets, a->sorted_pairs, a->workspace};
+                          a->expert_counts, a->expert_offsets, a->sorted_pairs, a->workspace,
+                          a->router_w, a->shared_gate_w, a->logits_out, a->shared_gate_out};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(W4A16_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
     if (a->y == a->x) return fail(W4A16_ERR_INVALID_ARG, "y must not alias x");
@@ -139,8 +146,26 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    // router logits and the shared expert's gate from x, ahead of everything else
+    const float* logits_in = a->router_logits;
+    const float* shared_gate = nullptr;
+    if (a->router_w || a->shared_gate_w) {
+        RouterArgs ra{};
+        ra.x = a->x;
+        ra.wr = a->router_w;
+        ra.wg = a->shared_gate_w;
+        ra.T = (int)a->T;
+        ra.n_router = a->router_w ? (int)a->E : 0;
+        ra.H = a->H;
+        ra.logits = a->logits_out ? a->logits_out : static_cast<float*>(at(L.logits));
+        ra.gate = a->shared_gate_out ? a->shared_gate_out : static_cast<float*>(at(L.gate));
+        if (int st = hip_status(launch_router(ra, s, timer), "router launch")) return st;
+        if (a->router_w) logits_in = ra.logits;
+        if (a->shared_gate_w) shared_gate = ra.gate;
+    }
+
     RouteArgs r{};
-    r.logits = a->router_logits;
+    r.logits = logits_in;
     r.T = (int)a->T;
     r.E = (int)a->E;
     r.k = (int)a->top_k;
@@ -180,7 +205,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
         d.H = a->H;
         d.routed = routed;
         d.shared = shared;
-        d.logits = a->router_logits;
+        d.logits = logits_in;
         d.ids = r.ids;
         d.wts = r.wts;
         d.counts = r.counts;
@@ -192,6 +217,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
         d.rows_a = (int)L.rows_a;
         d.tag_bytes = (uint32_t)tag_bytes;
         d.residual = a->residual;
+        d.shared_gate = shared_gate;
         d.y = a->y;
         const int64_t slots = a->T * a->top_k + (a->shared_bits ? 1 : 0);   // one per pair, + the shared expert
         d.n_rb = (int)(L.width_a / 16);
@@ -229,7 +255,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
             d.a_by_pair = 1;
             d.gk_stream = 1;
             d.route.pair_rows = 1;
-        } else if (a->router_logits && a->T > kSplitRouteT) {
+        } else if (logits_in && a->T > kSplitRouteT) {
             // routing spread over waves (one token each) in its own launch; the streaming
             // gate/up kernel, if it takes the shapes, then reads the tile records
             r.sync = static_cast<uint32_t*>(at(L.sync));
@@ -243,6 +269,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
                 if (int st = hip_status(launch_route_small(r, s, timer), "routing launch")) return st;
         }
         d.residual = a->residual;
+        d.shared_gate = shared_gate;
         d.y = a->y;
         return hip_status(launch_decode(d, s, timer), "decode launch");
     }
@@ -280,6 +307,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     p.asum = static_cast<float*>(at(L.asum));
     p.inv = r.inv;
     p.residual = a->residual;
+    p.shared_gate = shared_gate;
     p.y = a->y;
     return hip_status(launch_prefill(p, s, timer), "prefill launch");
 }

@@ -172,7 +172,7 @@ __device__ __forceinline__ uint32_t* sync_word(uint32_t* sync, int i) { return s
 
 struct WsLayout {
     size_t sync, ids, wts, counts, offsets, sorted, active, meta, hist, lrank, tiles, xsum, abuf, part,
-        ystage, inv, asum, tokw, rec, trec, xp, total;
+        ystage, inv, asum, tokw, rec, trec, xp, logits, gate, total;
     int64_t rows_a;     // rows of the gate/up output buffer (routed pairs + shared tokens)
     int64_t width_a;    // columns of that buffer: max(I, shared_I)
     int nblk;           // routing blocks of the large-batch path
@@ -260,6 +260,20 @@ hipError_t launch_route_small(const RouteArgs& a, hipStream_t s, StageTimer* t =
 hipError_t launch_route_split(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
+// Router logits (rows [0, n_router) of the right operand) and the shared-expert gate (row
+// n_router when wg is given, through the sigmoid) of every token: a bf16 product on MFMA.
+struct RouterArgs {
+    const uint16_t* x;    // bf16 [T, H]
+    const uint16_t* wr;   // bf16 [n_router, H] (n_router 0: none)
+    const uint16_t* wg;   // bf16 [H] or NULL
+    int T, n_router;
+    int64_t H;
+    float* logits;        // [T, n_router]
+    float* gate;          // [T]
+};
+constexpr int kRouterSmallT = 256;   // up to this many tokens: split-K workgroups per (16 tokens, 16 rows)
+hipError_t launch_router(const RouterArgs& a, hipStream_t s, StageTimer* t = nullptr);
+
 struct ExpertSet {       // one family of experts sharing a code width
     const int32_t* w13;
     const uint16_t* s13;
@@ -291,6 +305,7 @@ struct DecodeArgs {
     float* ystage;              // [rows_a, H] unweighted down-projection rows (streaming path)
     int64_t rows_a;             // rows of abuf and ystage: T * k routed, then T shared
     const uint16_t* residual;
+    const float* shared_gate;   // [T] weight of each token's shared-expert row, or NULL: 1
     uint16_t* y;
     int gk_stream;              // 1: gate/up by the streaming kernel (stream_fits), else one workgroup per tile
     int fused_route;            // 1: the streaming gate/up kernel routes the batch itself
@@ -335,6 +350,7 @@ struct TinyArgs {
     int rows_a;                 // T * k routed rows, then T shared rows
     uint32_t tag_bytes;
     const uint16_t* residual;
+    const float* shared_gate;   // [T] weight of each token's shared-expert row, or NULL: 1
     uint16_t* y;
     int n_gk;                   // gate/up workgroups: (T * k pairs + shared) * n_rb
     int n_rb;                   // 16-row blocks per slot: max(I, shared I) / 16
@@ -368,6 +384,7 @@ struct PrefillArgs {
     uint16_t* ystage;           // [rows_a, H] bf16: down output of each sorted row (unweighted)
     const int32_t* inv;         // [T*k] sorted position of each pair (-1: dropped)
     const uint16_t* residual;
+    const float* shared_gate;   // [T] weight of each token's shared-expert row, or NULL: 1
     uint16_t* y;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);

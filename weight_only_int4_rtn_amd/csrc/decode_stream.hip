@@ -779,8 +779,9 @@ __global__ __launch_bounds__(256) void dk_finalize_kernel(DecodeArgs a) {
         s0 += w[j] * v[j].x;
         s1 += w[j] * v[j].y;
     }
-    s0 += sh.x;
-    s1 += sh.y;
+    const float g = a.shared_gate ? a.shared_gate[t] : 1.0f;
+    s0 += g * sh.x;
+    s1 += g * sh.y;
     if (a.residual) {
         s0 += bf16_to_f32(res & 0xffffu);
         s1 += bf16_to_f32(res >> 16);

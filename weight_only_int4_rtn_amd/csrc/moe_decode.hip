@@ -221,7 +221,7 @@ __device__ __forceinline__ void dk_load_codes(DkUnit& u, u32x4_t (&bw)[kDkChunk]
 // halves the MFMAs of a unit.
 template <int BITS, bool XSUM, typename TokW, typename AFetch, typename XSum>
 __device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], TokW tokw, AFetch afetch, XSum xsum,
-                        float* yacc) {
+                        float* yacc, const float* sgate) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, ml = lane & 15;
     const int g0 = u.col0 / kGroup;
@@ -234,7 +234,7 @@ __device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], TokW 
             pr[r] = u.pos0 + m;
             if (u.shared) {
                 tk[r] = m;
-                wk[r] = 1.0f;
+                wk[r] = sgate ? sgate[m] : 1.0f;
             } else {
                 const int2 tw = tokw(u.pos0 + m);
                 tk[r] = tw.x;
@@ -360,8 +360,8 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
             return load16_or_zero(p, ok, p);
         };
         auto nox = [](int, int) { return 0.f; };
-        if (bits == BITS) dk_unit<BITS, false>(cu, cur, tw, af, nox, yacc);
-        else if constexpr (SBITS != 0) dk_unit<SBITS, false>(cu, cur, tw, af, nox, yacc);
+        if (bits == BITS) dk_unit<BITS, false>(cu, cur, tw, af, nox, yacc, a.shared_gate);
+        else if constexpr (SBITS != 0) dk_unit<SBITS, false>(cu, cur, tw, af, nox, yacc, a.shared_gate);
         if (un >= n_units) break;
 #pragma unroll
         for (int j = 0; j < kDkChunk; ++j) {
@@ -438,6 +438,7 @@ struct TinyRoute {
     float w[kTinyP];          // per pair: router weight
     int pair_at[kTinyP];      // per sorted position: pair
     int2 tw[kTinyP];          // per sorted position: (token, weight bits)
+    float sg[kTinyP];         // per token: weight of its shared-expert row (the gate, or 1)
     int4 slot[kTinyP];        // per active expert, ascending: (expert, first position, count, 0)
     int n_active, n_valid;
 };
@@ -465,6 +466,7 @@ __device__ void tiny_route(const TinyArgs& a, TinyRoute& r, bool writer) {
             r.w[t * k + lane] = w;
         }
     }
+    if ((int)threadIdx.x < T) r.sg[threadIdx.x] = a.shared_gate ? a.shared_gate[threadIdx.x] : 1.0f;
     __syncthreads();
     if (wave == 0) {   // stable order by (expert, pair): rank of each key among the P keys
         const int e = lane < P ? r.ids[lane] : -1;
@@ -663,7 +665,7 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
             acc += sc * (d[j][rr] - code_offset<BITS>() * xs[xr * G + g]);
         }
         if (m < t.count) {
-            const int2 tw = t.shared ? int2{m, __float_as_int(1.0f)} : r.tw[p];
+            const int2 tw = t.shared ? int2{m, __float_as_int(r.sg[m])} : r.tw[p];
             atomicAdd(&yacc[tw.x * 16 + ml], __int_as_float(tw.y) * acc);
         }
     }

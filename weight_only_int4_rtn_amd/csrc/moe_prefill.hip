@@ -537,7 +537,8 @@ __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
 }
 
 // y[t] = sum over slots j in order of w[t, j] times the staged row of pair (t, j), then
-// the shared expert's row, then the residual; rounded once to bf16.  A token's row is
+// the shared expert's row (times its gate value when there is one), then the residual;
+// rounded once to bf16.  A token's row is
 // split over ceil(H / 2048) blocks of 256 threads x 8 columns.  No atomics anywhere.
 __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
     const int nbx = (int)((a.H / 8 + 255) / 256);
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
         const int pos = a.inv[(int64_t)t * a.k + j];
         if (pos >= 0) add_row(pos, a.wts[(int64_t)t * a.k + j]);
     }
-    if (a.shared.bits) add_row((int64_t)a.T * a.k + t, 1.0f);
+    if (a.shared.bits) add_row((int64_t)a.T * a.k + t, a.shared_gate ? a.shared_gate[t] : 1.0f);
     const int64_t o = (int64_t)t * a.H + c;
     if (a.residual) {
         const u32x4_t r = *reinterpret_cast<const u32x4_t*>(a.residual + o);
