@@ -18,6 +18,9 @@ computes, written from the model-card pages this project follows:
   gate_proj / up_proj / down_proj triple (a SwiGLU MLP); the router
   (``mlp.gate``) and the ``shared_expert_gate`` stay BF16.
 
+* ``oracle.formats``: the FP8 E4M3 per-channel and MXFP4 expert formats of the
+  pages "Nex-N2.5-mini-mixed-NVFP4-FP8" and "Nex-N2.5-mini-MXFP4-MxWave".
+
 Where the pages leave a step open, the reading taken is stated at the function.
 """
 
@@ -31,6 +34,7 @@ from .rtn_moe import (  # noqa: F401
     unpack_codes,
     quantize_pack,
     dequantize,
+    dequantize_as,
     route,
     router_logits,
     shared_gate,
@@ -38,3 +42,5 @@ from .rtn_moe import (  # noqa: F401
     moe_ffn,
     moe_layer,
 )
+
+from . import formats  # noqa: E402,F401

@@ -267,8 +267,23 @@ def expert_ffn(x, w13, w2):
     return w2 @ a
 
 
+def dequantize_as(packed, scales, bits: int, weight_format: str = "int") -> np.ndarray:
+    """Dequantize one packed matrix in any of the expert weight formats, fp64:
+    ``int`` (RTN group 128, bf16 scales: :func:`dequantize`), ``fp8`` (E4M3 codes with
+    one fp32 scale per row) or ``mxfp4`` (E2M1 codes with E8M0 scales per 32 columns);
+    see ``oracle.formats``."""
+    if weight_format == "int":
+        return dequantize(packed, scales, bits).astype(np.float64)
+    from . import formats
+    if weight_format == "fp8":
+        return formats.fp8_dequantize(packed, scales)
+    if weight_format == "mxfp4":
+        return formats.mxfp4_dequantize(packed, scales)
+    raise ValueError(f"unknown weight format {weight_format!r}")
+
+
 def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
-            shared=None, residual_bits=None, shared_gate=None):
+            shared=None, residual_bits=None, shared_gate=None, weight_format: str = "int"):
     """Router-weighted sum of the selected W4A16 experts, fp64.
 
     ``y_t = sum_j w[t,j] * FFN_{ids[t,j]}(x_t)`` over the slots in order, then
@@ -283,7 +298,9 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
     ``shared`` is a dict with keys ``w13, s13, w2, s2, bits`` (one expert,
     leading axis absent); ``shared_gate`` (``[T]``, see :func:`shared_gate`)
     scales its output per token instead of the weight 1.  Returns fp64
-    ``[len(tokens), H]``.
+    ``[len(tokens), H]``.  ``weight_format`` names the routed experts' format
+    (``int``, ``fp8`` or ``mxfp4``, see :func:`dequantize_as`); the shared expert is
+    always the ``int`` format.
     """
     x = f32_from_bf16_bits(x_bits).astype(np.float64)
     T, k = ids.shape
@@ -296,8 +313,8 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
             by_expert[int(ids[t, j])].append((ti, j))
     out = np.zeros((len(tokens), k, H))
     for e in sorted(by_expert):
-        W13 = dequantize(w13[e], s13[e], bits).astype(np.float64)
-        W2 = dequantize(w2[e], s2[e], bits).astype(np.float64)
+        W13 = dequantize_as(w13[e], s13[e], bits, weight_format)
+        W2 = dequantize_as(w2[e], s2[e], bits, weight_format)
         rows = by_expert[e]
         # every (token, slot) routed to e at once: token activations as the columns
         X = x[[tokens[ti] for ti, _ in rows]].T
@@ -322,9 +339,10 @@ def moe_ffn(x_bits, ids, w, w13, s13, w2, s2, bits: int, tokens=None,
 
 
 def moe_layer(x_bits, logits, k: int, w13, s13, w2, s2, bits: int, tokens=None,
-              shared=None, residual_bits=None, shared_gate=None):
+              shared=None, residual_bits=None, shared_gate=None, weight_format: str = "int"):
     """Routing followed by the routed sum: ``(y fp64, route outputs)``."""
     r = route(logits, k)
     y = moe_ffn(x_bits, r[0], r[1], w13, s13, w2, s2, bits, tokens=tokens,
-                shared=shared, residual_bits=residual_bits, shared_gate=shared_gate)
+                shared=shared, residual_bits=residual_bits, shared_gate=shared_gate,
+                weight_format=weight_format)
     return y, r
