@@ -127,22 +127,31 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     eager_ms = start.elapsed_time(end) / steps
 
     # the same steps replayed from a HIP graph (one graph holds a full rotation of n_logits
-    # steps), which removes host launch cost as a decode loop does in serving
+    # steps), which removes host launch cost as a decode loop does in serving; an event pair
+    # around every replay gives the distribution of the per-step time over replays
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(n_logits):
             step(i)
     graph.replay()
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // n_logits))
+    reps = max(25, -(-steps // n_logits))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     start.record()
-    for _ in range(reps):
+    for r in range(reps):
+        evs[r][0].record()
         graph.replay()
+        evs[r][1].record()
     end.record()
     torch.cuda.synchronize()
     graph_ms = start.elapsed_time(end) / (reps * n_logits)
+    samples = sorted(a.elapsed_time(b) / n_logits for a, b in evs)
+    pct = {"p10": samples[len(samples) // 10], "p50": samples[len(samples) // 2],
+           "p90": samples[(9 * len(samples)) // 10], "samples": len(samples), "steps_per_sample": n_logits}
     del graph
-    ms_per_step = graph_ms
+    # the faster of the two launch modes is the step time (both are reported)
+    launch_mode = "graph" if graph_ms <= eager_ms else "eager"
+    ms_per_step = min(graph_ms, eager_ms)
 
     # per-kernel durations with HIP events around each kernel, same rotation
     per = {}
@@ -153,6 +162,8 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
         for nm, ms in tk:
             per.setdefault(nm, []).append(ms)
     kernels = {nm: sum(v) / len(v) * 1e3 for nm, v in per.items()}   # average us per launch
+    kernel_pct = {nm: {"p10": round(sorted(v)[len(v) // 10] * 1e3, 2), "p90": round(sorted(v)[(9 * len(v)) // 10] * 1e3, 2)}
+                  for nm, v in per.items()}
 
     d_mean = sum(distinct[(warmup + i) % n_logits] for i in range(steps)) / steps
     gu, dn = expert_bytes()
@@ -160,12 +171,15 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     flops = 2.0 * T * K * 3 * H * I
     res = {
         "T": T, "ms_per_step": ms_per_step, "eager_ms_per_step": eager_ms, "eager_wall_ms_per_step": wall_ms / steps,
+        "graph_ms_per_step": graph_ms, "launch_mode": launch_mode,
         "tok_per_s": T / (ms_per_step / 1e3),
         "distinct_experts_mean": d_mean,
         "expert_weight_bytes_per_step": weight_bytes,
         "expert_weight_GBps": weight_bytes / (ms_per_step / 1e3) / 1e9,
         "TFLOPs": flops / (ms_per_step / 1e3) / 1e12,
         "kernels_us": {k: round(v, 2) for k, v in kernels.items()},
+        "kernels_us_p10_p90": kernel_pct,
+        "step_ms_pct": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in pct.items()},
         "copies": n_copies,
     }
     # algorithmic bytes and flops of the two expert kernels, per launch
@@ -175,7 +189,7 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     res["kernel_bytes"]["all"] = d_mean * (gu + dn) + act_in + T * E * 4 + T * H * 2
     res["kernel_flops"] = {"gate_up": 2.0 * T * K * 2 * I * H, "down": 2.0 * T * K * H * I}
     res["kernel_flops"]["all"] = res["kernel_flops"]["gate_up"] + res["kernel_flops"]["down"]
-    log(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step (graph; eager {eager_ms * 1e3:.1f}, host wall "
+    log(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step (graph {graph_ms * 1e3:.1f}; eager {eager_ms * 1e3:.1f}, host wall "
         f"{wall_ms / steps * 1e3:.1f}), {res['tok_per_s']:.1f} tok/s, "
         f"{res['expert_weight_GBps']:.0f} GB/s expert weights, {res['TFLOPs']:.1f} TFLOP/s, kernels {res['kernels_us']}")
     del ws, out, logits, xs
@@ -340,26 +354,126 @@ def measure_stack(T, layers, steps, warmup, seed):
         graph.replay()
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / (reps * n_logits)
+    graph_ms = start.elapsed_time(end) / (reps * n_logits)
     del graph
+    ms = min(graph_ms, eager_ms)
     nbytes = 0.0
     for i in range(steps):
         for l, lay in enumerate(layers):
             gu, dn = expert_bytes(lay["bits"])
             nbytes += distinct[l][(warmup + i) % n_logits] * (gu + dn) + sum(expert_bytes(8))
     nbytes /= steps
-    res = {"T": T, "layers": L, "ms_per_step": ms, "eager_ms_per_step": eager_ms,
+    res = {"T": T, "layers": L, "ms_per_step": ms, "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+           "launch_mode": "graph" if graph_ms <= eager_ms else "eager",
            "eager_wall_ms_per_step": wall_ms / steps,
            "tok_per_s": T / (ms / 1e3), "weight_bytes_per_step": nbytes,
            "expert_weight_GBps": nbytes / (ms / 1e3) / 1e9}
-    log(f"[bench] stack{L}: {ms * 1e3:.1f} us/step (graph; eager {eager_ms * 1e3:.1f}), {res['tok_per_s']:.1f} tok/s, "
+    log(f"[bench] stack{L}: {ms * 1e3:.1f} us/step (graph {graph_ms * 1e3:.1f}; eager {eager_ms * 1e3:.1f}), "
+        f"{res['tok_per_s']:.1f} tok/s, "
         f"{res['expert_weight_GBps']:.0f} GB/s expert weights ({nbytes / 1e9:.2f} GB per step)")
     del ws
     return res
 
 
-def cpu_baseline(seconds):
-    """The oracle, as it stands, on single-token decode of the same layer shape."""
+class SclkSampler:
+    """Polls rocm-smi for the current shader clock while the GPU is busy (a thread)."""
+
+    def __init__(self):
+        import threading
+        self.mhz = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self.stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                for key, val in re.findall(r'"(sclk[^"]*)":\s*"([^"]*)"', out):
+                    m = re.search(r"(\d+)\s*Mhz", val, flags=re.I)
+                    if m:
+                        self.mhz.append(int(m.group(1)))
+            except Exception:
+                return
+            self.stop.wait(0.2)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join(timeout=15)
+
+    def enough(self):
+        return len(self.mhz) >= 5
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        v = sorted(self.mhz)
+        return {"median_mhz": v[len(v) // 2], "max_mhz": v[-1], "min_mhz": v[0], "samples": len(v),
+                "source": "rocm-smi --showclocks while the 8192-token prefill step runs"}
+
+
+def keep_busy(T, layers, seconds, sampler):
+    """Back-to-back forwards of a T-token batch until `seconds` pass or the sampler has enough."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    x = synth.device_normal((T, H), 1.0, 5, dev, torch.bfloat16)
+    logits = synth.device_normal((T, E), 1.0, 6, dev)
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, K), dev)
+    call = w4.MoeCall(x, *layers[0], top_k=K, workspace=ws)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end and not sampler.enough():
+        for _ in range(20):
+            call(x, out, router_logits=logits)
+        torch.cuda.synchronize()
+    del ws
+
+
+def time_router(layers, seed):
+    """The router GEMM (bf16 [256, 2048]) plus the shared-expert gate ahead of the routing:
+    its kernel time at 1, 32 and 8192 tokens, from self-routed forwards."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    out = {}
+    sh = dict(w13=torch.zeros((2 * I, H // 8), dtype=torch.int32, device=dev),
+              s13=torch.zeros((2 * I, H // 128), dtype=torch.bfloat16, device=dev),
+              w2=torch.zeros((H, I // 8), dtype=torch.int32, device=dev),
+              s2=torch.zeros((H, I // 128), dtype=torch.bfloat16, device=dev), bits=4)
+    wr = synth.device_normal((E, H), H ** -0.5, seed, dev, torch.bfloat16)
+    wg = synth.device_normal((H,), H ** -0.5, seed + 1, dev, torch.bfloat16)
+    for T in (1, 32, 8192):
+        x = synth.device_normal((T, H), 1.0, seed + T, dev, torch.bfloat16)
+        ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, K, 4, I), dev)
+        ts = []
+        for i in range(12):
+            _, tk = w4.moe_w4a16_forward_timed(x, *layers[i % len(layers)], top_k=K, router_w=wr, shared=sh,
+                                               shared_gate_w=wg, workspace=ws)
+            if i >= 2:
+                ts += [ms for nm, ms in tk if nm == "router"]
+        us = sum(ts) / len(ts) * 1e3
+        nbytes = (E + 1) * H * 2 + T * H * 2 + T * (E + 1) * 4
+        out[f"T{T}"] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                        "TFLOPs": round(2.0 * T * (E + 1) * H / us / 1e6, 2)}
+        del ws, x
+    log(f"[bench] router + shared gate: {out}")
+    return out
+
+
+def _cpu_child(spec):
+    """One CPU-oracle timing run in its own process (BLAS threads fixed by its environment).
+    Phase (i): dequantize + expert MLPs + weighted sum per forward, on bounded samples of
+    decode1, decode32, the prefill chunk and one stack layer; phase (ii): the quantizer
+    on a sample of experts, extrapolated to one full layer (805 M weights)."""
     import numpy as np
     import oracle
     import synth
@@ -368,34 +482,100 @@ def cpu_baseline(seconds):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    n_tok = 8
-    logits = synth.router_logits(1, n_tok, E)
-    x = synth.activations_bf16(1, n_tok, H)
-    ids, *_ = oracle.route(logits, K)
-    packed = {}
-    for e in sorted(set(ids.ravel().tolist())):
-        p13, s13 = oracle.quantize_pack(synth.expert_w13(1, 0, e, H, I), 4)
-        p2, s2 = oracle.quantize_pack(synth.expert_w2(1, 0, e, H, I), 4)
-        packed[e] = (p13, s13, p2, s2)
+    budget = float(spec["seconds"])
+    rng = np.random.default_rng(5)
+
+    # packed experts with random valid codes and bf16 scales: the oracle's arithmetic and
+    # its time do not depend on the values (the FFN is a dense product either way)
+    def rand_packed(shape_words):
+        return rng.integers(-2 ** 31, 2 ** 31, size=shape_words, dtype=np.int64).astype(np.int32)
+
+    n_pool = 64
+    pool = [(rand_packed((2 * I, H // 8)), np.full((2 * I, H // 128), 0x3B80, np.uint16),
+             rand_packed((H, I // 8)), np.full((H, I // 128), 0x3B80, np.uint16)) for _ in range(n_pool)]
 
     class View:
         def __init__(self, i):
             self.i = i
 
         def __getitem__(self, e):
-            return packed[int(e)][self.i]
+            return pool[int(e) % n_pool][self.i]
 
     views = [View(i) for i in range(4)]
-    done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        t = done % n_tok
-        oracle.moe_layer(x[t:t + 1], logits[t:t + 1], K, *views, 4)
-        done += 1
-    el = time.perf_counter() - t0
-    return {"value": round(done / el, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} single-token forwards of the 256-expert top-8 H=2048 I=512 INT4 layer "
-                      f"(route + dequant + fp64 SwiGLU + weighted sum), {el:.1f} s, numpy on the host"}
+    sh8 = dict(w13=rand_packed((2 * I, H // 4)), s13=np.full((2 * I, H // 128), 0x3B80, np.uint16),
+               w2=rand_packed((H, I // 4)), s2=np.full((H, I // 128), 0x3B80, np.uint16), bits=8)
+
+    def timed(fn, per_call_tokens, max_s):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            fn(done)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= max_s:
+                break
+        return {"tok_per_s": round(done * per_call_tokens / el, 4), "calls": done, "seconds": round(el, 2)}
+
+    phases = {}
+    l1 = synth.router_logits(1, 8, E)
+    x1 = synth.activations_bf16(1, 8, H)
+    phases["decode1"] = timed(lambda i: oracle.moe_layer(x1[i % 8:i % 8 + 1], l1[i % 8:i % 8 + 1], K, *views, 4),
+                              1, budget * 0.2)
+    l32 = synth.router_logits(2, 32, E)
+    x32 = synth.activations_bf16(2, 32, H)
+    phases["decode32"] = timed(lambda i: oracle.moe_layer(x32, l32, K, *views, 4), 32, budget * 0.25)
+    lp = synth.router_logits(3, 8192, E)[:64]
+    xp = synth.activations_bf16(3, 64, H)
+    phases["prefill8192_sample64"] = timed(lambda i: oracle.moe_layer(xp, lp, K, *views, 4), 64, budget * 0.25)
+    l4 = synth.router_logits(4, 4, E)
+    x4 = synth.activations_bf16(4, 4, H)
+    st = timed(lambda i: oracle.moe_layer(x4, l4, K, *views, 4, shared=sh8, residual_bits=x4), 4, budget * 0.15)
+    st["stack40_tok_per_s"] = round(st["tok_per_s"] / 40, 4)   # 40 such layers per stack step
+    phases["stack40_one_layer"] = st
+    # phase (ii): quantize + pack experts' fp32 weights, extrapolated to one full layer
+    w13 = synth.expert_w13(1, 0, 0, H, I)
+    w2 = synth.expert_w2(1, 0, 0, H, I)
+    q = timed(lambda i: (oracle.quantize_pack(w13, 4), oracle.quantize_pack(w2, 4)), 1, budget * 0.15)
+    per_expert_s = 1.0 / q["tok_per_s"]
+    phases["quantize_full_layer"] = {"weights_per_s": round(3 * H * I / per_expert_s), "experts_timed": q["calls"],
+                                     "seconds_per_layer_extrapolated": round(per_expert_s * E, 2)}
+    return {"threads": threads, "phases": phases}
+
+
+def cpu_baseline(seconds):
+    """The oracle as it stands, timed on the host in child processes with the BLAS thread
+    count fixed before import: all host threads, then one."""
+    import subprocess
+    try:
+        model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
+                     "unknown")
+    except OSError:
+        model = "unknown"
+    nproc = len(os.sched_getaffinity(0))
+    runs = {}
+    for n in (nproc, 1):
+        env = dict(os.environ)
+        for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+            env[var] = str(n)
+        env["CUDA_VISIBLE_DEVICES"] = ""
+        env["HIP_VISIBLE_DEVICES"] = ""
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child",
+                            json.dumps({"seconds": seconds})], capture_output=True, text=True, env=env, timeout=600)
+        if r.returncode != 0:
+            log(f"[bench] cpu child ({n} threads) failed: {r.stderr[-500:]}")
+            continue
+        runs[n] = json.loads(r.stdout.strip().splitlines()[-1])
+        log(f"[bench] cpu oracle, {n} threads: {runs[n]}")
+    if not runs:
+        return None
+    main_run = runs.get(nproc) or next(iter(runs.values()))
+    d1 = main_run["phases"]["decode1"]
+    return {"value": d1["tok_per_s"], "unit": "tok/s", "cores": main_run["threads"], "kind": "oracle",
+            "sample": f"{d1['calls']} single-token forwards of the 256-expert top-8 H=2048 I=512 INT4 layer "
+                      f"(route + dequant + fp64 SwiGLU + weighted sum) in {d1['seconds']} s, numpy",
+            "cpu_model": model, "nproc": nproc,
+            "phases_all_threads": main_run["phases"],
+            "phases_one_thread": runs[1]["phases"] if 1 in runs else None,
+            "one_thread_cores": runs[1]["threads"] if 1 in runs else None}
 
 
 def main():
@@ -405,12 +585,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=16, help="layer copies rotated through in decode runs")
     ap.add_argument("--only", default="", help="comma list of decode1,decode32,prefill8192,stack40 (default all)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU oracle budget per thread setting")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-quant", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy kernel of known size (for scaling HBM byte counters)")
+    ap.add_argument("--no-router", action="store_true")
+    ap.add_argument("--cpu-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_child is not None:
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        print(json.dumps(_cpu_child(json.loads(args.cpu_child))), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -435,8 +621,14 @@ def main():
         results["decode32"] = measure("decode32", 32, layers, args.steps, args.warmup, min(args.steps, 100), 12)
     if "prefill8192" in only:
         pst = max(5, args.steps // 10)
-        results["prefill8192"] = measure("prefill8192", 8192, layers[:4], pst, max(2, args.warmup // 4),
-                                         min(pst, 10), 13)
+        with SclkSampler() as sampler:
+            results["prefill8192"] = measure("prefill8192", 8192, layers[:4], pst, max(2, args.warmup // 4),
+                                             min(pst, 10), 13)
+            keep_busy(8192, layers[:4], 4.0, sampler)   # the MFMA-bound step while the clock is sampled
+        sclk = sampler.summary()
+    else:
+        sclk = None
+    router = None if args.no_router else time_router(layers[:4], 17)
     quant = None if args.no_quant else time_quantizer()
     del layers
     torch.cuda.empty_cache()
@@ -480,14 +672,19 @@ def main():
                                f"INT4 sym group-128 weights, bf16 activations, T={head['T']} tokens",
                    "global_batch": head["T"], "seq_len": 1, "parallelism": "none (1 GPU)"},
         "expert_weight_GBps": round(head["expert_weight_GBps"], 1),
-        "launch": "HIP graph replay of the timed steps (eager stream launches reported as eager_*)",
+        "launch": f"{head['launch_mode']}: the faster of HIP graph replay of the timed steps and eager stream "
+                  f"launches of one library call per step (both below)",
         "eager_tok_per_s": round(head["T"] / head["eager_ms_per_step"] * 1e3, 2),
         "eager_ms_per_step": round(head["eager_ms_per_step"], 5),
+        "graph_tok_per_s": round(head["T"] / head["graph_ms_per_step"] * 1e3, 2),
+        "graph_ms_per_step": round(head["graph_ms_per_step"], 5),
         "roofline": roofline_for(head, "mfma" if head_name == "prefill8192" else "hbm", head_name),
     }
     if stack is not None:
         line["stack40"] = {"tok_per_s": round(stack["tok_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
                            "eager_ms_per_step": round(stack["eager_ms_per_step"], 4),
+                           "graph_ms_per_step": round(stack["graph_ms_per_step"], 4),
+                           "launch_mode": stack["launch_mode"],
                            "expert_weight_GBps": round(stack["expert_weight_GBps"], 1),
                            "weight_GB_per_step": round(stack["weight_bytes_per_step"] / 1e9, 3),
                            "frac_hbm": round(stack["expert_weight_GBps"] / HBM_PEAK_GBPS, 4),
@@ -501,11 +698,18 @@ def main():
             continue
         line[nm] = {"tok_per_s": round(r["tok_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
                     "eager_ms_per_step": round(r["eager_ms_per_step"], 5),
+                    "graph_ms_per_step": round(r["graph_ms_per_step"], 5), "launch_mode": r["launch_mode"],
                     "expert_weight_GBps": round(r["expert_weight_GBps"], 1), "TFLOPs": round(r["TFLOPs"], 2),
                     "distinct_experts_mean": r["distinct_experts_mean"], "kernels_us": r["kernels_us"],
+                    "kernels_us_p10_p90": r["kernels_us_p10_p90"], "step_ms_pct": r["step_ms_pct"],
                     "roofline": roofline_for(r, "mfma" if nm == "prefill8192" else "hbm", nm)}
+    line["step_ms_pct"] = head["step_ms_pct"]
+    line["kernels_us_p10_p90"] = head["kernels_us_p10_p90"]
     if quant:
         line["quantize"] = quant
+    if router:
+        line["router"] = router
+    line["sclk"] = sclk
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 5
+#define W4A16_ABI_VERSION 6
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -95,6 +95,59 @@ const char* w4a16_last_error(void);
  */
 int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols,
                       int bits, int group, int32_t* packed, uint16_t* scales, void* stream);
+
+/* Formats of the routed experts' weights (moe_w4a16_args.weight_format). */
+typedef enum w4a16_format {
+    W4A16_FORMAT_INT = 0,       /* rtn_quantize_pack codes: INT4 / INT8, bf16 scale per 128 columns    */
+    W4A16_FORMAT_FP8_E4M3 = 1,  /* fp8_quantize_pack codes: E4M3 bytes, one fp32 scale per row (bits 8) */
+    W4A16_FORMAT_MXFP4 = 2      /* mxfp4_quantize_pack codes: E2M1 nibbles, E8M0 per 32 columns (bits 4) */
+} w4a16_format;
+
+/* Scale choice of mxfp4_quantize_pack. */
+typedef enum w4a16_mxfp4_method {
+    W4A16_MXFP4_RTN = 0,        /* exponent floor(log2 amax) - 2 (round-to-nearest)                  */
+    W4A16_MXFP4_MSE = 1         /* exponent searched by weight MSE (see mxfp4_quantize_pack)          */
+} w4a16_mxfp4_method;
+
+/*
+ * fp8_quantize_pack - per-output-channel FP8 E4M3 round-to-nearest.
+ *
+ * Page "Nex-N2.5-mini-mixed-NVFP4-FP8", What's quantized to what: the routed experts of
+ * the six most sensitive layers in FP8 E4M3 with one scale per output channel, weights-only
+ * round-to-nearest, no calibration.  For each row of each of n_mats matrices [rows, cols]:
+ *     s = max |w| / 448            (fp32, IEEE division; 448 = the largest E4M3 value)
+ *     q = E4M3( w / s )            (IEEE division, rounded to nearest even; s == 0: q = 0)
+ *   w        device, [n_mats, rows, cols], fp32 or bf16 (w_dtype), finite
+ *   cols     multiple of 4 (a multiple of 128 for use by moe_w4a16_forward)
+ *   packed   device out, int32 [n_mats, rows, cols/4]: column c in byte c % 4 of word c/4
+ *   scales   device out, fp32 [n_mats, rows]
+ * Codes and scales are bit-identical to the definition above.  Errors as rtn_quantize_pack.
+ */
+int fp8_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols, int32_t* packed,
+                      float* scales, void* stream);
+
+/*
+ * mxfp4_quantize_pack - MXFP4 (E2M1 codes, one E8M0 power-of-two scale per 32 columns).
+ *
+ * Page "Nex-N2.5-mini-MXFP4-MxWave", Model summary (MXFP4 W4A16 routed experts) and
+ * Quantization method.  For each block of 32 consecutive columns of a row, with
+ * amax = max |w| over the block:
+ *   W4A16_MXFP4_RTN: e = floor(log2 amax) - 2;
+ *   W4A16_MXFP4_MSE: e minimises sum (w - Q_e(w))^2 over the candidates
+ *       floor(log2(p / 6)) - 4 .. floor(log2(p / 6)) + 1 and the smallest e with
+ *       amax <= 6 * 2^e, where p = a + (b - a) * 0.845 is the block's 99.5th percentile of
+ *       |w| (a, b: its two largest |w|; fp64); the error is summed in fp64 in the fixed
+ *       order (i + 16, i + 8, i + 4, i + 2, i + 1); equal errors take the smaller e;
+ *   an all-zero block has e = -127; e is kept in [-127, 127];
+ *   Q_e(w) = E2M1( w / 2^e ) * 2^e, rounded to nearest with ties to the even code and
+ *       saturating at 6; the code's sign bit is w's sign bit.
+ *   cols     multiple of 32 (a multiple of 128 for use by moe_w4a16_forward)
+ *   packed   device out, int32 [n_mats, rows, cols/8]: column c in bits 4 (c % 8) of word c/8
+ *   scales   device out, uint8 [n_mats, rows, cols/32]: e + 127
+ * Codes and scales are bit-identical to the definition above.  Errors as rtn_quantize_pack.
+ */
+int mxfp4_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols, int method,
+                        int32_t* packed, uint8_t* scales, void* stream);
 
 /*
  * Arguments of one routed-expert MoE FFN call.
@@ -166,6 +219,12 @@ typedef struct moe_w4a16_args {
     const uint16_t* shared_gate_w; /* bf16 [H], or NULL                                     */
     float* logits_out;             /* optional out, fp32 [T, E]: logits from router_w       */
     float* shared_gate_out;        /* optional out, fp32 [T]: g from shared_gate_w          */
+    /* Routed experts' weight format (w4a16_format).  FP8_E4M3 (bits 8): w13/w2 hold E4M3
+     * bytes as fp8_quantize_pack writes them and s13/s2 point to fp32 [E, 2I] / [E, H] row
+     * scales (NVFP4-FP8 page, What's quantized to what).  MXFP4 (bits 4): E2M1 nibbles as
+     * mxfp4_quantize_pack writes them and s13/s2 point to E8M0 bytes [E, 2I, H/32] /
+     * [E, H, I/32] (MXFP4-MxWave page, Model summary).  The shared expert stays INT. */
+    int32_t weight_format;
 } moe_w4a16_args;
 
 /* Device workspace bytes moe_w4a16_forward needs for T tokens, hidden H, intermediate I,

@@ -47,7 +47,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 5
+    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 6
     assert _lib.status_string(0) == "W4A16_OK"
     assert _lib.status_string(3) == "W4A16_ERR_WORKSPACE"
     assert _lib.status_string(5) == "W4A16_ERR_TIMEOUT"
@@ -215,3 +215,32 @@ def test_binding_shape_checks_on_the_host():
     with pytest.raises(ValueError):
         w4._shape(torch.empty((3, H), **m), "out", (4, H))
     w4._shape(None, "residual", (4, H))                  # absent optional tensors pass
+
+
+@pytest.mark.parametrize("fn,args,expect", [
+    ("fp8", (FAKE, 0, 1, 8, 254), _lib.W4A16_ERR_INVALID_ARG),          # cols % 4
+    ("fp8", (FAKE, 3, 1, 8, 256), _lib.W4A16_ERR_INVALID_ARG),          # dtype
+    ("fp8", (None, 0, 1, 8, 256), _lib.W4A16_ERR_INVALID_ARG),          # NULL w
+    ("fp8", (MISALIGNED, 0, 1, 8, 256), _lib.W4A16_ERR_INVALID_ARG),
+    ("fp8", (None, 0, 0, 8, 256), _lib.W4A16_OK),                       # nothing to do
+    ("mx", (FAKE, 0, 1, 8, 48, 1), _lib.W4A16_ERR_INVALID_ARG),         # cols % 32
+    ("mx", (FAKE, 0, 1, 8, 256, 2), _lib.W4A16_ERR_INVALID_ARG),        # method
+    ("mx", (FAKE, 0, -1, 8, 256, 1), _lib.W4A16_ERR_INVALID_ARG),
+    ("mx", (None, 1, 2, 0, 256, 0), _lib.W4A16_OK),
+])
+def test_format_quantizer_validation(L, fn, args, expect):
+    if fn == "fp8":
+        w, dt, n, r, c = args
+        st = L.fp8_quantize_pack(w, dt, n, r, c, None if w is None else FAKE, None if w is None else FAKE, None)
+    else:
+        w, dt, n, r, c, m = args
+        st = L.mxfp4_quantize_pack(w, dt, n, r, c, m, None if w is None else FAKE, None if w is None else FAKE, None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("fmt,bits,expect", [(1, 4, _lib.W4A16_ERR_INVALID_ARG), (2, 8, _lib.W4A16_ERR_INVALID_ARG),
+                                             (3, 4, _lib.W4A16_ERR_INVALID_ARG), (-1, 4, _lib.W4A16_ERR_INVALID_ARG)])
+def test_forward_rejects_bad_weight_format(L, fmt, bits, expect):
+    a = base_args(bits=bits)
+    a.weight_format = fmt
+    assert forward_status(L, a) == expect

@@ -21,7 +21,7 @@ import ctypes as C
 from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
-__all__ = ["rtn_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
+__all__ = ["rtn_quantize_pack", "fp8_quantize_pack", "mxfp4_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
            "moe_w4a16_workspace_init", "moe_w4a16_workspace_check", "new_workspace",
            "MoeCall", "w4a16_abi_version", "W4A16Error", "library_path"]
 
@@ -88,10 +88,14 @@ def _check_bits(bits, name="bits"):
         raise ValueError(f"{name} = {bits}, must be 4 or 8")
 
 
-def _check_experts(w13, s13, w2, s2, bits, H):
-    """Shapes of a routed-expert bank for code width ``bits`` and hidden size ``H``:
-    returns (E, I)."""
+def _check_experts(w13, s13, w2, s2, bits, H, fmt="int"):
+    """Shapes of a routed-expert bank for code width ``bits``, hidden size ``H`` and
+    weight format ``fmt`` (int / fp8 / mxfp4): returns (E, I)."""
     _check_bits(bits)
+    if fmt not in _lib.FORMATS:
+        raise ValueError(f"weight_format {fmt!r}: one of {tuple(_lib.FORMATS)}")
+    if (fmt == "fp8" and bits != 8) or (fmt == "mxfp4" and bits != 4):
+        raise ValueError(f"{fmt} experts have {8 if fmt == 'fp8' else 4}-bit codes, not {bits}")
     if w13.dim() != 3 or w2.dim() != 3:
         raise ValueError("w13 and w2 must be 3-D")
     E, twoI = w13.shape[0], w13.shape[1]
@@ -99,10 +103,22 @@ def _check_experts(w13, s13, w2, s2, bits, H):
         raise ValueError(f"H = {H} and I = {twoI / 2} must be multiples of {GROUP}")
     I = twoI // 2
     _shape(w13, "w13", (E, 2 * I, H * bits // 32))
-    _shape(s13, "s13", (E, 2 * I, H // GROUP))
     _shape(w2, "w2", (E, H, I * bits // 32))
-    _shape(s2, "s2", (E, H, I // GROUP))
+    if fmt == "int":
+        _shape(s13, "s13", (E, 2 * I, H // GROUP))
+        _shape(s2, "s2", (E, H, I // GROUP))
+    elif fmt == "fp8":
+        _shape(s13, "s13", (E, 2 * I))
+        _shape(s2, "s2", (E, H))
+    else:
+        _shape(s13, "s13", (E, 2 * I, H // 32))
+        _shape(s2, "s2", (E, H, I // 32))
     return E, I
+
+
+def _scale_types(fmt):
+    torch = _torch()
+    return _bf16_types() if fmt == "int" else (torch.float32,) if fmt == "fp8" else (torch.uint8,)
 
 
 def _check_shared(shared, H, dev):
@@ -159,9 +175,69 @@ def rtn_quantize_pack(w, bits: int = 4, group: int = GROUP, packed=None, scales=
     return packed, scales
 
 
+def _quantize_common(w, col_mult):
+    torch = _torch()
+    _need(w, "w", (torch.float32, torch.bfloat16))
+    if w.dim() < 2:
+        raise ValueError("w must have at least 2 dims")
+    rows, cols = w.shape[-2], w.shape[-1]
+    if cols % col_mult:
+        raise ValueError(f"cols = {cols} is not a multiple of {col_mult}")
+    n_mats = w.numel() // max(1, rows * cols) if rows * cols else 0
+    dt = _lib.W4A16_F32 if w.dtype == torch.float32 else _lib.W4A16_BF16
+    return rows, cols, n_mats, tuple(w.shape[:-1]), dt
+
+
+def fp8_quantize_pack(w, packed=None, scales=None, stream=None):
+    """Per-output-channel FP8 E4M3 of ``w[..., rows, cols]`` (fp32 or bf16, on the GPU).
+
+    Returns ``(packed int32 [..., rows, cols/4], scales fp32 [..., rows])``.
+    """
+    torch = _torch()
+    rows, cols, n_mats, lead, dt = _quantize_common(w, 4)
+    with _on(stream):
+        if packed is None:
+            packed = torch.empty(lead + (cols // 4,), dtype=torch.int32, device=w.device)
+        if scales is None:
+            scales = torch.empty(lead, dtype=torch.float32, device=w.device)
+    _need(packed, "packed", (torch.int32,), w.device)
+    _need(scales, "scales", (torch.float32,), w.device)
+    _shape(packed, "packed", lead + (cols // 4,))
+    _shape(scales, "scales", lead)
+    st = _lib.lib().fp8_quantize_pack(_ptr(w), dt, n_mats, rows, cols, _ptr(packed), _ptr(scales),
+                                      _stream(w.device, stream))
+    _lib.check(st, "fp8_quantize_pack")
+    return packed, scales
+
+
+def mxfp4_quantize_pack(w, method: str = "mse", packed=None, scales=None, stream=None):
+    """MXFP4 of ``w[..., rows, cols]``: E2M1 codes and one E8M0 scale per 32 columns, the
+    scale exponent by weight-MSE search (``mse``) or round-to-nearest (``rtn``).
+
+    Returns ``(packed int32 [..., rows, cols/8], scales uint8 [..., rows, cols/32])``.
+    """
+    torch = _torch()
+    if method not in _lib.MXFP4_METHODS:
+        raise ValueError(f"method {method!r}: one of {tuple(_lib.MXFP4_METHODS)}")
+    rows, cols, n_mats, lead, dt = _quantize_common(w, 32)
+    with _on(stream):
+        if packed is None:
+            packed = torch.empty(lead + (cols // 8,), dtype=torch.int32, device=w.device)
+        if scales is None:
+            scales = torch.empty(lead + (cols // 32,), dtype=torch.uint8, device=w.device)
+    _need(packed, "packed", (torch.int32,), w.device)
+    _need(scales, "scales", (torch.uint8,), w.device)
+    _shape(packed, "packed", lead + (cols // 8,))
+    _shape(scales, "scales", lead + (cols // 32,))
+    st = _lib.lib().mxfp4_quantize_pack(_ptr(w), dt, n_mats, rows, cols, _lib.MXFP4_METHODS[method], _ptr(packed),
+                                        _ptr(scales), _stream(w.device, stream))
+    _lib.check(st, "mxfp4_quantize_pack")
+    return packed, scales
+
+
 def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
           counts, offsets, sorted_pairs, workspace, router_w=None, shared_gate_w=None, logits_out=None,
-          gate_out=None):
+          gate_out=None, weight_format="int"):
     a = MoeArgs()
     T, H = x.shape
     E, twoI = w13.shape[0], w13.shape[1]
@@ -181,6 +257,7 @@ def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, sha
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.router_w, a.shared_gate_w = _ptr(router_w), _ptr(shared_gate_w)
     a.logits_out, a.shared_gate_out = _ptr(logits_out), _ptr(gate_out)
+    a.weight_format = _lib.FORMATS[weight_format]
     return a
 
 
@@ -230,7 +307,8 @@ def new_workspace(nbytes: int, device, stream=None):
 
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,
                       topk_ids=None, topk_w=None, shared=None, residual=None, out=None, workspace=None,
-                      routing_out: bool = False, stream=None, router_w=None, shared_gate_w=None, _timed=None):
+                      routing_out: bool = False, stream=None, router_w=None, shared_gate_w=None,
+                      weight_format: str = "int", _timed=None):
     """One routed-expert MoE FFN on the GPU.
 
     ``x`` bf16 ``[T, H]``; ``w13`` int32 ``[E, 2I, H*bits/32]`` and ``s13`` bf16
@@ -245,18 +323,25 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
     must be None); ``shared_gate_w`` bf16 ``[H]`` scales the shared expert's output per
     token by ``sigmoid(x . shared_gate_w)``.  With ``routing_out`` the routing dict then
     also holds ``logits`` fp32 ``[T, E]`` and ``shared_gate`` fp32 ``[T]``.
+
+    ``weight_format`` ``fp8`` (bits 8) or ``mxfp4`` (bits 4) takes routed experts packed by
+    :func:`fp8_quantize_pack` / :func:`mxfp4_quantize_pack`: ``s13``/``s2`` are then fp32
+    ``[E, 2I]`` / ``[E, H]`` row scales, or uint8 E8M0 ``[E, 2I, H/32]`` / ``[E, H, I/32]``.
     """
     torch = _torch()
     bf = _bf16_types()
     _need(x, "x", bf)
     dev = x.device
-    for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, bf), ("w2", w2, (torch.int32,)),
-                        ("s2", s2, bf)):
+    if weight_format not in _lib.FORMATS:
+        raise ValueError(f"weight_format {weight_format!r}: one of {tuple(_lib.FORMATS)}")
+    sdt = _scale_types(weight_format)
+    for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, sdt), ("w2", w2, (torch.int32,)),
+                        ("s2", s2, sdt)):
         _need(t, name, dt, dev)
     if x.dim() != 2:
         raise ValueError("x must be 2-D [T, H]")
     T, H = x.shape
-    E, I = _check_experts(w13, s13, w2, s2, bits, H)
+    E, I = _check_experts(w13, s13, w2, s2, bits, H, weight_format)
     if not 1 <= top_k <= E:
         raise ValueError(f"top_k = {top_k} not in [1, E = {E}]")
     if router_w is not None:
@@ -315,7 +400,8 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
         if workspace is None:
             workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)   # zero head: see workspace_init
         a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
-                  counts, offsets, sorted_pairs, workspace, router_w, shared_gate_w, logits_out, gate_out)
+                  counts, offsets, sorted_pairs, workspace, router_w, shared_gate_w, logits_out, gate_out,
+                  weight_format)
         if _timed is None:
             st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, None))
             _lib.check(st, "moe_w4a16_forward")
@@ -345,18 +431,21 @@ class MoeCall:
     """
 
     def __init__(self, x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, shared=None, workspace=None,
-                 stream=None, router_w=None, shared_gate_w=None):
+                 stream=None, router_w=None, shared_gate_w=None, weight_format: str = "int"):
         torch = _torch()
         bf = _bf16_types()
         _need(x, "x", bf)
         dev = x.device
-        for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, bf), ("w2", w2, (torch.int32,)),
-                            ("s2", s2, bf)):
+        if weight_format not in _lib.FORMATS:
+            raise ValueError(f"weight_format {weight_format!r}: one of {tuple(_lib.FORMATS)}")
+        sdt = _scale_types(weight_format)
+        for name, t, dt in (("w13", w13, (torch.int32,)), ("s13", s13, sdt), ("w2", w2, (torch.int32,)),
+                            ("s2", s2, sdt)):
             _need(t, name, dt, dev)
         if x.dim() != 2:
             raise ValueError("x must be 2-D [T, H]")
         self.T, self.H = x.shape
-        self.E, I = _check_experts(w13, s13, w2, s2, bits, self.H)
+        self.E, I = _check_experts(w13, s13, w2, s2, bits, self.H, weight_format)
         if not 1 <= top_k <= self.E:
             raise ValueError(f"top_k = {top_k} not in [1, E = {self.E}]")
         self.top_k = top_k
@@ -381,7 +470,7 @@ class MoeCall:
         self._keep = (w13, s13, w2, s2, shared, workspace, router_w, shared_gate_w)
         self.workspace = workspace
         self.args = _args(x, w13, s13, w2, s2, top_k, bits, None, None, None, shared, None, None, None, None, None,
-                          workspace, router_w, shared_gate_w)
+                          workspace, router_w, shared_gate_w, weight_format=weight_format)
         self.device = dev
         self.stream = None if stream is None else _stream(dev, stream)   # None: the current stream per call
         self._fn = _lib.lib().moe_w4a16_forward

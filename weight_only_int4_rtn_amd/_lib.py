@@ -12,7 +12,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 WORKSPACE_HEAD_BYTES = 147456   # W4A16_WORKSPACE_HEAD_BYTES
 WORKSPACE_ERROR_OFFSET = 12928  # W4A16_WORKSPACE_ERROR_OFFSET
 NOALLOC_SCRATCH_BYTES = 64 << 20  # W4A16_NOALLOC_SCRATCH_BYTES
@@ -27,11 +27,16 @@ W4A16_ERR_TIMEOUT = 5
 W4A16_F32 = 0
 W4A16_BF16 = 1
 
+FORMATS = {"int": 0, "fp8": 1, "mxfp4": 2}   # w4a16_format
+MXFP4_METHODS = {"rtn": 0, "mse": 1}         # w4a16_mxfp4_method
+
 EXPORTED = (
     "w4a16_abi_version",
     "w4a16_status_string",
     "w4a16_last_error",
     "rtn_quantize_pack",
+    "fp8_quantize_pack",
+    "mxfp4_quantize_pack",
     "moe_w4a16_workspace_size",
     "moe_w4a16_workspace_init",
     "moe_w4a16_workspace_check",
@@ -60,6 +65,7 @@ class MoeArgs(C.Structure):
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
         ("router_w", C.c_void_p), ("shared_gate_w", C.c_void_p),
         ("logits_out", C.c_void_p), ("shared_gate_out", C.c_void_p),
+        ("weight_format", C.c_int32),
     ]
 
 
@@ -89,6 +95,12 @@ def lib():
     L.rtn_quantize_pack.restype = C.c_int
     L.rtn_quantize_pack.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int,
                                     C.c_void_p, C.c_void_p, C.c_void_p]
+    L.fp8_quantize_pack.restype = C.c_int
+    L.fp8_quantize_pack.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                    C.c_void_p]
+    L.mxfp4_quantize_pack.restype = C.c_int
+    L.mxfp4_quantize_pack.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_void_p,
+                                      C.c_void_p, C.c_void_p]
     L.moe_w4a16_workspace_size.restype = C.c_size_t
     L.moe_w4a16_workspace_size.argtypes = [C.c_int64] * 6
     L.moe_w4a16_workspace_init.restype = C.c_int

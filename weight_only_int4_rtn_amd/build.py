@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "quant.hip", "route.hip", "router.hip", "moe_decode.hip", "decode_stream.hip",
-           "moe_prefill.hip"]
+SOURCES = ["api.hip", "quant.hip", "quant_fmt.hip", "route.hip", "router.hip", "moe_decode.hip",
+           "decode_stream.hip", "moe_prefill.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -52,5 +52,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage(sources=None) -> str:
+    """Per-kernel register, LDS and scratch use of every gfx950 kernel, from the compiler's
+    kernel-resource-usage remarks (the device pass of each source, nothing linked)."""
+    import re
+    import subprocess as sp
+    rows = []
+    for src in sources or SOURCES:
+        cmd = [HIPCC, *FLAGS, "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+               "-Rpass-analysis=kernel-resource-usage"]
+        r = sp.run(cmd, capture_output=True, text=True)
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]"
+                          r"|LDS Size \[bytes/block\]|SGPRs): (\S+)", line)
+            if not m:
+                continue
+            key, val = m.group(1), m.group(2)
+            if key == "Function Name":
+                cur = {"kernel": val, "file": src}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key.split()[0]] = val
+    names = {}
+    try:
+        out = sp.run(["c++filt"], input="\n".join(r["kernel"] for r in rows), capture_output=True, text=True).stdout
+        names = dict(zip([r["kernel"] for r in rows], out.splitlines()))
+    except OSError:
+        pass
+    lines = [f"{'file':<18} {'VGPRs':>5} {'AGPRs':>5} {'SGPRs':>5} {'scratch':>7} {'LDS':>6} {'occ':>3}  kernel"]
+    for r in rows:
+        nm = names.get(r["kernel"], r["kernel"]).replace("w4a16::", "").replace("(anonymous namespace)::", "")
+        lines.append(f"{r['file']:<18} {r.get('VGPRs', '?'):>5} {r.get('AGPRs', '?'):>5} {r.get('SGPRs', '?'):>5} "
+                     f"{r.get('ScratchSize', '?'):>7} {r.get('LDS', '?'):>6} {r.get('Occupancy', '?'):>3}  {nm}")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if len(sys.argv) > 1 and sys.argv[1] == "--resource-usage":
+        print(resource_usage(sys.argv[2:] or None))
+    else:
+        print(build(verbose=True))

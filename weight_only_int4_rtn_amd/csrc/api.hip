@@ -55,6 +55,12 @@ int check_shapes(const moe_w4a16_args* a) {
     if (a->T * a->H * 2 >= (int64_t(1) << 32) ||
         (a->T + a->T * a->top_k) * std::max(a->I, a->shared_bits ? a->shared_I : (int64_t)0) * 2 >= (int64_t(1) << 32))
         return fail(W4A16_ERR_UNSUPPORTED, "T = %lld too large for these shapes", (long long)a->T);
+    if (a->weight_format < W4A16_FORMAT_INT || a->weight_format > W4A16_FORMAT_MXFP4)
+        return fail(W4A16_ERR_INVALID_ARG, "weight_format = %d", a->weight_format);
+    if (a->weight_format == W4A16_FORMAT_FP8_E4M3 && a->bits != 8)
+        return fail(W4A16_ERR_INVALID_ARG, "FP8 E4M3 experts have 8-bit codes: bits = %d", a->bits);
+    if (a->weight_format == W4A16_FORMAT_MXFP4 && a->bits != 4)
+        return fail(W4A16_ERR_INVALID_ARG, "MXFP4 experts have 4-bit codes: bits = %d", a->bits);
     if (a->shared_bits != 0) {
         if (a->shared_bits != 4 && a->shared_bits != 8)
             return fail(W4A16_ERR_INVALID_ARG, "shared_bits = %d, must be 0, 4 or 8", a->shared_bits);
@@ -184,8 +190,9 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     r.trec = static_cast<int4*>(at(L.trec));
     r.max_slots = (int)std::min(a->E, a->T * a->top_k);
 
-    ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits};
-    ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits};
+    ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits, a->weight_format};
+    ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits, 0};
+    const bool int_codes = a->weight_format == W4A16_FORMAT_INT;   // the single-launch and streaming kernels
     uint16_t* abuf = static_cast<uint16_t*>(at(L.abuf));
 
     // single launch for tiny batches when the tagged a words fit the workspace head, the
@@ -194,7 +201,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     const size_t tag_bytes = (size_t)L.rows_a * L.width_a * 4;
     const size_t tiny_lds = 8 * (size_t)a->T * 16 * 4 + (size_t)L.rows_a * (L.width_a + kTinyPad) * 2 + 1024 +
                             (size_t)L.rows_a * (L.width_a / kGroup) * 4;
-    if (allow_single_launch && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
+    if (allow_single_launch && int_codes && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
         tiny_lds <= kTinyMaxLds &&
         a->H / 16 <= tiny_max_down_workgroups(a->bits, a->shared_bits)) {
         TinyArgs d{};
@@ -255,7 +262,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
             d.a_by_pair = 1;
             d.gk_stream = 1;
             d.route.pair_rows = 1;
-        } else if (logits_in && a->T > kSplitRouteT) {
+        } else if (logits_in && int_codes && a->T > kSplitRouteT) {
             // routing spread over waves (one token each) in its own launch; the streaming
             // gate/up kernel, if it takes the shapes, then reads the tile records
             r.sync = static_cast<uint32_t*>(at(L.sync));
@@ -382,6 +389,52 @@ int rtn_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, 
     return hip_status(launch_quantize(w, w_dtype == W4A16_BF16, total_rows, cols, bits, packed, scales,
                                       static_cast<hipStream_t>(stream)),
                       "rtn_quantize_pack launch");
+}
+
+// Shared host checks of the format quantizers; 0 when the call may go ahead (or is empty).
+static int check_quant_args(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols, int col_mult,
+                            const void* packed, const void* scales, bool* empty) {
+    *empty = false;
+    if (w_dtype != W4A16_F32 && w_dtype != W4A16_BF16) return fail(W4A16_ERR_INVALID_ARG, "w_dtype = %d", w_dtype);
+    if (n_mats < 0 || rows < 0 || cols < 0) return fail(W4A16_ERR_INVALID_ARG, "negative size");
+    if (cols % col_mult) return fail(W4A16_ERR_INVALID_ARG, "cols = %lld is not a multiple of %d", (long long)cols, col_mult);
+    if (n_mats != 0 && rows > INT64_MAX / n_mats) return fail(W4A16_ERR_INVALID_ARG, "size overflow");
+    const int64_t total_rows = n_mats * rows;
+    if (total_rows == 0 || cols == 0) {
+        *empty = true;
+        return W4A16_OK;
+    }
+    if (cols > (int64_t(1) << 40) / total_rows || total_rows >= (int64_t(1) << 31))
+        return fail(W4A16_ERR_UNSUPPORTED, "matrix too large");
+    if (!w || !packed || !scales) return fail(W4A16_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(scales))
+        return fail(W4A16_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    return W4A16_OK;
+}
+
+int fp8_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols, int32_t* packed,
+                      float* scales, void* stream) {
+    g_last_error.clear();
+    bool empty;
+    if (int st = check_quant_args(w, w_dtype, n_mats, rows, cols, 4, packed, scales, &empty)) return st;
+    if (empty) return W4A16_OK;
+    return hip_status(launch_fp8_quantize(w, w_dtype == W4A16_BF16, n_mats * rows, cols, packed, scales,
+                                          static_cast<hipStream_t>(stream)),
+                      "fp8_quantize_pack launch");
+}
+
+int mxfp4_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows, int64_t cols, int method,
+                        int32_t* packed, uint8_t* scales, void* stream) {
+    g_last_error.clear();
+    if (method != W4A16_MXFP4_RTN && method != W4A16_MXFP4_MSE)
+        return fail(W4A16_ERR_INVALID_ARG, "method = %d", method);
+    bool empty;
+    if (int st = check_quant_args(w, w_dtype, n_mats, rows, cols, 32, packed, scales, &empty)) return st;
+    if (empty) return W4A16_OK;
+    return hip_status(launch_mxfp4_quantize(w, w_dtype == W4A16_BF16, n_mats * rows, cols,
+                                            method == W4A16_MXFP4_MSE, packed, scales,
+                                            static_cast<hipStream_t>(stream)),
+                      "mxfp4_quantize_pack launch");
 }
 
 size_t moe_w4a16_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t shared_I) {

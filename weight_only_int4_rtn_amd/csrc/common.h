@@ -95,6 +95,52 @@ __device__ __forceinline__ void dq8(uint32_t w0, uint32_t w1, u32x4_t& lo, u32x4
     }
 }
 
+// ------------------------------------------------- other code formats
+//
+// A code format CF is a template constant: 4 and 8 are the INT4 / INT8 group-128 RTN
+// codes above; kCfFp8 is FP8 E4M3 with one fp32 scale per output row; kCfMx4 is MXFP4,
+// E2M1 codes with one E8M0 (power-of-two) scale per 32 columns.  Both dequantise to
+// exact bf16 through the gfx950 conversions, so they need no offset seed; FP8's row scale
+// multiplies the fp32 partials like a group scale, MXFP4's block scale is applied inside
+// the conversion (a power of two: exact).
+constexpr int kCfFp8 = 0x18, kCfMx4 = 0x24;
+constexpr int cf_bits(int cf) { return cf & 0xF; }
+constexpr bool cf_int(int cf) { return cf == 4 || cf == 8; }
+// w4a16 weight_format values (0 INT, 1 FP8, 2 MXFP4) and the code format of each
+constexpr int cf_of(int fmt, int bits) { return fmt == 1 ? kCfFp8 : fmt == 2 ? kCfMx4 : bits; }
+
+// FP8 words w0 = k0..k3, w1 = k4..k7 (one E4M3 byte each) -> bf16 pairs in the K order
+// of dq4: (k0,k4) (k1,k5) (k2,k6) (k3,k7).  Exact (E4M3 is a subset of bf16).
+__device__ __forceinline__ u32x4_t dq_fp8(uint32_t w0, uint32_t w1) {
+    const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);   // w0.b0 w1.b0 w0.b1 w1.b1
+    const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);   // w0.b2 w1.b2 w0.b3 w1.b3
+    u32x4_t r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t1, 1.0f, true));
+    return r;
+}
+
+// MXFP4 word w = k0..k7 (one E2M1 nibble each, k0 lowest) -> bf16 pairs (k0,k4) (k1,k5)
+// (k2,k6) (k3,k7), each value times `scale` (a power of two: exact).
+__device__ __forceinline__ u32x4_t dq_mx4(uint32_t w, float scale) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;   // k0 k2 k4 k6 / k1 k3 k5 k7
+    const uint32_t x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);      // k0 k1 k2 k3
+    const uint32_t y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);      // k4 k5 k6 k7
+    const uint32_t b = x | (y << 4);                                    // bytes k_j | k_{j+4} << 4
+    u32x4_t r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 3));
+    return r;
+}
+
+// The power of two 2^(code - 127) of an E8M0 scale code (code 0: 0, outside the range the
+// quantizer produces for nonzero blocks).
+__device__ __forceinline__ float e8m0_scale(uint32_t code) { return __uint_as_float((code & 0xffu) << 23); }
+
 // Reorder eight natural-order bf16 activations X = (x0,x1)(x2,x3)(x4,x5)(x6,x7) to the
 // K order of the weight operands: (x0,x4) (x1,x5) (x2,x6) (x3,x7).  Within each block
 // of 8 columns, logical column j sits at position 2*(j % 4) + j / 4.
@@ -225,6 +271,12 @@ inline void launch(StageTimer* t, const char* name, void (*kernel)(KArgs...), di
 
 hipError_t launch_quantize(const void* w, bool bf16_in, int64_t total_rows, int64_t cols, int bits,
                            int32_t* packed, uint16_t* scales, hipStream_t s);
+// FP8 E4M3 with one fp32 scale per row; MXFP4 with one E8M0 scale per 32 columns (mse:
+// the scale-exponent search, else round-to-nearest exponents).
+hipError_t launch_fp8_quantize(const void* w, bool bf16_in, int64_t total_rows, int64_t cols, int32_t* packed,
+                               float* scales, hipStream_t s);
+hipError_t launch_mxfp4_quantize(const void* w, bool bf16_in, int64_t total_rows, int64_t cols, bool mse,
+                                 int32_t* packed, uint8_t* scales, hipStream_t s);
 
 struct RouteArgs {
     const float* logits;  // NULL: ids/wts are inputs
@@ -274,13 +326,14 @@ struct RouterArgs {
 constexpr int kRouterSmallT = 256;   // up to this many tokens: split-K workgroups per (16 tokens, 16 rows)
 hipError_t launch_router(const RouterArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
-struct ExpertSet {       // one family of experts sharing a code width
+struct ExpertSet {       // one family of experts sharing a code format
     const int32_t* w13;
-    const uint16_t* s13;
+    const uint16_t* s13;     // scales: bf16 [.., G] (INT), fp32 [..] (FP8) or E8M0 bytes [.., K/32] (MXFP4)
     const int32_t* w2;
     const uint16_t* s2;
     int64_t I;
-    int bits;
+    int bits;                // code width: 4 or 8 (FP8: 8, MXFP4: 4)
+    int fmt;                 // 0 INT (RTN group 128), 1 FP8 E4M3 per row, 2 MXFP4
 };
 
 struct DecodeArgs {

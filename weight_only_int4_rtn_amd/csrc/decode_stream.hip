@@ -839,6 +839,7 @@ int stream_workgroups() {
 
 bool stream_fits(const DecodeArgs& a, int max_tiles) {
     const int nwg = stream_workgroups() - (a.a_by_pair ? 1 : 0);   // pair mode: workgroup 0 only routes
+    if (a.routed.fmt != 0) return false;                           // INT codes only
     if (nwg <= 0 || a.H > kSMaxH || a.T > kSmallT) return false;
     const int64_t G = a.H / kGroup, KH = (G + 7) / 8;
     // the scale copies read 16 bytes from each row's first group of a K chunk: with an
@@ -881,7 +882,7 @@ bool pair_fits(const DecodeArgs& a) {
 }
 
 bool dk_stream_fits(const DecodeArgs& a) {
-    if (stream_workgroups() <= 0) return false;
+    if (stream_workgroups() <= 0 || a.routed.fmt != 0) return false;   // INT codes only
     if (a.routed.I > kDMaxI || (a.shared.bits && a.shared.I > kDMaxI)) return false;
     return a.H % 32 == 0 && a.rows_a * a.H * 4 < (int64_t)kDSkip;
 }

@@ -32,21 +32,25 @@ constexpr int kDkChunk = 2;   // groups of K per down work unit (group_dot2 assu
 namespace {
 
 // Two groups at once (two independent MFMA chains, interleaved), each started from `t`.
-template <int BITS>
+template <int CF>
 __device__ __forceinline__ void group_dot2(const u32x4_t (&av)[kDkChunk][4], const u32x4_t (&bw)[kDkChunk][2],
-                                           f32x4_t (&t)[kDkChunk]) {
+                                           f32x4_t (&t)[kDkChunk], const float (&xs)[kDkChunk]) {
     const uint32_t M = nibble_mask();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < kDkChunk; ++j) {
-            if constexpr (BITS == 4) {
+            if constexpr (CF == 4) {
                 t[j] = mfma16(av[j][i], dq4(bw[j][0][i], M), t[j]);
-            } else {
+            } else if constexpr (CF == 8) {
                 u32x4_t lo, hi;
                 dq8(bw[j][i >> 1][(2 * i) & 3], bw[j][i >> 1][(2 * i + 1) & 3], lo, hi, M);
                 t[j] = mfma16(av[j][i], lo, t[j]);
                 t[j] = mfma16(av[j][i], hi, t[j]);
+            } else if constexpr (CF == kCfFp8) {
+                t[j] = mfma16(av[j][i], dq_fp8(bw[j][i >> 1][(2 * i) & 3], bw[j][i >> 1][(2 * i + 1) & 3]), t[j]);
+            } else {
+                t[j] = mfma16(av[j][i], dq_mx4(bw[j][0][i], xs[j]), t[j]);
             }
         }
 }
@@ -60,11 +64,12 @@ __device__ __forceinline__ void group_dot2(const u32x4_t (&av)[kDkChunk][4], con
 // perm_pos(j)), so the down projection reads its A fragments as they lie.  TAGGED: one
 // 32-bit word per value, bf16 in the low half and `tag` in the high half, written through
 // to memory (sc1) for a reader on another XCD in the same launch; else plain bf16.
-template <int BITS, bool TAGGED = false>
+template <int CF, bool TAGGED = false>
 __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, const int32_t* __restrict__ w13e,
-                        const uint16_t* __restrict__ s13e, int n0, int tok, bool xok, int row_base, int rows,
+                        const uint8_t* __restrict__ s13e, int n0, int tok, bool xok, int row_base, int rows,
                         void* __restrict__ abuf, int64_t width_a, float* s_red, uint32_t abuf_bytes = 0,
                         uint32_t tag = 0) {
+    constexpr int BITS = cf_bits(CF);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int G = (int)(H / kGroup);
@@ -73,15 +78,13 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
     const int64_t row_bytes = H * BITS / 8;
     const uint8_t* wg = reinterpret_cast<const uint8_t*>(w13e) + (int64_t)(n0 + ml) * row_bytes + q * kLaneBytes;
     const uint8_t* wu = reinterpret_cast<const uint8_t*>(w13e) + (int64_t)(I_e + n0 + ml) * row_bytes + q * kLaneBytes;
-    const uint16_t* sg = s13e + (int64_t)(n0 + ml) * G;
-    const uint16_t* su = s13e + (int64_t)(I_e + n0 + ml) * G;
     const uint16_t* xr = x + (int64_t)tok * H + 32 * q;   // tok is a real token even when !xok
 
     f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
     constexpr int kGkPass = BITS == 4 ? kGkPass4 : 1;
     for (int gb = wave; gb < G; gb += kGkWaves * kGkPass) {
         u32x4_t bg[kGkPass][BITS / 4], bu[kGkPass][BITS / 4], av[kGkPass][4];
-        float scg[kGkPass], scu[kGkPass];
+        float scg[kGkPass], scu[kGkPass], xsg[kGkPass], xsu[kGkPass];
 #pragma unroll
         for (int j = 0; j < kGkPass; ++j) {
             const int g = gb + kGkWaves * j;
@@ -91,18 +94,18 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
                     bg[j][c] = load_stream16(wg + (int64_t)g * kGroupBytes + 16 * c);
                     bu[j][c] = load_stream16(wu + (int64_t)g * kGroupBytes + 16 * c);
                 }
-                scg[j] = bf16_to_f32(sg[g]);
-                scu[j] = bf16_to_f32(su[g]);
+                load_scales<CF>(s13e, scale_at<CF>(n0 + ml, G, g), q, &scg[j], &xsg[j]);
+                load_scales<CF>(s13e, scale_at<CF>(I_e + n0 + ml, G, g), q, &scu[j], &xsu[j]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) av[j][i] = load_act<BITS>(xr, xok, (int64_t)g * kGroup + 8 * i);
+                for (int i = 0; i < 4; ++i) av[j][i] = load_act<CF>(xr, xok, (int64_t)g * kGroup + 8 * i);
             }
         }
 #pragma unroll
         for (int j = 0; j < kGkPass; ++j) {
             if (gb + kGkWaves * j < G) {
-                const f32x4_t seed = offset_seed<BITS>(av[j]);
-                const f32x4_t tg = group_dot<BITS>(av[j], bg[j], seed);
-                const f32x4_t tu = group_dot<BITS>(av[j], bu[j], seed);
+                const f32x4_t seed = offset_seed<CF>(av[j]);
+                const f32x4_t tg = group_dot<CF>(av[j], bg[j], seed, xsg[j]);
+                const f32x4_t tu = group_dot<CF>(av[j], bu[j], seed, xsu[j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     accg[r] += scg[j] * tg[r];
@@ -141,7 +144,7 @@ __device__ void gk_tile(const uint16_t* __restrict__ x, int64_t H, int64_t I_e, 
 
 }  // namespace
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(64 * kGkWaves) void gk_decode_kernel(DecodeArgs a) {
     __shared__ float s_red[kGkWaves * 8 * 64];
     const int slot = blockIdx.y;
@@ -169,16 +172,17 @@ __global__ __launch_bounds__(64 * kGkWaves) void gk_decode_kernel(DecodeArgs a) 
         const int rows = min(16, count - mt);
         if (shared) {
             if constexpr (SBITS != 0)
-                gk_tile<SBITS>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? m : mt, ok, pos0 + mt, rows,
-                               a.abuf, a.width_a, s_red);
+                gk_tile<SBITS>(a.x, a.H, I_e, a.shared.w13, reinterpret_cast<const uint8_t*>(a.shared.s13), n0,
+                               ok ? m : mt, ok, pos0 + mt, rows, a.abuf, a.width_a, s_red);
         } else {
             const int mm = ok ? m : mt;
             const int tok = mm < kRecTokens ? (toks >> (kRecTokBits * mm)) & ((1 << kRecTokBits) - 1)
                                             : a.tokw[pos0 + mm].x;
-            const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
-            gk_tile<BITS>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
-                          a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, tok, ok, pos0 + mt, rows,
-                          a.abuf, a.width_a, s_red);
+            const int64_t w13_words = 2 * I_e * a.H * cf_bits(CF) / 32;
+            const uint8_t* s13e = reinterpret_cast<const uint8_t*>(a.routed.s13) +
+                                  (int64_t)e * expert_scale_bytes<CF>(2 * I_e, (int)(a.H / kGroup));
+            gk_tile<CF>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words, s13e, n0, tok, ok, pos0 + mt, rows,
+                        a.abuf, a.width_a, s_red);
         }
     }
 }
@@ -189,27 +193,33 @@ namespace {
 // kDkChunk groups of its K = I columns, for the workgroup's 16 output rows.
 struct DkUnit {
     const uint8_t* wrow;    // this lane's code bytes in row h0 + ml at the chunk's first group
-    const uint16_t* srow;   // scales of row h0 + ml at the chunk's first group
-    int pos0, count, ngroups, col0;
+    const uint8_t* sbase;   // scales of the unit's expert
+    int64_t srow;           // row h0 + ml of those scales
+    int G2;                 // groups along the expert's K = I
+    int pos0, count, ngroups, col0, g0;
     bool shared;
-    float sc[kDkChunk];     // the chunk's group scales, loaded with the codes
+    float sc[kDkChunk];     // the chunk's partial-sum scales, loaded with the codes (0: no group)
+    float xs[kDkChunk];     // the chunk's conversion scales (MXFP4 blocks; else 1)
 };
 
 // Issues the unit's code and scale loads (nothing waits for them here).
-template <int BITS>
+template <int CF>
 __device__ __forceinline__ void dk_load_codes(DkUnit& u, u32x4_t (&bw)[kDkChunk][2]) {
+    constexpr int BITS = cf_bits(CF);
     constexpr int kGroupBytes = kGroup * BITS / 8;
+    const int q = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int j = 0; j < kDkChunk; ++j)
         if (j < u.ngroups) {
 #pragma unroll
             for (int c = 0; c < BITS / 4; ++c)
                 bw[j][c] = load_stream16(u.wrow + (int64_t)j * kGroupBytes + 16 * c);
-            u.sc[j] = bf16_to_f32(u.srow[j]);
+            load_scales<CF>(u.sbase, scale_at<CF>(u.srow, u.G2, u.g0 + j), q, &u.sc[j], &u.xs[j]);
         } else {
 #pragma unroll
             for (int c = 0; c < 2; ++c) bw[j][c] = u32x4_t{0u, 0u, 0u, 0u};
             u.sc[j] = 0.f;
+            u.xs[j] = 1.f;
         }
 }
 
@@ -219,7 +229,7 @@ __device__ __forceinline__ void dk_load_codes(DkUnit& u, u32x4_t (&bw)[kDkChunk]
 // seed -OFF * sum(a); with them (xsum(pos, g) = sum of a row's group g, fp32) the MFMA
 // chains start at zero and the offset term is removed with one FMA per element, which
 // halves the MFMAs of a unit.
-template <int BITS, bool XSUM, typename TokW, typename AFetch, typename XSum>
+template <int CF, bool XSUM, typename TokW, typename AFetch, typename XSum>
 __device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], TokW tokw, AFetch afetch, XSum xsum,
                         float* yacc, const float* sgate) {
     const int lane = threadIdx.x & 63;
@@ -257,15 +267,15 @@ __device__ void dk_unit(const DkUnit& u, const u32x4_t (&bw)[kDkChunk][2], TokW 
         }
         f32x4_t t[kDkChunk];
 #pragma unroll
-        for (int j = 0; j < kDkChunk; ++j) t[j] = XSUM ? f32x4_t{0.f, 0.f, 0.f, 0.f} : offset_seed<BITS>(av[j]);
-        group_dot2<BITS>(av, bw, t);   // a missing second group has zero a and scale 0
+        for (int j = 0; j < kDkChunk; ++j) t[j] = XSUM ? f32x4_t{0.f, 0.f, 0.f, 0.f} : offset_seed<CF>(av[j]);
+        group_dot2<CF>(av, bw, t, u.xs);   // a missing second group has zero a and scale 0
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kDkChunk; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = t[j][r];
-                if constexpr (XSUM) v -= code_offset<BITS>() * xsum(pr[r], g0 + (j < u.ngroups ? j : 0));
+                if constexpr (XSUM && cf_int(CF)) v -= code_offset<CF>() * xsum(pr[r], g0 + (j < u.ngroups ? j : 0));
                 acc[r] += u.sc[j] * v;   // sc is 0 for a missing group
             }
 #pragma unroll
@@ -307,16 +317,21 @@ __device__ __forceinline__ DkUnit dk_make_unit(const ExpertSet& routed, const Ex
     const int g0 = chunk * kDkChunk;
     r.ngroups = min(kDkChunk, G2 - g0);
     r.col0 = g0 * kGroup;
+    r.g0 = g0;
+    r.G2 = G2;
     const int64_t row_bytes = I_e * es->bits / 8;
     const uint8_t* w2e = reinterpret_cast<const uint8_t*>(es->w2) + ebase * H * row_bytes;
     r.wrow = w2e + (int64_t)(h0 + ml) * row_bytes + (int64_t)g0 * (kGroup * es->bits / 8) + q * (32 * es->bits / 8);
-    r.srow = es->s2 + ebase * H * G2 + (int64_t)(h0 + ml) * G2 + g0;
+    // scales: INT bf16 [H, G2]; FP8 fp32 [H]; MXFP4 E8M0 [H, 4 G2]  (per expert)
+    const int64_t es_bytes = es->fmt == 1 ? H * 4 : es->fmt == 2 ? H * G2 * 4 : H * G2 * 2;
+    r.sbase = reinterpret_cast<const uint8_t*>(es->s2) + ebase * es_bytes;
+    r.srow = h0 + ml;
     return r;
 }
 
 }  // namespace
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) {
     __shared__ float s_y[kDkWaves][kSmallT * 16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -335,21 +350,25 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
     auto recf = [rec](int slot) { return rec[slot]; };
     // software pipeline: the next unit's codes are in flight while this one computes
     u32x4_t cur[kDkChunk][2], nxt[kDkChunk][2];
-    int bits = BITS;
+    // a unit uses the routed code format unless it is a shared-expert unit of another one
+    int bits = 0;
+    bool rt = true;
     DkUnit cu;
     if (u < n_units) {
         cu = dk_make_unit(a.routed, a.shared, a.H, a.T, a.k, recf, u, n_routed_units, nch, nch_s, h0, &bits);
-        if (bits == BITS) dk_load_codes<BITS>(cu, cur);
-        else if constexpr (SBITS != 0) dk_load_codes<SBITS>(cu, cur);
+        rt = !cu.shared || SBITS == CF;
+        if (rt) dk_load_codes<CF>(cu, cur);
+        else if constexpr (SBITS != 0 && SBITS != CF) dk_load_codes<SBITS>(cu, cur);
     }
     while (u < n_units) {
         const int un = u + V;
-        int nbits = BITS;
+        bool nrt = true;
         DkUnit nu;
         if (un < n_units) {
-            nu = dk_make_unit(a.routed, a.shared, a.H, a.T, a.k, recf, un, n_routed_units, nch, nch_s, h0, &nbits);
-            if (nbits == BITS) dk_load_codes<BITS>(nu, nxt);
-            else if constexpr (SBITS != 0) dk_load_codes<SBITS>(nu, nxt);
+            nu = dk_make_unit(a.routed, a.shared, a.H, a.T, a.k, recf, un, n_routed_units, nch, nch_s, h0, &bits);
+            nrt = !nu.shared || SBITS == CF;
+            if (nrt) dk_load_codes<CF>(nu, nxt);
+            else if constexpr (SBITS != 0 && SBITS != CF) dk_load_codes<SBITS>(nu, nxt);
         }
         const int2* tokw = a.tokw;
         auto tw = [tokw](int pos) { return tokw[pos]; };
@@ -360,8 +379,8 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
             return load16_or_zero(p, ok, p);
         };
         auto nox = [](int, int) { return 0.f; };
-        if (bits == BITS) dk_unit<BITS, false>(cu, cur, tw, af, nox, yacc, a.shared_gate);
-        else if constexpr (SBITS != 0) dk_unit<SBITS, false>(cu, cur, tw, af, nox, yacc, a.shared_gate);
+        if (rt) dk_unit<CF, false>(cu, cur, tw, af, nox, yacc, a.shared_gate);
+        else if constexpr (SBITS != 0 && SBITS != CF) dk_unit<SBITS, false>(cu, cur, tw, af, nox, yacc, a.shared_gate);
         if (un >= n_units) break;
 #pragma unroll
         for (int j = 0; j < kDkChunk; ++j) {
@@ -369,7 +388,7 @@ __global__ __launch_bounds__(64 * kDkWaves) void dk_decode_kernel(DecodeArgs a) 
             cur[j][1] = nxt[j][1];
         }
         cu = nu;
-        bits = nbits;
+        rt = nrt;
         u = un;
     }
     __syncthreads();
@@ -530,14 +549,14 @@ __device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
         if (e < 0) return;   // dropped pair: the down workgroups skip its row
         const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
         gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
-                            a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup), n0, t, ml == 0, p, 1, a.tags,
-                            a.width_a, s_red, a.tag_bytes, tag);
+                            reinterpret_cast<const uint8_t*>(a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup)),
+                            n0, t, ml == 0, p, 1, a.tags, a.width_a, s_red, a.tag_bytes, tag);
     } else if constexpr (SBITS != 0) {
         const int64_t I_e = a.shared.I;
         if (p > Tk || n0 >= I_e) return;
         const bool ok = ml < a.T;
-        gk_tile<SBITS, true>(a.x, a.H, I_e, a.shared.w13, a.shared.s13, n0, ok ? ml : 0, ok, Tk, a.T, a.tags,
-                             a.width_a, s_red, a.tag_bytes, tag);
+        gk_tile<SBITS, true>(a.x, a.H, I_e, a.shared.w13, reinterpret_cast<const uint8_t*>(a.shared.s13), n0,
+                             ok ? ml : 0, ok, Tk, a.T, a.tags, a.width_a, s_red, a.tag_bytes, tag);
     }
 }
 
@@ -883,7 +902,7 @@ __global__ __launch_bounds__(256) void head_init_kernel(uint32_t* head) {
 
 namespace {
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int max_active = (int)std::min<int64_t>((int64_t)a.E, (int64_t)a.T * a.k);
     if (a.gk_stream) {   // stream_fits (or pair_fits) holds
@@ -891,11 +910,11 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     } else {
         const int64_t Imax = std::max(a.routed.I, SBITS ? a.shared.I : (int64_t)0);
         const dim3 gk_grid((unsigned)(Imax / 16), (unsigned)(max_active + (SBITS ? 1 : 0)));
-        launch(t, "gk_decode", gk_decode_kernel<BITS, SBITS>, gk_grid, dim3(64 * kGkWaves), s, 0u, a);
+        launch(t, "gk_decode", gk_decode_kernel<CF, SBITS>, gk_grid, dim3(64 * kGkWaves), s, 0u, a);
     }
     if (dk_stream_fits(a)) return launch_dk_stream(a, s, t);
     const dim3 dk_grid((unsigned)(a.H / 16), (unsigned)a.splits);
-    launch(t, "dk_decode", dk_decode_kernel<BITS, SBITS>, dk_grid, dim3(64 * kDkWaves), s, 0u, a);
+    launch(t, "dk_decode", dk_decode_kernel<CF, SBITS>, dk_grid, dim3(64 * kDkWaves), s, 0u, a);
     if (a.splits > 1) {
         const int64_t n = (int64_t)a.T * a.H;
         launch(t, "dk_combine", dk_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u,
@@ -904,18 +923,23 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     return hipGetLastError();
 }
 
+template <int CF>
+hipError_t launch_decode_cf(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (sb == 0) return launch_decode_t<CF, 0>(a, s, t);
+    if (sb == 4) return launch_decode_t<CF, 4>(a, s, t);
+    return launch_decode_t<CF, 8>(a, s, t);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
-    const int sb = a.shared.bits;
-    if (a.routed.bits == 4) {
-        if (sb == 0) return launch_decode_t<4, 0>(a, s, t);
-        if (sb == 4) return launch_decode_t<4, 4>(a, s, t);
-        return launch_decode_t<4, 8>(a, s, t);
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_decode_cf<4>(a, s, t);
+        case 8: return launch_decode_cf<8>(a, s, t);
+        case kCfFp8: return launch_decode_cf<kCfFp8>(a, s, t);
+        default: return launch_decode_cf<kCfMx4>(a, s, t);
     }
-    if (sb == 0) return launch_decode_t<8, 0>(a, s, t);
-    if (sb == 4) return launch_decode_t<8, 4>(a, s, t);
-    return launch_decode_t<8, 8>(a, s, t);
 }
 
 }  // namespace w4a16

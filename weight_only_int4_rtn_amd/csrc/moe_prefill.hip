@@ -21,11 +21,16 @@
 // s_waitcnt vmcnt and a plain s_barrier covers the other waves; a __syncthreads() there
 // would also wait for the later steps' loads.
 //
-// Codes enter the MFMA as exact bf16 integers (see dq4 / dq8 in common.h): the
+// INT codes enter the MFMA as exact bf16 integers (see dq4 / dq8 in common.h): the
 // accumulator of a group starts from -OFF * (sum of the group's activations) and the
-// group scale multiplies the fp32 partial.
+// group scale multiplies the fp32 partial.  FP8 E4M3 codes (one fp32 scale per code row)
+// and MXFP4 codes (an E8M0 scale per 32 columns) become exact bf16 values through the
+// hardware conversions (dq_fp8 / dq_mx4): no seed; the FP8 row scale multiplies the
+// partial like a group scale, the MXFP4 block scale is applied by the conversion.  The
+// per-step scale copy brings one 4-byte word per code row in every format: the word
+// holding the bf16 group scale, the fp32 row scale, or the group's four E8M0 bytes.
 //
-// Routed items (code width BITS) and the shared expert's items (SBITS) are walked as two
+// Routed items (code format CF) and the shared expert's items (SCF, INT) are walked as two
 // separate streams by every workgroup.
 #include "common.h"
 #include "dma.h"
@@ -138,9 +143,29 @@ struct IssueState {
     uint32_t s_off;       // byte offset of the lane's scale at group 0 (kOob: lanes 32..63)
 };
 
-template <int BITS, bool GATE_UP>
+// Byte offset of code row `row`'s scale word at group 0, and the scale buffer's bytes, of
+// an expert whose rows hold K columns (INT: bf16 [rows, K/128]; FP8: fp32 [rows];
+// MXFP4: E8M0 bytes [rows, K/32]).
+template <int CF>
+__device__ __forceinline__ uint32_t scale_off(int row, int G) {
+    if constexpr (CF == kCfFp8) return (uint32_t)row * 4;
+    else if constexpr (CF == kCfMx4) return (uint32_t)row * G * 4;
+    else return (uint32_t)row * G * 2;
+}
+template <int CF>
+__device__ __forceinline__ int64_t scale_bytes(int64_t rows, int G) {
+    return CF == kCfFp8 ? rows * 4 : CF == kCfMx4 ? rows * G * 4 : rows * G * 2;
+}
+// The scale buffer of expert eb (its rows x K/128 groups).
+template <int CF>
+__device__ __forceinline__ const uint8_t* scale_base(const uint16_t* s, int64_t eb, int64_t rows, int G) {
+    return reinterpret_cast<const uint8_t*>(s) + eb * scale_bytes<CF>(rows, G);
+}
+
+template <int CF, bool GATE_UP>
 __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const ExpertSet& es, const int (&tok)[5],
                               IssueState& st) {
+    constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t I_e = es.I;
@@ -165,8 +190,8 @@ __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const Expert
         }
         st.seed_r = dma_rsrc(a.xsum, (uint32_t)(a.T * G * 4));
         st.seed_off = lane < 16 ? (uint32_t)tok[4] * G * 4 : kOob;
-        st.s_r = dma_rsrc(es.s13 + eb * 2 * I_e * G, (uint32_t)(2 * I_e * G * 2));
-        st.s_off = lane < 32 ? (uint32_t)(gk_code_row(32 * wave + lane, it.nblk, I_e) * G * 2) : kOob;
+        st.s_r = dma_rsrc(scale_base<CF>(es.s13, eb, 2 * I_e, G), (uint32_t)scale_bytes<CF>(2 * I_e, G));
+        st.s_off = lane < 32 ? scale_off<CF>(gk_code_row(32 * wave + lane, it.nblk, I_e), G) : kOob;
     } else {
         const int G2 = (int)(I_e / kGroup);
         const int GW = (int)(a.width_a / kGroup);
@@ -188,8 +213,8 @@ __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const Expert
         }
         st.seed_r = dma_rsrc(a.asum, (uint32_t)(a.rows_a * GW * 4));
         st.seed_off = lane < 16 ? (uint32_t)(it.orow0 + min(16 * wave + lane, it.count - 1)) * GW * 4 : kOob;
-        st.s_r = dma_rsrc(es.s2 + eb * a.H * G2, (uint32_t)(a.H * G2 * 2));
-        st.s_off = lane < 32 ? (uint32_t)((h0 + 32 * wave + lane) * G2 * 2) : kOob;
+        st.s_r = dma_rsrc(scale_base<CF>(es.s2, eb, a.H, G2), (uint32_t)scale_bytes<CF>(a.H, G2));
+        st.s_off = lane < 32 ? scale_off<CF>(h0 + 32 * wave + lane, G2) : kOob;
     }
 }
 
@@ -226,8 +251,9 @@ __device__ __forceinline__ void item_tokens(const Item& it, const int* s_tok, in
 }
 
 // stage: LDS byte address of the stage the step goes to.
-template <int BITS>
+template <int CF>
 __device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t stage) {
+    constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t A = stage, B = stage + kAStageBytes, S = B + P::kBStageBytes, SC = S + kSeedSlots * 4;
@@ -237,7 +263,9 @@ __device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t
     for (int j = 0; j < P::kBLoads; ++j)
         dma16(st.b_r, B + (wave * P::kBLoads + j) * 1024, st.b_off[j], (uint32_t)g * P::kRowBytes);
     dma4(st.seed_r, S + wave * 256, st.seed_off, (uint32_t)g * 4);
-    dma4(st.s_r, SC + wave * 256, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
+    if constexpr (CF == kCfFp8) dma4(st.s_r, SC + wave * 256, st.s_off, 0);   // the row's one scale
+    else if constexpr (CF == kCfMx4) dma4(st.s_r, SC + wave * 256, st.s_off + (uint32_t)g * 4, 0);
+    else dma4(st.s_r, SC + wave * 256, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
 }
 
 // ------------------------------------------------------------------- compute
@@ -245,10 +273,11 @@ __device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t
 // One step of one wave: its 64 x 64 block (4 M-subtiles x 4 code subtiles) for one
 // group, accumulated into acc with the group scales (D column ml is code row R's).
 // sodd: bit b set when code subtile b's scale sits in the high half of its word.
-template <int BITS>
+template <int CF>
 __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4]) {
+    constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
-    constexpr float kOff = BITS == 4 ? 136.0f : 2304.0f;
+    constexpr float kOff = CF == 4 ? 136.0f : CF == 8 ? 2304.0f : 0.0f;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int wm = wave >> 2, wn = wave & 3;
@@ -265,9 +294,13 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
         const int r = 64 * wm + 16 * mi + ml;
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[mi][i] = *reinterpret_cast<const u32x4_t*>(A + a_swz(r, 4 * q + i) * 8);
-        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(S + seed_slot(64 * wm + 16 * mi + 4 * q));
+        if constexpr (cf_int(CF)) {
+            const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(S + seed_slot(64 * wm + 16 * mi + 4 * q));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) seed[mi][e] = -kOff * xs[e];
+            for (int e = 0; e < 4; ++e) seed[mi][e] = -kOff * xs[e];
+        } else {
+            seed[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -279,28 +312,38 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
             braw[c] = *reinterpret_cast<const u32x4_t*>(B + R * P::kRowBytes + ((lc ^ b_swizzle<BITS>(R)) * 16));
         }
         const uint32_t sw = SC[scale_slot(R)];
-        const float sc = bf16_to_f32(((sodd >> b) & 1) ? (sw >> 16) : (sw & 0xffffu));
+        float sc = 1.f, xs = 1.f;   // partial's scale; MXFP4: the conversion's block scale
+        if constexpr (CF == kCfFp8) sc = __uint_as_float(sw);
+        else if constexpr (CF == kCfMx4) xs = e8m0_scale(sw >> (8 * q));   // this lane's block: columns 32q..
+        else sc = bf16_to_f32(((sodd >> b) & 1) ? (sw >> 16) : (sw & 0xffffu));
         f32x4_t t[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) t[mi] = seed[mi];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             u32x4_t lo, hi;
-            if constexpr (BITS == 4) {
+            if constexpr (CF == 4) {
                 lo = dq4(braw[0][i], M);
-            } else {
+            } else if constexpr (CF == 8) {
                 dq8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3], lo, hi, M);
+            } else if constexpr (CF == kCfFp8) {
+                lo = dq_fp8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3]);
+            } else {
+                lo = dq_mx4(braw[0][i], xs);
             }
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 t[mi] = mfma16(av[mi][i], lo, t[mi]);
-                if constexpr (BITS == 8) t[mi] = mfma16(av[mi][i], hi, t[mi]);
+                if constexpr (CF == 8) t[mi] = mfma16(av[mi][i], hi, t[mi]);
             }
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) acc[mi][b][r2] += sc * t[mi][r2];
+            for (int r2 = 0; r2 < 4; ++r2) {
+                if constexpr (CF == kCfMx4) acc[mi][b][r2] += t[mi][r2];
+                else acc[mi][b][r2] += sc * t[mi][r2];
+            }
     }
 }
 
@@ -376,10 +419,10 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
 // remapped so that each XCD, w mod 8, takes one contiguous range: an expert's tiles share
 // that XCD's L2).  The items are resolved once into LDS; the steps of all of them form
 // one pipelined stream.
-template <int BITS, bool GATE_UP, bool SHARED>
+template <int CF, bool GATE_UP, bool SHARED>
 __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int total, uint8_t* smem,
                           Item* s_items, float* s_asum, int* s_cnt, int* s_tok) {
-    using P = Pipe<BITS>;
+    using P = Pipe<cf_bits(CF)>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = (total + 7) / 8;
     __syncthreads();   // the previous walk's LDS use is over
@@ -424,10 +467,10 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         item_tokens(s_items[0], s_tok, tok);
     }
     IssueState st;
-    prepare_issue<BITS, GATE_UP>(a, s_items[0], es, tok, st);
+    prepare_issue<CF, GATE_UP>(a, s_items[0], es, tok, st);
     const uint32_t lds0 = lds_offset(smem);
     auto issue_next = [&]() {
-        issue_step<BITS>(st, gi, lds0 + (uint32_t)(issued % P::kStages) * P::kStageBytes);
+        issue_step<CF>(st, gi, lds0 + (uint32_t)(issued % P::kStages) * P::kStageBytes);
         ++issued;
         if (++gi == G && ii + 1 < n_items) {
             ++ii;
@@ -437,7 +480,7 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
                 if (__builtin_amdgcn_readfirstlane(wave) == 0 && ii + 1 < n_items)
                     copy_item_tokens(a, s_items[ii + 1], lds_tok + ((ii + 1) & 1) * MT * 4);
             }
-            prepare_issue<BITS, GATE_UP>(a, s_items[ii], es, tok, st);
+            prepare_issue<CF, GATE_UP>(a, s_items[ii], es, tok, st);
         }
     };
     for (int p = 0; p < P::kStages - 1 && issued < total_steps; ++p) issue_next();
@@ -486,7 +529,7 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         bar();   // every wave's step-s data is in LDS, and stage (s - 1) is no longer read
         if (epi) finish_item();
         if (issued < total_steps) issue_next();
-        compute_step<BITS>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc);
+        compute_step<CF>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc);
         if (++gc == G) {
             epi = true;
             gc = 0;
@@ -496,25 +539,25 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
     if (epi) finish_item();
 }
 
-template <int BITS>
+template <int CF>
 constexpr uint32_t pipe_lds_bytes() {
-    return Pipe<BITS>::kStages * Pipe<BITS>::kStageBytes;
+    return Pipe<cf_bits(CF)>::kStages * Pipe<cf_bits(CF)>::kStageBytes;
 }
 
 }  // namespace
 
 // Dynamic LDS: the stages of the larger pipeline, then the item list and the row-sum
 // scratch.
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(kPThreads) void gk_prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
+    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<CF>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
     Item* s_items = reinterpret_cast<Item*>(smem + kPipe);
     float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
     int* s_tok = reinterpret_cast<int*>(s_asum + 4 * MT);   // two items' tokens
     __shared__ int s_cnt[kPWaves];
     const int nb = (int)(a.routed.I / kGroup);
-    run_items<BITS, true, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, s_tok);
+    run_items<CF, true, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, s_tok);
     if constexpr (SBITS != 0) {
         const int nbs = (int)(a.shared.I / kGroup);
         run_items<SBITS, true, true>(a, a.shared, nbs, ((a.T + MT - 1) / MT) * nbs, smem, s_items, s_asum, s_cnt,
@@ -522,15 +565,15 @@ __global__ __launch_bounds__(kPThreads) void gk_prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
+    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<CF>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
     Item* s_items = reinterpret_cast<Item*>(smem + kPipe);
     float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
     __shared__ int s_cnt[kPWaves];
     const int nb = (int)((a.H + NT - 1) / NT);
-    run_items<BITS, false, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, nullptr);
+    run_items<CF, false, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, nullptr);
     if constexpr (SBITS != 0)
         run_items<SBITS, false, true>(a, a.shared, nb, ((a.T + MT - 1) / MT) * nb, smem, s_items, s_asum, s_cnt,
                                       nullptr);
@@ -583,15 +626,15 @@ unsigned prefill_grid(int64_t max_items) {
     return (unsigned)((g + 7) / 8 * 8);
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
-    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<BITS>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
+    constexpr uint32_t kPipe = std::max(pipe_lds_bytes<CF>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
     constexpr uint32_t lds = kPipe + kMaxItems * sizeof(Item) + 4 * MT * 4 + 2 * MT * 4;
     static_assert(lds + 64 <= 160 * 1024, "LDS budget of one workgroup");
     static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gk_prefill_kernel<BITS, SBITS>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gk_prefill_kernel<CF, SBITS>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dk_prefill_kernel<BITS, SBITS>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dk_prefill_kernel<CF, SBITS>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         return true;
     }();
@@ -599,24 +642,29 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) 
     const int64_t shared_tiles = SBITS ? (a.T + MT - 1) / MT : 0;
     const int64_t gk_items = std::max(a.max_tiles * (a.routed.I / kGroup), shared_tiles * (a.shared.I / kGroup));
     const int64_t dk_items = std::max(a.max_tiles, shared_tiles) * ((a.H + NT - 1) / NT);
-    launch(t, "gk_prefill", gk_prefill_kernel<BITS, SBITS>, dim3(prefill_grid(gk_items)), dim3(kPThreads), s, lds, a);
-    launch(t, "dk_prefill", dk_prefill_kernel<BITS, SBITS>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
+    launch(t, "gk_prefill", gk_prefill_kernel<CF, SBITS>, dim3(prefill_grid(gk_items)), dim3(kPThreads), s, lds, a);
+    launch(t, "dk_prefill", dk_prefill_kernel<CF, SBITS>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
     launch(t, "finalize", finalize_kernel, dim3((unsigned)((a.H / 8 + 255) / 256 * a.T)), dim3(256), s, 0u, a);
     return hipGetLastError();
+}
+
+template <int CF>
+hipError_t launch_prefill_cf(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (sb == 0) return launch_prefill_t<CF, 0>(a, s, t);
+    if (sb == 4) return launch_prefill_t<CF, 4>(a, s, t);
+    return launch_prefill_t<CF, 8>(a, s, t);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
-    const int sb = a.shared.bits;
-    if (a.routed.bits == 4) {
-        if (sb == 0) return launch_prefill_t<4, 0>(a, s, t);
-        if (sb == 4) return launch_prefill_t<4, 4>(a, s, t);
-        return launch_prefill_t<4, 8>(a, s, t);
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_prefill_cf<4>(a, s, t);
+        case 8: return launch_prefill_cf<8>(a, s, t);
+        case kCfFp8: return launch_prefill_cf<kCfFp8>(a, s, t);
+        default: return launch_prefill_cf<kCfMx4>(a, s, t);
     }
-    if (sb == 0) return launch_prefill_t<8, 0>(a, s, t);
-    if (sb == 4) return launch_prefill_t<8, 4>(a, s, t);
-    return launch_prefill_t<8, 8>(a, s, t);
 }
 
 }  // namespace w4a16
