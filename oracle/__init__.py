@@ -41,6 +41,7 @@ from .rtn_moe import (  # noqa: F401
     expert_ffn,
     moe_ffn,
     moe_layer,
+    linear,
 )
 
 from . import formats  # noqa: E402,F401

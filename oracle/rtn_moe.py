@@ -346,3 +346,24 @@ def moe_layer(x_bits, logits, k: int, w13, s13, w2, s2, bits: int, tokens=None,
                 shared=shared, residual_bits=residual_bits, shared_gate=shared_gate,
                 weight_format=weight_format)
     return y, r
+
+
+# ---------------------------------------------------------------------------
+# Dense projections (the non-expert INT8 matrices of the recipe)
+# ---------------------------------------------------------------------------
+
+def linear(x_bits, packed, scales, bits: int, residual_bits=None, weight_format: str = "int"):
+    """``y = x . W_hat^T (+ residual)``, fp64, for a quantized ``[N, K]`` matrix.
+
+    Page "Nex-N2.5-mini Int4-Int8Mix", Recipe table: the attention q/k/v/o
+    projections and the Gated DeltaNet in_proj_qkv, in_proj_z and out_proj are
+    INT8, symmetric, group 128.  ``x_bits`` uint16 bf16 ``[T, K]``; ``packed`` /
+    ``scales`` as :func:`quantize_pack` (or the other formats, see
+    :func:`dequantize_as`).  Returns fp64 ``[T, N]``.
+    """
+    x = f32_from_bf16_bits(x_bits).astype(np.float64)
+    W = dequantize_as(packed, scales, bits, weight_format)
+    y = x @ W.T
+    if residual_bits is not None:
+        y = y + f32_from_bf16_bits(residual_bits).astype(np.float64)
+    return y

@@ -183,3 +183,34 @@ def test_shared_expert_and_residual_against_torch_functional(shared_bits):
     # the shared term is really there: dropping it moves the result by far more than rounding
     no_shared = oracle.moe_ffn(x_bits, ids, w, p13, s13, p2, s2, 4, residual_bits=res_bits)
     assert np.abs(no_shared - ys).max() > 1e-3
+
+
+# ------------------------------------------------------------ dense projections
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_linear_against_torch_functional(bits):
+    """y = x W_hat^T (+ residual) against torch.nn.functional.linear in fp64."""
+    T, K, N = 5, 384, 256
+    w = synth.expert_weight(12, 0, 0, 6, N, K)
+    p, s = oracle.quantize_pack(w, bits)
+    x_bits = synth.activations_bf16(12, T, K)
+    r_bits = synth.activations_bf16(13, T, N)
+    y = oracle.linear(x_bits, p, s, bits, residual_bits=r_bits)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).double()
+    r = torch.from_numpy(r_bits.view(np.int16)).view(torch.bfloat16).double()
+    ref = F.linear(x, torch.from_numpy(oracle.dequantize(p, s, bits)).double()) + r
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_linear_closed_form_on_a_lossless_grid():
+    """W = q * 2^-7 with one code 127 per group: y = (x . q^T) * 2^-7 exactly."""
+    rng = np.random.default_rng(3)
+    q = rng.integers(-127, 128, size=(16, 256))
+    q[:, 0] = 127
+    q[:, 128] = -127
+    w = (q * 2.0 ** -7).astype(np.float32)
+    p, s = oracle.quantize_pack(w, 8)
+    assert np.all(oracle.f32_from_bf16_bits(s) == 2.0 ** -7)
+    x_bits = synth.activations_bf16(14, 3, 256)
+    x = oracle.f32_from_bf16_bits(x_bits).astype(np.float64)
+    assert np.array_equal(oracle.linear(x_bits, p, s, 8), (x @ q.T.astype(np.float64)) * 2.0 ** -7)
