@@ -310,6 +310,39 @@ int moe_w4a16_forward(const moe_w4a16_args* args, void* stream);
 int moe_w4a16_forward_noalloc(const moe_w4a16_args* args, void* stream);
 
 /*
+ * w4a16_linear - a dense projection y = x . W^T (+ residual) with quantized W.
+ *
+ * Page "Nex-N2.5-mini Int4-Int8Mix", Recipe table: the attention q/k/v/o projections and
+ * the Gated DeltaNet in_proj_qkv, in_proj_z and out_proj are INT8, symmetric, group 128.
+ * Runs on the routed experts' down-projection kernels as one expert that every token uses
+ * with weight 1, so every code format of moe_w4a16_forward is accepted.
+ *   T tokens, K input columns (multiple of 128, <= 8192), N output rows (multiple of 128,
+ *   <= 16384); bits / weight_format as in moe_w4a16_args (INT: bits 4 or 8, group 128).
+ *   x        bf16 [T, K]
+ *   w, s     W packed [N, K*bits/32] and its scales, as the matching quantizer writes them
+ *            (INT: bf16 [N, K/128]; FP8: fp32 [N]; MXFP4: E8M0 bytes [N, K/32])
+ *   residual bf16 [T, N] added before the one rounding, or NULL; y may alias it, not x
+ *   y        bf16 [T, N]: fp32 accumulation, rounded once
+ *   workspace device scratch of w4a16_linear_workspace_size(T, K, N) bytes (no state is
+ *            kept in it between calls)
+ * Errors as moe_w4a16_forward.
+ */
+typedef struct w4a16_linear_args {
+    int64_t T, K, N;
+    int32_t bits, group, weight_format;
+    const uint16_t* x;
+    const int32_t* w;
+    const void* s;
+    const uint16_t* residual;
+    uint16_t* y;
+    void* workspace;
+    size_t workspace_bytes;
+} w4a16_linear_args;
+
+size_t w4a16_linear_workspace_size(int64_t T, int64_t K, int64_t N);
+int w4a16_linear(const w4a16_linear_args* args, void* stream);
+
+/*
  * moe_w4a16_forward_timed - the same work as moe_w4a16_forward, each kernel launched with
  * a start and a stop HIP event bound to its own dispatch (hipExtLaunchKernelGGL), then a
  * wait for the last stop event (this call synchronises with the stream's work up to that

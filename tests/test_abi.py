@@ -54,20 +54,21 @@ def test_abi_version_and_status_strings(L):
     assert _lib.status_string(99) == "W4A16_UNKNOWN_STATUS"
 
 
-def test_struct_layout_matches_c_compiler():
-    fields = [f[0] for f in _lib.MoeArgs._fields_]
+@pytest.mark.parametrize("cstruct,ctype", [(_lib.MoeArgs, "moe_w4a16_args"), (_lib.LinearArgs, "w4a16_linear_args")])
+def test_struct_layout_matches_c_compiler(cstruct, ctype):
+    fields = [f[0] for f in cstruct._fields_]
     prog = "#include <stdio.h>\n#include <stddef.h>\n#include \"w4a16.h\"\nint main(void){\n"
-    prog += 'printf("%zu\\n", sizeof(moe_w4a16_args));\n'
+    prog += f'printf("%zu\\n", sizeof({ctype}));\n'
     for f in fields:
-        prog += f'printf("%zu\\n", offsetof(moe_w4a16_args, {f}));\n'
+        prog += f'printf("%zu\\n", offsetof({ctype}, {f}));\n'
     prog += "return 0;}\n"
     with tempfile.TemporaryDirectory() as d:
         src, exe = os.path.join(d, "p.c"), os.path.join(d, "p")
         open(src, "w").write(prog)
         subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
         got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
-    assert got[0] == C.sizeof(_lib.MoeArgs)
-    assert got[1:] == [getattr(_lib.MoeArgs, f).offset for f in fields]
+    assert got[0] == C.sizeof(cstruct)
+    assert got[1:] == [getattr(cstruct, f).offset for f in fields]
 
 
 def base_args(T=1, H=2048, I=512, E=256, k=8, bits=4):
@@ -244,3 +245,26 @@ def test_forward_rejects_bad_weight_format(L, fmt, bits, expect):
     a = base_args(bits=bits)
     a.weight_format = fmt
     assert forward_status(L, a) == expect
+
+
+def test_linear_validation(L):
+    def args(T=4, K=2048, N=512, bits=8, fmt=0):
+        a = _lib.LinearArgs()
+        a.T, a.K, a.N, a.bits, a.group, a.weight_format = T, K, N, bits, 128, fmt
+        a.x, a.w, a.s, a.y = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+        return a
+    for kw, expect in ((dict(K=2000), _lib.W4A16_ERR_INVALID_ARG), (dict(N=100), _lib.W4A16_ERR_INVALID_ARG),
+                       (dict(bits=5), _lib.W4A16_ERR_INVALID_ARG), (dict(fmt=1, bits=4), _lib.W4A16_ERR_INVALID_ARG),
+                       (dict(K=16384), _lib.W4A16_ERR_UNSUPPORTED), (dict(T=-1), _lib.W4A16_ERR_INVALID_ARG)):
+        assert L.w4a16_linear(C.byref(args(**kw)), None) == expect, kw
+    a = args()
+    need = L.w4a16_linear_workspace_size(4, 2048, 512)
+    assert need > 0
+    a.workspace, a.workspace_bytes = FAKE + 0x10000, need - 1
+    assert L.w4a16_linear(C.byref(a), None) == _lib.W4A16_ERR_WORKSPACE
+    a = args()
+    a.y = a.x
+    a.workspace, a.workspace_bytes = FAKE + 0x10000, need
+    assert L.w4a16_linear(C.byref(a), None) == _lib.W4A16_ERR_INVALID_ARG
+    assert L.w4a16_linear(C.byref(args(T=0)), None) == _lib.W4A16_OK
+    assert L.w4a16_linear_workspace_size(1, 100, 512) == 0

@@ -22,7 +22,7 @@ from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
 __all__ = ["rtn_quantize_pack", "fp8_quantize_pack", "mxfp4_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
-           "moe_w4a16_workspace_init", "moe_w4a16_workspace_check", "new_workspace",
+           "moe_w4a16_workspace_init", "moe_w4a16_workspace_check", "new_workspace", "w4a16_linear",
            "MoeCall", "w4a16_abi_version", "W4A16Error", "library_path"]
 
 GROUP = 128
@@ -413,6 +413,56 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
             _lib.check(st, "moe_w4a16_forward_timed")
             _timed.extend((names[i].decode(), float(ms[i])) for i in range(n.value))
     return (out, routing) if routing_out else out
+
+
+def w4a16_linear(x, w, s, *, bits: int = 8, weight_format: str = "int", residual=None, out=None, workspace=None,
+                 stream=None):
+    """Dense projection ``y = x . W^T (+ residual)`` with ``W`` packed ``[N, K*bits/32]``
+    and its scales (INT: bf16 ``[N, K/128]``; fp8: fp32 ``[N]``; mxfp4: uint8 ``[N, K/32]``),
+    on the expert down-projection kernels.  ``x`` bf16 ``[T, K]``; returns bf16 ``[T, N]``."""
+    torch = _torch()
+    bf = _bf16_types()
+    _need(x, "x", bf)
+    dev = x.device
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-D")
+    _check_bits(bits)
+    if weight_format not in _lib.FORMATS:
+        raise ValueError(f"weight_format {weight_format!r}: one of {tuple(_lib.FORMATS)}")
+    T, K = x.shape
+    N = w.shape[0]
+    if K % GROUP or N % GROUP:
+        raise ValueError(f"K = {K} and N = {N} must be multiples of {GROUP}")
+    _need(w, "w", (torch.int32,), dev)
+    _need(s, "s", _scale_types(weight_format), dev)
+    _shape(w, "w", (N, K * bits // 32))
+    _shape(s, "s", (N, K // GROUP) if weight_format == "int" else (N,) if weight_format == "fp8" else (N, K // 32))
+    if residual is not None:
+        _need(residual, "residual", bf, dev)
+        _shape(residual, "residual", (T, N))
+    if out is not None:
+        _need(out, "out", bf, dev)
+        _shape(out, "out", (T, N))
+    need = _lib.lib().w4a16_linear_workspace_size(T, K, N) if T > 0 else 0
+    if T > 0 and need == 0:
+        raise W4A16Error(_lib.W4A16_ERR_INVALID_ARG, "w4a16_linear_workspace_size", _lib.last_error())
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        a = _lib.LinearArgs()
+        a.T, a.K, a.N = T, K, N
+        a.bits, a.group, a.weight_format = bits, GROUP, _lib.FORMATS[weight_format]
+        a.x, a.w, a.s, a.residual, a.y = _ptr(x), _ptr(w), _ptr(s), _ptr(residual), _ptr(out)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+        st = _lib.lib().w4a16_linear(C.byref(a), _stream(dev, None))
+        _lib.check(st, "w4a16_linear")
+    return out
 
 
 def moe_w4a16_forward_timed(*args, **kwargs):

@@ -43,6 +43,8 @@ EXPORTED = (
     "moe_w4a16_forward",
     "moe_w4a16_forward_timed",
     "moe_w4a16_forward_noalloc",
+    "w4a16_linear_workspace_size",
+    "w4a16_linear",
 )
 
 
@@ -66,6 +68,16 @@ class MoeArgs(C.Structure):
         ("router_w", C.c_void_p), ("shared_gate_w", C.c_void_p),
         ("logits_out", C.c_void_p), ("shared_gate_out", C.c_void_p),
         ("weight_format", C.c_int32),
+    ]
+
+
+class LinearArgs(C.Structure):
+    """Mirror of ``w4a16_linear_args``."""
+    _fields_ = [
+        ("T", C.c_int64), ("K", C.c_int64), ("N", C.c_int64),
+        ("bits", C.c_int32), ("group", C.c_int32), ("weight_format", C.c_int32),
+        ("x", C.c_void_p), ("w", C.c_void_p), ("s", C.c_void_p), ("residual", C.c_void_p), ("y", C.c_void_p),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
     ]
 
 
@@ -109,6 +121,10 @@ def lib():
     L.moe_w4a16_workspace_check.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p]
     L.moe_w4a16_forward.restype = C.c_int
     L.moe_w4a16_forward.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
+    L.w4a16_linear_workspace_size.restype = C.c_size_t
+    L.w4a16_linear_workspace_size.argtypes = [C.c_int64] * 3
+    L.w4a16_linear.restype = C.c_int
+    L.w4a16_linear.argtypes = [C.POINTER(LinearArgs), C.c_void_p]
     L.moe_w4a16_forward_noalloc.restype = C.c_int
     L.moe_w4a16_forward_noalloc.argtypes = [C.POINTER(MoeArgs), C.c_void_p]
     L.moe_w4a16_forward_timed.restype = C.c_int

@@ -437,6 +437,148 @@ int mxfp4_quantize_pack(const void* w, int w_dtype, int64_t n_mats, int64_t rows
                       "mxfp4_quantize_pack launch");
 }
 
+// ------------------------------------------------------------------ dense projection
+
+static int check_linear_shapes(int64_t T, int64_t K, int64_t N) {
+    if (T < 0) return fail(W4A16_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
+    if (K <= 0 || K % kGroup) return fail(W4A16_ERR_INVALID_ARG, "K = %lld is not a positive multiple of 128", (long long)K);
+    if (N <= 0 || N % kGroup) return fail(W4A16_ERR_INVALID_ARG, "N = %lld is not a positive multiple of 128", (long long)N);
+    if (K > 8192) return fail(W4A16_ERR_UNSUPPORTED, "K = %lld > 8192", (long long)K);
+    if (N > 16384) return fail(W4A16_ERR_UNSUPPORTED, "N = %lld > 16384", (long long)N);
+    if (T >= (int64_t(1) << 24) || T * K * 2 >= (int64_t(1) << 32) || T * N * 2 >= (int64_t(1) << 32))
+        return fail(W4A16_ERR_UNSUPPORTED, "T = %lld too large for these shapes", (long long)T);
+    return W4A16_OK;
+}
+
+struct LinearLayout {
+    size_t abuf, asum, rec, meta, tokw, offsets, tiles, wts, inv, ystage, part, total;
+    int splits;
+};
+
+static LinearLayout linear_layout(int64_t T, int64_t K, int64_t N) {
+    LinearLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L.abuf = take((size_t)T * K * 2);
+    L.rec = take(16);
+    L.meta = take(64);
+    L.tokw = take((size_t)T * 8);
+    L.offsets = take(8);
+    L.tiles = take((size_t)((T + kPrefillMT - 1) / kPrefillMT) * 8);
+    L.wts = take((size_t)T * 4);
+    L.inv = take((size_t)T * 4);
+    if (T <= kSmallT) {
+        const int64_t units = (K / kGroup + 1) / 2;   // the down kernel's 2-group K chunks
+        L.splits = (int)std::min<int64_t>(16, std::max<int64_t>(1, (units + 15) / 16));
+        if (L.splits > 1) L.part = take((size_t)L.splits * T * N * 4);
+    } else {
+        L.splits = 1;
+        L.asum = take((size_t)T * (K / kGroup) * 4);
+        L.ystage = take((size_t)T * N * 2);
+    }
+    L.total = off;
+    return L;
+}
+
+size_t w4a16_linear_workspace_size(int64_t T, int64_t K, int64_t N) {
+    g_last_error.clear();
+    if (check_linear_shapes(T, K, N)) return 0;
+    return std::max<size_t>(linear_layout(T, K, N).total, 256);
+}
+
+int w4a16_linear(const w4a16_linear_args* a, void* stream) {
+    g_last_error.clear();
+    if (!a) return fail(W4A16_ERR_INVALID_ARG, "args is NULL");
+    if (int st = check_linear_shapes(a->T, a->K, a->N)) return st;
+    if (a->group != kGroup) return fail(W4A16_ERR_INVALID_ARG, "group = %d, only 128 is supported", a->group);
+    if (a->weight_format < W4A16_FORMAT_INT || a->weight_format > W4A16_FORMAT_MXFP4)
+        return fail(W4A16_ERR_INVALID_ARG, "weight_format = %d", a->weight_format);
+    const int want_bits = a->weight_format == W4A16_FORMAT_FP8_E4M3 ? 8 : a->weight_format == W4A16_FORMAT_MXFP4 ? 4 : 0;
+    if ((a->bits != 4 && a->bits != 8) || (want_bits && a->bits != want_bits))
+        return fail(W4A16_ERR_INVALID_ARG, "bits = %d for weight_format %d", a->bits, a->weight_format);
+    if (a->T == 0) return W4A16_OK;
+    if (!a->x || !a->w || !a->s || !a->y) return fail(W4A16_ERR_INVALID_ARG, "NULL x, w, s or y");
+    const void* ptrs[] = {a->x, a->w, a->s, a->residual, a->y, a->workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(W4A16_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (a->y == a->x) return fail(W4A16_ERR_INVALID_ARG, "y must not alias x");
+    const LinearLayout L = linear_layout(a->T, a->K, a->N);
+    if (!a->workspace || a->workspace_bytes < L.total)
+        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    char* ws = static_cast<char*>(a->workspace);
+    auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool small = a->T <= kSmallT;
+
+    LinearPrep p{};
+    p.x = a->x;
+    p.T = (int)a->T;
+    p.K = a->K;
+    p.abuf = static_cast<uint16_t*>(at(L.abuf));
+    p.asum = small ? nullptr : static_cast<float*>(at(L.asum));
+    p.rec = static_cast<int4*>(at(L.rec));
+    p.meta = static_cast<int32_t*>(at(L.meta));
+    p.tokw = static_cast<int2*>(at(L.tokw));
+    p.offsets = static_cast<int32_t*>(at(L.offsets));
+    p.tiles = static_cast<int32_t*>(at(L.tiles));
+    p.wts = static_cast<float*>(at(L.wts));
+    p.inv = static_cast<int32_t*>(at(L.inv));
+    if (int st = hip_status(launch_linear_prep(p, s), "linear set-up launch")) return st;
+
+    // the projection as the down matrix of one expert: K = its intermediate size, N = hidden
+    const ExpertSet w{nullptr, nullptr, a->w, static_cast<const uint16_t*>(a->s), a->K, a->bits, a->weight_format};
+    const ExpertSet none{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+    if (small) {
+        DecodeArgs d{};
+        d.x = a->x;
+        d.T = (int)a->T;
+        d.E = 1;
+        d.k = 1;
+        d.H = a->N;
+        d.routed = w;
+        d.shared = none;
+        d.meta = p.meta;
+        d.rec = p.rec;
+        d.tokw = p.tokw;
+        d.abuf = p.abuf;
+        d.width_a = a->K;
+        d.splits = L.splits;
+        d.part = L.splits > 1 ? static_cast<float*>(at(L.part)) : nullptr;
+        d.rows_a = a->T;
+        d.residual = a->residual;
+        d.y = a->y;
+        return hip_status(launch_down_decode(d, s), "linear launch");
+    }
+    PrefillArgs q{};
+    q.x = a->x;
+    q.T = (int)a->T;
+    q.E = 1;
+    q.k = 1;
+    q.H = a->N;
+    q.routed = w;
+    q.shared = none;
+    q.offsets = p.offsets;
+    q.meta = p.meta;
+    q.tiles = p.tiles;
+    q.tokw = p.tokw;
+    q.max_tiles = (a->T + kPrefillMT - 1) / kPrefillMT;
+    q.abuf = p.abuf;
+    q.rows_a = a->T;
+    q.width_a = a->K;
+    q.asum = p.asum;
+    q.ystage = static_cast<uint16_t*>(at(L.ystage));
+    q.wts = p.wts;
+    q.inv = p.inv;
+    q.residual = a->residual;
+    q.y = a->y;
+    return hip_status(launch_down_prefill(q, s), "linear launch");
+}
+
 size_t moe_w4a16_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t shared_I) {
     g_last_error.clear();
     if (shared_I < 0) {

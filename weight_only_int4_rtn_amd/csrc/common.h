@@ -442,4 +442,29 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
+// The down-projection kernels alone, for a dense projection run as one expert of weight 1
+// over all tokens: the small-batch kernel (dk_decode, + dk_combine) or the grouped GEMM
+// with its slot-order finalize.
+hipError_t launch_down_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
+hipError_t launch_down_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);
+
+// Set-up of a dense projection on those kernels: x in the codes' K order (abuf), each
+// row's fp32 group sums (asum; large batches), and the routing records of one expert that
+// every token uses with weight 1 (rec, meta, tokw, offsets, tiles, wts, inv).
+struct LinearPrep {
+    const uint16_t* x;   // bf16 [T, K]
+    int T;
+    int64_t K;
+    uint16_t* abuf;      // [T, K]
+    float* asum;         // [T, K / 128] or NULL
+    int4* rec;           // [1]
+    int32_t* meta;       // [2]: active experts, M-tiles
+    int2* tokw;          // [T]
+    int32_t* offsets;    // [2]
+    int32_t* tiles;      // [ceil(T / 128), 2]
+    float* wts;          // [T]
+    int32_t* inv;        // [T]
+};
+hipError_t launch_linear_prep(const LinearPrep& p, hipStream_t s, StageTimer* t = nullptr);
+
 }  // namespace w4a16

@@ -933,6 +933,29 @@ hipError_t launch_decode_cf(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
 
 }  // namespace
 
+namespace {
+template <int CF>
+hipError_t launch_down_decode_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    const dim3 dk_grid((unsigned)(a.H / 16), (unsigned)a.splits);
+    launch(t, "dk_decode", dk_decode_kernel<CF, 0>, dk_grid, dim3(64 * kDkWaves), s, 0u, a);
+    if (a.splits > 1) {
+        const int64_t n = (int64_t)a.T * a.H;
+        launch(t, "dk_combine", dk_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u,
+               (const float*)a.part, a.splits, n, a.residual, a.y);
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_down_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_down_decode_t<4>(a, s, t);
+        case 8: return launch_down_decode_t<8>(a, s, t);
+        case kCfFp8: return launch_down_decode_t<kCfFp8>(a, s, t);
+        default: return launch_down_decode_t<kCfMx4>(a, s, t);
+    }
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     switch (cf_of(a.routed.fmt, a.routed.bits)) {
         case 4: return launch_decode_cf<4>(a, s, t);

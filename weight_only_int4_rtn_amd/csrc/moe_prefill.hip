@@ -649,6 +649,21 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) 
 }
 
 template <int CF>
+hipError_t launch_down_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
+    constexpr uint32_t lds = pipe_lds_bytes<CF>() + kMaxItems * sizeof(Item) + 4 * MT * 4 + 2 * MT * 4;
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dk_prefill_kernel<CF, 0>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        return true;
+    }();
+    (void)attr;
+    const int64_t dk_items = a.max_tiles * ((a.H + NT - 1) / NT);
+    launch(t, "dk_prefill", dk_prefill_kernel<CF, 0>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
+    launch(t, "finalize", finalize_kernel, dim3((unsigned)((a.H / 8 + 255) / 256 * a.T)), dim3(256), s, 0u, a);
+    return hipGetLastError();
+}
+
+template <int CF>
 hipError_t launch_prefill_cf(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
     const int sb = a.shared.bits;
     if (sb == 0) return launch_prefill_t<CF, 0>(a, s, t);
@@ -657,6 +672,15 @@ hipError_t launch_prefill_cf(const PrefillArgs& a, hipStream_t s, StageTimer* t)
 }
 
 }  // namespace
+
+hipError_t launch_down_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_down_prefill_t<4>(a, s, t);
+        case 8: return launch_down_prefill_t<8>(a, s, t);
+        case kCfFp8: return launch_down_prefill_t<kCfFp8>(a, s, t);
+        default: return launch_down_prefill_t<kCfMx4>(a, s, t);
+    }
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
     switch (cf_of(a.routed.fmt, a.routed.bits)) {
