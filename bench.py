@@ -418,6 +418,171 @@ class SclkSampler:
                 "source": "rocm-smi --showclocks while the 8192-token prefill step runs"}
 
 
+def make_fmt_layers(fmt, n_copies, seed):
+    """n_copies layers with routed experts in FP8 E4M3 per channel or MXFP4 (MSE scales)."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    bits = 8 if fmt == "fp8" else 4
+    layers = []
+    chunk = 32
+    for c in range(n_copies):
+        w13 = torch.empty((E, 2 * I, H * bits // 32), dtype=torch.int32, device=dev)
+        w2 = torch.empty((E, H, I * bits // 32), dtype=torch.int32, device=dev)
+        if fmt == "fp8":
+            s13 = torch.empty((E, 2 * I), dtype=torch.float32, device=dev)
+            s2 = torch.empty((E, H), dtype=torch.float32, device=dev)
+        else:
+            s13 = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+            s2 = torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev)
+        for e0 in range(0, E, chunk):
+            sl = slice(e0, e0 + chunk)
+            f13 = synth.device_normal((chunk, 2 * I, H), synth.WEIGHT_STD, seed * 1000 + c * 64 + e0 // chunk, dev)
+            f2 = synth.device_normal((chunk, H, I), synth.WEIGHT_STD, seed * 1000 + c * 64 + 32 + e0 // chunk, dev)
+            if fmt == "fp8":
+                w4.fp8_quantize_pack(f13, packed=w13[sl], scales=s13[sl])
+                w4.fp8_quantize_pack(f2, packed=w2[sl], scales=s2[sl])
+            else:
+                w4.mxfp4_quantize_pack(f13, "mse", packed=w13[sl], scales=s13[sl])
+                w4.mxfp4_quantize_pack(f2, "mse", packed=w2[sl], scales=s2[sl])
+            del f13, f2
+        layers.append((w13, s13, w2, s2))
+    torch.cuda.synchronize()
+    return layers
+
+
+def fmt_expert_bytes(fmt):
+    """Algorithmic bytes of one expert in FP8 (codes + fp32 row scales) or MXFP4 (codes +
+    one E8M0 byte per 32 columns)."""
+    if fmt == "fp8":
+        return 2 * I * H + 2 * I * 4, H * I + H * 4
+    return 2 * I * H // 2 + 2 * I * H // 32, H * I // 2 + H * I // 32
+
+
+def measure_fmt(fmt, T, layers, steps, warmup, seed):
+    """Step time of a T-token batch with FP8 / MXFP4 routed experts (eager launches, one call
+    per step), the per-kernel event times, and the expert bytes and flops per step."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    bits = 8 if fmt == "fp8" else 4
+    n_logits = 16
+    logits = [synth.device_normal((T, E), 1.0, seed * 7919 + i, dev) for i in range(n_logits)]
+    x = synth.device_normal((T, H), 1.0, seed, dev, torch.bfloat16)
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, K), dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    calls = [w4.MoeCall(x, *lay, top_k=K, bits=bits, weight_format=fmt, workspace=ws) for lay in layers]
+    distinct = [int(torch.topk(l, K, dim=1).indices.unique().numel()) for l in logits]
+
+    def step(i):
+        calls[i % len(calls)](x, out, router_logits=logits[i % n_logits])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(warmup + i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per = {}
+    for i in range(min(steps, 20)):
+        _, tk = w4.moe_w4a16_forward_timed(x, *layers[i % len(layers)], top_k=K, bits=bits, weight_format=fmt,
+                                           router_logits=logits[i % n_logits], out=out, workspace=ws)
+        for nm, t in tk:
+            per.setdefault(nm, []).append(t)
+    kernels = {nm: round(sum(v) / len(v) * 1e3, 2) for nm, v in per.items()}
+    gu, dn = fmt_expert_bytes(fmt)
+    d_mean = sum(distinct[(warmup + i) % n_logits] for i in range(steps)) / steps
+    wbytes = d_mean * (gu + dn)
+    flops = 2.0 * T * K * 3 * H * I
+    res = {"T": T, "ms_per_step": round(ms, 5), "tok_per_s": round(T / ms * 1e3, 1),
+           "expert_weight_GBps": round(wbytes / ms / 1e6, 1), "TFLOPs": round(flops / ms / 1e9, 2),
+           "kernels_us": kernels}
+    gk = next((k for k in kernels if k.startswith("gk_")), None)
+    if gk is not None:
+        if T > 64:
+            res["roofline"] = {"bound": "mfma", "kernel": gk,
+                               "achieved": round(2.0 * T * K * 2 * I * H / kernels[gk] / 1e6, 1),
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            res["roofline"] = {"bound": "hbm", "kernel": gk,
+                               "achieved": round((d_mean * gu + T * H * 2) / kernels[gk] / 1e3, 1),
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+        res["roofline"]["frac"] = round(res["roofline"]["achieved"] / res["roofline"]["peak"], 4)
+    log(f"[bench] {fmt} T={T}: {ms * 1e3:.1f} us/step, {res['tok_per_s']} tok/s, {res['expert_weight_GBps']} GB/s, "
+        f"{res['TFLOPs']} TFLOP/s, kernels {kernels}")
+    del ws, out, logits
+    return res
+
+
+# The INT8 group-128 projections of one attention and one Gated DeltaNet layer at hidden
+# 2048, (N, K): q_proj with its output gate, k_proj, v_proj, o_proj; in_proj_qkv,
+# in_proj_z, out_proj.
+DENSE_SHAPES = [("attn.q_proj", 8192, 2048), ("attn.k_proj", 512, 2048), ("attn.v_proj", 512, 2048),
+                ("attn.o_proj", 2048, 4096), ("deltanet.in_proj_qkv", 8192, 2048),
+                ("deltanet.in_proj_z", 4096, 2048), ("deltanet.out_proj", 2048, 4096)]
+
+
+def measure_linear(T, copies, steps, seed):
+    """The seven projections back to back at T tokens (eager launches), rotating through
+    `copies` weight sets so that decode reads them from HBM; per-projection kernel times."""
+    import torch
+    import synth
+    import weight_only_int4_rtn_amd as w4
+    dev = torch.device("cuda:0")
+    sets = []
+    for c in range(copies):
+        ws = []
+        for i, (nm, N, Kd) in enumerate(DENSE_SHAPES):
+            w = synth.device_normal((N, Kd), synth.WEIGHT_STD, seed * 100 + c * 10 + i, dev)
+            ws.append(w4.rtn_quantize_pack(w, 8))
+            del w
+        sets.append(ws)
+    xs = {Kd: synth.device_normal((T, Kd), 1.0, seed + Kd, dev, torch.bfloat16) for Kd in (2048, 4096)}
+    outs = {N: torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _, N, _ in DENSE_SHAPES}
+    wsp = torch.empty((max(w4._lib.lib().w4a16_linear_workspace_size(T, Kd, N) for _, N, Kd in DENSE_SHAPES),),
+                      dtype=torch.uint8, device=dev)
+
+    def step(i):
+        for (nm, N, Kd), (p, sc) in zip(DENSE_SHAPES, sets[i % copies]):
+            w4.w4a16_linear(xs[Kd], p, sc, out=outs[N], workspace=wsp)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per = {}
+    for i in range(min(steps, 10)):
+        for (nm, N, Kd), (p, sc) in zip(DENSE_SHAPES, sets[i % copies]):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            w4.w4a16_linear(xs[Kd], p, sc, out=outs[N], workspace=wsp)
+            e1.record()
+            torch.cuda.synchronize()
+            per.setdefault(nm, []).append(e0.elapsed_time(e1))
+    nbytes = sum(N * Kd + N * (Kd // 128) * 2 for _, N, Kd in DENSE_SHAPES)
+    flops = sum(2.0 * T * N * Kd for _, N, Kd in DENSE_SHAPES)
+    res = {"T": T, "ms_per_step": round(ms, 5), "weight_GBps": round(nbytes / ms / 1e6, 1),
+           "TFLOPs": round(flops / ms / 1e9, 2), "weight_bytes": nbytes,
+           "per_projection_us": {nm: round(sum(v) / len(v) * 1e3, 2) for nm, v in per.items()}}
+    res["frac"] = round((res["weight_GBps"] / HBM_PEAK_GBPS) if T <= 64 else (res["TFLOPs"] / BF16_PEAK_TFLOPS), 4)
+    log(f"[bench] dense INT8 projections T={T}: {ms * 1e3:.1f} us for all seven, {res['weight_GBps']} GB/s, "
+        f"{res['TFLOPs']} TFLOP/s")
+    del sets, wsp
+    return res
+
+
 def keep_busy(T, layers, seconds, sampler):
     """Back-to-back forwards of a T-token batch until `seconds` pass or the sampler has enough."""
     import torch
@@ -591,6 +756,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy kernel of known size (for scaling HBM byte counters)")
     ap.add_argument("--no-router", action="store_true")
+    ap.add_argument("--no-formats", action="store_true", help="skip the FP8 / MXFP4 expert runs")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense INT8 projection runs")
     ap.add_argument("--cpu-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_child is not None:
@@ -629,9 +796,21 @@ def main():
     else:
         sclk = None
     router = None if args.no_router else time_router(layers[:4], 17)
-    quant = None if args.no_quant else time_quantizer()
     del layers
     torch.cuda.empty_cache()
+    formats = {}
+    if not args.no_formats:
+        for fmt in ("fp8", "mxfp4"):
+            log(f"[bench] building {fmt} layers")
+            fl = make_fmt_layers(fmt, 4, seed=21)
+            formats[fmt] = {f"T{T}": measure_fmt(fmt, T, fl, st, 5, 31 + T)
+                            for T, st in ((1, 100), (32, 100), (8192, 10))}
+            del fl
+            torch.cuda.empty_cache()
+    dense = None
+    if not args.no_dense:
+        dense = {f"T{T}": measure_linear(T, 4, st, 41) for T, st in ((1, 50), (32, 50), (8192, 5))}
+    quant = None if args.no_quant else time_quantizer()
     stack = None
     if "stack40" in only:
         log("[bench] building the 40-layer stack")
@@ -709,6 +888,10 @@ def main():
         line["quantize"] = quant
     if router:
         line["router"] = router
+    if formats:
+        line["formats"] = formats
+    if dense:
+        line["dense_int8"] = dense
     line["sclk"] = sclk
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
