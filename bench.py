@@ -583,6 +583,29 @@ def measure_linear(T, copies, steps, seed):
     return res
 
 
+def read_floor(nbytes, n_buffers, reps):
+    """The achievable time to read `nbytes` from HBM in one launch: a plain reduction kernel
+    (torch.sum over int32 words) over one of `n_buffers` buffers, rotated so that every read
+    misses the 256 MB Infinity Cache; returns us per read (event-timed, back to back)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = nbytes // 4
+    bufs = [torch.ones(n, dtype=torch.int32, device=dev) for _ in range(n_buffers)]
+    out = torch.empty((), dtype=torch.int64, device=dev)
+    for i in range(n_buffers):
+        torch.sum(bufs[i], out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        torch.sum(bufs[i % n_buffers], out=out)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    del bufs
+    return us
+
+
 def keep_busy(T, layers, seconds, sampler):
     """Back-to-back forwards of a T-token batch until `seconds` pass or the sampler has enough."""
     import torch
@@ -758,6 +781,8 @@ def main():
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-formats", action="store_true", help="skip the FP8 / MXFP4 expert runs")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense INT8 projection runs")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="do not sample the shader clock (it starts rocm-smi; use under a profiler)")
     ap.add_argument("--cpu-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_child is not None:
@@ -786,15 +811,29 @@ def main():
         results["decode1"] = measure("decode1", 1, layers, args.steps, args.warmup, min(args.steps, 100), 11)
     if "decode32" in only:
         results["decode32"] = measure("decode32", 32, layers, args.steps, args.warmup, min(args.steps, 100), 12)
+    sclk = None
     if "prefill8192" in only:
         pst = max(5, args.steps // 10)
-        with SclkSampler() as sampler:
-            results["prefill8192"] = measure("prefill8192", 8192, layers[:4], pst, max(2, args.warmup // 4),
-                                             min(pst, 10), 13)
-            keep_busy(8192, layers[:4], 4.0, sampler)   # the MFMA-bound step while the clock is sampled
-        sclk = sampler.summary()
-    else:
-        sclk = None
+        results["prefill8192"] = measure("prefill8192", 8192, layers[:4], pst, max(2, args.warmup // 4),
+                                         min(pst, 10), 13)
+        if not args.no_sclk:
+            with SclkSampler() as sampler:
+                keep_busy(8192, layers[:4], 4.0, sampler)   # the MFMA-bound step while the clock is sampled
+            sclk = sampler.summary()
+    floor = None
+    if "decode1" in results:
+        # the single-token layer's expert bytes (8 experts) read once by a plain kernel, and
+        # the same for the 32-token batch's distinct experts
+        nb1 = int(results["decode1"]["kernel_bytes"]["all"])
+        floor = {"decode1_bytes": nb1, "decode1_read_us": round(read_floor(nb1, 40, 400), 2)}
+        floor["decode1_frac_of_hbm"] = round(nb1 / floor["decode1_read_us"] / 1e3 / HBM_PEAK_GBPS, 4)
+        floor["tiny_decode_over_floor"] = round(results["decode1"]["kernels_us"].get("tiny_decode", 0) /
+                                                floor["decode1_read_us"], 2)
+        if "decode32" in results:
+            nb32 = int(results["decode32"]["expert_weight_bytes_per_step"])
+            floor["decode32_bytes"] = nb32
+            floor["decode32_read_us"] = round(read_floor(nb32, 3, 60), 2)
+        log(f"[bench] read floor: {floor}")
     router = None if args.no_router else time_router(layers[:4], 17)
     del layers
     torch.cuda.empty_cache()
@@ -888,6 +927,8 @@ def main():
         line["quantize"] = quant
     if router:
         line["router"] = router
+    if floor:
+        line["read_floor"] = floor
     if formats:
         line["formats"] = formats
     if dense:
