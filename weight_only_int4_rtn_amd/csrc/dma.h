@@ -46,6 +46,17 @@ __device__ __forceinline__ void dma4(i32x4_t r, uint32_t lds, uint32_t voff, uin
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
+// The same copies without a memory clobber, for a pipeline whose LDS reads never touch
+// the stage being filled and whose barriers and waits carry every ordering: the compiler
+// may then schedule LDS reads and arithmetic around them.
+__device__ __forceinline__ void dma16_free(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "m0");
+}
+__device__ __forceinline__ void dma4_free(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "m0");
+}
 #pragma clang diagnostic pop
 
 constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every staged array: reads zero

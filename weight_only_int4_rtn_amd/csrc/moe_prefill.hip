@@ -126,10 +126,18 @@ __device__ __forceinline__ int seed_slot(int r) { return (r >> 4) * 64 + (r & 15
 __device__ __forceinline__ int scale_slot(int R) { return (R >> 5) * 64 + (R & 31); }
 
 // Gate/up code row of stage row R for N block nblk (one group of I): wave wn's subtiles
-// 0, 1 are gate rows, 2, 3 the matching up rows.
+// 0, 1 are gate rows, 2, 3 the matching up rows.  Lane ml of subtile b & 1 = ns takes
+// column 8 (ml / 4) + ml % 4 + 4 ns of the wave's 32, so that a lane's two output columns
+// j and j + 4 of one block of 8 sit next to each other in the down GEMM's K order.
 __device__ __forceinline__ int gk_code_row(int R, int nblk, int64_t I_e) {
     const int wn = R >> 6, b = (R >> 4) & 3, ml = R & 15;
-    return (b >= 2 ? (int)I_e : 0) + nblk * kGroup + 32 * wn + 16 * (b & 1) + ml;
+    return (b >= 2 ? (int)I_e : 0) + nblk * kGroup + 32 * wn + 8 * (ml >> 2) + (ml & 3) + 4 * (b & 1);
+}
+// Down code row (output column) of stage row R for N block nblk: lane ml of subtile b
+// takes column 4 ml + b of the wave's 64, so that a lane's four outputs of one row are
+// adjacent columns.
+__device__ __forceinline__ int dk_code_row(int R, int nblk) {
+    return nblk * NT + 64 * (R >> 6) + 4 * (R & 15) + ((R >> 4) & 3);
 }
 
 // --------------------------------------------------------------- per-item issue state
@@ -203,18 +211,18 @@ __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const Expert
             a_coords(j, &r, &c);
             st.a_off[j] = ((uint32_t)(it.orow0 + min(r, it.count - 1)) * (uint32_t)a.width_a + c * 8) * 2;
         }
-        const int h0 = it.nblk * NT;   // rows past H read zeros (the buffer ends at H)
+        // rows past H read zeros (the buffer ends at H)
         st.b_r = dma_rsrc(es.w2 + eb * (a.H * I_e * BITS / 32), (uint32_t)(a.H * row_bytes));
 #pragma unroll
         for (int j = 0; j < P::kBLoads; ++j) {
             int R, c;
             b_coords<BITS>(j, &R, &c);
-            st.b_off[j] = (uint32_t)((h0 + R) * row_bytes) + c * 16;
+            st.b_off[j] = (uint32_t)(dk_code_row(R, it.nblk) * row_bytes) + c * 16;
         }
         st.seed_r = dma_rsrc(a.asum, (uint32_t)(a.rows_a * GW * 4));
         st.seed_off = lane < 16 ? (uint32_t)(it.orow0 + min(16 * wave + lane, it.count - 1)) * GW * 4 : kOob;
         st.s_r = dma_rsrc(scale_base<CF>(es.s2, eb, a.H, G2), (uint32_t)scale_bytes<CF>(a.H, G2));
-        st.s_off = lane < 32 ? scale_off<CF>(h0 + 32 * wave + lane, G2) : kOob;
+        st.s_off = lane < 32 ? scale_off<CF>(dk_code_row(32 * wave + lane, it.nblk), G2) : kOob;
     }
 }
 
@@ -250,22 +258,30 @@ __device__ __forceinline__ void item_tokens(const Item& it, const int* s_tok, in
     }
 }
 
-// stage: LDS byte address of the stage the step goes to.
+// stage: LDS byte address of the stage the step goes to.  The copies go out in four
+// parts (0: activation chunks 0-1, 1: chunks 2-3, 2: code rows, 3: row sums and scales),
+// so that a step's copies can be spread over the previous step's MFMAs; part -1: all.
 template <int CF>
-__device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t stage) {
+__device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t stage, int part = -1) {
     constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t A = stage, B = stage + kAStageBytes, S = B + P::kBStageBytes, SC = S + kSeedSlots * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(st.a_r, A + (wave * 4 + j) * 1024, st.a_off[j], (uint32_t)g * kGroup * 2);
+    for (int j = 0; j < 4; ++j)
+        if (part < 0 || part == j / 2)
+            dma16_free(st.a_r, A + (wave * 4 + j) * 1024, st.a_off[j], (uint32_t)g * kGroup * 2);
+    if (part < 0 || part == 2) {
 #pragma unroll
-    for (int j = 0; j < P::kBLoads; ++j)
-        dma16(st.b_r, B + (wave * P::kBLoads + j) * 1024, st.b_off[j], (uint32_t)g * P::kRowBytes);
-    dma4(st.seed_r, S + wave * 256, st.seed_off, (uint32_t)g * 4);
-    if constexpr (CF == kCfFp8) dma4(st.s_r, SC + wave * 256, st.s_off, 0);   // the row's one scale
-    else if constexpr (CF == kCfMx4) dma4(st.s_r, SC + wave * 256, st.s_off + (uint32_t)g * 4, 0);
-    else dma4(st.s_r, SC + wave * 256, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
+        for (int j = 0; j < P::kBLoads; ++j)
+            dma16_free(st.b_r, B + (wave * P::kBLoads + j) * 1024, st.b_off[j], (uint32_t)g * P::kRowBytes);
+    }
+    if (part < 0 || part == 3) {
+        dma4_free(st.seed_r, S + wave * 256, st.seed_off, (uint32_t)g * 4);
+        if constexpr (CF == kCfFp8) dma4_free(st.s_r, SC + wave * 256, st.s_off, 0);   // the row's one scale
+        else if constexpr (CF == kCfMx4) dma4_free(st.s_r, SC + wave * 256, st.s_off + (uint32_t)g * 4, 0);
+        else dma4_free(st.s_r, SC + wave * 256, (st.s_off + (uint32_t)g * 2) & ~3u, 0);
+    }
 }
 
 // ------------------------------------------------------------------- compute
@@ -273,8 +289,14 @@ __device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t
 // One step of one wave: its 64 x 64 block (4 M-subtiles x 4 code subtiles) for one
 // group, accumulated into acc with the group scales (D column ml is code row R's).
 // sodd: bit b set when code subtile b's scale sits in the high half of its word.
-template <int CF>
-__device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4]) {
+// The K slice (32 columns) is the outer loop: the lane's code chunks of all four code
+// subtiles and their scales are read at the start (8-bit codes: the second chunk half-way),
+// the four activation fragments once per slice, and each dequantised code fragment feeds
+// the four M-subtiles' MFMAs.  The 16 tiles' group partials start from the offset seeds
+// (MXFP4: from the accumulators themselves, its block scale being inside the conversion).
+// hook(i) runs after slice i's MFMAs (the next step's copies go out there).
+template <int CF, typename Hook>
+__device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4], Hook&& hook) {
     constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
     constexpr float kOff = CF == 4 ? 136.0f : CF == 8 ? 2304.0f : 0.0f;
@@ -287,64 +309,78 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
     const uint32_t* SC = reinterpret_cast<const uint32_t*>(S + kSeedSlots);
     const uint32_t M = nibble_mask();
 
-    u32x4_t av[4][4];
+    // the lane's chunk c (its K slice of the group) of code subtile b
+    auto read_codes = [&](int c, u32x4_t (&dst)[4]) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int R = 64 * wn + 16 * b + ml;
+            const int lc = (BITS / 4) * q + c;
+            dst[b] = *reinterpret_cast<const u32x4_t*>(B + R * P::kRowBytes + ((lc ^ b_swizzle<BITS>(R)) * 16));
+        }
+    };
+    u32x4_t bw[4];
+    read_codes(0, bw);
+    float sc[4], xs[4];   // partial's scale; MXFP4: the conversion's block scale
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t sw = SC[scale_slot(64 * wn + 16 * b + ml)];
+        sc[b] = 1.f;
+        xs[b] = 1.f;
+        if constexpr (CF == kCfFp8) sc[b] = __uint_as_float(sw);
+        else if constexpr (CF == kCfMx4) xs[b] = e8m0_scale(sw >> (8 * q));   // this lane's block: columns 32q..
+        else sc[b] = bf16_to_f32(((sodd >> b) & 1) ? (sw >> 16) : (sw & 0xffffu));
+    }
     f32x4_t seed[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-        const int r = 64 * wm + 16 * mi + ml;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[mi][i] = *reinterpret_cast<const u32x4_t*>(A + a_swz(r, 4 * q + i) * 8);
         if constexpr (cf_int(CF)) {
-            const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(S + seed_slot(64 * wm + 16 * mi + 4 * q));
+            const f32x4_t xsum = *reinterpret_cast<const f32x4_t*>(S + seed_slot(64 * wm + 16 * mi + 4 * q));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) seed[mi][e] = -kOff * xs[e];
+            for (int e = 0; e < 4; ++e) seed[mi][e] = -kOff * xsum[e];
         } else {
             seed[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
+    f32x4_t t[4][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int R = 64 * wn + 16 * b + ml;
-        u32x4_t braw[BITS / 4];
+    for (int i = 0; i < 4; ++i) {
+        if (BITS == 8 && i == 2) read_codes(1, bw);
+        u32x4_t av[4];
 #pragma unroll
-        for (int c = 0; c < BITS / 4; ++c) {
-            const int lc = (BITS / 4) * q + c;   // logical chunk: this lane's K slice
-            braw[c] = *reinterpret_cast<const u32x4_t*>(B + R * P::kRowBytes + ((lc ^ b_swizzle<BITS>(R)) * 16));
-        }
-        const uint32_t sw = SC[scale_slot(R)];
-        float sc = 1.f, xs = 1.f;   // partial's scale; MXFP4: the conversion's block scale
-        if constexpr (CF == kCfFp8) sc = __uint_as_float(sw);
-        else if constexpr (CF == kCfMx4) xs = e8m0_scale(sw >> (8 * q));   // this lane's block: columns 32q..
-        else sc = bf16_to_f32(((sodd >> b) & 1) ? (sw >> 16) : (sw & 0xffffu));
-        f32x4_t t[4];
+        for (int mi = 0; mi < 4; ++mi)
+            av[mi] = *reinterpret_cast<const u32x4_t*>(A + a_swz(64 * wm + 16 * mi + ml, 4 * q + i) * 8);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) t[mi] = seed[mi];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int b = 0; b < 4; ++b) {
             u32x4_t lo, hi;
             if constexpr (CF == 4) {
-                lo = dq4(braw[0][i], M);
+                lo = dq4(bw[b][i], M);
             } else if constexpr (CF == 8) {
-                dq8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3], lo, hi, M);
+                dq8(bw[b][(2 * i) & 3], bw[b][(2 * i + 1) & 3], lo, hi, M);
             } else if constexpr (CF == kCfFp8) {
-                lo = dq_fp8(braw[i >> 1][(2 * i) & 3], braw[i >> 1][(2 * i + 1) & 3]);
+                lo = dq_fp8(bw[b][(2 * i) & 3], bw[b][(2 * i + 1) & 3]);
             } else {
-                lo = dq_mx4(braw[0][i], xs);
+                lo = dq_mx4(bw[b][i], xs[b]);
             }
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                t[mi] = mfma16(av[mi][i], lo, t[mi]);
-                if constexpr (CF == 8) t[mi] = mfma16(av[mi][i], hi, t[mi]);
+                const f32x4_t c0 = i > 0 ? t[mi][b] : CF == kCfMx4 ? acc[mi][b] : seed[mi];
+                t[mi][b] = mfma16(av[mi], lo, c0);
+                if constexpr (CF == 8) t[mi][b] = mfma16(av[mi], hi, t[mi][b]);
             }
         }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) {
-                if constexpr (CF == kCfMx4) acc[mi][b][r2] += t[mi][r2];
-                else acc[mi][b][r2] += sc * t[mi][r2];
-            }
+        hook(i);
     }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if constexpr (CF == kCfMx4) {
+                acc[mi][b] = t[mi][b];
+            } else {
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) acc[mi][b][r2] += sc[b] * t[mi][b][r2];
+            }
+        }
 }
 
 // ------------------------------------------------------------------- epilogues
@@ -361,17 +397,14 @@ __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 64 * wm + 16 * mi + 4 * q + r;
-            float rs = 0.f;
-#pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-                const uint32_t v = cvt_bf16(silu_mul(acc[mi][ns][r], acc[mi][2 + ns][r]));
-                rs += bf16_to_f32(v);
-                if (m < it.count) {
-                    const int col = perm_pos(it.nblk * kGroup + 32 * wn + 16 * ns + ml);
-                    a.abuf[(int64_t)(it.orow0 + m) * a.width_a + col] = (uint16_t)v;
-                }
+            const uint32_t v0 = cvt_bf16(silu_mul(acc[mi][0][r], acc[mi][2][r]));
+            const uint32_t v1 = cvt_bf16(silu_mul(acc[mi][1][r], acc[mi][3][r]));
+            float rs = bf16_to_f32(v0) + bf16_to_f32(v1);
+            if (m < it.count) {   // columns j and j + 4 of a block of 8: adjacent in K order
+                const int col = perm_pos(it.nblk * kGroup + 32 * wn + 8 * (ml >> 2) + (ml & 3));
+                *reinterpret_cast<uint32_t*>(a.abuf + (int64_t)(it.orow0 + m) * a.width_a + col) = v0 | (v1 << 16);
             }
-            rs += __shfl_xor(rs, 1, 16);   // sum over the row's 16 lanes (columns ml)
+            rs += __shfl_xor(rs, 1, 16);   // sum over the row's 16 lanes
             rs += __shfl_xor(rs, 2, 16);
             rs += __shfl_xor(rs, 4, 16);
             rs += __shfl_xor(rs, 8, 16);
@@ -388,27 +421,23 @@ __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
     bar();   // s_asum is reused by the next item
 }
 
-// The unweighted output rows of a down item, rounded to bf16, at their sorted positions
-// (pairs of adjacent columns, exchanged between neighbouring lanes, go out as 4 bytes).
+// The unweighted output rows of a down item, rounded to bf16, at their sorted positions:
+// a lane's four columns of a row are adjacent (see dk_code_row) and go out as 8 bytes.
 __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t (&acc)[4][4]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int wm = wave >> 2, wn = wave & 3;
-    const int h = it.nblk * NT + 64 * wn + ml;
+    const int h = it.nblk * NT + 64 * wn + 4 * ml;   // H is a multiple of 128: h < H covers h + 3
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 64 * wm + 16 * mi + 4 * q + r;
-            uint16_t* yrow = a.ystage + (int64_t)(it.orow0 + m) * a.H;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t v = cvt_bf16(acc[mi][b][r]);
-                // the neighbouring column: DPP quad_perm [1,0,3,2] swaps adjacent lanes
-                const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false);
-                // even lanes store (col, col + 1); the row and columns are in range for both lanes
-                if (m < it.count && (ml & 1) == 0 && h + 16 * b < a.H)
-                    *reinterpret_cast<uint32_t*>(yrow + h + 16 * b) = v | (nb << 16);
+            if (m < it.count && h < a.H) {
+                uint2 v;
+                v.x = cvt_bf16(acc[mi][0][r]) | (cvt_bf16(acc[mi][1][r]) << 16);
+                v.y = cvt_bf16(acc[mi][2][r]) | (cvt_bf16(acc[mi][3][r]) << 16);
+                *reinterpret_cast<uint2*>(a.ystage + (int64_t)(it.orow0 + m) * a.H + h) = v;
             }
         }
 }
@@ -469,8 +498,12 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
     IssueState st;
     prepare_issue<CF, GATE_UP>(a, s_items[0], es, tok, st);
     const uint32_t lds0 = lds_offset(smem);
-    auto issue_next = [&]() {
-        issue_step<CF>(st, gi, lds0 + (uint32_t)(issued % P::kStages) * P::kStageBytes);
+    // part p of the next step's copies (p = -1: all of them) ...
+    auto issue_next = [&](int p) {
+        issue_step<CF>(st, gi, lds0 + (uint32_t)(issued % P::kStages) * P::kStageBytes, p);
+    };
+    // ... and, once they are all out, the issue side moves on to the following step
+    auto advance = [&]() {
         ++issued;
         if (++gi == G && ii + 1 < n_items) {
             ++ii;
@@ -483,7 +516,10 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
             prepare_issue<CF, GATE_UP>(a, s_items[ii], es, tok, st);
         }
     };
-    for (int p = 0; p < P::kStages - 1 && issued < total_steps; ++p) issue_next();
+    for (int p = 0; p < P::kStages - 1 && issued < total_steps; ++p) {
+        issue_next(-1);
+        advance();
+    }
 
     // compute side
     int ci = 0, gc = 0;
@@ -501,7 +537,7 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int R = 64 * wn + 16 * b + ml;
-            const int crow = GATE_UP ? gk_code_row(R, it.nblk, es.I) : it.nblk * NT + R;
+            const int crow = GATE_UP ? gk_code_row(R, it.nblk, es.I) : dk_code_row(R, it.nblk);
             p |= (uint32_t)((crow * G) & 1) << b;
         }
         return p;
@@ -528,8 +564,16 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         else wait_vmcnt<0>();
         bar();   // every wave's step-s data is in LDS, and stage (s - 1) is no longer read
         if (epi) finish_item();
-        if (issued < total_steps) issue_next();
-        compute_step<CF>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc);
+        // step s + kStages - 1's copies go out after one of this step's four K slices: waves
+        // 2j and 2j + 1 (on two different SIMDs) after slice j, so that at any time only two
+        // waves wait for the load path while the others keep the matrix units busy
+        const bool more = issued < total_steps;
+        const int slot = __builtin_amdgcn_readfirstlane(wave >> 1);
+        compute_step<CF>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
+                         [&](int i) {
+                             if (more && i == slot) issue_next(-1);
+                         });
+        if (more) advance();
         if (++gc == G) {
             epi = true;
             gc = 0;
