@@ -95,6 +95,17 @@ __device__ __forceinline__ void dq8(uint32_t w0, uint32_t w1, u32x4_t& lo, u32x4
     }
 }
 
+// The same INT8 words as one operand: each byte u (0..255) converted to fp32 and packed
+// to bf16, exact (bf16 holds every integer up to 256), pairs in the K order of dq4.  One
+// MFMA per 8 codes with OFF = 128 (q = u - 128), at 12 VALU instructions.
+__device__ __forceinline__ u32x4_t dq8_cvt(uint32_t w0, uint32_t w1) {
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        r[j] = cvt_bf16x2((float)((w0 >> (8 * j)) & 0xffu), (float)((w1 >> (8 * j)) & 0xffu));
+    return r;
+}
+
 // ------------------------------------------------- other code formats
 //
 // A code format CF is a template constant: 4 and 8 are the INT4 / INT8 group-128 RTN

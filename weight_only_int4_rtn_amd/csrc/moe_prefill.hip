@@ -194,7 +194,7 @@ __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const Expert
         for (int j = 0; j < P::kBLoads; ++j) {
             int R, c;
             b_coords<BITS>(j, &R, &c);
-            st.b_off[j] = (uint32_t)(gk_code_row(R, it.nblk, I_e) * row_bytes) + c * 16;
+            st.b_off[j] = (uint32_t)gk_code_row(R, it.nblk, I_e) * (uint32_t)row_bytes + c * 16;
         }
         st.seed_r = dma_rsrc(a.xsum, (uint32_t)(a.T * G * 4));
         st.seed_off = lane < 16 ? (uint32_t)tok[4] * G * 4 : kOob;
@@ -217,7 +217,7 @@ __device__ void prepare_issue(const PrefillArgs& a, const Item& it, const Expert
         for (int j = 0; j < P::kBLoads; ++j) {
             int R, c;
             b_coords<BITS>(j, &R, &c);
-            st.b_off[j] = (uint32_t)(dk_code_row(R, it.nblk) * row_bytes) + c * 16;
+            st.b_off[j] = (uint32_t)dk_code_row(R, it.nblk) * (uint32_t)row_bytes + c * 16;
         }
         st.seed_r = dma_rsrc(a.asum, (uint32_t)(a.rows_a * GW * 4));
         st.seed_off = lane < 16 ? (uint32_t)(it.orow0 + min(16 * wave + lane, it.count - 1)) * GW * 4 : kOob;
@@ -299,7 +299,7 @@ template <int CF, typename Hook>
 __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4], Hook&& hook) {
     constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
-    constexpr float kOff = CF == 4 ? 136.0f : CF == 8 ? 2304.0f : 0.0f;
+    constexpr float kOff = CF == 4 ? 136.0f : CF == 8 ? 128.0f : 0.0f;   // INT8 through dq8_cvt
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int wm = wave >> 2, wn = wave & 3;
@@ -309,17 +309,19 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
     const uint32_t* SC = reinterpret_cast<const uint32_t*>(S + kSeedSlots);
     const uint32_t M = nibble_mask();
 
-    // the lane's chunk c (its K slice of the group) of code subtile b
-    auto read_codes = [&](int c, u32x4_t (&dst)[4]) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int R = 64 * wn + 16 * b + ml;
-            const int lc = (BITS / 4) * q + c;
-            dst[b] = *reinterpret_cast<const u32x4_t*>(B + R * P::kRowBytes + ((lc ^ b_swizzle<BITS>(R)) * 16));
-        }
+    // 4-bit codes: the lane's 16-byte chunk (its 32 columns of the group) of code subtile b,
+    // word i for slice i.  8-bit codes: the two words of slice i (chunk i / 2, words 2i % 4
+    // and 2i % 4 + 1), read per slice.
+    auto code_addr = [&](int b, int c) {
+        const int R = 64 * wn + 16 * b + ml;
+        const int lc = (BITS / 4) * q + c;
+        return B + R * P::kRowBytes + ((lc ^ b_swizzle<BITS>(R)) * 16);
     };
     u32x4_t bw[4];
-    read_codes(0, bw);
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bw[b] = *reinterpret_cast<const u32x4_t*>(code_addr(b, 0));
+    }
     float sc[4], xs[4];   // partial's scale; MXFP4: the conversion's block scale
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -341,46 +343,59 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
             seed[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
-    f32x4_t t[4][4];
+    // 8-bit codes take the code subtiles in two passes of two (half the partials live at a
+    // time, the activation fragments read once per pass)
+    constexpr int NB = BITS == 8 ? 2 : 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (BITS == 8 && i == 2) read_codes(1, bw);
-        u32x4_t av[4];
+    for (int b0 = 0; b0 < 4; b0 += NB) {
+        f32x4_t t[4][NB];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (BITS == 8) {
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(code_addr(b0 + bb, i >> 1) + (2 * i & 3) * 4);
+                    bw[b0 + bb][0] = w.x;
+                    bw[b0 + bb][1] = w.y;
+                }
+            }
+            u32x4_t av[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                av[mi] = *reinterpret_cast<const u32x4_t*>(A + a_swz(64 * wm + 16 * mi + ml, 4 * q + i) * 8);
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                const int b = b0 + bb;
+                u32x4_t lo;
+                if constexpr (CF == 4) {
+                    lo = dq4(bw[b][i], M);
+                } else if constexpr (CF == 8) {
+                    lo = dq8_cvt(bw[b][0], bw[b][1]);
+                } else if constexpr (CF == kCfFp8) {
+                    lo = dq_fp8(bw[b][0], bw[b][1]);
+                } else {
+                    lo = dq_mx4(bw[b][i], xs[b]);
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const f32x4_t c0 = i > 0 ? t[mi][bb] : CF == kCfMx4 ? acc[mi][b] : seed[mi];
+                    t[mi][bb] = mfma16(av[mi], lo, c0);
+                }
+            }
+            if (b0 == 0) hook(i);
+        }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
-            av[mi] = *reinterpret_cast<const u32x4_t*>(A + a_swz(64 * wm + 16 * mi + ml, 4 * q + i) * 8);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            u32x4_t lo, hi;
-            if constexpr (CF == 4) {
-                lo = dq4(bw[b][i], M);
-            } else if constexpr (CF == 8) {
-                dq8(bw[b][(2 * i) & 3], bw[b][(2 * i + 1) & 3], lo, hi, M);
-            } else if constexpr (CF == kCfFp8) {
-                lo = dq_fp8(bw[b][(2 * i) & 3], bw[b][(2 * i + 1) & 3]);
-            } else {
-                lo = dq_mx4(bw[b][i], xs[b]);
-            }
+            for (int bb = 0; bb < NB; ++bb) {
+                if constexpr (CF == kCfMx4) {
+                    acc[mi][b0 + bb] = t[mi][bb];
+                } else {
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const f32x4_t c0 = i > 0 ? t[mi][b] : CF == kCfMx4 ? acc[mi][b] : seed[mi];
-                t[mi][b] = mfma16(av[mi], lo, c0);
-                if constexpr (CF == 8) t[mi][b] = mfma16(av[mi], hi, t[mi][b]);
+                    for (int r2 = 0; r2 < 4; ++r2) acc[mi][b0 + bb][r2] += sc[b0 + bb] * t[mi][bb][r2];
+                }
             }
-        }
-        hook(i);
     }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if constexpr (CF == kCfMx4) {
-                acc[mi][b] = t[mi][b];
-            } else {
-#pragma unroll
-                for (int r2 = 0; r2 < 4; ++r2) acc[mi][b][r2] += sc[b] * t[mi][b][r2];
-            }
-        }
 }
 
 // ------------------------------------------------------------------- epilogues
@@ -543,6 +558,7 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         return p;
     };
     uint32_t cpar = row_parity(s_items[0]);
+    int ccount = s_items[0].count;   // valid rows of the compute item
     // An item's epilogue runs after the next step's wait and barrier, before that step's
     // copies go out: its stores are then older than every copy batch still awaited, so
     // the in-order vmcnt waits never hold a batch back behind them.
@@ -569,15 +585,22 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         // waves wait for the load path while the others keep the matrix units busy
         const bool more = issued < total_steps;
         const int slot = __builtin_amdgcn_readfirstlane(wave >> 1);
-        compute_step<CF>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
-                         [&](int i) {
-                             if (more && i == slot) issue_next(-1);
-                         });
+        if (64 * (slot >> 1) < ccount) {
+            compute_step<CF>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
+                             [&](int i) {
+                                 if (more && i == slot) issue_next(-1);
+                             });
+        } else if (more) {
+            issue_next(-1);   // the wave's 64 rows of a ragged last tile are all padding
+        }
         if (more) advance();
         if (++gc == G) {
             epi = true;
             gc = 0;
-            if (++ci < n_items) cpar = row_parity(s_items[ci]);
+            if (++ci < n_items) {
+                cpar = row_parity(s_items[ci]);
+                ccount = s_items[ci].count;
+            }
         }
     }
     if (epi) finish_item();
