@@ -299,7 +299,7 @@ struct RouteArgs {
     int32_t* sorted;
     int32_t* active;
     int32_t* meta;        // [0] active experts, [1] M-tiles (routed)
-    int32_t* hist;        // large path: [nblk, E]
+    int32_t* hist;        // large path: [E, nblk] per-block counts, then first ranks
     int32_t* lrank;       // large path: [T*k]
     int32_t* tiles;       // large path: [max_tiles, 2] (expert, first row)
     const uint16_t* x;    // large path: activations for the group sums

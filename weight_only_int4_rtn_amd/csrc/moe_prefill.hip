@@ -402,11 +402,15 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
 
 // a = SiLU(gate) * up for the item's 128 x 128 block, bf16, columns in the reordered K
 // order of the down GEMM; and each row's fp32 sum of those bf16 values (one group of I).
+// The lane's 16 row partials (mi, r) are summed over the 16 lanes of its row group by a
+// reduce-scatter (halves exchanged with lane ^ 8, ^ 4, ^ 2, ^ 1: 15 exchanges), after
+// which lane ml holds the sum of row partial ml.
 __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t (&acc)[4][4], float* s_asum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
     const int wm = wave >> 2, wn = wave & 3;
     const int GW = (int)(a.width_a / kGroup);
+    float v[16];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -414,17 +418,23 @@ __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
             const int m = 64 * wm + 16 * mi + 4 * q + r;
             const uint32_t v0 = cvt_bf16(silu_mul(acc[mi][0][r], acc[mi][2][r]));
             const uint32_t v1 = cvt_bf16(silu_mul(acc[mi][1][r], acc[mi][3][r]));
-            float rs = bf16_to_f32(v0) + bf16_to_f32(v1);
+            v[4 * mi + r] = bf16_to_f32(v0) + bf16_to_f32(v1);
             if (m < it.count) {   // columns j and j + 4 of a block of 8: adjacent in K order
                 const int col = perm_pos(it.nblk * kGroup + 32 * wn + 8 * (ml >> 2) + (ml & 3));
                 *reinterpret_cast<uint32_t*>(a.abuf + (int64_t)(it.orow0 + m) * a.width_a + col) = v0 | (v1 << 16);
             }
-            rs += __shfl_xor(rs, 1, 16);   // sum over the row's 16 lanes
-            rs += __shfl_xor(rs, 2, 16);
-            rs += __shfl_xor(rs, 4, 16);
-            rs += __shfl_xor(rs, 8, 16);
-            if (ml == 0) s_asum[wn * MT + m] = rs;
         }
+#pragma unroll
+    for (int h = 8; h >= 1; h >>= 1) {
+        const bool up = (ml & h) != 0;
+#pragma unroll
+        for (int j = 0; j < h; ++j) {
+            const float send = up ? v[j] : v[j + h];
+            const float keep = up ? v[j + h] : v[j];
+            v[j] = keep + __shfl_xor(send, h, 16);
+        }
+    }
+    s_asum[wn * MT + 64 * wm + 16 * (ml >> 2) + 4 * q + (ml & 3)] = v[0];
     wait_lgkm0();
     bar();
     if ((int)threadIdx.x < it.count) {

@@ -14,8 +14,9 @@
 // from logits, route_split_kernel: one token per wave over ceil(T / 8) workgroups, and the
 // last workgroup to arrive finishes the routing of the whole batch.
 // Large batches: route_block_kernel (top-k, block histogram, in-block ranks, activation
-// group sums) -> route_scan_kernel (offsets, active experts, GEMM tile list) ->
-// route_scatter_kernel (sorted pair list).
+// group sums) -> route_colscan_kernel (per expert: ranks of each block's first pair, total)
+// -> route_scan_kernel (offsets, active experts, GEMM tile list) -> route_scatter_kernel
+// (sorted pair list).
 #include "common.h"
 #include "route_dev.h"
 #include "route_small.h"
@@ -140,72 +141,48 @@ __global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
         }
         a.lrank[(int64_t)t0 * k + p] = e >= 0 ? (e << 8 | rank) : -1;   // rank < 64 fits 8 bits
     }
-    for (int e = tid; e < E; e += blockDim.x) a.hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+    for (int e = tid; e < E; e += blockDim.x) a.hist[(int64_t)e * a.nblk + blockIdx.x] = s_cnt[e];
 }
 
-// One 1024-thread workgroup: per-expert totals over blocks, offsets, per-block bases
-// (written over the histogram), the active list and the M-tile list of the grouped GEMM.
-// Thread (e, part) owns expert e and a contiguous range of blocks, so the histogram is
-// read with many loads in flight instead of one long dependent walk.
+// One 256-thread workgroup per expert: the exclusive prefix of the expert's per-block
+// counts (expert-major, in place: each block's first rank within the expert) and the
+// expert's total.
+__global__ __launch_bounds__(256) void route_colscan_kernel(RouteArgs a) {
+    __shared__ int s_tmp[64];
+    const int e = blockIdx.x, tid = threadIdx.x, nblk = a.nblk;
+    int32_t* h = a.hist + (int64_t)e * nblk;
+    int carry = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 256) {
+        const int b = b0 + tid;
+        const int v = b < nblk ? h[b] : 0;
+        int tot = 0;
+        const int ex = block_exclusive_scan(v, s_tmp, &tot);
+        if (b < nblk) h[b] = carry + ex;
+        carry += tot;
+    }
+    if (tid == 0) a.counts[e] = carry;
+}
+
+// One 1024-thread workgroup: offsets from the experts' totals, the active list and the
+// M-tile list of the grouped GEMM.
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
     __shared__ int s_tmp[64];
-    __shared__ int s_part[1024];
-    const int tid = threadIdx.x, E = a.E, nblk = a.nblk;
-    const int Epad = (E + 63) & ~63;
-    const int parts = max(1, (int)blockDim.x / Epad);
-    const int e = tid % Epad, part = tid / Epad;
-    const bool owner = e < E && part < parts;
-    const int per = (nblk + parts - 1) / parts;
-    const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
-    int mine = 0;
-    if (owner) {
-        int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = a.hist[(int64_t)(b + j) * E + e];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) mine += v[j];
-        }
-        for (; b < b1; ++b) mine += a.hist[(int64_t)b * E + e];
-    }
-    s_part[tid] = mine;
-    __syncthreads();
-    int c = 0, lower = 0;
-    if (owner) {
-        for (int p = 0; p < parts; ++p) {
-            const int v = s_part[p * Epad + e];
-            c += v;
-            if (p < part) lower += v;
-        }
-    }
-    const bool lead = owner && part == 0;
+    const int e = threadIdx.x, E = a.E;
+    const int c = e < E ? a.counts[e] : 0;
     int total = 0, n_active = 0, n_tiles = 0;
-    const int off = block_exclusive_scan(lead ? c : 0, s_tmp, &total);
-    const int act = block_exclusive_scan(lead && c > 0 ? 1 : 0, s_tmp, &n_active);
-    const int nt = lead ? (c + kPrefillMT - 1) / kPrefillMT : 0;
+    const int off = block_exclusive_scan(c, s_tmp, &total);
+    const int act = block_exclusive_scan(c > 0 ? 1 : 0, s_tmp, &n_active);
+    const int nt = (c + kPrefillMT - 1) / kPrefillMT;
     const int toff = block_exclusive_scan(nt, s_tmp, &n_tiles);
-    if (lead) {
-        s_part[e] = off;   // every part of this expert reads the offset below
+    if (e < E) {
         a.offsets[e] = off;
-        a.counts[e] = c;
         if (c > 0) a.active[act] = e;
         for (int i = 0; i < nt && toff + i < a.max_tiles; ++i) {
             a.tiles[2 * (toff + i)] = e;
             a.tiles[2 * (toff + i) + 1] = i * kPrefillMT;
         }
     }
-    __syncthreads();
-    if (owner) {
-        int run = s_part[e] + lower;
-        for (int b = b0; b < b1; ++b) {
-            const int64_t i = (int64_t)b * E + e;
-            const int h = a.hist[i];
-            a.hist[i] = run;
-            run += h;
-        }
-    }
-    if (tid == 0) {
+    if (e == 0) {
         a.offsets[E] = total;
         a.meta[0] = n_active;
         a.meta[1] = (int)min((int64_t)n_tiles, a.max_tiles);
@@ -223,7 +200,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
     const int e = v >> 8, rank = v & 255;
     const int t = (int)(p / a.k);
     const int b = t / kRouteBlockT;
-    const int pos = a.hist[(int64_t)b * a.E + e] + rank;
+    const int pos = a.offsets[e] + a.hist[(int64_t)e * a.nblk + b] + rank;
     a.sorted[pos] = (int)p;
     a.tokw[pos] = int2{t, __float_as_int(a.wts[p])};
     a.inv[p] = pos;
@@ -242,6 +219,7 @@ hipError_t launch_route_split(const RouteArgs& a, hipStream_t s, StageTimer* t) 
 
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t s, StageTimer* t) {
     launch(t, "route_block", route_block_kernel, dim3(a.nblk), dim3(1024), s, 0u, a);
+    launch(t, "route_colscan", route_colscan_kernel, dim3((unsigned)a.E), dim3(256), s, 0u, a);
     launch(t, "route_scan", route_scan_kernel, dim3(1), dim3(1024), s, 0u, a);
     const int64_t P = (int64_t)a.T * a.k;
     launch(t, "route_scatter", route_scatter_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), s, 0u, a);
