@@ -70,7 +70,8 @@ __global__ __launch_bounds__(64 * kSplitWaves) void route_split_kernel(RouteArgs
 
 // ------------------------------------------------------------------ large batch
 
-// One workgroup per block of kRouteBlockT tokens (16 waves, 2 tokens each).
+// One workgroup per block of kRouteBlockT = 32 tokens (16 waves, 2 tokens each).
+static_assert(kRouteBlockT == 32, "route_block_kernel: two tokens per wave, 16 waves");
 __global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
     __shared__ int s_ids[kRouteBlockT * kMaxK];
     __shared__ int s_cnt[kMaxE];
@@ -82,35 +83,67 @@ __global__ __launch_bounds__(1024) void route_block_kernel(RouteArgs a) {
     const int nt = min(kRouteBlockT, a.T - t0);
     for (int e = tid; e < E; e += blockDim.x) { s_cnt[e] = 0; s_mlo[e] = 0; s_mhi[e] = 0; }
 
-    for (int tl = wave; tl < nt; tl += 16) {
+    // Wave w takes tokens w and w + 16 of the block.  Their activations (lane: 32 columns of
+    // each 2048) are loaded before anything else, all at once, so that the latency overlaps
+    // the top-k; from logits with E <= 256 the two selections run interleaved.
+    const int tl0 = wave, tl1 = wave + 16;
+    const int ntok = (tl0 < nt) + (tl1 < nt);
+    u32x4_t r[2][4];
+    auto load_x = [&](int j, int64_t c) {
+        const uint16_t* xr = a.x + (int64_t)(t0 + (j ? tl1 : tl0)) * a.H;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[j][i] = *reinterpret_cast<const u32x4_t*>(xr + c + 8 * i);
+    };
+    if (lane * 32 < a.H) {
+        if (ntok > 0) load_x(0, lane * 32);
+        if (ntok > 1) load_x(1, lane * 32);
+    }
+    auto put = [&](int tl, int my_id, float my_w) {
         const int t = t0 + tl;
-        if (a.logits) {
-            int my_id;
-            float my_w;
-            wave_topk_any(a.logits + (int64_t)t * E, E, k, &my_id, &my_w);
-            if (lane < k) {
-                a.ids[(int64_t)t * k + lane] = my_id;
-                a.wts[(int64_t)t * k + lane] = my_w;
-                s_ids[tl * k + lane] = my_id;
-            }
-        } else if (lane < k) {
-            s_ids[tl * k + lane] = checked_id(a.ids + (int64_t)t * k, lane, E);
+        if (lane < k) {
+            a.ids[(int64_t)t * k + lane] = my_id;
+            a.wts[(int64_t)t * k + lane] = my_w;
+            s_ids[tl * k + lane] = my_id;
         }
-        // sums of the bf16 activations over each group of 128 columns (lane: 32 columns),
-        // and the row copied with every 8-column block in the MFMA operand order
-        const uint16_t* xr = a.x + (int64_t)t * a.H;
+    };
+    if (a.logits && E <= 256 && ntok == 2) {
+        float raw[2][4];
+        wave_topk_load<4>(a.logits + (int64_t)(t0 + tl0) * E, E, raw[0]);
+        wave_topk_load<4>(a.logits + (int64_t)(t0 + tl1) * E, E, raw[1]);
+        int my_id[2];
+        float my_w[2];
+        wave_topk_multi<2>(raw, E, k, my_id, my_w);
+        put(tl0, my_id[0], my_w[0]);
+        put(tl1, my_id[1], my_w[1]);
+    } else {
+        for (int j = 0; j < ntok; ++j) {
+            const int tl = j ? tl1 : tl0, t = t0 + tl;
+            if (a.logits) {
+                int my_id;
+                float my_w;
+                wave_topk_any(a.logits + (int64_t)t * E, E, k, &my_id, &my_w);
+                put(tl, my_id, my_w);
+            } else if (lane < k) {
+                s_ids[tl * k + lane] = checked_id(a.ids + (int64_t)t * k, lane, E);
+            }
+        }
+    }
+    // sums of the bf16 activations over each group of 128 columns (lane: 32 columns), and
+    // the row copied with every 8-column block in the MFMA operand order
+    for (int j = 0; j < ntok; ++j) {
+        const int t = t0 + (j ? tl1 : tl0);
         uint16_t* xpr = a.xp + (int64_t)t * a.H;
         for (int64_t c0 = 0; c0 < a.H; c0 += 64 * 32) {
             const int64_t c = c0 + lane * 32;
             float sum = 0.0f;
             if (c < a.H) {
+                if (c0 > 0) load_x(j, c);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const u32x4_t r = *reinterpret_cast<const u32x4_t*>(xr + c + 8 * i);
-                    *reinterpret_cast<u32x4_t*>(xpr + c + 8 * i) = perm_act(r);
+                    *reinterpret_cast<u32x4_t*>(xpr + c + 8 * i) = perm_act(r[j][i]);
 #pragma unroll
                     for (int h = 0; h < 4; ++h)
-                        sum += __uint_as_float(r[h] << 16) + __uint_as_float(r[h] & 0xffff0000u);
+                        sum += __uint_as_float(r[j][i][h] << 16) + __uint_as_float(r[j][i][h] & 0xffff0000u);
                 }
             }
             sum += __shfl_xor(sum, 1);
