@@ -584,21 +584,22 @@ def measure_linear(T, copies, steps, seed):
 
 
 def read_floor(nbytes, n_buffers, reps):
-    """The achievable time to read `nbytes` from HBM in one launch: a plain reduction kernel
-    (torch.sum over int32 words) over one of `n_buffers` buffers, rotated so that every read
-    misses the 256 MB Infinity Cache; returns us per read (event-timed, back to back)."""
+    """The achievable time to read `nbytes` from HBM in one launch: a plain row reduction
+    (torch.sum over rows of 4096 int32 words, one output word per 16 KB row) over one of
+    `n_buffers` buffers, rotated so that every read misses the 256 MB Infinity Cache;
+    returns us per read (event-timed, back to back)."""
     import torch
     dev = torch.device("cuda:0")
-    n = nbytes // 4
-    bufs = [torch.ones(n, dtype=torch.int32, device=dev) for _ in range(n_buffers)]
-    out = torch.empty((), dtype=torch.int64, device=dev)
+    rows = max(1, nbytes // (4 * 4096))
+    bufs = [torch.ones((rows, 4096), dtype=torch.int32, device=dev) for _ in range(n_buffers)]
+    out = torch.empty((rows,), dtype=torch.int64, device=dev)
     for i in range(n_buffers):
-        torch.sum(bufs[i], out=out)
+        torch.sum(bufs[i], dim=1, out=out)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(reps):
-        torch.sum(bufs[i % n_buffers], out=out)
+        torch.sum(bufs[i % n_buffers], dim=1, out=out)
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / reps * 1e3
