@@ -32,6 +32,7 @@ METRIC = "decode tok/s + expert-weight HBM GB/s (bs1/32); prefill TFLOP/s at 819
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 E, K, H, I = 256, 8, 2048, 512
+NO_GRAPH = False   # set by --no-graph
 
 
 def log(*a):
@@ -129,28 +130,32 @@ def measure(name, T, layers, steps, warmup, timed_steps, seed):
     # the same steps replayed from a HIP graph (one graph holds a full rotation of n_logits
     # steps), which removes host launch cost as a decode loop does in serving; an event pair
     # around every replay gives the distribution of the per-step time over replays
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(n_logits):
-            step(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = max(25, -(-steps // n_logits))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    start.record()
-    for r in range(reps):
-        evs[r][0].record()
+    if NO_GRAPH:   # counter-collection runs: eager launches only (reported in both fields)
+        graph_ms = eager_ms
+        pct = {"p10": eager_ms, "p50": eager_ms, "p90": eager_ms, "samples": 1, "steps_per_sample": steps}
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_logits):
+                step(i)
         graph.replay()
-        evs[r][1].record()
-    end.record()
-    torch.cuda.synchronize()
-    graph_ms = start.elapsed_time(end) / (reps * n_logits)
-    samples = sorted(a.elapsed_time(b) / n_logits for a, b in evs)
-    pct = {"p10": samples[len(samples) // 10], "p50": samples[len(samples) // 2],
-           "p90": samples[(9 * len(samples)) // 10], "samples": len(samples), "steps_per_sample": n_logits}
-    del graph
+        torch.cuda.synchronize()
+        reps = max(25, -(-steps // n_logits))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        start.record()
+        for r in range(reps):
+            evs[r][0].record()
+            graph.replay()
+            evs[r][1].record()
+        end.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(end) / (reps * n_logits)
+        samples = sorted(a.elapsed_time(b) / n_logits for a, b in evs)
+        pct = {"p10": samples[len(samples) // 10], "p50": samples[len(samples) // 2],
+               "p90": samples[(9 * len(samples)) // 10], "samples": len(samples), "steps_per_sample": n_logits}
+        del graph
     # the faster of the two launch modes is the step time (both are reported)
-    launch_mode = "graph" if graph_ms <= eager_ms else "eager"
+    launch_mode = "eager" if NO_GRAPH or graph_ms > eager_ms else "graph"
     ms_per_step = min(graph_ms, eager_ms)
 
     # per-kernel durations with HIP events around each kernel, same rotation
@@ -584,22 +589,23 @@ def measure_linear(T, copies, steps, seed):
 
 
 def read_floor(nbytes, n_buffers, reps):
-    """The achievable time to read `nbytes` from HBM in one launch: a plain row reduction
-    (torch.sum over rows of 4096 int32 words, one output word per 16 KB row) over one of
-    `n_buffers` buffers, rotated so that every read misses the 256 MB Infinity Cache;
-    returns us per read (event-timed, back to back)."""
+    """The achievable time to read `nbytes` from HBM in one launch: the library's plain
+    streaming read (w4a16_stream_read: 16-byte vector loads, grid-stride, XOR-folded into
+    one word) over one of `n_buffers` buffers, rotated so that every read misses the 256 MB
+    Infinity Cache; returns us per read (event-timed, back to back)."""
     import torch
+    import weight_only_int4_rtn_amd as w4
     dev = torch.device("cuda:0")
-    rows = max(1, nbytes // (4 * 4096))
-    bufs = [torch.ones((rows, 4096), dtype=torch.int32, device=dev) for _ in range(n_buffers)]
-    out = torch.empty((rows,), dtype=torch.int64, device=dev)
+    n = (nbytes + 15) // 16 * 4
+    bufs = [torch.ones(n, dtype=torch.int32, device=dev) for _ in range(n_buffers)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
     for i in range(n_buffers):
-        torch.sum(bufs[i], dim=1, out=out)
+        w4.stream_read(bufs[i], sink)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(reps):
-        torch.sum(bufs[i % n_buffers], dim=1, out=out)
+        w4.stream_read(bufs[i % n_buffers], sink)
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / reps * 1e3
@@ -782,10 +788,14 @@ def main():
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-formats", action="store_true", help="skip the FP8 / MXFP4 expert runs")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense INT8 projection runs")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP graph capture; for counter-collection runs)")
     ap.add_argument("--no-sclk", action="store_true",
                     help="do not sample the shader clock (it starts rocm-smi; use under a profiler)")
     ap.add_argument("--cpu-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    global NO_GRAPH
+    NO_GRAPH = args.no_graph
     if args.cpu_child is not None:
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
         print(json.dumps(_cpu_child(json.loads(args.cpu_child))), flush=True)
@@ -859,6 +869,11 @@ def main():
         del stack_layers
         torch.cuda.empty_cache()
 
+    if not results and stack is None:   # side measurements only (a profiling run): no headline
+        side = {"router": router, "formats": formats or None, "dense_int8": dense, "quantize": quant}
+        print(json.dumps({"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1,
+                          **{k: v for k, v in side.items() if v}}), flush=True)
+        return
     if not results:   # only the stack was asked for: it is the headline
         line = {"metric": METRIC, "value": round(stack["tok_per_s"], 2), "unit": "tok/s", "n_gpus": 1,
                 "steps": max(5, args.steps // 20), "warmup": max(2, args.warmup // 5),

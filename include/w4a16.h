@@ -357,6 +357,17 @@ int w4a16_linear(const w4a16_linear_args* args, void* stream);
 int moe_w4a16_forward_timed(const moe_w4a16_args* args, void* stream, int max_kernels, float* kernel_ms,
                             const char** kernel_names, int* n_kernels);
 
+/*
+ * w4a16_stream_read - a plain streaming read of `bytes` bytes at device address `buf`
+ * (16-byte aligned, bytes a multiple of 16): every 32-bit word is read once and their XOR
+ * is XOR-ed into the device word *sink.  Asynchronous on `stream`.  A measurement aid: its
+ * launch time is the achievable time to read that many bytes in one kernel, the reference
+ * for the decode kernels' reads of the same byte count.
+ * Errors: W4A16_ERR_INVALID_ARG for a NULL pointer, a misaligned buffer or a byte count
+ * that is negative or not a multiple of 16.
+ */
+int w4a16_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

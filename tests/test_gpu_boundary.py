@@ -131,3 +131,26 @@ def test_binding_rejects_mismatched_shapes():
     y = fwd()
     torch.cuda.synchronize()
     assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("n_words", [4, 64, 4 * 1000 + 4, 1 << 22])
+def test_stream_read_xor(n_words):
+    """The measurement aid's fold of every word read (a ragged tail past the 4-vector loop)."""
+    import numpy as np
+    rng = np.random.default_rng(n_words)
+    host = rng.integers(0, 2 ** 32, size=n_words, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to("cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    w4.stream_read(buf, sink)
+    w4.stream_read(buf, sink)   # twice: the fold cancels
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    w4.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == np.bitwise_xor.reduce(host)
+
+
+def test_stream_read_argument_rules():
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    with pytest.raises(Exception):
+        w4.stream_read(torch.zeros(5, dtype=torch.int32, device="cuda:0"), sink)   # 20 bytes

@@ -21,7 +21,7 @@ import ctypes as C
 from . import _lib
 from ._lib import W4A16Error, MoeArgs  # noqa: F401
 
-__all__ = ["rtn_quantize_pack", "fp8_quantize_pack", "mxfp4_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
+__all__ = ["stream_read", "rtn_quantize_pack", "fp8_quantize_pack", "mxfp4_quantize_pack", "moe_w4a16_forward", "moe_w4a16_forward_timed", "moe_w4a16_workspace_size",
            "moe_w4a16_workspace_init", "moe_w4a16_workspace_check", "new_workspace", "w4a16_linear",
            "MoeCall", "w4a16_abi_version", "W4A16Error", "library_path"]
 
@@ -557,3 +557,17 @@ class MoeCall:
         if st:
             _lib.check(st, "moe_w4a16_forward")
         return out
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """A plain streaming read of ``buf`` (a contiguous device tensor of a multiple of 16
+    bytes): the XOR of its 32-bit words is XOR-ed into ``sink`` (one int32 on the same
+    device).  The measurement aid ``w4a16_stream_read``."""
+    if not (buf.is_cuda and sink.is_cuda and buf.device == sink.device):
+        raise ValueError("stream_read: buf and sink must be tensors on one GPU")
+    if not buf.is_contiguous() or sink.dtype != _torch().int32 or sink.numel() != 1:
+        raise ValueError("stream_read: contiguous buf and a one-element int32 sink")
+    nbytes = buf.numel() * buf.element_size()
+    st = _lib.lib().w4a16_stream_read(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
+                                      _stream(buf.device, stream))
+    _lib.check(st, "w4a16_stream_read")

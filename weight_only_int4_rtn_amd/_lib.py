@@ -45,6 +45,7 @@ EXPORTED = (
     "moe_w4a16_forward_noalloc",
     "w4a16_linear_workspace_size",
     "w4a16_linear",
+    "w4a16_stream_read",
 )
 
 
@@ -130,6 +131,8 @@ def lib():
     L.moe_w4a16_forward_timed.restype = C.c_int
     L.moe_w4a16_forward_timed.argtypes = [C.POINTER(MoeArgs), C.c_void_p, C.c_int, C.POINTER(C.c_float),
                                           C.POINTER(C.c_char_p), C.POINTER(C.c_int)]
+    L.w4a16_stream_read.restype = C.c_int
+    L.w4a16_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
     if L.w4a16_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH}: ABI version {L.w4a16_abi_version()}, expected {ABI_VERSION}")
     _lib = L

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 SOURCES = ["api.hip", "quant.hip", "quant_fmt.hip", "route.hip", "router.hip", "linear.hip", "moe_decode.hip",
-           "decode_stream.hip", "moe_prefill.hip"]
+           "decode_stream.hip", "moe_prefill.hip", "stream_read.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

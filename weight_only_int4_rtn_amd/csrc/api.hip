@@ -644,6 +644,14 @@ int moe_w4a16_forward_noalloc(const moe_w4a16_args* a, void* stream) {
     return forward_impl(&b, stream, nullptr, /*allow_single_launch=*/false);
 }
 
+int w4a16_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    g_last_error.clear();
+    if (!buf || !sink) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer or sink");
+    if (bytes < 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "stream_read needs a 16-byte aligned buffer and a multiple of 16 bytes");
+    return hip_status(launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)), "stream_read");
+}
+
 int moe_w4a16_forward_timed(const moe_w4a16_args* a, void* stream, int max_kernels, float* kernel_ms,
                             const char** kernel_names, int* n_kernels) {
     g_last_error.clear();

@@ -477,5 +477,6 @@ struct LinearPrep {
     int32_t* inv;        // [T]
 };
 hipError_t launch_linear_prep(const LinearPrep& p, hipStream_t s, StageTimer* t = nullptr);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace w4a16
