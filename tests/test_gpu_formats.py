@@ -249,3 +249,32 @@ def test_ffn_shapes(fmt, T, E, H, I, k):
     torch.cuda.synchronize()
     y0_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), BITS[fmt], weight_format=fmt)
     check_ffn(y0, y0_ref, f"{fmt} T={T} routed only")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("T,shared_bits", [(1, 0), (2, 4), (2, 8)])
+def test_single_launch_formats(fmt, T, shared_bits):
+    """One- and two-token layers of the float formats take the single-launch kernel (routing,
+    gate/up and down in one launch), with or without an INT shared expert; three calls in a
+    row on one workspace (the launch epoch advances between them)."""
+    from gpu_util import OracleExperts
+    E, H, I, k = 64, 1024, 256, 8
+    layer = fmt_layer(fmt, 81, 0, E, H, I)
+    ref = FmtExperts(fmt, 81, 0, H, I)
+    kw, sh_ref, sI = {}, None, 0
+    if shared_bits:
+        sI = 512
+        kw = dict(shared=gpu_layer(81, 0, 1, H, sI, shared_bits, shared=True))
+        sh_ref = OracleExperts(81, 0, H, sI, shared_bits, shared=True).shared_dict()
+    say(f"{fmt} single launch T={T} shared={shared_bits}")
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, k, shared_bits, sI), DEV)
+    for it in range(3):
+        x = synth.activations_bf16(700 + 10 * T + it, T, H)
+        logits = synth.router_logits(700 + 10 * T + it, T, E)
+        y, tk = w4.moe_w4a16_forward_timed(bf16_to_dev(x), *layer, top_k=k, bits=BITS[fmt], weight_format=fmt,
+                                           router_logits=f32_to_dev(logits), workspace=ws, **kw)
+        assert [nm for nm, _ in tk] == ["tiny_decode"], tk
+        ids, wts, *_ = oracle.route(logits, k)
+        ref.prefetch(np.unique(ids))
+        y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), BITS[fmt], weight_format=fmt, shared=sh_ref)
+        check_ffn(y, y_ref, f"{fmt} single launch T={T} shared={shared_bits} call {it}")

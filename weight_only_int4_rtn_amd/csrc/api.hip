@@ -201,9 +201,9 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     const size_t tag_bytes = (size_t)L.rows_a * L.width_a * 4;
     const size_t tiny_lds = 8 * (size_t)a->T * 16 * 4 + (size_t)L.rows_a * (L.width_a + kTinyPad) * 2 + 1024 +
                             (size_t)L.rows_a * (L.width_a / kGroup) * 4;
-    if (allow_single_launch && int_codes && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
+    if (allow_single_launch && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
         tiny_lds <= kTinyMaxLds &&
-        a->H / 16 <= tiny_max_down_workgroups(a->bits, a->shared_bits)) {
+        a->H / 16 <= tiny_max_down_workgroups(a->weight_format, a->bits, a->shared_bits)) {
         TinyArgs d{};
         d.x = a->x;
         d.T = (int)a->T;

@@ -423,7 +423,7 @@ struct TinyArgs {
 hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t = nullptr);
 // Down workgroups the single-launch path may use on the current device: half of the
 // workgroups of its kernel that the device holds at once (0 when unknown).
-int tiny_max_down_workgroups(int bits, int sbits);
+int tiny_max_down_workgroups(int fmt, int bits, int sbits);
 hipError_t launch_head_init(uint32_t* head, hipStream_t s);
 
 struct PrefillArgs {

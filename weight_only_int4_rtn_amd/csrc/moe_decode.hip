@@ -533,9 +533,10 @@ __device__ void tiny_route(const TinyArgs& a, TinyRoute& r, bool writer) {
 
 // Gate/up workgroup b: pair p = b / n_rb (token p / k, rank p % k) and its 16-row block
 // b % n_rb, writing row p of the tag area; or, after the pairs, a row block of the shared
-// expert for every token (rows T * k + t).
-template <int BITS, int SBITS>
+// expert for every token (rows T * k + t).  CF: the routed experts' code format.
+template <int CF, int SBITS>
 __device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
+    constexpr int BITS = cf_bits(CF);
     const int b = blockIdx.x - (int)(a.H / 16);   // down workgroups come first in the grid
     const int Tk = a.T * a.k;
     const int p = b / a.n_rb, rb = b % a.n_rb;
@@ -548,9 +549,10 @@ __device__ void tiny_gate_up(const TinyArgs& a, float* s_red, uint32_t tag) {
         const int e = pair_expert<true>(a.logits, a.ids, a.E, a.k, t, p % a.k);
         if (e < 0) return;   // dropped pair: the down workgroups skip its row
         const int64_t w13_words = 2 * I_e * a.H * BITS / 32;
-        gk_tile<BITS, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
-                            reinterpret_cast<const uint8_t*>(a.routed.s13 + (int64_t)e * 2 * I_e * (a.H / kGroup)),
-                            n0, t, ml == 0, p, 1, a.tags, a.width_a, s_red, a.tag_bytes, tag);
+        gk_tile<CF, true>(a.x, a.H, I_e, a.routed.w13 + (int64_t)e * w13_words,
+                          reinterpret_cast<const uint8_t*>(a.routed.s13) +
+                              (int64_t)e * expert_scale_bytes<CF>(2 * I_e, (int)(a.H / kGroup)),
+                          n0, t, ml == 0, p, 1, a.tags, a.width_a, s_red, a.tag_bytes, tag);
     } else if constexpr (SBITS != 0) {
         const int64_t I_e = a.shared.I;
         if (p > Tk || n0 >= I_e) return;
@@ -568,20 +570,24 @@ constexpr int kTinyCh = BITS == 4 ? 4 : 2;
 
 struct TinyUnit {
     const uint8_t* wrow;    // this lane's code bytes: row h0 + ml, the unit's first group, quarter q
-    const uint16_t* srow;   // scales of row h0 + ml from the unit's first group
+    const uint8_t* sexp;    // the expert's scale buffer (bytes; layout of its code format)
+    int64_t srow;           // row h0 + ml of it
+    int G;                  // groups of K = I
     int pos0, count;        // a rows pos0 .. pos0 + count - 1
     int g0, ngroups;        // first group, groups present
     int shared;
 };
 
-template <int BITS>
+template <int CF>
 struct TinyCodes {
-    u32x4_t w[kTinyCh<BITS>][BITS / 4];
-    uint32_t s[kTinyCh<BITS>];   // raw bf16 scales, 0 for an absent group
+    u32x4_t w[kTinyCh<cf_bits(CF)>][cf_bits(CF) / 4];
+    uint32_t s[kTinyCh<cf_bits(CF)>];   // raw scales: INT bf16, FP8 fp32 bits, MXFP4 the lane's E8M0 byte
 };
 
 // Unit `u` of this workgroup: routed slots (kTinyCh-group chunks) first, then the shared
-// expert's chunks.  Returns the unit's code width.
+// expert's chunks.  CF: the routed experts' code format (the shared expert's is INT).
+// Returns the unit's code width.
+template <int CF>
 __device__ __forceinline__ int tiny_make_unit(const TinyArgs& a, const TinyRoute& r, int u, int nch, int h0,
                                               TinyUnit& t) {
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
@@ -609,20 +615,28 @@ __device__ __forceinline__ int tiny_make_unit(const TinyArgs& a, const TinyRoute
     const int64_t row_bytes = es.I * es.bits / 8;
     t.wrow = reinterpret_cast<const uint8_t*>(es.w2) + e * a.H * row_bytes + (int64_t)(h0 + ml) * row_bytes +
              (int64_t)t.g0 * (kGroup * es.bits / 8) + q * (32 * es.bits / 8);
-    t.srow = es.s2 + e * a.H * G + (int64_t)(h0 + ml) * G + t.g0;
+    t.G = G;
+    t.srow = h0 + ml;
+    t.sexp = reinterpret_cast<const uint8_t*>(es.s2) +
+             e * (t.shared ? expert_scale_bytes<4>(a.H, G) : expert_scale_bytes<CF>(a.H, G));
     return es.bits;
 }
 
 // Issues the unit's code and scale loads; nothing waits for them here.
-template <int BITS>
-__device__ __forceinline__ void tiny_load_unit(const TinyUnit& t, TinyCodes<BITS>& c) {
+template <int CF>
+__device__ __forceinline__ void tiny_load_unit(const TinyUnit& t, TinyCodes<CF>& c) {
+    constexpr int BITS = cf_bits(CF);
     constexpr int kGroupBytes = kGroup * BITS / 8;
+    const int q = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int j = 0; j < kTinyCh<BITS>; ++j) {
         const int jj = min(j, t.ngroups - 1);
 #pragma unroll
         for (int v = 0; v < BITS / 4; ++v) c.w[j][v] = load_stream16(t.wrow + (int64_t)jj * kGroupBytes + 16 * v);
-        c.s[j] = t.srow[jj];
+        const uint8_t* sp = t.sexp + scale_at<CF>(t.srow, t.G, t.g0 + jj);
+        if constexpr (CF == kCfFp8) c.s[j] = *reinterpret_cast<const uint32_t*>(sp);
+        else if constexpr (CF == kCfMx4) c.s[j] = sp[q];
+        else c.s[j] = *reinterpret_cast<const uint16_t*>(sp);
     }
 }
 
@@ -632,10 +646,11 @@ __device__ __forceinline__ void tiny_load_unit(const TinyUnit& t, TinyCodes<BITS
 // A fragments come from the staged rows (stride Ws, padded so that the 16 rows of an
 // M-tile fall in different LDS banks); a padding lane reads its own 16 bytes of the zero
 // block `zb` instead, so no two lanes of a read share an address.
-template <int BITS>
-__device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BITS>& c, const uint16_t* stage,
+template <int CF>
+__device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<CF>& c, const uint16_t* stage,
                                           const float* xs, int Ws, int G, const uint16_t* zb, const TinyRoute& r,
                                           float* yacc) {
+    constexpr int BITS = cf_bits(CF);
     constexpr int CH = kTinyCh<BITS>;
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const bool real = ml < t.count;
@@ -662,12 +677,16 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
             for (int jj = 0; jj < 2; ++jj) {
                 const int j = j0 + jj;
                 const f32x4_t c0 = i == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : d[j];
-                if constexpr (BITS == 4) {
+                if constexpr (CF == 4) {
                     d[j] = mfma16(av[jj][i], dq4(c.w[j][0][i], M), c0);
-                } else {
+                } else if constexpr (CF == 8) {
                     u32x4_t lo, hi;
                     dq8(c.w[j][i >> 1][(2 * i) & 3], c.w[j][i >> 1][(2 * i + 1) & 3], lo, hi, M);
                     d[j] = mfma16(av[jj][i], hi, mfma16(av[jj][i], lo, c0));
+                } else if constexpr (CF == kCfFp8) {
+                    d[j] = mfma16(av[jj][i], dq_fp8(c.w[j][i >> 1][(2 * i) & 3], c.w[j][i >> 1][(2 * i + 1) & 3]), c0);
+                } else {
+                    d[j] = mfma16(av[jj][i], dq_mx4(c.w[j][0][i], e8m0_scale(c.s[j])), c0);
                 }
             }
     }
@@ -680,8 +699,12 @@ __device__ __forceinline__ void tiny_unit(const TinyUnit& t, const TinyCodes<BIT
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int g = t.g0 + min(j, t.ngroups - 1);
-            const float sc = j < t.ngroups ? bf16_to_f32(c.s[j]) : 0.f;
-            acc += sc * (d[j][rr] - code_offset<BITS>() * xs[xr * G + g]);
+            // INT: the group's scale, offset seed from the row's group sum; FP8: the row's
+            // scale; MXFP4: 1 (the block scale is inside the conversion)
+            float sc = CF == kCfFp8 ? __uint_as_float(c.s[j]) : CF == kCfMx4 ? 1.f : bf16_to_f32(c.s[j]);
+            sc = j < t.ngroups ? sc : 0.f;
+            if constexpr (cf_int(CF)) acc += sc * (d[j][rr] - code_offset<CF>() * xs[xr * G + g]);
+            else acc += sc * d[j][rr];
         }
         if (m < t.count) {
             const int2 tw = t.shared ? int2{m, __float_as_int(r.sg[m])} : r.tw[p];
@@ -760,7 +783,7 @@ __device__ bool tiny_collect_unit(const TinyArgs& a, const TinyRoute& r, const T
     return timed_out;
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, uint32_t epoch_word) {
     __shared__ int s_last;
     __shared__ int s_bad;   // a wait of this workgroup timed out, or an earlier call's did
@@ -785,25 +808,27 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     __syncthreads();   // the zero block is read by every wave
 
     // units: kTinyCh-group chunks of every active slot, then of the shared expert
+    constexpr int BITS = cf_bits(CF);
+    // shared-expert units use their own code type when their format differs from the routed one
+    constexpr bool kSep = SBITS != 0 && SBITS != CF;
     const int nch = (int)((a.routed.I / kGroup + kTinyCh<BITS> - 1) / kTinyCh<BITS>);
     const int nch_s = SBITS != 0 ? (int)((a.shared.I / kGroup + kTinyCh<SBITS> - 1) / kTinyCh<SBITS>) : 0;
     const int n_units = r.n_active * nch + nch_s;
     const int V = kDkWaves;
     int u = wave;
     TinyUnit cu, nu;
-    TinyCodes<BITS> cc, nc;
-    TinyCodes<SBITS ? SBITS : 4> cs, ns;   // shared-expert codes when their width differs
-    int cbits = BITS, nbits = BITS;
+    TinyCodes<CF> cc, nc;
+    TinyCodes<SBITS ? SBITS : 4> cs, ns;   // shared-expert codes when their format differs
     // the first two units' codes go out before the wait for the a rows
     if (u < n_units) {
-        cbits = tiny_make_unit(a, r, u, nch, h0, cu);
-        if (cbits == BITS) tiny_load_unit<BITS>(cu, cc);
-        else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(cu, cs);
+        tiny_make_unit<CF>(a, r, u, nch, h0, cu);
+        if (!kSep || !cu.shared) tiny_load_unit<CF>(cu, cc);
+        else if constexpr (kSep) tiny_load_unit<SBITS>(cu, cs);
     }
     if (u + V < n_units) {
-        nbits = tiny_make_unit(a, r, u + V, nch, h0, nu);
-        if (nbits == BITS) tiny_load_unit<BITS>(nu, nc);
-        else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
+        tiny_make_unit<CF>(a, r, u + V, nch, h0, nu);
+        if (!kSep || !nu.shared) tiny_load_unit<CF>(nu, nc);
+        else if constexpr (kSep) tiny_load_unit<SBITS>(nu, ns);
     }
 
     // each wave waits for the a values of its own units only, unit by unit, so a wave whose
@@ -813,18 +838,17 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     bool bad = false;
     while (u < n_units) {
         bad |= tiny_collect_unit(a, r, cu, tag, stage, Ws, xs, G, spin_limit);
-        if (cbits == BITS) tiny_unit<BITS>(cu, cc, stage, xs, Ws, G, zb, r, yacc);
-        else if constexpr (SBITS != 0 && SBITS != BITS) tiny_unit<SBITS>(cu, cs, stage, xs, Ws, G, zb, r, yacc);
+        if (!kSep || !cu.shared) tiny_unit<CF>(cu, cc, stage, xs, Ws, G, zb, r, yacc);
+        else if constexpr (kSep) tiny_unit<SBITS>(cu, cs, stage, xs, Ws, G, zb, r, yacc);
         u += V;
         if (u >= n_units) break;
         cu = nu;
         cc = nc;
-        if constexpr (SBITS != 0 && SBITS != BITS) cs = ns;
-        cbits = nbits;
+        if constexpr (kSep) cs = ns;
         if (u + V < n_units) {
-            nbits = tiny_make_unit(a, r, u + V, nch, h0, nu);
-            if (nbits == BITS) tiny_load_unit<BITS>(nu, nc);
-            else if constexpr (SBITS != 0 && SBITS != BITS) tiny_load_unit<SBITS>(nu, ns);
+            tiny_make_unit<CF>(a, r, u + V, nch, h0, nu);
+            if (!kSep || !nu.shared) tiny_load_unit<CF>(nu, nc);
+            else if constexpr (kSep) tiny_load_unit<SBITS>(nu, ns);
         }
     }
     if (bad) s_bad = 1;   // (benign race: every writer stores 1)
@@ -865,7 +889,7 @@ __device__ void tiny_down(const TinyArgs& a, const TinyRoute& r, float* s_dyn, u
     }
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __device__ __forceinline__ void tiny_decode_body(const TinyArgs& a) {
     __shared__ TinyRoute route;
     // 16-byte aligned: the static route table before it would leave it at a 4-byte boundary
@@ -874,24 +898,26 @@ __device__ __forceinline__ void tiny_decode_body(const TinyArgs& a) {
     const uint32_t epoch_word =
         __hip_atomic_load(sync_word(a.sync, kSyncEpoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int)blockIdx.x >= (int)(a.H / 16)) {
-        tiny_gate_up<BITS, SBITS>(a, s_dyn, (epoch_word + 1) << 16);
+        tiny_gate_up<CF, SBITS>(a, s_dyn, (epoch_word + 1) << 16);
     } else {
         tiny_route(a, route, blockIdx.x == 0);
-        tiny_down<BITS, SBITS>(a, route, s_dyn, epoch_word);
+        tiny_down<CF, SBITS>(a, route, s_dyn, epoch_word);
     }
 }
 
 // Two workgroups per CU where the registers allow it without spilling (4-bit codes with
 // no 8-bit expert), one otherwise.
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(64 * kDkWaves) __attribute__((amdgpu_waves_per_eu(4))) void tiny_decode_kernel(
     TinyArgs a) {
-    tiny_decode_body<BITS, SBITS>(a);
+    tiny_decode_body<CF, SBITS>(a);
 }
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(64 * kDkWaves) void tiny_decode_wide_kernel(TinyArgs a) {
-    tiny_decode_body<BITS, SBITS>(a);
+    tiny_decode_body<CF, SBITS>(a);
 }
+template <int CF, int SBITS>
+constexpr bool tiny_narrow() { return (CF == 4 && SBITS != 8) || (CF == kCfMx4 && SBITS == 0); }
 
 __global__ __launch_bounds__(256) void head_init_kernel(uint32_t* head) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < (int)(kHeadBytes / 16); i += gridDim.x * blockDim.x)
@@ -970,14 +996,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
 namespace w4a16 {
 
 namespace {
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 hipError_t launch_tiny_t(const TinyArgs& a, hipStream_t s, StageTimer* t) {
     const int n_dk = (int)(a.H / 16);
-    if constexpr (BITS == 4 && SBITS != 8)
-        launch(t, "tiny_decode", tiny_decode_kernel<BITS, SBITS>, dim3((unsigned)(a.n_gk + n_dk)),
+    if constexpr (tiny_narrow<CF, SBITS>())
+        launch(t, "tiny_decode", tiny_decode_kernel<CF, SBITS>, dim3((unsigned)(a.n_gk + n_dk)),
                dim3(64 * kDkWaves), s, a.lds_bytes, a);
     else
-        launch(t, "tiny_decode", tiny_decode_wide_kernel<BITS, SBITS>, dim3((unsigned)(a.n_gk + n_dk)),
+        launch(t, "tiny_decode", tiny_decode_wide_kernel<CF, SBITS>, dim3((unsigned)(a.n_gk + n_dk)),
                dim3(64 * kDkWaves), s, a.lds_bytes, a);
     return hipGetLastError();
 }
@@ -986,7 +1012,7 @@ hipError_t launch_tiny_t(const TinyArgs& a, hipStream_t s, StageTimer* t) {
 namespace {
 // Workgroups of the single-launch kernel that the current device holds at once (CUs times
 // the occupancy at the largest dynamic LDS the path allows), cached per device.
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 int tiny_capacity_t() {
     static int cache[64];   // 0: not yet known, -1: query failed
     int dev = 0;
@@ -995,37 +1021,51 @@ int tiny_capacity_t() {
         int cus = 0, nb = 0;
         hipError_t st = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (st == hipSuccess) {
-            if constexpr (BITS == 4 && SBITS != 8)
+            if constexpr (tiny_narrow<CF, SBITS>())
                 st = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &nb, reinterpret_cast<const void*>(tiny_decode_kernel<BITS, SBITS>), 64 * kDkWaves, kTinyMaxLds);
+                    &nb, reinterpret_cast<const void*>(tiny_decode_kernel<CF, SBITS>), 64 * kDkWaves, kTinyMaxLds);
             else
                 st = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &nb, reinterpret_cast<const void*>(tiny_decode_wide_kernel<BITS, SBITS>), 64 * kDkWaves,
+                    &nb, reinterpret_cast<const void*>(tiny_decode_wide_kernel<CF, SBITS>), 64 * kDkWaves,
                     kTinyMaxLds);
         }
         cache[dev] = (st == hipSuccess && cus > 0 && nb > 0) ? cus * nb : -1;
     }
     return cache[dev] > 0 ? cache[dev] : 0;
 }
+
+template <int CF>
+int tiny_capacity_cf(int sbits) {
+    return sbits == 0 ? tiny_capacity_t<CF, 0>() : sbits == 4 ? tiny_capacity_t<CF, 4>() : tiny_capacity_t<CF, 8>();
+}
+
+template <int CF>
+hipError_t launch_tiny_cf(const TinyArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (sb == 0) return launch_tiny_t<CF, 0>(a, s, t);
+    if (sb == 4) return launch_tiny_t<CF, 4>(a, s, t);
+    return launch_tiny_t<CF, 8>(a, s, t);
+}
 }  // namespace
 
-int tiny_max_down_workgroups(int bits, int sbits) {
+int tiny_max_down_workgroups(int fmt, int bits, int sbits) {
     int cap;
-    if (bits == 4) cap = sbits == 0 ? tiny_capacity_t<4, 0>() : sbits == 4 ? tiny_capacity_t<4, 4>() : tiny_capacity_t<4, 8>();
-    else cap = sbits == 0 ? tiny_capacity_t<8, 0>() : sbits == 4 ? tiny_capacity_t<8, 4>() : tiny_capacity_t<8, 8>();
+    switch (cf_of(fmt, bits)) {
+        case 4: cap = tiny_capacity_cf<4>(sbits); break;
+        case 8: cap = tiny_capacity_cf<8>(sbits); break;
+        case kCfFp8: cap = tiny_capacity_cf<kCfFp8>(sbits); break;
+        default: cap = tiny_capacity_cf<kCfMx4>(sbits); break;
+    }
     return cap / 2;
 }
 
 hipError_t launch_tiny(const TinyArgs& a, hipStream_t s, StageTimer* t) {
-    const int sb = a.shared.bits;
-    if (a.routed.bits == 4) {
-        if (sb == 0) return launch_tiny_t<4, 0>(a, s, t);
-        if (sb == 4) return launch_tiny_t<4, 4>(a, s, t);
-        return launch_tiny_t<4, 8>(a, s, t);
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_tiny_cf<4>(a, s, t);
+        case 8: return launch_tiny_cf<8>(a, s, t);
+        case kCfFp8: return launch_tiny_cf<kCfFp8>(a, s, t);
+        default: return launch_tiny_cf<kCfMx4>(a, s, t);
     }
-    if (sb == 0) return launch_tiny_t<8, 0>(a, s, t);
-    if (sb == 4) return launch_tiny_t<8, 4>(a, s, t);
-    return launch_tiny_t<8, 8>(a, s, t);
 }
 
 hipError_t launch_head_init(uint32_t* head, hipStream_t s) {
