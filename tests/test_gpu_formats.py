@@ -278,3 +278,37 @@ def test_single_launch_formats(fmt, T, shared_bits):
         ref.prefetch(np.unique(ids))
         y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), BITS[fmt], weight_format=fmt, shared=sh_ref)
         check_ffn(y, y_ref, f"{fmt} single launch T={T} shared={shared_bits} call {it}")
+
+
+@pytest.fixture(scope="module", params=["fp8", "mxfp4"])
+def stream_fmt_layer(request):
+    fmt = request.param
+    return fmt, fmt_layer(fmt, 83, 0, 64, 2048, 256), FmtExperts(fmt, 83, 0, 2048, 256)
+
+
+@pytest.mark.parametrize("T,shared_bits", [(3, 8), (4, 0), (8, 0), (16, 4), (24, 4), (40, 8), (64, 0), (64, 8)])
+def test_stream_formats(stream_fmt_layer, T, shared_bits):
+    """Small batches of the float formats on the streaming kernels: pair mode (3, 4 tokens of
+    64 experts), routing fused into the gate/up kernel (8..24) and routing in its own launch
+    (40, 64), with or without an INT shared expert; two calls on one workspace."""
+    from gpu_util import OracleExperts
+    fmt, layer, ref = stream_fmt_layer
+    E, H, I, k = 64, 2048, 256, 8
+    kw, sh_ref, sI = {}, None, 0
+    if shared_bits:
+        sI = 512
+        kw = dict(shared=gpu_layer(83, 0, 1, H, sI, shared_bits, shared=True))
+        sh_ref = OracleExperts(83, 0, H, sI, shared_bits, shared=True).shared_dict()
+    say(f"{fmt} stream T={T} shared={shared_bits}")
+    ws = w4.new_workspace(w4.moe_w4a16_workspace_size(T, H, I, E, k, shared_bits, sI), DEV)
+    for it in range(2):
+        x = synth.activations_bf16(800 + 10 * T + it, T, H)
+        logits = synth.router_logits(800 + 10 * T + it, T, E)
+        y, tk = w4.moe_w4a16_forward_timed(bf16_to_dev(x), *layer, top_k=k, bits=BITS[fmt], weight_format=fmt,
+                                           router_logits=f32_to_dev(logits), workspace=ws, **kw)
+        names = [nm for nm, _ in tk]
+        assert ("gk_stream" in names or "gk_pair_stream" in names) and "dk_stream" in names, names
+        ids, wts, *_ = oracle.route(logits, k)
+        ref.prefetch(np.unique(ids))
+        y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), BITS[fmt], weight_format=fmt, shared=sh_ref)
+        check_ffn(y, y_ref, f"{fmt} stream T={T} shared={shared_bits} call {it}")

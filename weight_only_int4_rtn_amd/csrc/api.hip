@@ -192,7 +192,6 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
 
     ExpertSet routed{a->w13, a->s13, a->w2, a->s2, a->I, a->bits, a->weight_format};
     ExpertSet shared{a->shared_w13, a->shared_s13, a->shared_w2, a->shared_s2, a->shared_I, a->shared_bits, 0};
-    const bool int_codes = a->weight_format == W4A16_FORMAT_INT;   // the single-launch and streaming kernels
     uint16_t* abuf = static_cast<uint16_t*>(at(L.abuf));
 
     // single launch for tiny batches when the tagged a words fit the workspace head, the
@@ -262,7 +261,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
             d.a_by_pair = 1;
             d.gk_stream = 1;
             d.route.pair_rows = 1;
-        } else if (logits_in && int_codes && a->T > kSplitRouteT) {
+        } else if (logits_in && a->T > kSplitRouteT) {
             // routing spread over waves (one token each) in its own launch; the streaming
             // gate/up kernel, if it takes the shapes, then reads the tile records
             r.sync = static_cast<uint32_t*>(at(L.sync));

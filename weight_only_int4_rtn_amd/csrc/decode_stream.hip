@@ -20,9 +20,11 @@
 // item computes; larger tiles (rare at decode) load their rows straight into registers.
 //
 // Within an item, wave w computes K group 8 * kh + w of the item's rows with 16x16x32 bf16
-// MFMAs (codes as exact bf16 integers, offset removed by the seed, see dq4 / dq8 in
-// common.h); the fp32 partial sums of the 8 waves meet in LDS after the row block's last
-// K chunk, and the epilogue stores a = SiLU(g) * u as bf16 in MFMA operand order.
+// MFMAs (INT codes as exact bf16 integers, offset removed by the seed, see dq4 / dq8 in
+// common.h; FP8 and MXFP4 codes as their exact bf16 values, see dq_fp8 / dq_mx4); the
+// fp32 partial sums of the 8 waves meet in LDS after the row block's last K chunk, and
+// the epilogue stores a = SiLU(g) * u as bf16 in MFMA operand order.  The code bytes of
+// an item are laid out alike for every format of one width; only the scale copies differ.
 #include "common.h"
 #include "decode_dev.h"
 #include "dma.h"
@@ -155,6 +157,7 @@ __device__ __forceinline__ bool s_advance(SCursor& c, const SLayout& L, const in
 struct SIssueTile {
     i32x4_t wr, sr;        // codes and scales of the tile's expert
     int64_t I_e, row_bytes;
+    int fmt;               // the expert's code format (0 INT, 1 FP8, 2 MXFP4): its scale layout
     uint32_t v_code;       // lane part of a code copy offset
     uint32_t v_scale;      // lane part of the scale copy offset (kOob: idle lane)
 };
@@ -168,10 +171,21 @@ __device__ __forceinline__ void s_issue_tile(const DecodeArgs& a, const SLayout&
     const int64_t e = c.tl.e;
     st.wr = uniform_rsrc(dma_rsrc(reinterpret_cast<const uint8_t*>(es.w13) + e * 2 * st.I_e * st.row_bytes,
                                   (uint32_t)(2 * st.I_e * st.row_bytes)));
-    st.sr = uniform_rsrc(dma_rsrc(es.s13 + e * 2 * st.I_e * L.G, (uint32_t)(2 * st.I_e * L.G * 2)));
+    st.fmt = es.fmt;
+    // scale bytes of one gate/up row: INT bf16 per group, FP8 one fp32, MXFP4 one E8M0 byte
+    // per 32 columns
+    const int64_t srow = es.fmt == 1 ? 4 : es.fmt == 2 ? 4 * L.G : 2 * L.G;
+    st.sr = uniform_rsrc(dma_rsrc(reinterpret_cast<const uint8_t*>(es.s13) + e * 2 * st.I_e * srow,
+                                  (uint32_t)(2 * st.I_e * srow)));
     st.v_code = (uint32_t)(ml * st.row_bytes + q * (c.bits == 4 ? 16 : 32));
-    if (c.bits == 4) st.v_scale = lane < 32 ? (uint32_t)((((lane >> 4) * st.I_e + ml) * L.G) * 2) : kOob;
-    else st.v_scale = lane < 16 ? (uint32_t)(lane * L.G * 2) : kOob;
+    if (es.fmt == 1)        // the 16 rows' fp32 scales: 64 contiguous bytes
+        st.v_scale = lane < 4 ? (uint32_t)(lane * 16) : kOob;
+    else if (es.fmt == 2)   // 32 bytes (8 groups x 4 blocks) of each of the 32 gate and up rows
+        st.v_scale = (uint32_t)((((lane >> 5) * st.I_e + ((lane >> 1) & 15)) * L.G) * 4 + (lane & 1) * 16);
+    else if (c.bits == 4)   // 16 bytes (8 groups) of each of the 32 gate and up rows
+        st.v_scale = lane < 32 ? (uint32_t)((((lane >> 4) * st.I_e + ml) * L.G) * 2) : kOob;
+    else
+        st.v_scale = lane < 16 ? (uint32_t)(lane * L.G * 2) : kOob;
 }
 
 // Issues producer wave w's copies of the cursor's item into `stage`: code blocks
@@ -201,8 +215,11 @@ __device__ __forceinline__ int s_issue(const DecodeArgs& a, const SLayout& L, co
         for (int i = 0; i < 8; ++i, m0 += 1024) dma16(wr, m0, st.v_code, soff + (i >> 1) * 128 + (i & 1) * 16);
     }
     int n = 8;
-    if (wave == 0) {   // scales: 8 groups (16 B) of each row this item needs
-        const int soff = c.bits == 4 ? (n0 * L.G + 8 * kh) * 2 : (int)(((half * st.I_e + n0) * L.G + 8 * kh) * 2);
+    if (wave == 0) {   // scales of the item's rows and groups
+        const int soff = st.fmt == 1   ? (int)((half * st.I_e + n0) * 4)
+                         : st.fmt == 2 ? (n0 * L.G + 8 * kh) * 4
+                         : c.bits == 4 ? (n0 * L.G + 8 * kh) * 2
+                                       : (int)(((half * st.I_e + n0) * L.G + 8 * kh) * 2);
         dma16(uniform_rsrc(st.sr), __builtin_amdgcn_readfirstlane(stage + kSCodeBytes), st.v_scale,
               __builtin_amdgcn_readfirstlane(soff));
         ++n;
@@ -227,7 +244,7 @@ __device__ __forceinline__ int s_issue(const DecodeArgs& a, const SLayout& L, co
 // (padding rows zero), and their MFMA offset seeds.  Each branch computes the seeds
 // itself: the register path's loads are then complete before the branches join, so the
 // compiler puts no wait for them (a wait for every copy in flight) on the LDS path.
-template <int BITS>
+template <int CF>
 __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, const STile& tl, const uint8_t* smem,
                                          const uint8_t* abuf, u32x4_t (&A)[kSKH][4], f32x4_t (&seed)[kSKH]) {
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
@@ -246,45 +263,60 @@ __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, 
             }
         }
 #pragma unroll
-        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<BITS>(A[kh]);
+        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<CF>(A[kh]);
     } else {   // more rows than an A buffer holds: straight from memory into registers
         const uint16_t* xr = a.x + (int64_t)stile_token(tl, real ? ml : 0) * a.H + 32 * q;
 #pragma unroll
         for (int kh = 0; kh < kSKH; ++kh) {
             const int g = min(8 * kh + wave, L.G - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) A[kh][i] = load_act<BITS>(xr, real && 8 * kh + wave < L.G, g * kGroup + 8 * i);
+            for (int i = 0; i < 4; ++i) A[kh][i] = load_act<CF>(xr, real && 8 * kh + wave < L.G, g * kGroup + 8 * i);
         }
 #pragma unroll
-        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<BITS>(A[kh]);
+        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<CF>(A[kh]);
     }
 }
 
-// One item's MFMAs for this wave: K group 8 * kh + wave of the item's rows.
-template <int BITS>
+// One item's MFMAs for this wave: K group 8 * kh + wave of the item's rows.  Scales in the
+// stage: INT 8 bf16 per row (gate rows, then up rows); FP8 the 16 rows' fp32; MXFP4 32
+// E8M0 bytes per row (group j's four blocks at 4 j), applied inside the conversion.
+template <int CF>
 __device__ __forceinline__ void s_compute(const SLayout& L, int kh, int half, const uint8_t* stage,
                                           const u32x4_t (&A)[4], f32x4_t seed, f32x4_t& accg, f32x4_t& accu) {
-    const int lane = threadIdx.x & 63, ml = lane & 15;
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (8 * kh + wave >= L.G) return;
-    const uint16_t* sc = reinterpret_cast<const uint16_t*>(stage + kSCodeBytes);
-    if constexpr (BITS == 4) {
+    const uint8_t* sb = stage + kSCodeBytes;
+    if constexpr (cf_bits(CF) == 4) {
         const u32x4_t bg[1] = {*reinterpret_cast<const u32x4_t*>(stage + wave * 1024 + lane * 16)};
         const u32x4_t bu[1] = {*reinterpret_cast<const u32x4_t*>(stage + (8 + wave) * 1024 + lane * 16)};
-        const float sg = bf16_to_f32(sc[ml * 8 + wave]), su = bf16_to_f32(sc[(16 + ml) * 8 + wave]);
-        const f32x4_t tg = group_dot<4>(A, bg, seed);
-        const f32x4_t tu = group_dot<4>(A, bu, seed);
+        if constexpr (CF == kCfMx4) {
+            const float xg = e8m0_scale(sb[ml * 32 + 4 * wave + q]), xu = e8m0_scale(sb[(16 + ml) * 32 + 4 * wave + q]);
+            const f32x4_t tg = group_dot<CF>(A, bg, seed, xg);
+            const f32x4_t tu = group_dot<CF>(A, bu, seed, xu);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            accg[r] += sg * tg[r];
-            accu[r] += su * tu[r];
+            for (int r = 0; r < 4; ++r) {
+                accg[r] += tg[r];
+                accu[r] += tu[r];
+            }
+        } else {
+            const uint16_t* sc = reinterpret_cast<const uint16_t*>(sb);
+            const float sg = bf16_to_f32(sc[ml * 8 + wave]), su = bf16_to_f32(sc[(16 + ml) * 8 + wave]);
+            const f32x4_t tg = group_dot<CF>(A, bg, seed);
+            const f32x4_t tu = group_dot<CF>(A, bu, seed);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                accg[r] += sg * tg[r];
+                accu[r] += su * tu[r];
+            }
         }
     } else {
         const u32x4_t bw[2] = {*reinterpret_cast<const u32x4_t*>(stage + (2 * wave) * 1024 + lane * 16),
                                *reinterpret_cast<const u32x4_t*>(stage + (2 * wave + 1) * 1024 + lane * 16)};
-        const float s = bf16_to_f32(sc[ml * 8 + wave]);
+        const float s = CF == kCfFp8 ? reinterpret_cast<const float*>(sb)[ml]
+                                     : bf16_to_f32(reinterpret_cast<const uint16_t*>(sb)[ml * 8 + wave]);
         const float sg = half == 0 ? s : 0.f, su = half == 0 ? 0.f : s;   // selects, no branch
-        const f32x4_t t = group_dot<8>(A, bw, seed);
+        const f32x4_t t = group_dot<CF>(A, bw, seed);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             accg[r] += sg * t[r];
@@ -301,10 +333,14 @@ __device__ __forceinline__ int s_unit_at(int N_items, int b, int n, int U_r, int
     return min(U, U_r + (i - U_r * sub_r + sub_s - 1) / sub_s);
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 // One workgroup of ten waves per CU (its LDS ring takes the CU): three waves share a SIMD at most.
 __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) void gk_stream_kernel(
     DecodeArgs a) {
+    constexpr int BITS = cf_bits(CF);
+    // an INT shared expert beside routed experts of another code format takes its own code
+    // path, chosen by the tile; else by the code width
+    constexpr bool kSep = SBITS != 0 && SBITS != CF;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, ml = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -459,17 +495,18 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
             epilogue();
             ep_pending = 0;
         }
+        const bool sep = kSep && cc.tl.shared;
         if (c_start) {
             const uint8_t* abuf = smem + kSOffA + ((cc.tile - first_tile) & 1) * kSABytes;
-            if (cc.bits == BITS) s_load_a<BITS>(a, L, cc.tl, smem, abuf, A, seed);
-            else if constexpr (SBITS != 0 && SBITS != BITS) s_load_a<SBITS>(a, L, cc.tl, smem, abuf, A, seed);
+            if (!sep) s_load_a<CF>(a, L, cc.tl, smem, abuf, A, seed);
+            else if constexpr (kSep) s_load_a<SBITS>(a, L, cc.tl, smem, abuf, A, seed);
         }
         const uint8_t* stage = smem + c_stage * kSStageBytes;
         const int kh = cc.bits == 4 ? cc.sub : cc.sub >> 1, half = cc.bits == 4 ? 0 : cc.sub & 1;
-        if (cc.bits == BITS) {
-            if (kh == 0) s_compute<BITS>(L, kh, half, stage, A[0], seed[0], accg, accu);
-            else s_compute<BITS>(L, kh, half, stage, A[1], seed[1], accg, accu);
-        } else if constexpr (SBITS != 0 && SBITS != BITS) {
+        if (!sep) {
+            if (kh == 0) s_compute<CF>(L, kh, half, stage, A[0], seed[0], accg, accu);
+            else s_compute<CF>(L, kh, half, stage, A[1], seed[1], accg, accu);
+        } else if constexpr (kSep) {
             if (kh == 0) s_compute<SBITS>(L, kh, half, stage, A[0], seed[0], accg, accu);
             else s_compute<SBITS>(L, kh, half, stage, A[1], seed[1], accg, accu);
         }
@@ -516,7 +553,7 @@ constexpr uint32_t kDSkip = 0x40000000u;           // scalar offset that puts a 
 
 struct DCursor {
     int tile, hb, kh;
-    int n_kh, bits, G2;
+    int n_kh, bits, fmt, G2;   // fmt: the tile's code format (0 INT, 1 FP8, 2 MXFP4)
     STile tl;
 };
 
@@ -526,6 +563,7 @@ __device__ __forceinline__ void d_uniform(DCursor& c) {
     c.kh = __builtin_amdgcn_readfirstlane(c.kh);
     c.n_kh = __builtin_amdgcn_readfirstlane(c.n_kh);
     c.bits = __builtin_amdgcn_readfirstlane(c.bits);
+    c.fmt = __builtin_amdgcn_readfirstlane(c.fmt);
     c.G2 = __builtin_amdgcn_readfirstlane(c.G2);
     c.tl.e = __builtin_amdgcn_readfirstlane(c.tl.e);
     c.tl.row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
@@ -538,6 +576,7 @@ __device__ __forceinline__ void d_set_tile(const DecodeArgs& a, DCursor& c, int 
     const bool shared = c.tile >= n_tiles_r;
     const ExpertSet& es = shared ? a.shared : a.routed;
     c.bits = shared ? SBITS : BITS;
+    c.fmt = es.fmt;
     c.G2 = (int)(es.I / kGroup);
     c.n_kh = c.bits == 4 ? 1 : (c.G2 + 1) / 2;
     if (!shared) {
@@ -570,7 +609,11 @@ __device__ __forceinline__ void d_issue(const DecodeArgs& a, const DCursor& c, u
     const int64_t e = c.tl.e;
     const i32x4_t wr = uniform_rsrc(dma_rsrc(reinterpret_cast<const uint8_t*>(es.w2) + e * a.H * row_bytes,
                                              (uint32_t)(a.H * row_bytes)));
-    const i32x4_t sr = uniform_rsrc(dma_rsrc(es.s2 + e * a.H * c.G2, (uint32_t)(a.H * c.G2 * 2)));
+    // scale bytes of one down row: INT bf16 per group, FP8 one fp32, MXFP4 one E8M0 byte per
+    // 32 columns; the 16 rows' scales are contiguous (at most 256 bytes, 4 per lane)
+    const int srow = c.fmt == 1 ? 4 : c.fmt == 2 ? 4 * c.G2 : 2 * c.G2;
+    const i32x4_t sr = uniform_rsrc(dma_rsrc(reinterpret_cast<const uint8_t*>(es.s2) + e * a.H * srow,
+                                             (uint32_t)(a.H * srow)));
     const int h0 = c.hb * 16;
     const uint32_t v = (uint32_t)(ml * row_bytes + q * (c.bits == 4 ? 16 : 32));
     const int base = __builtin_amdgcn_readfirstlane((int)(h0 * row_bytes));
@@ -580,9 +623,8 @@ __device__ __forceinline__ void d_issue(const DecodeArgs& a, const DCursor& c, u
         const int off = c.bits == 4 ? g * 64 : g * 128 + (b & 1) * 16;
         dma16(wr, stage + b * 1024, v, g < c.G2 ? base + off : (int)kDSkip);
     }
-    // the 16 rows' scales are contiguous: 16 * G2 bf16 = 32 * G2 bytes, 4 per lane
-    dma4(sr, stage + kDCodeBytes, lane < 8 * c.G2 ? (uint32_t)(lane * 4) : kOob,
-         __builtin_amdgcn_readfirstlane(h0 * c.G2 * 2));
+    dma4(sr, stage + kDCodeBytes, lane < 4 * srow ? (uint32_t)(lane * 4) : kOob,
+         __builtin_amdgcn_readfirstlane(h0 * srow));
 }
 
 // The tile's a rows as MFMA A fragments (groups 0..3, padding rows zero); d_seed gives
@@ -601,27 +643,35 @@ __device__ __forceinline__ void d_load_a(const DecodeArgs& a, const DCursor& c, 
             A[g][i] = load16_or_zero(row + gg * kGroup + 8 * i, real && g < c.G2, row);
         }
 }
-template <int BITS>
+template <int CF>
 __device__ __forceinline__ void d_seed(const u32x4_t (&A)[4][4], f32x4_t (&seed)[4]) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) seed[g] = offset_seed<BITS>(A[g]);
+    for (int g = 0; g < 4; ++g) seed[g] = offset_seed<CF>(A[g]);
 }
 
 // One item's MFMAs: groups of this K part, partial sums (rows 4q + r, column ml) into acc.
-template <int BITS>
+// Row ml's scales in the stage: INT G2 bf16; FP8 one fp32; MXFP4 4 G2 E8M0 bytes (group
+// g's four blocks at 4 g), applied inside the conversion.
+template <int CF>
 __device__ __forceinline__ void d_compute(const DCursor& c, const uint8_t* stage, const u32x4_t (&A)[4][4],
                                           const f32x4_t (&seed)[4], f32x4_t& acc) {
-    const int lane = threadIdx.x & 63, ml = lane & 15;
-    const uint16_t* sc = reinterpret_cast<const uint16_t*>(stage + kDCodeBytes) + ml * c.G2;
-    if constexpr (BITS == 4) {
+    const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
+    const uint8_t* sb = stage + kDCodeBytes;
+    if constexpr (cf_bits(CF) == 4) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             if (g < c.G2) {
                 const u32x4_t bw[1] = {*reinterpret_cast<const u32x4_t*>(stage + g * 1024 + lane * 16)};
-                const float s = bf16_to_f32(sc[g]);
-                const f32x4_t t = group_dot<4>(A[g], bw, seed[g]);
+                if constexpr (CF == kCfMx4) {
+                    const f32x4_t t = group_dot<CF>(A[g], bw, seed[g], e8m0_scale(sb[ml * 4 * c.G2 + 4 * g + q]));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += s * t[r];
+                    for (int r = 0; r < 4; ++r) acc[r] += t[r];
+                } else {
+                    const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(sb)[ml * c.G2 + g]);
+                    const f32x4_t t = group_dot<CF>(A[g], bw, seed[g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] += s * t[r];
+                }
             }
         }
     } else {
@@ -631,8 +681,9 @@ __device__ __forceinline__ void d_compute(const DCursor& c, const uint8_t* stage
             if (g < c.G2) {
                 const u32x4_t bw[2] = {*reinterpret_cast<const u32x4_t*>(stage + (2 * j) * 1024 + lane * 16),
                                        *reinterpret_cast<const u32x4_t*>(stage + (2 * j + 1) * 1024 + lane * 16)};
-                const float s = bf16_to_f32(sc[g]);
-                const f32x4_t t = c.kh == 0 ? group_dot<8>(A[j], bw, seed[j]) : group_dot<8>(A[2 + j], bw, seed[2 + j]);
+                const float s = CF == kCfFp8 ? reinterpret_cast<const float*>(sb)[ml]
+                                             : bf16_to_f32(reinterpret_cast<const uint16_t*>(sb)[ml * c.G2 + g]);
+                const f32x4_t t = c.kh == 0 ? group_dot<CF>(A[j], bw, seed[j]) : group_dot<CF>(A[2 + j], bw, seed[2 + j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] += s * t[r];
             }
@@ -640,8 +691,10 @@ __device__ __forceinline__ void d_compute(const DCursor& c, const uint8_t* stage
     }
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 __global__ __launch_bounds__(64 * kDWaves) void dk_stream_kernel(DecodeArgs a) {
+    constexpr int BITS = cf_bits(CF);
+    constexpr bool kSep = SBITS != 0 && SBITS != CF;   // as in gk_stream_kernel
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, q = lane >> 4, ml = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -708,14 +761,15 @@ __global__ __launch_bounds__(64 * kDWaves) void dk_stream_kernel(DecodeArgs a) {
             d_issue(a, ic, ring + ((rel + kDStages - 1) % kDStages) * kDStageBytes);
             advance(ic);
         }
+        const bool sep = kSep && cc.tl.shared;
         if (c_start) {
             if (rel > 0) d_load_a(a, cc, A);
-            if (cc.bits == BITS) d_seed<BITS>(A, seed);
-            else if constexpr (SBITS != 0 && SBITS != BITS) d_seed<SBITS>(A, seed);
+            if (!sep) d_seed<CF>(A, seed);
+            else if constexpr (kSep) d_seed<SBITS>(A, seed);
         }
         const uint8_t* stage = ring_p + (rel % kDStages) * kDStageBytes;
-        if (cc.bits == BITS) d_compute<BITS>(cc, stage, A, seed, acc);
-        else if constexpr (SBITS != 0 && SBITS != BITS) d_compute<SBITS>(cc, stage, A, seed, acc);
+        if (!sep) d_compute<CF>(cc, stage, A, seed, acc);
+        else if constexpr (kSep) d_compute<SBITS>(cc, stage, A, seed, acc);
         int nst = 0;
         if (cc.kh == cc.n_kh - 1) {   // the row block is complete: rows 4q + r, column ml
             const int h = cc.hb * 16 + ml;
@@ -789,16 +843,16 @@ __global__ __launch_bounds__(256) void dk_finalize_kernel(DecodeArgs a) {
     *reinterpret_cast<uint32_t*>(a.y + o) = cvt_bf16x2(s0, s1);
 }
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 hipError_t launch_dk_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(dk_stream_kernel<BITS, SBITS>),
+        const hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(dk_stream_kernel<CF, SBITS>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, kDLdsBytes);
         if (st != hipSuccess) return st;
         attr_set = true;
     }
-    launch(t, "dk_stream", dk_stream_kernel<BITS, SBITS>, dim3((unsigned)stream_workgroups()),
+    launch(t, "dk_stream", dk_stream_kernel<CF, SBITS>, dim3((unsigned)stream_workgroups()),
            dim3(64 * kDWaves), s, (uint32_t)kDLdsBytes, a);
     const int64_t nb = (int64_t)a.T * ((a.H + kFinCols - 1) / kFinCols);
     if (a.k == 8) launch(t, "dk_finalize", dk_finalize_kernel<8>, dim3((unsigned)nb), dim3(256), s, 0u, a);
@@ -808,16 +862,16 @@ hipError_t launch_dk_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t)
 
 int g_stream_wgs[64];   // per device: CUs (0: not yet known, -1: query failed)
 
-template <int BITS, int SBITS>
+template <int CF, int SBITS>
 hipError_t launch_stream_t(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(gk_stream_kernel<BITS, SBITS>),
+        const hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(gk_stream_kernel<CF, SBITS>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, kSLdsBytes);
         if (st != hipSuccess) return st;
         attr_set = true;
     }
-    launch(t, a.a_by_pair ? "gk_pair_stream" : "gk_stream", gk_stream_kernel<BITS, SBITS>,
+    launch(t, a.a_by_pair ? "gk_pair_stream" : "gk_stream", gk_stream_kernel<CF, SBITS>,
            dim3((unsigned)stream_workgroups()), dim3(kSThreads), s, (uint32_t)kSLdsBytes, a);
     return hipGetLastError();
 }
@@ -839,12 +893,12 @@ int stream_workgroups() {
 
 bool stream_fits(const DecodeArgs& a, int max_tiles) {
     const int nwg = stream_workgroups() - (a.a_by_pair ? 1 : 0);   // pair mode: workgroup 0 only routes
-    if (a.routed.fmt != 0) return false;                           // INT codes only
     if (nwg <= 0 || a.H > kSMaxH || a.T > kSmallT) return false;
     const int64_t G = a.H / kGroup, KH = (G + 7) / 8;
-    // the scale copies read 16 bytes from each row's first group of a K chunk: with an
-    // even group count every such address is 4-byte aligned
-    if (G % 2 != 0) return false;
+    // the INT scale copies read 16 bytes from each row's first bf16 group of a K chunk:
+    // with an even group count every such address is 4-byte aligned (FP8 and MXFP4 scale
+    // addresses are multiples of 4 at any group count)
+    if (G % 2 != 0 && (a.routed.fmt == 0 || a.shared.bits)) return false;
     // a 4-bit row block must span two K chunks: its partial sums are read back one item
     // after they are written and rewritten no sooner than two items later
     if (KH < 2 && (a.routed.bits == 4 || a.shared.bits == 4)) return false;
@@ -860,16 +914,30 @@ bool stream_fits(const DecodeArgs& a, int max_tiles) {
     return (cap_r + n_rb_r - 1) / n_rb_r + 1 <= kSMaxTiles;
 }
 
-hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+namespace {
+template <int CF>
+hipError_t launch_gk_stream_cf(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
     const int sb = a.shared.bits;
-    if (a.routed.bits == 4) {
-        if (sb == 0) return launch_stream_t<4, 0>(a, s, t);
-        if (sb == 4) return launch_stream_t<4, 4>(a, s, t);
-        return launch_stream_t<4, 8>(a, s, t);
+    if (sb == 0) return launch_stream_t<CF, 0>(a, s, t);
+    if (sb == 4) return launch_stream_t<CF, 4>(a, s, t);
+    return launch_stream_t<CF, 8>(a, s, t);
+}
+template <int CF>
+hipError_t launch_dk_stream_cf(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    const int sb = a.shared.bits;
+    if (sb == 0) return launch_dk_stream_t<CF, 0>(a, s, t);
+    if (sb == 4) return launch_dk_stream_t<CF, 4>(a, s, t);
+    return launch_dk_stream_t<CF, 8>(a, s, t);
+}
+}  // namespace
+
+hipError_t launch_gk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_gk_stream_cf<4>(a, s, t);
+        case 8: return launch_gk_stream_cf<8>(a, s, t);
+        case kCfFp8: return launch_gk_stream_cf<kCfFp8>(a, s, t);
+        default: return launch_gk_stream_cf<kCfMx4>(a, s, t);
     }
-    if (sb == 0) return launch_stream_t<8, 0>(a, s, t);
-    if (sb == 4) return launch_stream_t<8, 4>(a, s, t);
-    return launch_stream_t<8, 8>(a, s, t);
 }
 
 bool pair_fits(const DecodeArgs& a) {
@@ -882,21 +950,18 @@ bool pair_fits(const DecodeArgs& a) {
 }
 
 bool dk_stream_fits(const DecodeArgs& a) {
-    if (stream_workgroups() <= 0 || a.routed.fmt != 0) return false;   // INT codes only
+    if (stream_workgroups() <= 0) return false;
     if (a.routed.I > kDMaxI || (a.shared.bits && a.shared.I > kDMaxI)) return false;
     return a.H % 32 == 0 && a.rows_a * a.H * 4 < (int64_t)kDSkip;
 }
 
 hipError_t launch_dk_stream(const DecodeArgs& a, hipStream_t s, StageTimer* t) {
-    const int sb = a.shared.bits;
-    if (a.routed.bits == 4) {
-        if (sb == 0) return launch_dk_stream_t<4, 0>(a, s, t);
-        if (sb == 4) return launch_dk_stream_t<4, 4>(a, s, t);
-        return launch_dk_stream_t<4, 8>(a, s, t);
+    switch (cf_of(a.routed.fmt, a.routed.bits)) {
+        case 4: return launch_dk_stream_cf<4>(a, s, t);
+        case 8: return launch_dk_stream_cf<8>(a, s, t);
+        case kCfFp8: return launch_dk_stream_cf<kCfFp8>(a, s, t);
+        default: return launch_dk_stream_cf<kCfMx4>(a, s, t);
     }
-    if (sb == 0) return launch_dk_stream_t<8, 0>(a, s, t);
-    if (sb == 4) return launch_dk_stream_t<8, 4>(a, s, t);
-    return launch_dk_stream_t<8, 8>(a, s, t);
 }
 
 }  // namespace w4a16
