@@ -134,17 +134,19 @@ __device__ __forceinline__ u32x4_t dq_fp8(uint32_t w0, uint32_t w1) {
 }
 
 // MXFP4 word w = k0..k7 (one E2M1 nibble each, k0 lowest) -> bf16 pairs (k0,k4) (k1,k5)
-// (k2,k6) (k3,k7), each value times `scale` (a power of two: exact).
+// (k2,k6) (k3,k7), each value times `scale` (a power of two: exact).  Byte j of w holds
+// k_2j (low nibble) and k_2j+1, which one conversion turns into the bf16 pair
+// (k_2j, k_2j+1); byte permutes then regroup the halves.
 __device__ __forceinline__ u32x4_t dq_mx4(uint32_t w, float scale) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;   // k0 k2 k4 k6 / k1 k3 k5 k7
-    const uint32_t x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);      // k0 k1 k2 k3
-    const uint32_t y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);      // k4 k5 k6 k7
-    const uint32_t b = x | (y << 4);                                    // bytes k_j | k_{j+4} << 4
+    const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    const uint32_t p45 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    const uint32_t p67 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
     u32x4_t r;
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 0));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 1));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 2));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, scale, 3));
+    r[0] = __builtin_amdgcn_perm(p45, p01, 0x05040100u);   // k0 k4: low halves
+    r[1] = __builtin_amdgcn_perm(p45, p01, 0x07060302u);   // k1 k5: high halves
+    r[2] = __builtin_amdgcn_perm(p67, p23, 0x05040100u);   // k2 k6
+    r[3] = __builtin_amdgcn_perm(p67, p23, 0x07060302u);   // k3 k7
     return r;
 }
 
