@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 6
+#define W4A16_ABI_VERSION 7
 
 typedef enum w4a16_status {
     W4A16_OK = 0,
@@ -102,6 +102,16 @@ typedef enum w4a16_format {
     W4A16_FORMAT_FP8_E4M3 = 1,  /* fp8_quantize_pack codes: E4M3 bytes, one fp32 scale per row (bits 8) */
     W4A16_FORMAT_MXFP4 = 2      /* mxfp4_quantize_pack codes: E2M1 nibbles, E8M0 per 32 columns (bits 4) */
 } w4a16_format;
+
+/* Launch flags (moe_w4a16_args.flags). */
+typedef enum w4a16_flags {
+    /* Run no kernel whose workgroups wait for each other.  The single-launch path of tiny
+     * batches (T * top_k <= 16) needs its gate/up and down workgroups resident on the device
+     * together, that is, no other work on the GPU while it runs (see
+     * moe_w4a16_workspace_check for what a failed wait does).  With this flag those batches
+     * take the multi-launch streaming path, whose result agrees to rounding. */
+    W4A16_FLAG_NO_COOPERATIVE = 1
+} w4a16_flags;
 
 /* Scale choice of mxfp4_quantize_pack. */
 typedef enum w4a16_mxfp4_method {
@@ -225,6 +235,7 @@ typedef struct moe_w4a16_args {
      * mxfp4_quantize_pack writes them and s13/s2 point to E8M0 bytes [E, 2I, H/32] /
      * [E, H, I/32] (MXFP4-MxWave page, Model summary).  The shared expert stays INT. */
     int32_t weight_format;
+    int32_t flags;                 /* w4a16_flags, or 0                                      */
 } moe_w4a16_args;
 
 /* Device workspace bytes moe_w4a16_forward needs for T tokens, hidden H, intermediate I,

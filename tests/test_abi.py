@@ -47,7 +47,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 6
+    assert L.w4a16_abi_version() == _lib.ABI_VERSION == 7
     assert _lib.status_string(0) == "W4A16_OK"
     assert _lib.status_string(3) == "W4A16_ERR_WORKSPACE"
     assert _lib.status_string(5) == "W4A16_ERR_TIMEOUT"

@@ -237,7 +237,7 @@ def mxfp4_quantize_pack(w, method: str = "mse", packed=None, scales=None, stream
 
 def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
           counts, offsets, sorted_pairs, workspace, router_w=None, shared_gate_w=None, logits_out=None,
-          gate_out=None, weight_format="int"):
+          gate_out=None, weight_format="int", cooperative=True):
     a = MoeArgs()
     T, H = x.shape
     E, twoI = w13.shape[0], w13.shape[1]
@@ -258,6 +258,7 @@ def _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, sha
     a.router_w, a.shared_gate_w = _ptr(router_w), _ptr(shared_gate_w)
     a.logits_out, a.shared_gate_out = _ptr(logits_out), _ptr(gate_out)
     a.weight_format = _lib.FORMATS[weight_format]
+    a.flags = 0 if cooperative else _lib.W4A16_FLAG_NO_COOPERATIVE
     return a
 
 
@@ -308,7 +309,7 @@ def new_workspace(nbytes: int, device, stream=None):
 def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_logits=None,
                       topk_ids=None, topk_w=None, shared=None, residual=None, out=None, workspace=None,
                       routing_out: bool = False, stream=None, router_w=None, shared_gate_w=None,
-                      weight_format: str = "int", _timed=None):
+                      weight_format: str = "int", cooperative: bool = True, _timed=None):
     """One routed-expert MoE FFN on the GPU.
 
     ``x`` bf16 ``[T, H]``; ``w13`` int32 ``[E, 2I, H*bits/32]`` and ``s13`` bf16
@@ -327,6 +328,10 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
     ``weight_format`` ``fp8`` (bits 8) or ``mxfp4`` (bits 4) takes routed experts packed by
     :func:`fp8_quantize_pack` / :func:`mxfp4_quantize_pack`: ``s13``/``s2`` are then fp32
     ``[E, 2I]`` / ``[E, H]`` row scales, or uint8 E8M0 ``[E, 2I, H/32]`` / ``[E, H, I/32]``.
+
+    ``cooperative=False`` keeps to launches whose workgroups never wait for each other
+    (``W4A16_FLAG_NO_COOPERATIVE``; 1- and 2-token batches then skip the single-launch
+    kernel): for callers that share the GPU with other work.
     """
     torch = _torch()
     bf = _bf16_types()
@@ -401,7 +406,7 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, router_
             workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)   # zero head: see workspace_init
         a = _args(x, w13, s13, w2, s2, top_k, bits, router_logits, topk_ids, topk_w, shared, residual, out,
                   counts, offsets, sorted_pairs, workspace, router_w, shared_gate_w, logits_out, gate_out,
-                  weight_format)
+                  weight_format, cooperative)
         if _timed is None:
             st = _lib.lib().moe_w4a16_forward(C.byref(a), _stream(dev, None))
             _lib.check(st, "moe_w4a16_forward")
@@ -481,7 +486,8 @@ class MoeCall:
     """
 
     def __init__(self, x, w13, s13, w2, s2, *, top_k: int, bits: int = 4, shared=None, workspace=None,
-                 stream=None, router_w=None, shared_gate_w=None, weight_format: str = "int"):
+                 stream=None, router_w=None, shared_gate_w=None, weight_format: str = "int",
+                 cooperative: bool = True):
         torch = _torch()
         bf = _bf16_types()
         _need(x, "x", bf)
@@ -520,7 +526,8 @@ class MoeCall:
         self._keep = (w13, s13, w2, s2, shared, workspace, router_w, shared_gate_w)
         self.workspace = workspace
         self.args = _args(x, w13, s13, w2, s2, top_k, bits, None, None, None, shared, None, None, None, None, None,
-                          workspace, router_w, shared_gate_w, weight_format=weight_format)
+                          workspace, router_w, shared_gate_w, weight_format=weight_format,
+                          cooperative=cooperative)
         self.device = dev
         self.stream = None if stream is None else _stream(dev, stream)   # None: the current stream per call
         self._fn = _lib.lib().moe_w4a16_forward

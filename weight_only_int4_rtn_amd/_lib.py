@@ -12,7 +12,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 WORKSPACE_HEAD_BYTES = 147456   # W4A16_WORKSPACE_HEAD_BYTES
 WORKSPACE_ERROR_OFFSET = 12928  # W4A16_WORKSPACE_ERROR_OFFSET
 NOALLOC_SCRATCH_BYTES = 64 << 20  # W4A16_NOALLOC_SCRATCH_BYTES
@@ -28,6 +28,7 @@ W4A16_F32 = 0
 W4A16_BF16 = 1
 
 FORMATS = {"int": 0, "fp8": 1, "mxfp4": 2}   # w4a16_format
+W4A16_FLAG_NO_COOPERATIVE = 1                  # w4a16_flags
 MXFP4_METHODS = {"rtn": 0, "mse": 1}         # w4a16_mxfp4_method
 
 EXPORTED = (
@@ -69,6 +70,7 @@ class MoeArgs(C.Structure):
         ("router_w", C.c_void_p), ("shared_gate_w", C.c_void_p),
         ("logits_out", C.c_void_p), ("shared_gate_out", C.c_void_p),
         ("weight_format", C.c_int32),
+        ("flags", C.c_int32),
     ]
 
 

@@ -123,8 +123,10 @@ WsLayout layout(const moe_w4a16_args* a) {
     return L;
 }
 
-int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool allow_single_launch = true) {
+int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool allow_coop = true) {
     if (int st = check_shapes(a)) return st;
+    if (a->flags & ~W4A16_FLAG_NO_COOPERATIVE) return fail(W4A16_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+    if (a->flags & W4A16_FLAG_NO_COOPERATIVE) allow_coop = false;
     if (a->T == 0) return W4A16_OK;
     if (!a->x || !a->w13 || !a->s13 || !a->w2 || !a->s2 || !a->y)
         return fail(W4A16_ERR_INVALID_ARG, "NULL x, w13, s13, w2, s2 or y");
@@ -200,7 +202,7 @@ int forward_impl(const moe_w4a16_args* a, void* stream, StageTimer* timer, bool 
     const size_t tag_bytes = (size_t)L.rows_a * L.width_a * 4;
     const size_t tiny_lds = 8 * (size_t)a->T * 16 * 4 + (size_t)L.rows_a * (L.width_a + kTinyPad) * 2 + 1024 +
                             (size_t)L.rows_a * (L.width_a / kGroup) * 4;
-    if (allow_single_launch && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
+    if (allow_coop && a->T * a->top_k <= kTinyP && a->H <= kTinyMaxH && tag_bytes <= kTagBytes &&
         tiny_lds <= kTinyMaxLds &&
         a->H / 16 <= tiny_max_down_workgroups(a->weight_format, a->bits, a->shared_bits)) {
         TinyArgs d{};
@@ -640,7 +642,7 @@ int moe_w4a16_forward_noalloc(const moe_w4a16_args* a, void* stream) {
     moe_w4a16_args b = *a;
     b.workspace = ptr;
     b.workspace_bytes = W4A16_NOALLOC_SCRATCH_BYTES;
-    return forward_impl(&b, stream, nullptr, /*allow_single_launch=*/false);
+    return forward_impl(&b, stream, nullptr, /*allow_coop=*/false);
 }
 
 int w4a16_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {

@@ -36,26 +36,28 @@ __device__ __forceinline__ i32x4_t uniform_rsrc(i32x4_t r) {
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
+// The LDS address and the scalar offset are wave-uniform by contract; readfirstlane says
+// so where the compiler cannot prove it (it folds away where it can).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is set here, on purpose
 __device__ __forceinline__ void dma16(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 // The same copies without a memory clobber, for a pipeline whose LDS reads never touch
 // the stage being filled and whose barriers and waits carry every ordering: the compiler
 // may then schedule LDS reads and arithmetic around them.
 __device__ __forceinline__ void dma16_free(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "m0");
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
 }
 __device__ __forceinline__ void dma4_free(i32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "m0");
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)) : "m0");
 }
 #pragma clang diagnostic pop
 
