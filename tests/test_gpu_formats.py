@@ -312,3 +312,30 @@ def test_stream_formats(stream_fmt_layer, T, shared_bits):
         ref.prefetch(np.unique(ids))
         y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), BITS[fmt], weight_format=fmt, shared=sh_ref)
         check_ffn(y, y_ref, f"{fmt} stream T={T} shared={shared_bits} call {it}")
+
+
+def test_full_layer_prefill_sampled(full_fmt_layer):
+    """The 8192-token step over the full 256-expert layer in each float format.  The first
+    1024 tokens route only among every fourth expert (their other logits are -inf); the
+    other tokens route freely, so all experts are active and every one of those 64 experts'
+    M-tiles mixes compared and uncompared rows.  Every output row of the 1024 tokens is
+    compared, against the oracle quantizing just those 64 experts."""
+    fmt, layer = full_fmt_layer
+    T, E, k, H, I = 8192, 256, 8, 2048, 512
+    say(f"{fmt} prefill 8192 sampled")
+    x = synth.activations_bf16(520, T, H)
+    logits = synth.router_logits(520, T, E)
+    subset = np.arange(0, E, 4)
+    n_cmp = 1024
+    logits[:n_cmp, np.setdiff1d(np.arange(E), subset)] = -np.inf
+    y, tk = w4.moe_w4a16_forward_timed(bf16_to_dev(x), *layer, top_k=k, bits=BITS[fmt], weight_format=fmt,
+                                       router_logits=f32_to_dev(logits))
+    assert "gk_prefill" in [n for n, _ in tk], tk
+    ids, wts, counts, *_ = oracle.route(logits, k)
+    assert np.all(counts > 0) and np.all(np.isin(ids[:n_cmp], subset))
+    assert np.any(counts[subset] % 128 != 0)   # ragged last tiles among the compared experts
+    tokens = np.arange(n_cmp)
+    ref = FmtExperts(fmt, 1, 0, H, I)
+    ref.prefetch(np.unique(ids[tokens]))
+    y_ref = oracle.moe_ffn(x, ids, wts, *ref.as_args(), BITS[fmt], weight_format=fmt, tokens=tokens)
+    check_ffn(y[:n_cmp], y_ref, f"{fmt} prefill 8192, {n_cmp} tokens")
