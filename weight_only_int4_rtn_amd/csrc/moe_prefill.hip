@@ -660,28 +660,45 @@ __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
 // the shared expert's row (times its gate value when there is one), then the residual;
 // rounded once to bf16.  A token's row is
 // split over ceil(H / 2048) blocks of 256 threads x 8 columns.  No atomics anywhere.
+template <int KMAX>   // KMAX >= k: every position, weight and row load is issued before the first use
 __global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
     const int nbx = (int)((a.H / 8 + 255) / 256);
     const int t = (int)(blockIdx.x / nbx);
     const int64_t c = ((int64_t)(blockIdx.x % nbx) * blockDim.x + threadIdx.x) * 8;
     if (c >= a.H) return;
+    const int k = a.k;
+    int pos[KMAX];
+    float w[KMAX];
+    bool kept[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {   // slots past k repeat slot k - 1, not kept
+        const int64_t idx = (int64_t)t * k + min(j, k - 1);
+        const int p = a.inv[idx];
+        kept[j] = j < k && p >= 0;
+        pos[j] = max(p, 0);
+        w[j] = a.wts[idx];
+    }
+    u32x4_t v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(a.ystage + pos[j] * a.H + c);
+    u32x4_t vs = {0u, 0u, 0u, 0u};
+    if (a.shared.bits) vs = *reinterpret_cast<const u32x4_t*>(a.ystage + ((int64_t)a.T * k + t) * a.H + c);
+    const int64_t o = (int64_t)t * a.H + c;
+    u32x4_t r = {0u, 0u, 0u, 0u};
+    if (a.residual) r = *reinterpret_cast<const u32x4_t*>(a.residual + o);
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto add_row = [&](int64_t row, float w) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.ystage + row * a.H + c);
+    auto add_row = [&](const u32x4_t& x, float wt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            s[2 * e] += w * bf16_to_f32(v[e] & 0xffffu);
-            s[2 * e + 1] += w * bf16_to_f32(v[e] >> 16);
+            s[2 * e] += wt * bf16_to_f32(x[e] & 0xffffu);
+            s[2 * e + 1] += wt * bf16_to_f32(x[e] >> 16);
         }
     };
-    for (int j = 0; j < a.k; ++j) {
-        const int pos = a.inv[(int64_t)t * a.k + j];
-        if (pos >= 0) add_row(pos, a.wts[(int64_t)t * a.k + j]);
-    }
-    if (a.shared.bits) add_row((int64_t)a.T * a.k + t, a.shared_gate ? a.shared_gate[t] : 1.0f);
-    const int64_t o = (int64_t)t * a.H + c;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (kept[j]) add_row(v[j], w[j]);   // slot order; a dropped slot adds nothing
+    if (a.shared.bits) add_row(vs, a.shared_gate ? a.shared_gate[t] : 1.0f);
     if (a.residual) {
-        const u32x4_t r = *reinterpret_cast<const u32x4_t*>(a.residual + o);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             s[2 * e] += bf16_to_f32(r[e] & 0xffffu);
@@ -721,7 +738,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) 
     const int64_t dk_items = std::max(a.max_tiles, shared_tiles) * ((a.H + NT - 1) / NT);
     launch(t, "gk_prefill", gk_prefill_kernel<CF, SBITS>, dim3(prefill_grid(gk_items)), dim3(kPThreads), s, lds, a);
     launch(t, "dk_prefill", dk_prefill_kernel<CF, SBITS>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
-    launch(t, "finalize", finalize_kernel, dim3((unsigned)((a.H / 8 + 255) / 256 * a.T)), dim3(256), s, 0u, a);
+    const dim3 fin_grid((unsigned)((a.H / 8 + 255) / 256 * a.T));
+    if (a.k <= 8) launch(t, "finalize", finalize_kernel<8>, fin_grid, dim3(256), s, 0u, a);
+    else launch(t, "finalize", finalize_kernel<16>, fin_grid, dim3(256), s, 0u, a);
     return hipGetLastError();
 }
 
@@ -736,7 +755,9 @@ hipError_t launch_down_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer
     (void)attr;
     const int64_t dk_items = a.max_tiles * ((a.H + NT - 1) / NT);
     launch(t, "dk_prefill", dk_prefill_kernel<CF, 0>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
-    launch(t, "finalize", finalize_kernel, dim3((unsigned)((a.H / 8 + 255) / 256 * a.T)), dim3(256), s, 0u, a);
+    const dim3 fin_grid((unsigned)((a.H / 8 + 255) / 256 * a.T));
+    if (a.k <= 8) launch(t, "finalize", finalize_kernel<8>, fin_grid, dim3(256), s, 0u, a);
+    else launch(t, "finalize", finalize_kernel<16>, fin_grid, dim3(256), s, 0u, a);
     return hipGetLastError();
 }
 
