@@ -6,10 +6,12 @@ Only argument combinations that fail validation are passed with placeholder
 pointers, so no kernel is ever launched here.
 """
 
+import ast
 import ctypes as C
 import os
 import re
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -268,3 +270,17 @@ def test_linear_validation(L):
     assert L.w4a16_linear(C.byref(a), None) == _lib.W4A16_ERR_INVALID_ARG
     assert L.w4a16_linear(C.byref(args(T=0)), None) == _lib.W4A16_OK
     assert L.w4a16_linear_workspace_size(1, 100, 512) == 0
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading the library before anything imports torch still maps a single HIP runtime
+    (torch's): two runtimes in one process leave the library's own without the GPU."""
+    code = ("import weight_only_int4_rtn_amd as w4\n"
+            "w4._lib.lib()\n"
+            "import torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    runtimes = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes

@@ -100,6 +100,10 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m weight_only_int4_rtn_amd.build`")
+    # torch first: its HIP runtime is then the one the library's libamdhip64 dependency
+    # binds to.  Loaded the other way round, the process maps two HIP runtimes, and the
+    # library's own one need not see the GPU that torch uses.
+    import torch  # noqa: F401
     L = C.CDLL(LIB_PATH)
     L.w4a16_abi_version.restype = C.c_int
     L.w4a16_abi_version.argtypes = []
