@@ -325,8 +325,10 @@ int moe_w4a16_forward_noalloc(const moe_w4a16_args* args, void* stream);
  *
  * Page "Nex-N2.5-mini Int4-Int8Mix", Recipe table: the attention q/k/v/o projections and
  * the Gated DeltaNet in_proj_qkv, in_proj_z and out_proj are INT8, symmetric, group 128.
- * Runs on the routed experts' down-projection kernels as one expert that every token uses
- * with weight 1, so every code format of moe_w4a16_forward is accepted.
+ * Every code format of moe_w4a16_forward is accepted.  Up to 64 tokens (when K / 128 splits
+ * into at most 16 equal ranges of 1, 2 or 4 groups) one weight-streaming kernel computes y;
+ * otherwise the routed experts' down-projection kernels run it as one expert that every
+ * token uses with weight 1.
  *   T tokens, K input columns (multiple of 128, <= 8192), N output rows (multiple of 128,
  *   <= 16384); bits / weight_format as in moe_w4a16_args (INT: bits 4 or 8, group 128).
  *   x        bf16 [T, K]
@@ -335,7 +337,7 @@ int moe_w4a16_forward_noalloc(const moe_w4a16_args* args, void* stream);
  *   residual bf16 [T, N] added before the one rounding, or NULL; y may alias it, not x
  *   y        bf16 [T, N]: fp32 accumulation, rounded once
  *   workspace device scratch of w4a16_linear_workspace_size(T, K, N) bytes (no state is
- *            kept in it between calls)
+ *            kept in it between calls; the one-kernel small-batch path leaves it untouched)
  * Errors as moe_w4a16_forward.
  */
 typedef struct w4a16_linear_args {

@@ -80,3 +80,22 @@ def test_linear_residual_in_place_and_reproducible(T):
     w4.w4a16_linear(bf16_to_dev(x), p, s, residual=rd, out=rd)   # y overwrites the residual
     torch.cuda.synchronize()
     assert torch.equal(rd.view(torch.int16), y.view(torch.int16))
+
+
+# Small batches run one weight-streaming kernel when K / 128 splits into at most 16 equal
+# ranges of 1, 2 or 4 groups (at most 2 for 8-bit codes), else the down-projection path:
+# (N, K, bits, format) with K / 128 = 3 (3 waves of one group), 17 (too many ranges: the
+# down path), 64 (16 waves of 4 INT4 groups; INT8: the down path) and 1.
+@pytest.mark.parametrize("N,K,bits,fmt", [(256, 384, 8, "int"), (256, 2176, 8, "int"), (512, 8192, 4, "int"),
+                                          (512, 8192, 8, "int"), (128, 128, 4, "mxfp4"), (384, 1024, 8, "fp8")])
+@pytest.mark.parametrize("T", [1, 17, 64])
+def test_linear_small_batch_group_splits(N, K, bits, fmt, T):
+    say(f"linear small N={N} K={K} bits={bits} {fmt} T={T}")
+    (p, s), (pr, sr) = _weights(N, K, 11, fmt, bits)
+    x = synth.activations_bf16(700 + T, T, K)
+    y = w4.w4a16_linear(bf16_to_dev(x), p, s, bits=bits, weight_format=fmt)
+    torch.cuda.synchronize()
+    check_ffn(y, oracle.linear(x, pr, sr, bits, weight_format=fmt), f"N={N} K={K} {fmt}{bits} T={T}")
+    y2 = w4.w4a16_linear(bf16_to_dev(x), p, s, bits=bits, weight_format=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))   # partials summed in a fixed order

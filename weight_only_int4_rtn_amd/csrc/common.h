@@ -479,6 +479,22 @@ struct LinearPrep {
     int32_t* inv;        // [T]
 };
 hipError_t launch_linear_prep(const LinearPrep& p, hipStream_t s, StageTimer* t = nullptr);
+
+// Small-batch dense projection y[T, N] = x[T, K] . W^T (+ residual), T <= kSmallT, in one
+// launch with no workspace: N / 16 workgroups of K / (128 gw) waves, each wave a range of
+// gw 128-column groups (gw in {1, 2, 4}, at most 2 for 8-bit codes; see linear_small_gw).
+struct LinearSmall {
+    const uint16_t* x;          // bf16 [T, K]
+    const int32_t* w;           // codes [N, K * bits / 32]
+    const uint8_t* s;           // scales (INT bf16 [N, K/128]; FP8 fp32 [N]; MXFP4 E8M0 [N, K/32])
+    const uint16_t* residual;   // bf16 [T, N] or NULL (may alias y)
+    uint16_t* y;                // bf16 [T, N]
+    int T;
+    int64_t K, N;
+};
+// Waves' group count gw for the small-batch dense kernel, 0 when the shape does not fit it.
+int linear_small_gw(int64_t T, int64_t K, int64_t N, int bits);
+hipError_t launch_linear_small(const LinearSmall& p, int cf, int gw, hipStream_t s, StageTimer* t = nullptr);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace w4a16
