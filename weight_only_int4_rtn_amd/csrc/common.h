@@ -452,6 +452,8 @@ struct PrefillArgs {
     const uint16_t* residual;
     const float* shared_gate;   // [T] weight of each token's shared-expert row, or NULL: 1
     uint16_t* y;
+    int direct;                 // dense projection (one expert, rows in token order, weight 1):
+                                // the down epilogue writes y = bf16(row + residual), no staging
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);
 

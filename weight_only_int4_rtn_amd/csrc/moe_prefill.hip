@@ -459,10 +459,19 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
         for (int r = 0; r < 4; ++r) {
             const int m = 64 * wm + 16 * mi + 4 * q + r;
             if (m < it.count && h < a.H) {
+                const int64_t o = (int64_t)(it.orow0 + m) * a.H + h;
+                float f[4] = {acc[mi][0][r], acc[mi][1][r], acc[mi][2][r], acc[mi][3][r]};
+                if (a.direct && a.residual) {   // row orow0 + m is the token's
+                    const uint2 rv = *reinterpret_cast<const uint2*>(a.residual + o);
+                    f[0] += bf16_to_f32(rv.x & 0xffffu);
+                    f[1] += bf16_to_f32(rv.x >> 16);
+                    f[2] += bf16_to_f32(rv.y & 0xffffu);
+                    f[3] += bf16_to_f32(rv.y >> 16);
+                }
                 uint2 v;
-                v.x = cvt_bf16(acc[mi][0][r]) | (cvt_bf16(acc[mi][1][r]) << 16);
-                v.y = cvt_bf16(acc[mi][2][r]) | (cvt_bf16(acc[mi][3][r]) << 16);
-                *reinterpret_cast<uint2*>(a.ystage + (int64_t)(it.orow0 + m) * a.H + h) = v;
+                v.x = cvt_bf16(f[0]) | (cvt_bf16(f[1]) << 16);
+                v.y = cvt_bf16(f[2]) | (cvt_bf16(f[3]) << 16);
+                *reinterpret_cast<uint2*>((a.direct ? a.y : a.ystage) + o) = v;
             }
         }
 }
@@ -755,6 +764,7 @@ hipError_t launch_down_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer
     (void)attr;
     const int64_t dk_items = a.max_tiles * ((a.H + NT - 1) / NT);
     launch(t, "dk_prefill", dk_prefill_kernel<CF, 0>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
+    if (a.direct) return hipGetLastError();   // the epilogue wrote y
     const dim3 fin_grid((unsigned)((a.H / 8 + 255) / 256 * a.T));
     if (a.k <= 8) launch(t, "finalize", finalize_kernel<8>, fin_grid, dim3(256), s, 0u, a);
     else launch(t, "finalize", finalize_kernel<16>, fin_grid, dim3(256), s, 0u, a);
