@@ -515,9 +515,9 @@ int w4a16_linear(const w4a16_linear_args* a, void* stream) {
     auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
     hipStream_t s = static_cast<hipStream_t>(stream);
     // small batches: one weight-streaming launch that reads x itself (the workspace is unused)
-    if (const int gw = linear_small_gw(a->T, a->K, a->N, a->bits)) {
+    if (const int cfg = linear_small_cfg(a->T, a->K, a->N, a->bits)) {
         const LinearSmall ls{a->x, a->w, static_cast<const uint8_t*>(a->s), a->residual, a->y, (int)a->T, a->K, a->N};
-        return hip_status(launch_linear_small(ls, cf_of(a->weight_format, a->bits), gw, s), "linear launch");
+        return hip_status(launch_linear_small(ls, cf_of(a->weight_format, a->bits), cfg, s), "linear launch");
     }
     const bool small = a->T <= kSmallT;
 

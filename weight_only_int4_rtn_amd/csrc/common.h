@@ -483,8 +483,9 @@ struct LinearPrep {
 hipError_t launch_linear_prep(const LinearPrep& p, hipStream_t s, StageTimer* t = nullptr);
 
 // Small-batch dense projection y[T, N] = x[T, K] . W^T (+ residual), T <= kSmallT, in one
-// launch with no workspace: N / 16 workgroups of K / (128 gw) waves, each wave a range of
-// gw 128-column groups (gw in {1, 2, 4}, at most 2 for 8-bit codes; see linear_small_gw).
+// launch with no workspace: N / (16 rb) workgroups of K / (128 gw) waves, each wave a range
+// of gw 128-column groups of rb 16-row blocks (configuration cfg = gw | rb << 4, from
+// linear_small_cfg).
 struct LinearSmall {
     const uint16_t* x;          // bf16 [T, K]
     const int32_t* w;           // codes [N, K * bits / 32]
@@ -494,9 +495,9 @@ struct LinearSmall {
     int T;
     int64_t K, N;
 };
-// Waves' group count gw for the small-batch dense kernel, 0 when the shape does not fit it.
-int linear_small_gw(int64_t T, int64_t K, int64_t N, int bits);
-hipError_t launch_linear_small(const LinearSmall& p, int cf, int gw, hipStream_t s, StageTimer* t = nullptr);
+// Configuration of the small-batch dense kernel, 0 when the shape does not fit it.
+int linear_small_cfg(int64_t T, int64_t K, int64_t N, int bits);
+hipError_t launch_linear_small(const LinearSmall& p, int cf, int cfg, hipStream_t s, StageTimer* t = nullptr);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace w4a16
