@@ -582,7 +582,6 @@ int w4a16_linear(const w4a16_linear_args* a, void* stream) {
     q.inv = p.inv;
     q.residual = a->residual;
     q.y = a->y;
-    q.direct = 1;
     return hip_status(launch_down_prefill(q, s), "linear launch");
 }
 

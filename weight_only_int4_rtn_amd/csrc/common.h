@@ -452,14 +452,12 @@ struct PrefillArgs {
     const uint16_t* residual;
     const float* shared_gate;   // [T] weight of each token's shared-expert row, or NULL: 1
     uint16_t* y;
-    int direct;                 // dense projection (one expert, rows in token order, weight 1):
-                                // the down epilogue writes y = bf16(row + residual), no staging
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);
 
 // The down-projection kernels alone, for a dense projection run as one expert of weight 1
-// over all tokens: the small-batch kernel (dk_decode, + dk_combine) or the grouped GEMM
-// with its slot-order finalize.
+// over all tokens: the small-batch kernel (dk_decode, + dk_combine) or the grouped GEMM,
+// whose epilogue then writes y = bf16(row + residual) itself (rows are tokens).
 hipError_t launch_down_decode(const DecodeArgs& a, hipStream_t s, StageTimer* t = nullptr);
 hipError_t launch_down_prefill(const PrefillArgs& a, hipStream_t s, StageTimer* t = nullptr);
 

@@ -294,8 +294,12 @@ __device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t
 // the four activation fragments once per slice, and each dequantised code fragment feeds
 // the four M-subtiles' MFMAs.  The 16 tiles' group partials start from the offset seeds
 // (MXFP4: from the accumulators themselves, its block scale being inside the conversion).
-// hook(i) runs after slice i's MFMAs (the next step's copies go out there).
-template <int CF, typename Hook>
+// hook(i) runs before slice i's MFMAs with EARLY_FOLD, else after them (the next step's
+// copies go out there).  EARLY_FOLD: each code subtile's group scaling runs inside the last
+// slice, right after the next subtile's MFMAs go out, so that it overlaps them; the copy
+// issue then comes first in each slice, which keeps the compiler from sinking that scaling
+// past the issue branch to the end of the step.
+template <int CF, bool EARLY_FOLD, typename Hook>
 __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4], Hook&& hook) {
     constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
@@ -349,8 +353,21 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
 #pragma unroll
     for (int b0 = 0; b0 < 4; b0 += NB) {
         f32x4_t t[4][NB];
+        // the group partials of code subtile b0 + bb (complete after slice 3) into acc
+        auto fold = [&](int bb) {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                if constexpr (CF == kCfMx4) {
+                    acc[mi][b0 + bb] = t[mi][bb];
+                } else {
+#pragma unroll
+                    for (int r2 = 0; r2 < 4; ++r2) acc[mi][b0 + bb][r2] += sc[b0 + bb] * t[mi][bb][r2];
+                }
+            }
+        };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (EARLY_FOLD && b0 == 0) hook(i);
             if constexpr (BITS == 8) {
 #pragma unroll
                 for (int bb = 0; bb < NB; ++bb) {
@@ -381,20 +398,17 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
                     const f32x4_t c0 = i > 0 ? t[mi][bb] : CF == kCfMx4 ? acc[mi][b] : seed[mi];
                     t[mi][bb] = mfma16(av[mi], lo, c0);
                 }
+                // last slice: the previous subtile's partials are complete (their MFMAs went
+                // out four MFMAs ago), so their scaling FMAs issue while these MFMAs run
+                if (EARLY_FOLD && i == 3 && bb > 0) fold(bb - 1);
             }
-            if (b0 == 0) hook(i);
+            if (EARLY_FOLD && i == 3) fold(NB - 1);
+            if (!EARLY_FOLD && b0 == 0) hook(i);
         }
+        if constexpr (!EARLY_FOLD) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                if constexpr (CF == kCfMx4) {
-                    acc[mi][b0 + bb] = t[mi][bb];
-                } else {
-#pragma unroll
-                    for (int r2 = 0; r2 < 4; ++r2) acc[mi][b0 + bb][r2] += sc[b0 + bb] * t[mi][bb][r2];
-                }
-            }
+            for (int bb = 0; bb < NB; ++bb) fold(bb);
+        }
     }
 }
 
@@ -448,6 +462,7 @@ __device__ void gk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
 
 // The unweighted output rows of a down item, rounded to bf16, at their sorted positions:
 // a lane's four columns of a row are adjacent (see dk_code_row) and go out as 8 bytes.
+template <bool DIRECT>
 __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t (&acc)[4][4]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, ml = lane & 15;
@@ -461,7 +476,7 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
             if (m < it.count && h < a.H) {
                 const int64_t o = (int64_t)(it.orow0 + m) * a.H + h;
                 float f[4] = {acc[mi][0][r], acc[mi][1][r], acc[mi][2][r], acc[mi][3][r]};
-                if (a.direct && a.residual) {   // row orow0 + m is the token's
+                if (DIRECT && a.residual) {   // row orow0 + m is the token's
                     const uint2 rv = *reinterpret_cast<const uint2*>(a.residual + o);
                     f[0] += bf16_to_f32(rv.x & 0xffffu);
                     f[1] += bf16_to_f32(rv.x >> 16);
@@ -471,7 +486,7 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
                 uint2 v;
                 v.x = cvt_bf16(f[0]) | (cvt_bf16(f[1]) << 16);
                 v.y = cvt_bf16(f[2]) | (cvt_bf16(f[3]) << 16);
-                *reinterpret_cast<uint2*>((a.direct ? a.y : a.ystage) + o) = v;
+                *reinterpret_cast<uint2*>((DIRECT ? a.y : a.ystage) + o) = v;
             }
         }
 }
@@ -482,7 +497,9 @@ __device__ void dk_epilogue(const PrefillArgs& a, const Item& it, const f32x4_t 
 // remapped so that each XCD, w mod 8, takes one contiguous range: an expert's tiles share
 // that XCD's L2).  The items are resolved once into LDS; the steps of all of them form
 // one pipelined stream.
-template <int CF, bool GATE_UP, bool SHARED>
+// EARLY_FOLD: the group scaling of each step inside its last K slice (see compute_step);
+// DIRECT: the down epilogue writes y (dense projections).
+template <int CF, bool GATE_UP, bool SHARED, bool EARLY_FOLD = true, bool DIRECT = false>
 __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int total, uint8_t* smem,
                           Item* s_items, float* s_asum, int* s_cnt, int* s_tok) {
     using P = Pipe<cf_bits(CF)>;
@@ -585,7 +602,7 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
     auto finish_item = [&]() {   // the item before ci (its record stays in LDS)
         const Item eit = s_items[ci - 1];
         if constexpr (GATE_UP) gk_epilogue(a, eit, acc, s_asum);
-        else dk_epilogue(a, eit, acc);
+        else dk_epilogue<DIRECT>(a, eit, acc);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -599,13 +616,14 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         else wait_vmcnt<0>();
         bar();   // every wave's step-s data is in LDS, and stage (s - 1) is no longer read
         if (epi) finish_item();
-        // step s + kStages - 1's copies go out after one of this step's four K slices: waves
-        // 2j and 2j + 1 (on two different SIMDs) after slice j, so that at any time only two
-        // waves wait for the load path while the others keep the matrix units busy
+        // step s + kStages - 1's copies go out at one of this step's four K slices: waves
+        // 2j and 2j + 1 (on two different SIMDs) at slice j (before its MFMAs with the early
+        // fold, else after them), so that at any time only two waves wait for the load path
+        // while the others keep the matrix units busy
         const bool more = issued < total_steps;
         const int slot = __builtin_amdgcn_readfirstlane(wave >> 1);
         if (64 * (slot >> 1) < ccount) {
-            compute_step<CF>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
+            compute_step<CF, EARLY_FOLD>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
                              [&](int i) {
                                  if (more && i == slot) issue_next(-1);
                              });
@@ -651,7 +669,10 @@ __global__ __launch_bounds__(kPThreads) void gk_prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int CF, int SBITS>
+// DIRECT: a dense projection (one expert of weight 1, rows in token order): the epilogue
+// writes y itself.  With a shared stream the step keeps its scaling after the last K slice
+// (the early fold would spill there).
+template <int CF, int SBITS, bool DIRECT = false>
 __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr uint32_t kPipe = std::max(pipe_lds_bytes<CF>(), SBITS ? pipe_lds_bytes<SBITS>() : 0u);
@@ -659,10 +680,11 @@ __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
     float* s_asum = reinterpret_cast<float*>(s_items + kMaxItems);
     __shared__ int s_cnt[kPWaves];
     const int nb = (int)((a.H + NT - 1) / NT);
-    run_items<CF, false, false>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt, nullptr);
+    run_items<CF, false, false, SBITS == 0, DIRECT>(a, a.routed, nb, a.meta[1] * nb, smem, s_items, s_asum, s_cnt,
+                                                    nullptr);
     if constexpr (SBITS != 0)
-        run_items<SBITS, false, true>(a, a.shared, nb, ((a.T + MT - 1) / MT) * nb, smem, s_items, s_asum, s_cnt,
-                                      nullptr);
+        run_items<SBITS, false, true, false>(a, a.shared, nb, ((a.T + MT - 1) / MT) * nb, smem, s_items, s_asum,
+                                             s_cnt, nullptr);
 }
 
 // y[t] = sum over slots j in order of w[t, j] times the staged row of pair (t, j), then
@@ -757,18 +779,15 @@ template <int CF>
 hipError_t launch_down_prefill_t(const PrefillArgs& a, hipStream_t s, StageTimer* t) {
     constexpr uint32_t lds = pipe_lds_bytes<CF>() + kMaxItems * sizeof(Item) + 4 * MT * 4 + 2 * MT * 4;
     static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dk_prefill_kernel<CF, 0>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dk_prefill_kernel<CF, 0, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         return true;
     }();
     (void)attr;
     const int64_t dk_items = a.max_tiles * ((a.H + NT - 1) / NT);
-    launch(t, "dk_prefill", dk_prefill_kernel<CF, 0>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds, a);
-    if (a.direct) return hipGetLastError();   // the epilogue wrote y
-    const dim3 fin_grid((unsigned)((a.H / 8 + 255) / 256 * a.T));
-    if (a.k <= 8) launch(t, "finalize", finalize_kernel<8>, fin_grid, dim3(256), s, 0u, a);
-    else launch(t, "finalize", finalize_kernel<16>, fin_grid, dim3(256), s, 0u, a);
-    return hipGetLastError();
+    launch(t, "dk_prefill", dk_prefill_kernel<CF, 0, true>, dim3(prefill_grid(dk_items)), dim3(kPThreads), s, lds,
+           a);
+    return hipGetLastError();   // the epilogue wrote y
 }
 
 template <int CF>
