@@ -129,8 +129,8 @@ __global__ __launch_bounds__(1024) void linear_small_kernel(LinearSmall p) {
 constexpr int kLinearMaxLds = 128 * 1024;   // partial sums of 16 waves x 64 tokens x 32 rows
 
 template <int CF, int GW, int RB>
-void launch_linear_small_k(const LinearSmall& p, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
-                           StageTimer* t) {
+hipError_t launch_linear_small_k(const LinearSmall& p, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                                 StageTimer* t) {
     static const bool attr = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(linear_small_kernel<CF, GW, RB>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLinearMaxLds);
@@ -138,6 +138,7 @@ void launch_linear_small_k(const LinearSmall& p, dim3 grid, dim3 block, uint32_t
     }();
     (void)attr;
     launch(t, "linear_small", linear_small_kernel<CF, GW, RB>, grid, block, s, lds, p);
+    return hipGetLastError();
 }
 
 template <int CF>
@@ -147,13 +148,13 @@ hipError_t launch_linear_small_cf(const LinearSmall& p, int cfg, hipStream_t s, 
     const dim3 grid((unsigned)(p.N / (16 * rb))), block((unsigned)(64 * waves));
     const uint32_t lds = (uint32_t)(waves * p.T * 16 * rb * 4);
     if constexpr (cf_bits(CF) == 4) {
-        if (cfg == (4 | 1 << 4)) launch_linear_small_k<CF, 4, 1>(p, grid, block, lds, s, t);
-        if (cfg == (2 | 2 << 4)) launch_linear_small_k<CF, 2, 2>(p, grid, block, lds, s, t);
+        if (cfg == (4 | 1 << 4)) return launch_linear_small_k<CF, 4, 1>(p, grid, block, lds, s, t);
+        if (cfg == (2 | 2 << 4)) return launch_linear_small_k<CF, 2, 2>(p, grid, block, lds, s, t);
     }
-    if (cfg == (2 | 1 << 4)) launch_linear_small_k<CF, 2, 1>(p, grid, block, lds, s, t);
-    if (cfg == (1 | 2 << 4)) launch_linear_small_k<CF, 1, 2>(p, grid, block, lds, s, t);
-    if (cfg == (1 | 1 << 4)) launch_linear_small_k<CF, 1, 1>(p, grid, block, lds, s, t);
-    return hipGetLastError();
+    if (cfg == (2 | 1 << 4)) return launch_linear_small_k<CF, 2, 1>(p, grid, block, lds, s, t);
+    if (cfg == (1 | 2 << 4)) return launch_linear_small_k<CF, 1, 2>(p, grid, block, lds, s, t);
+    if (cfg == (1 | 1 << 4)) return launch_linear_small_k<CF, 1, 1>(p, grid, block, lds, s, t);
+    return hipErrorInvalidValue;   // a configuration linear_small_cfg does not produce
 }
 
 }  // namespace
