@@ -520,12 +520,15 @@ int w4a16_linear(const w4a16_linear_args* a, void* stream) {
         return hip_status(launch_linear_small(ls, cf_of(a->weight_format, a->bits), cfg, s), "linear launch");
     }
     const bool small = a->T <= kSmallT;
+    // 8-bit codes dequantise in natural column order in the grouped GEMM, which then reads x
+    // itself; the other widths read x reordered into the codes' K order by the set-up kernel
+    const bool natural = !small && a->bits == 8;
 
     LinearPrep p{};
     p.x = a->x;
     p.T = (int)a->T;
     p.K = a->K;
-    p.abuf = static_cast<uint16_t*>(at(L.abuf));
+    p.abuf = natural ? nullptr : static_cast<uint16_t*>(at(L.abuf));
     p.asum = small ? nullptr : static_cast<float*>(at(L.asum));
     p.rec = static_cast<int4*>(at(L.rec));
     p.meta = static_cast<int32_t*>(at(L.meta));
@@ -573,7 +576,7 @@ int w4a16_linear(const w4a16_linear_args* a, void* stream) {
     q.tiles = p.tiles;
     q.tokw = p.tokw;
     q.max_tiles = (a->T + kPrefillMT - 1) / kPrefillMT;
-    q.abuf = p.abuf;
+    q.abuf = natural ? const_cast<uint16_t*>(a->x) : p.abuf;   // only read
     q.rows_a = a->T;
     q.width_a = a->K;
     q.asum = p.asum;

@@ -468,7 +468,7 @@ struct LinearPrep {
     const uint16_t* x;   // bf16 [T, K]
     int T;
     int64_t K;
-    uint16_t* abuf;      // [T, K]
+    uint16_t* abuf;      // [T, K], or NULL: not written (8-bit codes, whose GEMM reads x itself)
     float* asum;         // [T, K / 128] or NULL
     int4* rec;           // [1]
     int32_t* meta;       // [2]: active experts, M-tiles

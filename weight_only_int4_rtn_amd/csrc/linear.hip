@@ -2,9 +2,10 @@
 // "Nex-N2.5-mini Int4-Int8Mix", Recipe table: the attention and Gated DeltaNet projections
 // at INT8 group 128).  A dense projection is one expert that every token uses with
 // weight 1: its input rows are x itself, so this kernel writes x in the K order of the
-// codes' MFMA operands (each 8-column block reordered, as the gate/up epilogue writes a),
-// each row's fp32 sums over 128-column groups (the INT codes' offset seeds, large batches),
-// and the routing records of that one expert.
+// codes' MFMA operands (each 8-column block reordered, as the gate/up epilogue writes a;
+// not for 8-bit codes, whose GEMM reads x unpermuted: abuf NULL), each row's fp32 sums
+// over 128-column groups (the INT codes' offset seeds, large batches), and the routing
+// records of that one expert.
 #include "common.h"
 #include "decode_dev.h"
 
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(LinearPrep p) {
     float sum = 0.f;
     if (ok) {
         const u32x4_t X = *reinterpret_cast<const u32x4_t*>(p.x + t * p.K + 8 * c8);
-        *reinterpret_cast<u32x4_t*>(p.abuf + t * p.K + 8 * c8) = perm_act(X);
+        if (p.abuf) *reinterpret_cast<u32x4_t*>(p.abuf + t * p.K + 8 * c8) = perm_act(X);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum += bf16_to_f32(X[e] & 0xffffu) + bf16_to_f32(X[e] >> 16);
     }

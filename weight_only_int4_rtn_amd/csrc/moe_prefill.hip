@@ -299,7 +299,32 @@ __device__ __forceinline__ void issue_step(const IssueState& st, int g, uint32_t
 // slice, right after the next subtile's MFMAs go out, so that it overlaps them; the copy
 // issue then comes first in each slice, which keeps the compiler from sinking that scaling
 // past the issue branch to the end of the step.
-template <int CF, bool EARLY_FOLD, typename Hook>
+// 8-bit codes w0 = k0..k3, w1 = k4..k7 (one byte each) as bf16 pairs in natural column
+// order, (k0,k1) (k2,k3) (k4,k5) (k6,k7), for activation tiles read unpermuted: INT8 codes
+// as exact bf16 integers (OFF = 128, as dq8_cvt), FP8 E4M3 bytes through the hardware
+// conversion (exact, as dq_fp8, without its byte permutes).
+template <int CF>
+__device__ __forceinline__ u32x4_t dq8_natural(uint32_t w0, uint32_t w1) {
+    u32x4_t r;
+    if constexpr (CF == kCfFp8) {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = j < 2 ? w0 : w1;
+            const int b = 16 * (j & 1);
+            r[j] = cvt_bf16x2((float)((w >> b) & 0xffu), (float)((w >> (b + 8)) & 0xffu));
+        }
+    }
+    return r;
+}
+
+// NATURAL: the activation tile holds unpermuted rows (a dense projection reading x itself);
+// only 8-bit codes take it.
+template <int CF, bool EARLY_FOLD, bool NATURAL, typename Hook>
 __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd, f32x4_t (&acc)[4][4], Hook&& hook) {
     constexpr int BITS = cf_bits(CF);
     using P = Pipe<BITS>;
@@ -387,9 +412,9 @@ __device__ __forceinline__ void compute_step(const uint8_t* stage, uint32_t sodd
                 if constexpr (CF == 4) {
                     lo = dq4(bw[b][i], M);
                 } else if constexpr (CF == 8) {
-                    lo = dq8_cvt(bw[b][0], bw[b][1]);
+                    lo = NATURAL ? dq8_natural<CF>(bw[b][0], bw[b][1]) : dq8_cvt(bw[b][0], bw[b][1]);
                 } else if constexpr (CF == kCfFp8) {
-                    lo = dq_fp8(bw[b][0], bw[b][1]);
+                    lo = NATURAL ? dq8_natural<CF>(bw[b][0], bw[b][1]) : dq_fp8(bw[b][0], bw[b][1]);
                 } else {
                     lo = dq_mx4(bw[b][i], xs[b]);
                 }
@@ -623,7 +648,7 @@ __device__ void run_items(const PrefillArgs& a, const ExpertSet& es, int nb, int
         const bool more = issued < total_steps;
         const int slot = __builtin_amdgcn_readfirstlane(wave >> 1);
         if (64 * (slot >> 1) < ccount) {
-            compute_step<CF, EARLY_FOLD>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
+            compute_step<CF, EARLY_FOLD, DIRECT && cf_bits(CF) == 8>(smem + (s % P::kStages) * P::kStageBytes, (gc & 1) ? (cpar ^ 0xfu) : cpar, acc,
                              [&](int i) {
                                  if (more && i == slot) issue_next(-1);
                              });
@@ -670,7 +695,7 @@ __global__ __launch_bounds__(kPThreads) void gk_prefill_kernel(PrefillArgs a) {
 }
 
 // DIRECT: a dense projection (one expert of weight 1, rows in token order): the epilogue
-// writes y itself.  With a shared stream the step keeps its scaling after the last K slice
+// writes y itself, and with 8-bit codes the activation rows are x itself, unpermuted.  With a shared stream the step keeps its scaling after the last K slice
 // (the early fold would spill there).
 template <int CF, int SBITS, bool DIRECT = false>
 __global__ __launch_bounds__(kPThreads) void dk_prefill_kernel(PrefillArgs a) {
