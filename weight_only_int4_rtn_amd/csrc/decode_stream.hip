@@ -472,6 +472,15 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     int ep_row0 = 0, ep_count = 0, ep_n0 = 0, ep_pending = 0;
     float* s_red = reinterpret_cast<float*>(smem + kSOffRed);
 
+    // FP8 / MXFP4 routed codes: the previous row block's epilogue runs after the item's
+    // MFMAs rather than before them.  Their items' MFMA blocks carry a wait for all of the
+    // wave's memory accesses (vmcnt, which counts the epilogue's stores too), so stores
+    // issued right after the barrier held up that item; issued after the MFMAs they are
+    // done by the next item.  (Same-box A/B at 32 tokens: FP8 gate/up 76 -> 72.6 us, MXFP4
+    // 53.5 -> 50.5 us; INT codes, without that wait, keep the early epilogue.)  A row block
+    // spans at least two items (stream_fits), so the epilogue never meets the rewrite of
+    // the partial sums it reads.
+    constexpr bool kLateEpilogue = !cf_int(CF);
     // waves 4..7: element r = wave - 4 of every lane (D row 4q + r, column ml)
     auto epilogue = [&]() {
         if (wave >= 4) {
@@ -491,7 +500,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     for (int rel = 0; rel < nI; ++rel) {
         wait_lgkm0();   // this wave's partial sums are in LDS before the barrier
         bar();          // item rel is in LDS (the producers waited); the partial sums are complete
-        if (ep_pending) {
+        if (!kLateEpilogue && ep_pending) {
             epilogue();
             ep_pending = 0;
         }
@@ -509,6 +518,10 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(3))) 
         } else if constexpr (kSep) {
             if (kh == 0) s_compute<SBITS>(L, kh, half, stage, A[0], seed[0], accg, accu);
             else s_compute<SBITS>(L, kh, half, stage, A[1], seed[1], accg, accu);
+        }
+        if (kLateEpilogue && ep_pending) {
+            epilogue();
+            ep_pending = 0;
         }
         if (cc.sub == cc.n_sub - 1) {   // the row block's last K chunk
 #pragma unroll
