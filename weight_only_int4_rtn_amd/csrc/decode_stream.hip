@@ -244,6 +244,22 @@ __device__ __forceinline__ int s_issue(const DecodeArgs& a, const SLayout& L, co
 // (padding rows zero), and their MFMA offset seeds.  Each branch computes the seeds
 // itself: the register path's loads are then complete before the branches join, so the
 // compiler puts no wait for them (a wait for every copy in flight) on the LDS path.
+// The seed of an item's MFMA chains: the INT offset seed; for the float formats (no
+// offset) zero, computed by the same four MFMAs on a zero operand so that, as with the INT
+// codes, the fragments' loads are read inside the branch that issued them (the compiler
+// then puts no wait for every memory access in flight into each item's MFMAs).
+template <int CF>
+__device__ __forceinline__ f32x4_t s_seed(const u32x4_t (&A)[4]) {
+    if constexpr (cf_int(CF)) {
+        return offset_seed<CF>(A);
+    } else {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = mfma16(A[i], u32x4_t{0u, 0u, 0u, 0u}, c);
+        return c;
+    }
+}
+
 template <int CF>
 __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, const STile& tl, const uint8_t* smem,
                                          const uint8_t* abuf, u32x4_t (&A)[kSKH][4], f32x4_t (&seed)[kSKH]) {
@@ -263,7 +279,7 @@ __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, 
             }
         }
 #pragma unroll
-        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<CF>(A[kh]);
+        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = s_seed<CF>(A[kh]);
     } else {   // more rows than an A buffer holds: straight from memory into registers
         const uint16_t* xr = a.x + (int64_t)stile_token(tl, real ? ml : 0) * a.H + 32 * q;
 #pragma unroll
@@ -273,7 +289,7 @@ __device__ __forceinline__ void s_load_a(const DecodeArgs& a, const SLayout& L, 
             for (int i = 0; i < 4; ++i) A[kh][i] = load_act<CF>(xr, real && 8 * kh + wave < L.G, g * kGroup + 8 * i);
         }
 #pragma unroll
-        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = offset_seed<CF>(A[kh]);
+        for (int kh = 0; kh < kSKH; ++kh) seed[kh] = s_seed<CF>(A[kh]);
     }
 }
 
